@@ -1,0 +1,201 @@
+"""Pins of the oracle's linear map, routing, permutation and expert FFN."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+
+from oracle import nvfp4_oracle as O
+
+
+def _frac(v):
+    return Fraction(float(v))
+
+
+def _rand_nvfp4(rng, n, k):
+    codes = rng.integers(0, 256, size=(n, k // 2), dtype=np.uint8)
+    scales = rng.integers(0x20, 0x48, size=(n, k // 16), dtype=np.uint8)
+    return codes, scales
+
+
+def test_linear_exact_rationals():
+    rng = np.random.default_rng(0)
+    m, n, k = 3, 5, 32
+    codes, scales = _rand_nvfp4(rng, n, k)
+    g = np.float32(0.0078125 * 3)                     # dyadic * 3
+    x = (rng.integers(-64, 64, size=(m, k)) / 16.0).astype(np.float32)
+    y, _ = O.linear(x, codes, scales, g)
+    el = O.unpack_nibbles(codes)
+    table = {c: _frac(v) for c, v in enumerate(O.decode_e2m1(np.arange(16)))}
+    for i in range(m):
+        for j in range(n):
+            acc = Fraction(0)
+            for kk in range(k):
+                s = _frac(O.decode_e4m3(scales[j, kk // 16]))
+                acc += _frac(x[i, kk]) * table[int(el[j, kk])] * s
+            exact = acc * _frac(g)
+            assert abs(_frac(y[i, j]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
+def test_linear_all_ones_gives_row_sums():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    codes = np.full((3, 32), 0x22, np.uint8)          # every element code 2 = 1.0
+    scales = np.full((3, 4), 0x38, np.uint8)          # every scale 1.0
+    y, _ = O.linear(x, codes, scales, np.float32(1.0))
+    assert np.allclose(y, x.astype(np.float64).sum(1)[:, None], rtol=1e-14, atol=1e-14)
+
+
+def test_linear_one_hot_picks_columns():
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((4, 32)).astype(np.float32)
+    el = np.zeros((32, 32), np.uint8)
+    for j in range(32):
+        el[j, (5 * j) % 32] = 2                       # 1.0 at column (5j mod 32)
+    codes = O.pack_nibbles(el)
+    scales = np.full((32, 2), 0x38, np.uint8)
+    y, _ = O.linear(x, codes, scales, np.float32(0.5))
+    assert np.array_equal(y, 0.5 * x.astype(np.float64)[:, (5 * np.arange(32)) % 32])
+
+
+def test_linear_w4a4_is_linear_on_dequantised_activations():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    codes, scales = _rand_nvfp4(rng, 8, 64)
+    y, gx = O.linear(x, codes, scales, np.float32(0.01), act_quant=True)
+    xc, xs, gx2 = O.quantize(x)
+    assert gx == gx2
+    y2, _ = O.linear(O.dequantize(xc, xs, gx), codes, scales, np.float32(0.01))
+    assert np.allclose(y, y2, rtol=1e-12, atol=0)
+
+
+def _check_topk_characterisation(logits, ids):
+    t, e = logits.shape
+    for i in range(t):
+        chosen = list(ids[i])
+        assert len(set(chosen)) == len(chosen)
+        key = lambda j: (-float(logits[i, j]), j)
+        # listed in order, and every chosen expert beats every other one
+        assert [key(j) for j in chosen] == sorted(key(j) for j in chosen)
+        rest = [j for j in range(e) if j not in chosen]
+        if rest:
+            assert max(key(j) for j in chosen) < min(key(j) for j in rest)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_topk_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    t, e, k = 8, 16, 4
+    logits = rng.integers(-3, 3, size=(t, e)).astype(np.float32)  # many ties
+    ids, w = O.route_topk(logits, k)
+    _check_topk_characterisation(logits, ids)
+    # brute force over all k-subsets: the chosen set maximises the logit sum,
+    # and among maximisers is the lexicographically smallest sorted index set
+    from itertools import combinations
+    for i in range(t):
+        best = max(combinations(range(e), k),
+                   key=lambda c: (sum(float(logits[i, j]) for j in c), [-j for j in c]))
+        assert sorted(ids[i]) == sorted(best)
+    assert np.allclose(w.sum(1), 1.0, atol=1e-15)
+
+
+def test_topk_weights_are_renormalised_softmax():
+    rng = np.random.default_rng(9)
+    logits = rng.standard_normal((5, 12)).astype(np.float32)
+    ids, w = O.route_topk(logits, 3)
+    p = scipy.special.softmax(logits.astype(np.float64), axis=1)
+    sel = np.take_along_axis(p, ids.astype(np.int64), axis=1)
+    assert np.allclose(w, sel / sel.sum(1, keepdims=True), rtol=1e-13)
+    ids2, w2 = O.route_topk(logits, 3, renormalize=False)
+    assert np.array_equal(ids, ids2) and np.allclose(w2, sel, rtol=1e-13)
+    # k = E with renormalisation is the softmax itself
+    ids3, w3 = O.route_topk(logits, 12)
+    full = np.take_along_axis(p, ids3.astype(np.int64), axis=1)
+    assert np.allclose(w3, full, rtol=1e-13)
+
+
+def test_permute_invariants():
+    rng = np.random.default_rng(4)
+    t, e, k = 37, 10, 3
+    ids, _ = O.route_topk(rng.standard_normal((t, e)).astype(np.float32), k)
+    offsets, pairs = O.permute(ids, e)
+    assert offsets[0] == 0 and offsets[-1] == t * k
+    assert np.all(np.diff(offsets) >= 0)
+    assert np.array_equal(np.sort(pairs), np.arange(t * k))
+    flat = ids.reshape(-1)
+    for ex in range(e):
+        seg = pairs[offsets[ex]:offsets[ex + 1]]
+        assert np.all(flat[seg] == ex)
+        assert np.all(np.diff(seg // k) > 0)          # ascending tokens
+        assert len(seg) == np.count_nonzero(flat == ex)
+
+
+def _rand_experts(rng, e, h, i):
+    def q(n, kk):
+        return O.quantize((rng.standard_normal((n, kk)) * 0.05).astype(np.float32))
+    mats = [[q(i, h) for _ in range(e)], [q(i, h) for _ in range(e)],
+            [q(h, i) for _ in range(e)]]
+    stack = lambda lst, j: np.stack([m[j] for m in lst])
+    return O.ExpertWeights(stack(mats[0], 0), stack(mats[0], 1), stack(mats[0], 2),
+                           stack(mats[1], 0), stack(mats[1], 1), stack(mats[1], 2),
+                           stack(mats[2], 0), stack(mats[2], 1), stack(mats[2], 2))
+
+
+def test_moe_single_expert_is_dense_mlp_from_linear():
+    rng = np.random.default_rng(5)
+    t, h, i = 6, 64, 32
+    w = _rand_experts(rng, 1, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    y, _ = O.moe_ffn(x, np.zeros((t, 1), np.int32), np.ones((t, 1)), w)
+    gate, _ = O.linear(x, w.gate_codes[0], w.gate_scales[0], w.gate_global[0])
+    up, _ = O.linear(x, w.up_codes[0], w.up_scales[0], w.up_global[0])
+    hh = O.bf16_rne(gate / (1 + np.exp(-gate)) * up)
+    y2, _ = O.linear(hh, w.down_codes[0], w.down_scales[0], w.down_global[0])
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-15)
+
+
+def test_moe_equal_logits_all_experts_is_mean():
+    rng = np.random.default_rng(6)
+    t, h, i, e = 4, 32, 32, 4
+    w = _rand_experts(rng, e, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    ids, wts = O.route_topk(np.zeros((t, e), np.float32), e)
+    assert np.array_equal(ids, np.tile(np.arange(e), (t, 1)))
+    assert np.allclose(wts, 1.0 / e)
+    y, _ = O.moe_ffn(x, ids, wts, w)
+    per = []
+    for ex in range(e):
+        ye, _ = O.moe_ffn(x, np.full((t, 1), ex, np.int32), np.ones((t, 1)), w)
+        per.append(ye)
+    assert np.allclose(y, np.mean(per, axis=0), rtol=1e-12, atol=1e-15)
+
+
+def test_moe_token_subset_matches_full():
+    rng = np.random.default_rng(7)
+    t, h, i, e, k = 12, 32, 32, 6, 2
+    w = _rand_experts(rng, e, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    ids, wts = O.route_topk(rng.standard_normal((t, e)).astype(np.float32), k)
+    y, _ = O.moe_ffn(x, ids, wts, w)
+    ys, _ = O.moe_ffn(x, ids, wts, w, tokens=[3, 0, 11])
+    assert np.array_equal(ys, y[[3, 0, 11]])
+
+
+def test_moe_w4a4_single_expert_composes_quantised_linears():
+    rng = np.random.default_rng(8)
+    t, h, i = 5, 64, 32
+    w = _rand_experts(rng, 1, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    y, info = O.moe_ffn(x, np.zeros((t, 1), np.int32), np.ones((t, 1)), w,
+                        act_quant=True)
+    gate, gx = O.linear(x, w.gate_codes[0], w.gate_scales[0], w.gate_global[0], act_quant=True)
+    up, _ = O.linear(x, w.up_codes[0], w.up_scales[0], w.up_global[0], act_quant=True)
+    hh = O.bf16_rne(gate / (1 + np.exp(-gate)) * up)
+    y2, gh = O.linear(hh.astype(np.float32), w.down_codes[0], w.down_scales[0],
+                      w.down_global[0], act_quant=True)
+    assert info["g_x"] == gx and info["g_h"] == gh
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-15)
+    # given globals reproduce the computed ones
+    y3, _ = O.moe_ffn(x, np.zeros((t, 1), np.int32), np.ones((t, 1)), w,
+                      act_quant=True, act_globals=(gx, gh), tokens=[1, 4])
+    assert np.array_equal(y3, y[[1, 4]])
