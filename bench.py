@@ -1,0 +1,318 @@
+"""Benchmark of the NVFP4 routed-expert FFN hot path on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input:
+top-k routing + permutation (moe_route_topk), then the grouped FFN
+(moe_grouped_nvfp4_ffn: plan, activation prep, gate/up GEMM with SiLU*up,
+h prep, down GEMM times routing weight, combine).  Inputs are resident in HBM
+before timing starts.  Steps are captured in a HIP graph and cycle over
+several copies of the expert weights, so every step streams its active
+experts from HBM instead of the 256 MB Infinity Cache (MALL).
+
+Prints one JSON line (see README of the metric in the design doc).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NVFP4 MoE FFN: decode HBM GB/s (% peak); prefill TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+
+
+def nv_bytes(n):
+    """NVFP4 bytes of n elements: n/2 code bytes + n/16 scale bytes."""
+    return n // 2 + n // 16
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="moe_decode",
+                    help="moe_decode | moe_prefill | moe_prefill_w4a4 | mlp_decode_m{1,8,32}")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="weight copies cycled per step (0 = enough for >= 2 GiB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the oracle sample (0 = workload default)")
+    ap.add_argument("--eager", action="store_true", help="no graph capture")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw HIP events (for the library's per-stage event hook)."""
+
+    def __init__(self, n):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(h))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed: {rc}")
+            self.arr[i] = h
+        self.n = n
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), self.arr[a], self.arr[b])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return out.value
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the routed-expert "
+                                   "FFN is measured on one GPU's share (see DESIGN.md for how "
+                                   "it would shard)", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from nvfp4_routed_expert_amd import native, synth, weights
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    act = native.W4A4 if wl.act == "w4a4" else native.W4A16
+    P = T * k
+
+    # ---- inputs (seeded synthetic, resident in HBM) -----------------------------
+    x_cpu = synth.activations(T, H)
+    logits_np = synth.router_logits(T, E, zipf_s=wl.zipf_s)
+    x = x_cpu.to(dev)
+    logits = torch.from_numpy(logits_np).to(dev)
+    t0 = time.time()
+    w0 = weights.synthetic_experts(E, H, I, 0, dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    bytes_all = 3 * E * (nv_bytes(H * I) + 4)
+    copies = args.copies or max(1, int(np.ceil(2 * 2 ** 30 / bytes_all)))
+    copies = min(copies, 16)
+    wcopies = [w0]
+    for _ in range(copies - 1):
+        wcopies.append(native.ExpertWeights(*[t.clone() for t in (
+            w0.gate_codes, w0.gate_scales, w0.gate_global, w0.up_codes, w0.up_scales,
+            w0.up_global, w0.down_codes, w0.down_scales, w0.down_global)]))
+
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    pairs = torch.empty(P, dtype=torch.int32, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(native.ffn_workspace_bytes(T, H, I, E, k, act), dtype=torch.uint8,
+                     device=dev)
+    ag = torch.empty(2, dtype=torch.float32, device=dev) if act == native.W4A4 else None
+    route = E > 1
+
+    def step(c):
+        if route:
+            native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs))
+        native.moe_grouped_nvfp4_ffn(x, wcopies[c], wts, off, pairs, k, act=act,
+                                     act_globals=None, out_dtype=torch.bfloat16,
+                                     workspace=ws, out=y)
+
+    if not route:   # one expert: the routing is fixed (all rows to expert 0)
+        native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs))
+    step(0)
+    torch.cuda.synchronize()
+
+    # ---- work accounting from the actual routing ---------------------------------
+    counts = np.diff(off.cpu().numpy())
+    active = int((counts > 0).sum())
+    w_bytes_active = 3 * active * (nv_bytes(H * I) + 4)
+    io_bytes = T * H * 2 * 2 + (T * E * 4 if route else 0)
+    alg_bytes = w_bytes_active + io_bytes
+    alg_flops = 6 * P * H * I
+    gateup_bytes = 2 * active * (nv_bytes(H * I) + 4) + T * H * 2
+    gateup_flops = 4 * P * H * I
+    prefill_mfma = wl.name == "moe_prefill_w4a4"
+
+    # ---- timed region: K steps (graph replays), HIP events on the stream -----------
+    use_graph = not args.eager
+    graphs = []
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for c in range(copies):
+                step(c)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        c = i % copies
+        if use_graph:
+            graphs[c].replay()
+        else:
+            step(c)
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        run(i)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - wall0) * 1e3
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # ---- stage timing: library stage events inside captured steps -----------------
+    nst = len(native.FFN_STAGES)
+    reps = min(args.steps, 64)
+    ev = HipEvents(2 * nst * reps)
+    L = native.lib()
+    stage_ms = {n: [] for n in native.FFN_STAGES}
+    sgraphs = []
+    try:
+        for r in range(reps):
+            base = ctypes.c_void_p(ctypes.addressof(ev.arr) +
+                                   2 * nst * r * ctypes.sizeof(ctypes.c_void_p))
+            L.nvfp4_set_ffn_stage_events(base)
+            if use_graph:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    step(r % copies)
+                sgraphs.append(g)
+            else:
+                step(r % copies)
+        L.nvfp4_set_ffn_stage_events(None)
+        torch.cuda.synchronize()
+        for g in sgraphs:
+            g.replay()
+        torch.cuda.synchronize()
+        for r in range(reps):
+            for si, n in enumerate(native.FFN_STAGES):
+                b = 2 * nst * r + 2 * si
+                stage_ms[n].append(ev.elapsed_ms(b, b + 1))
+    finally:
+        L.nvfp4_set_ffn_stage_events(None)
+    stage_avg_us = {n: 1e3 * float(np.mean(v)) for n, v in stage_ms.items()}
+    ev.close()
+
+    gu_s = stage_avg_us["gate_up"] * 1e-6
+    if prefill_mfma:
+        value = alg_flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = gateup_flops / gu_s / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = gateup_bytes / gu_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roofline["kernel"] = "grouped_gemm_kernel (gate/up, SiLU*up epilogue)"
+    roofline["kernel_avg_us"] = round(stage_avg_us["gate_up"], 3)
+
+    # ---- CPU oracle on a bounded sample (rank 0, N = 1) --------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "hidden": H, "intermediate": I,
+                   "experts": E, "top_k": k, "act": wl.act,
+                   "zipf_s": wl.zipf_s, "active_experts": active,
+                   "max_tokens_per_expert": int(counts.max()),
+                   "weight_copies_cycled": copies, "graph": use_graph,
+                   "parallelism": "single GPU"},
+        "alg_bytes_per_step": int(alg_bytes), "alg_flops_per_step": int(alg_flops),
+        "pct_of_peak": round(100 * (value / (MFMA_F16_PEAK_TFLOPS if prefill_mfma
+                                             else HBM_PEAK_GBS)), 2),
+        "stage_us": {n: round(v, 3) for n, v in stage_avg_us.items()},
+        "wall_ms_timed_region": round(wall_ms, 3),
+        "setup_s": round(setup_s, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts):
+    """Time the oracle (as it stands) on a bounded sample of the same step and
+    use it as the correctness gate for the GPU output rows it covers."""
+    import numpy as np
+    import threadpoolctl
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import LazyOracleExperts
+    from oracle import nvfp4_oracle as O
+
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    n_tok = args.cpu_tokens or {"moe_decode": 4, "moe_prefill": 8,
+                                "moe_prefill_w4a4": 1}.get(wl.name, 1)
+    tokens = list(range(0, T, max(1, T // n_tok)))[:n_tok]
+    rids, rw = O.route_topk(logits_np, k)
+    need = np.unique(rids[tokens])
+    w_ref = LazyOracleExperts(E, H, I, need, 0)        # weight quantisation is offline
+    xf = x_cpu.float().numpy()
+    a4 = wl.act == "w4a4"
+    act_globals = None
+    if a4:
+        # the online h scale needs every pair; the sample uses the GPU run's
+        # x scale (recomputed by the oracle) and a static h scale instead
+        act_globals = (O.tensor_global(xf), np.float32(0.05 / 2688))
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    ref, _ = O.moe_ffn(xf, rids, rw, w_ref, act_quant=a4, act_globals=act_globals,
+                       tokens=tokens)
+    dt = time.perf_counter() - t0
+    sample_bytes = 3 * len(need) * (nv_bytes(H * I) + 4) + len(tokens) * H * 4
+    sample_flops = 6 * len(tokens) * k * H * I
+    res = {"kind": "oracle", "cores": int(threads),
+           "sample": f"{len(tokens)} of {T} tokens ({len(need)} experts), "
+                     f"fp64 numpy oracle, {dt:.2f} s",
+           "seconds": round(dt, 3)}
+    if wl.name == "moe_prefill_w4a4":
+        res.update(value=round(sample_flops / dt / 1e12, 6), unit="TFLOP/s")
+    else:
+        res.update(value=round(sample_bytes / dt / 1e9, 4), unit="GB/s")
+    if not a4:
+        got = y_gpu.float().cpu().numpy()[tokens].astype(np.float64)
+        r = O.bf16_rne(ref)
+        res["gate_rel_frob_vs_oracle"] = float(np.linalg.norm(got - r) / np.linalg.norm(r))
+    return res
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * nvfp4moe.h - C ABI of the NVFP4 routed-expert FFN library for MI355X (gfx950).
+ *
+ * The library implements the quantised routed-expert (mixture-of-experts)
+ * feed-forward path over NVFP4 weights: 4-bit E2M1 elements, one FP8 E4M3
+ * scale per 16 consecutive elements along K and one fp32 scale per tensor.
+ * The routed experts of the Flash-Next NVFP4 checkpoint are NVFP4 "W4A4"
+ * (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card, "What this model is");
+ * other NVFP4 parts are quantised weight-only, "W4A16"
+ * (Qwen3.8-27B-nvfp4full-dflash2-NInfer model card, "Limits").  Decode runs
+ * it as a memory-bound grouped GEMV and prefill as an expert-grouped GEMM
+ * over chunks of up to 512 tokens that reuse the routed expert weights
+ * (Eider page, "Performance").
+ *
+ * Encodings (the pages name NVFP4 but do not define its bits; these are the
+ * OCP Microscaling Formats v1.0 element types):
+ *   E2M1 code c (4 bits): sign bit 3, exponent bits 2..1 (bias 1), mantissa
+ *     bit 0; magnitudes {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *   E4M3 byte: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0,
+ *     subnormals, largest finite 448 (0x7E).  Block scales are >= 0.
+ *   An NVFP4 matrix W[N, K] is
+ *     codes  uint8 [N, K/2]  row-major; element 2i of a row in the low nibble
+ *                            of byte i, element 2i+1 in the high nibble
+ *                            (each byte holds two NVFP4 values: same model
+ *                            card, "Why Hugging Face shows 68B parameters");
+ *     scales uint8 [N, K/16] row-major, one E4M3 per 16 elements, no swizzle;
+ *     global float           the decode multiplier g;
+ *   and W[n][k] = e2m1(code) * e4m3(scale[n][k/16]) * g.
+ *
+ * Conventions shared by every call:
+ *   - Every data pointer is a DEVICE pointer, 16-byte aligned, and owned by
+ *     the caller.  Struct arguments (nvfp4_matrix, nvfp4_expert_weights) are
+ *     host structs holding device pointers; they are read during the call
+ *     only.  The library allocates nothing, frees nothing and keeps no
+ *     pointer after returning; scratch memory comes from `workspace`, at
+ *     least the size the matching *_workspace_size query returns.
+ *   - All work is enqueued on `stream` (0 = the null stream).  No call
+ *     synchronises or copies between host and device, so buffers must stay
+ *     valid until the stream's work completes.
+ *   - Arguments are validated on the host before anything is enqueued.  On
+ *     failure the call returns the status, records a message for
+ *     nvfp4_last_error() and writes nothing.  A failed kernel launch returns
+ *     NVFP4_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation, as usual in HIP.
+ *   - Calls are deterministic: the same inputs give bit-identical outputs
+ *     (no floating-point atomics; maxima use order-independent integer
+ *     atomics).  The library has no global mutable state except the
+ *     thread-local last-error message.
+ *   - K (the contraction length: cols, H or I) must be a positive multiple
+ *     of 32, otherwise NVFP4_ERR_UNSUPPORTED_SHAPE.
+ *   - Inputs must be finite; NaN or infinite activations, logits or weights
+ *     are not checked and give unspecified results.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, bad enum */
+  NVFP4_ERR_UNSUPPORTED_SHAPE = 2,  /* K % 32 != 0, k > E, limits exceeded   */
+  NVFP4_ERR_MISALIGNED = 3,         /* a pointer is not 16-byte aligned       */
+  NVFP4_ERR_WORKSPACE_TOO_SMALL = 4,
+  NVFP4_ERR_HIP = 5                 /* a HIP launch failed                    */
+} nvfp4_status;
+
+typedef enum { NVFP4_DT_BF16 = 0, NVFP4_DT_F32 = 1 } nvfp4_dtype;
+
+/* Where the fp32 tensor scale of a quantised activation comes from. */
+typedef enum {
+  NVFP4_GLOBAL_COMPUTE = 0,  /* g = amax / 2688 over the tensor; written out */
+  NVFP4_GLOBAL_GIVEN = 1     /* g is read from the caller's pointer          */
+} nvfp4_global_mode;
+
+typedef enum {
+  NVFP4_W4A16 = 0,  /* weights NVFP4, activations bf16                      */
+  NVFP4_W4A4 = 1    /* activations also quantised to NVFP4 before each GEMM */
+} nvfp4_act_mode;
+
+/* One NVFP4 matrix [rows, cols] (layout in the header comment). */
+typedef struct {
+  const uint8_t *codes;        /* [rows, cols/2]                        */
+  const uint8_t *scales;       /* [rows, cols/16] E4M3                  */
+  const float *global_scale;   /* device pointer to the decode scale g  */
+  int64_t rows, cols;
+} nvfp4_matrix;
+
+/* E experts' gated-FFN weights, stacked along a leading expert axis. */
+typedef struct {
+  const uint8_t *gate_codes, *up_codes, *down_codes;    /* [E,I,H/2] [E,I,H/2] [E,H,I/2]    */
+  const uint8_t *gate_scales, *up_scales, *down_scales; /* [E,I,H/16] [E,I,H/16] [E,H,I/16] */
+  const float *gate_global, *up_global, *down_global;   /* [E] each                         */
+} nvfp4_expert_weights;
+
+/*
+ * nvfp4_quantize: quantise x [rows, cols] (row stride ld_x elements, bf16 or
+ * f32) to NVFP4.  codes [rows, cols/2], scales [rows, cols/16] are written.
+ * mode COMPUTE: g = amax(|x|) / 2688 (1.0 for an all-zero x), written to
+ * *global_scale.  mode GIVEN: g is read from *global_scale.
+ * Per 16-block: s = E4M3_rne_saturate(amax_b / (6 g)); per element:
+ * code = E2M1_rne_saturate(x * (1 / (e4m3(s) g))), sign kept, 0 codes when
+ * e4m3(s) g == 0; every step is an fp32 operation rounded to nearest-even.
+ * Requires cols % 32 == 0, ld_x >= cols, ld_x % 8 == 0.
+ */
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t rows,
+                            int64_t cols, int64_t ld_x, uint8_t *codes,
+                            uint8_t *scales, float *global_scale,
+                            nvfp4_global_mode mode, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
+
+/*
+ * nvfp4_dequantize: out [rows, cols] f32 = e2m1 * e4m3 * g, each element the
+ * correctly rounded fp32 product (a debug and test aid; not on the hot path).
+ */
+nvfp4_status nvfp4_dequantize(const nvfp4_matrix *w, float *out,
+                              hipStream_t stream);
+
+/*
+ * nvfp4_linear: y [M, N] = x [M, K] . W^T for an NVFP4 W [N, K], fp32
+ * accumulation, y in bf16 (round-to-nearest-even) or f32.  x is bf16,
+ * row-major, contiguous.  act W4A4: x is first quantised to NVFP4 with one
+ * tensor scale over all of x (mode COMPUTE writes it to *act_global, GIVEN
+ * reads it), and the product uses the dequantised x.  act_global may be
+ * NULL for W4A16.
+ */
+nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
+                          nvfp4_act_mode act, nvfp4_global_mode act_global_mode,
+                          float *act_global, void *y, nvfp4_dtype y_dtype,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K,
+                                   nvfp4_act_mode act);
+
+/*
+ * moe_route_topk: per token t of logits [T, E] (f32), the k experts with the
+ * largest logits in descending order, equal logits going to the lower expert
+ * index -> topk_ids [T, k] int32.  topk_weights [T, k] f32: with renormalize,
+ * exp(l_j - l_max) / sum over the k chosen (top-k of softmax, renormalised);
+ * without, softmax over all E.  The pairs p = t*k + j are then sorted by
+ * expert, ties by token: expert_offsets [E+1] int32 (rows of expert e are
+ * offsets[e] .. offsets[e+1]-1), sorted_pairs [T*k] int32.
+ * The ids, offsets and permutation are exact integers; the weights are fp32.
+ * Requires 1 <= k <= E <= 1024, k <= 32, 1 <= T <= 2^24 / k.
+ */
+nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E,
+                            int32_t k, int renormalize, int32_t *topk_ids,
+                            float *topk_weights, int32_t *expert_offsets,
+                            int32_t *sorted_pairs, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_grouped_nvfp4_ffn: routed-expert gated FFN.  For each pair p = t*k + j
+ * routed to expert e (from moe_route_topk's offsets / sorted_pairs / weights):
+ *   h_p = bf16_rne( silu(g_gate[e] x_t D_gate[e]^T) * (g_up[e] x_t D_up[e]^T) )
+ *   y_t = sum_j topk_weights[p] * g_down[e] h_p D_down[e]^T   (j ascending)
+ * with D the e2m1*e4m3 part of each NVFP4 matrix and fp32 accumulation.
+ * x [T, H] bf16; y [T, H] bf16 or f32.  act W4A4 quantises x (one scale over
+ * all T rows) and h (one scale over all T*k pairs) to NVFP4 before the gate/up
+ * and down products; act_globals[0..1] = {g_x, g_h} are written (COMPUTE) or
+ * read (GIVEN).  act_globals may be NULL for W4A16.
+ * Requires H % 32 == 0, I % 32 == 0, 1 <= k <= E, T >= 1.
+ */
+nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H,
+                                   int64_t I, int32_t E, int32_t k,
+                                   const float *topk_weights,
+                                   const int32_t *expert_offsets,
+                                   const int32_t *sorted_pairs,
+                                   const nvfp4_expert_weights *w,
+                                   nvfp4_act_mode act,
+                                   nvfp4_global_mode act_global_mode,
+                                   float *act_globals, void *y,
+                                   nvfp4_dtype y_dtype, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I,
+                                            int32_t E, int32_t k,
+                                            nvfp4_act_mode act);
+
+/*
+ * Profiling aid (not part of the computation).  While a non-NULL array is
+ * set, every moe_grouped_nvfp4_ffn call made on the calling thread records
+ * events[2*s] on its stream just before stage s and events[2*s+1] just after
+ * it, for the NVFP4_FFN_STAGES stages below; the caller creates the events
+ * (hipEventCreate) and reads them with hipEventElapsedTime.  NULL disables
+ * recording.  The setting is per thread and holds no other state.
+ */
+enum {
+  NVFP4_STAGE_PLAN = 0,     /* m-block list from the expert offsets              */
+  NVFP4_STAGE_X_PREP = 1,   /* x -> fp16 operands (W4A4: amax + quantisation)    */
+  NVFP4_STAGE_GATE_UP = 2,  /* grouped gate/up GEMM with the SiLU * up epilogue  */
+  NVFP4_STAGE_H_PREP = 3,   /* h -> fp16 operands (W4A4: quantisation)           */
+  NVFP4_STAGE_DOWN = 4,     /* grouped down GEMM times the routing weight        */
+  NVFP4_STAGE_COMBINE = 5,  /* sum of each token's k pairs                       */
+  NVFP4_FFN_STAGES = 6
+};
+void nvfp4_set_ffn_stage_events(hipEvent_t *events);
+
+/* Text of a status code; never NULL. */
+const char *nvfp4_status_string(nvfp4_status s);
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *nvfp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4MOE_H */

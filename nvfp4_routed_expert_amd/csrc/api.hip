@@ -1,0 +1,523 @@
+// C ABI of the NVFP4 routed-expert library: argument validation, workspace
+// layout and the launch sequence of each call (declared in include/nvfp4moe.h).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/nvfp4moe.h"
+#include "kernels.h"
+
+using namespace nvfp4;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+thread_local hipEvent_t *g_stage_events = nullptr;
+
+// Records the profiling event of stage s (before: 2s, after: 2s+1), if set.
+void mark(int s, bool after, hipStream_t stream) {
+  if (g_stage_events) (void)hipEventRecord(g_stage_events[2 * s + (after ? 1 : 0)], stream);
+}
+
+nvfp4_status fail(nvfp4_status st, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+nvfp4_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carving of a workspace into aligned regions.
+struct Carver {
+  char *base;
+  size_t used = 0;
+  explicit Carver(void *b) : base(static_cast<char *>(b)) {}
+  template <typename T>
+  T *take(size_t count) {
+    T *p = base ? reinterpret_cast<T *>(base + used) : nullptr;
+    used += round_up(count * sizeof(T));
+    return p;
+  }
+};
+
+#define CHECK_NULL(ptr)                                                         \
+  do {                                                                          \
+    if (!(ptr)) return fail(NVFP4_ERR_INVALID_ARGUMENT, "%s is NULL", #ptr);    \
+  } while (0)
+#define CHECK_ALIGN(ptr)                                                        \
+  do {                                                                          \
+    if (!aligned16(ptr))                                                        \
+      return fail(NVFP4_ERR_MISALIGNED, "%s is not 16-byte aligned", #ptr);     \
+  } while (0)
+
+nvfp4_status check_k(int64_t k, const char *name) {
+  if (k <= 0 || k % 32 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "%s = %lld must be a positive multiple of 32",
+                name, (long long)k);
+  if (k > (int64_t)1 << 30)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "%s = %lld is too large", name, (long long)k);
+  return NVFP4_OK;
+}
+
+nvfp4_status check_workspace(void *ws, size_t have, size_t need) {
+  if (have < need)
+    return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", have, need);
+  if (need > 0) {
+    CHECK_NULL(ws);
+    CHECK_ALIGN(ws);
+  }
+  return NVFP4_OK;
+}
+
+#define TRY(expr)                          \
+  do {                                     \
+    const nvfp4_status st_ = (expr);       \
+    if (st_ != NVFP4_OK) return st_;       \
+  } while (0)
+#define LAUNCH(expr, what) TRY(hip_status((expr), what))
+
+// ---- workspace layouts ---------------------------------------------------------
+
+struct QuantWs {
+  float *partials;
+};
+QuantWs carve_quant(Carver &c) { return QuantWs{c.take<float>(kMaxPartials)}; }
+
+struct LinearWs {
+  _Float16 *x16;
+  int32_t *shift;
+  float *partials;
+  float *g_x;
+};
+LinearWs carve_linear(Carver &c, int64_t M, int64_t K) {
+  LinearWs w;
+  w.x16 = c.take<_Float16>((size_t)(M * K));
+  w.shift = c.take<int32_t>((size_t)M);
+  w.partials = c.take<float>(kMaxPartials);
+  w.g_x = c.take<float>(4);
+  return w;
+}
+
+struct FfnWs {
+  _Float16 *x16;
+  int32_t *xshift;
+  uint16_t *h;
+  _Float16 *h16;
+  int32_t *hshift;
+  float *ypair;
+  int4 *mblocks;
+  int32_t *n_mblocks;
+  uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h
+  float *partials;
+};
+int ffn_bm(int64_t T, int64_t E, int64_t k) { return gemm_block_rows(2 * T * k / E); }
+int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) { return (P + bm - 1) / bm + E; }
+FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  const int64_t P = T * k;
+  FfnWs w;
+  w.x16 = c.take<_Float16>((size_t)(T * H));
+  w.xshift = c.take<int32_t>((size_t)T);
+  w.h = c.take<uint16_t>((size_t)(P * I));
+  w.h16 = c.take<_Float16>((size_t)(P * I));
+  w.hshift = c.take<int32_t>((size_t)P);
+  w.ypair = c.take<float>((size_t)(P * H));
+  w.mblocks = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
+  w.n_mblocks = c.take<int32_t>(4);
+  w.slots = c.take<uint32_t>(4);
+  w.partials = c.take<float>(kMaxPartials);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *nvfp4_status_string(nvfp4_status s) {
+  switch (s) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case NVFP4_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case NVFP4_ERR_MISALIGNED: return "misaligned pointer";
+    case NVFP4_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case NVFP4_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char *nvfp4_last_error(void) { return g_last_error; }
+
+void nvfp4_set_ffn_stage_events(hipEvent_t *events) { g_stage_events = events; }
+
+// ---- nvfp4_quantize ----------------------------------------------------------------
+
+size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) {
+  (void)rows;
+  (void)cols;
+  Carver c(nullptr);
+  carve_quant(c);
+  return c.used;
+}
+
+nvfp4_status nvfp4_quantize(const void *x, nvfp4_dtype x_dtype, int64_t rows, int64_t cols,
+                            int64_t ld_x, uint8_t *codes, uint8_t *scales,
+                            float *global_scale, nvfp4_global_mode mode, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(x);
+  CHECK_NULL(codes);
+  CHECK_NULL(scales);
+  CHECK_NULL(global_scale);
+  if (x_dtype != NVFP4_DT_BF16 && x_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "x_dtype %d is not BF16 or F32", (int)x_dtype);
+  if (mode != NVFP4_GLOBAL_COMPUTE && mode != NVFP4_GLOBAL_GIVEN)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "mode %d is not COMPUTE or GIVEN", (int)mode);
+  if (rows < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "rows = %lld < 1", (long long)rows);
+  TRY(check_k(cols, "cols"));
+  if (ld_x < cols || ld_x % 8 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "ld_x = %lld must be >= cols and a multiple of 8",
+                (long long)ld_x);
+  CHECK_ALIGN(x);
+  CHECK_ALIGN(codes);
+  CHECK_ALIGN(scales);
+  if ((reinterpret_cast<uintptr_t>(global_scale) & 3u) != 0)
+    return fail(NVFP4_ERR_MISALIGNED, "global_scale is not 4-byte aligned");
+  TRY(check_workspace(workspace, workspace_bytes, nvfp4_quantize_workspace_size(rows, cols)));
+  Carver c(workspace);
+  const QuantWs w = carve_quant(c);
+  const InType t = x_dtype == NVFP4_DT_BF16 ? InType::BF16 : InType::F32;
+  if (mode == NVFP4_GLOBAL_COMPUTE) {
+    const int n = amax_partials_grid(rows, cols);
+    LAUNCH(launch_amax_partials(x, t, rows, cols, ld_x, w.partials, n, stream), "amax");
+    LAUNCH(launch_quantize(x, t, rows, cols, ld_x, codes, scales, w.partials, n, nullptr,
+                           global_scale, stream),
+           "quantize");
+  } else {
+    LAUNCH(launch_quantize(x, t, rows, cols, ld_x, codes, scales, nullptr, 0, global_scale,
+                           nullptr, stream),
+           "quantize");
+  }
+  return NVFP4_OK;
+}
+
+// ---- nvfp4_dequantize --------------------------------------------------------------
+
+static nvfp4_status check_matrix(const nvfp4_matrix *w) {
+  CHECK_NULL(w);
+  CHECK_NULL(w->codes);
+  CHECK_NULL(w->scales);
+  CHECK_NULL(w->global_scale);
+  if (w->rows < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "w->rows < 1");
+  TRY(check_k(w->cols, "w->cols"));
+  CHECK_ALIGN(w->codes);
+  CHECK_ALIGN(w->scales);
+  return NVFP4_OK;
+}
+
+nvfp4_status nvfp4_dequantize(const nvfp4_matrix *w, float *out, hipStream_t stream) {
+  g_last_error[0] = 0;
+  TRY(check_matrix(w));
+  CHECK_NULL(out);
+  CHECK_ALIGN(out);
+  LAUNCH(launch_dequantize(w->codes, w->scales, w->global_scale, w->rows, w->cols, out, stream),
+         "dequantize");
+  return NVFP4_OK;
+}
+
+// ---- nvfp4_linear -------------------------------------------------------------------
+
+size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, nvfp4_act_mode act) {
+  (void)N;
+  (void)act;
+  if (M < 1 || K < 1) return 0;
+  Carver c(nullptr);
+  carve_linear(c, M, K);
+  return c.used;
+}
+
+nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
+                          nvfp4_act_mode act, nvfp4_global_mode act_global_mode,
+                          float *act_global, void *y, nvfp4_dtype y_dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(x);
+  CHECK_NULL(y);
+  TRY(check_matrix(w));
+  if (M < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "M = %lld < 1", (long long)M);
+  if (M > (1 << 30) || w->rows > (1 << 30))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "M or N exceeds 2^30");
+  if (act != NVFP4_W4A16 && act != NVFP4_W4A4)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "act %d is not W4A16 or W4A4", (int)act);
+  if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "y_dtype %d is not BF16 or F32", (int)y_dtype);
+  if (act == NVFP4_W4A4) {
+    if (act_global_mode != NVFP4_GLOBAL_COMPUTE && act_global_mode != NVFP4_GLOBAL_GIVEN)
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "act_global_mode %d invalid", (int)act_global_mode);
+    if (act_global_mode == NVFP4_GLOBAL_GIVEN) CHECK_NULL(act_global);
+  }
+  CHECK_ALIGN(x);
+  CHECK_ALIGN(y);
+  const int64_t K = w->cols, N = w->rows;
+  TRY(check_workspace(workspace, workspace_bytes, nvfp4_linear_workspace_size(M, N, K, act)));
+  Carver c(workspace);
+  const LinearWs ws = carve_linear(c, M, K);
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  if (act == NVFP4_W4A16) {
+    LAUNCH(launch_row_prep(xb, M, K, PrepMode::SHIFT, ws.x16, ws.shift, nullptr, 0, nullptr,
+                           nullptr, nullptr, stream),
+           "row_prep");
+  } else if (act_global_mode == NVFP4_GLOBAL_GIVEN) {
+    LAUNCH(launch_row_prep(xb, M, K, PrepMode::QUANT, ws.x16, nullptr, nullptr, 0, act_global,
+                           ws.g_x, nullptr, stream),
+           "row_prep");
+  } else {
+    const int n = amax_partials_grid(M, K);
+    LAUNCH(launch_amax_partials(x, InType::BF16, M, K, K, ws.partials, n, stream), "amax");
+    LAUNCH(launch_row_prep(xb, M, K, PrepMode::QUANT, ws.x16, nullptr, ws.partials, n, nullptr,
+                           ws.g_x, act_global, stream),
+           "row_prep");
+  }
+  GemmArgs a = {};
+  a.A = ws.x16;
+  a.lda = K;
+  a.a_shift = act == NVFP4_W4A16 ? ws.shift : nullptr;
+  a.b_codes[0] = w->codes;
+  a.b_scales[0] = w->scales;
+  a.b_global[0] = w->global_scale;
+  a.N = (int)N;
+  a.K = (int)K;
+  const int bm = gemm_block_rows(M);
+  a.mblocks = nullptr;
+  a.dense_rows = M;
+  a.n_mblocks = (int)((M + bm - 1) / bm);
+  a.extra_scale = act == NVFP4_W4A4 ? ws.g_x : nullptr;
+  a.out = y;
+  a.ldo = N;
+  a.out_type = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
+  LAUNCH(launch_gemm(Epi::LINEAR, a, bm, stream), "gemm");
+  return NVFP4_OK;
+}
+
+// ---- moe_route_topk -------------------------------------------------------------------
+
+size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k) {
+  (void)T;
+  (void)E;
+  (void)k;
+  return 0;
+}
+
+nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
+                            int renormalize, int32_t *topk_ids, float *topk_weights,
+                            int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  (void)workspace;
+  (void)workspace_bytes;
+  CHECK_NULL(logits);
+  CHECK_NULL(topk_ids);
+  CHECK_NULL(topk_weights);
+  CHECK_NULL(expert_offsets);
+  CHECK_NULL(sorted_pairs);
+  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (E < 1 || E > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
+  if (k < 1 || k > E || k > 32)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k = %d outside 1..min(E, 32)", (int)k);
+  if (T * (int64_t)k > ((int64_t)1 << 24))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*k = %lld exceeds 2^24", (long long)(T * k));
+  CHECK_ALIGN(logits);
+  CHECK_ALIGN(topk_ids);
+  CHECK_ALIGN(topk_weights);
+  CHECK_ALIGN(expert_offsets);
+  CHECK_ALIGN(sorted_pairs);
+  LAUNCH(launch_route_topk(logits, T, E, k, renormalize, topk_ids, topk_weights, stream), "topk");
+  LAUNCH(launch_route_permute(topk_ids, T, E, k, expert_offsets, sorted_pairs, stream), "permute");
+  return NVFP4_OK;
+}
+
+// ---- moe_grouped_nvfp4_ffn -----------------------------------------------------------
+
+size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E,
+                                            int32_t k, nvfp4_act_mode act) {
+  (void)act;
+  if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1) return 0;
+  Carver c(nullptr);
+  carve_ffn(c, T, H, I, E, k);
+  return c.used;
+}
+
+nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t I, int32_t E,
+                                   int32_t k, const float *topk_weights,
+                                   const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                                   const nvfp4_expert_weights *w, nvfp4_act_mode act,
+                                   nvfp4_global_mode act_global_mode, float *act_globals,
+                                   void *y, nvfp4_dtype y_dtype, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(x);
+  CHECK_NULL(topk_weights);
+  CHECK_NULL(expert_offsets);
+  CHECK_NULL(sorted_pairs);
+  CHECK_NULL(w);
+  CHECK_NULL(y);
+  CHECK_NULL(w->gate_codes);
+  CHECK_NULL(w->up_codes);
+  CHECK_NULL(w->down_codes);
+  CHECK_NULL(w->gate_scales);
+  CHECK_NULL(w->up_scales);
+  CHECK_NULL(w->down_scales);
+  CHECK_NULL(w->gate_global);
+  CHECK_NULL(w->up_global);
+  CHECK_NULL(w->down_global);
+  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  TRY(check_k(H, "H"));
+  TRY(check_k(I, "I"));
+  if (E < 1 || E > (1 << 20))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..2^20", (int)E);
+  if (k < 1 || k > E) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k = %d outside 1..E", (int)k);
+  if (T * (int64_t)k > ((int64_t)1 << 24))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*k exceeds 2^24");
+  if (act != NVFP4_W4A16 && act != NVFP4_W4A4)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "act %d is not W4A16 or W4A4", (int)act);
+  if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "y_dtype %d is not BF16 or F32", (int)y_dtype);
+  if (act == NVFP4_W4A4) {
+    if (act_global_mode != NVFP4_GLOBAL_COMPUTE && act_global_mode != NVFP4_GLOBAL_GIVEN)
+      return fail(NVFP4_ERR_INVALID_ARGUMENT, "act_global_mode %d invalid", (int)act_global_mode);
+    if (act_global_mode == NVFP4_GLOBAL_GIVEN) CHECK_NULL(act_globals);
+  }
+  CHECK_ALIGN(x);
+  CHECK_ALIGN(y);
+  CHECK_ALIGN(topk_weights);
+  CHECK_ALIGN(expert_offsets);
+  CHECK_ALIGN(sorted_pairs);
+  CHECK_ALIGN(w->gate_codes);
+  CHECK_ALIGN(w->up_codes);
+  CHECK_ALIGN(w->down_codes);
+  CHECK_ALIGN(w->gate_scales);
+  CHECK_ALIGN(w->up_scales);
+  CHECK_ALIGN(w->down_scales);
+  TRY(check_workspace(workspace, workspace_bytes,
+                      moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act)));
+  Carver c(workspace);
+  const FfnWs ws = carve_ffn(c, T, H, I, E, k);
+  const int64_t P = T * k;
+  const int bm = ffn_bm(T, E, k);
+  const bool a4 = act == NVFP4_W4A4;
+  const bool given = a4 && act_global_mode == NVFP4_GLOBAL_GIVEN;
+  float *slot_gx = reinterpret_cast<float *>(ws.slots + 1);
+  float *slot_gh = reinterpret_cast<float *>(ws.slots + 2);
+
+  // 1. plan (m-blocks per expert) and zeroed |h| maximum
+  mark(NVFP4_STAGE_PLAN, false, stream);
+  LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots, 1, stream),
+         "plan");
+  mark(NVFP4_STAGE_PLAN, true, stream);
+  // 2. activation rows -> fp16 operands
+  mark(NVFP4_STAGE_X_PREP, false, stream);
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  if (!a4) {
+    LAUNCH(launch_row_prep(xb, T, H, PrepMode::SHIFT, ws.x16, ws.xshift, nullptr, 0, nullptr,
+                           nullptr, nullptr, stream),
+           "x prep");
+  } else if (given) {
+    LAUNCH(launch_row_prep(xb, T, H, PrepMode::QUANT, ws.x16, nullptr, nullptr, 0, act_globals,
+                           slot_gx, nullptr, stream),
+           "x quant");
+  } else {
+    const int n = amax_partials_grid(T, H);
+    LAUNCH(launch_amax_partials(x, InType::BF16, T, H, H, ws.partials, n, stream), "x amax");
+    LAUNCH(launch_row_prep(xb, T, H, PrepMode::QUANT, ws.x16, nullptr, ws.partials, n, nullptr,
+                           slot_gx, act_globals, stream),
+           "x quant");
+  }
+  mark(NVFP4_STAGE_X_PREP, true, stream);
+  // 3. gate/up grouped GEMM with the SiLU * up epilogue -> h (bf16, expert-sorted rows)
+  GemmArgs g = {};
+  g.A = ws.x16;
+  g.lda = H;
+  g.a_rowmap = sorted_pairs;
+  g.a_rowdiv = k;
+  g.a_shift = a4 ? nullptr : ws.xshift;
+  g.b_codes[0] = w->gate_codes;
+  g.b_codes[1] = w->up_codes;
+  g.b_scales[0] = w->gate_scales;
+  g.b_scales[1] = w->up_scales;
+  g.b_global[0] = w->gate_global;
+  g.b_global[1] = w->up_global;
+  g.b_codes_estride = I * (H / 2);
+  g.b_scales_estride = I * (H / 16);
+  g.N = (int)I;
+  g.K = (int)H;
+  g.mblocks = ws.mblocks;
+  g.n_mblocks_dev = ws.n_mblocks;
+  g.n_mblocks = (int)ffn_max_mblocks(P, E, bm);
+  g.extra_scale = a4 ? slot_gx : nullptr;
+  g.out = ws.h;
+  g.ldo = I;
+  g.out_type = OutType::BF16;
+  g.amax_slot = a4 ? ws.slots : nullptr;
+  mark(NVFP4_STAGE_GATE_UP, false, stream);
+  LAUNCH(launch_gemm(Epi::SWIGLU, g, bm, stream), "gate/up");
+  mark(NVFP4_STAGE_GATE_UP, true, stream);
+  // 4. h rows -> fp16 operands
+  mark(NVFP4_STAGE_H_PREP, false, stream);
+  if (!a4) {
+    LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::SHIFT, ws.h16, ws.hshift, nullptr, 0, nullptr,
+                           nullptr, nullptr, stream),
+           "h prep");
+  } else if (given) {
+    LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::QUANT, ws.h16, nullptr, nullptr, 0,
+                           act_globals + 1, slot_gh, nullptr, stream),
+           "h quant");
+  } else {
+    LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::QUANT, ws.h16, nullptr,
+                           reinterpret_cast<const float *>(ws.slots), 1, nullptr, slot_gh,
+                           act_globals ? act_globals + 1 : nullptr, stream),
+           "h quant");
+  }
+  mark(NVFP4_STAGE_H_PREP, true, stream);
+  // 5. down grouped GEMM, weighted by the routing weight -> Y per pair (fp32)
+  GemmArgs d = {};
+  d.A = ws.h16;
+  d.lda = I;
+  d.a_shift = a4 ? nullptr : ws.hshift;
+  d.b_codes[0] = w->down_codes;
+  d.b_scales[0] = w->down_scales;
+  d.b_global[0] = w->down_global;
+  d.b_codes_estride = H * (I / 2);
+  d.b_scales_estride = H * (I / 16);
+  d.N = (int)H;
+  d.K = (int)I;
+  d.mblocks = ws.mblocks;
+  d.n_mblocks_dev = ws.n_mblocks;
+  d.n_mblocks = (int)ffn_max_mblocks(P, E, bm);
+  d.extra_scale = a4 ? slot_gh : nullptr;
+  d.out = ws.ypair;
+  d.ldo = H;
+  d.out_type = OutType::F32;
+  d.pair_weights = topk_weights;
+  d.sorted_pairs = sorted_pairs;
+  mark(NVFP4_STAGE_DOWN, false, stream);
+  LAUNCH(launch_gemm(Epi::DOWN, d, bm, stream), "down");
+  mark(NVFP4_STAGE_DOWN, true, stream);
+  // 6. combine the k pairs of every token in slot order
+  mark(NVFP4_STAGE_COMBINE, false, stream);
+  LAUNCH(launch_combine(ws.ypair, T, H, k, y,
+                        y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16, stream),
+         "combine");
+  mark(NVFP4_STAGE_COMBINE, true, stream);
+  return NVFP4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Host-side launchers of the NVFP4 kernels (internal to the library; the
+// public C ABI is include/nvfp4moe.h).  Every launcher only enqueues work on
+// `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+enum class InType : int { BF16 = 0, F32 = 1 };
+enum class OutType : int { BF16 = 0, F32 = 1 };
+
+// ---- quantisation (quant.hip) ------------------------------------------------
+
+// Partial maxima of |x| over a [rows, cols] matrix (row stride ld): one fp32
+// per workgroup, `n_partials` workgroups.  Returns the launch status.
+constexpr int kMaxPartials = 1024;
+int amax_partials_grid(int64_t rows, int64_t cols);
+hipError_t launch_amax_partials(const void *x, InType t, int64_t rows, int64_t cols,
+                                int64_t ld, float *partials, int n_partials,
+                                hipStream_t s);
+
+// NVFP4 quantisation of x into codes/scales.  The decode scale g is either
+// derived from `amax_src` (n_amax floats, maximum taken) or read from
+// `g_given` when it is non-null.  g_out (if non-null) receives g.
+hipError_t launch_quantize(const void *x, InType t, int64_t rows, int64_t cols,
+                           int64_t ld, uint8_t *codes, uint8_t *scales,
+                           const float *amax_src, int n_amax, const float *g_given,
+                           float *g_out, hipStream_t s);
+
+// Debug dequantisation to fp32.
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales,
+                             const float *g, int64_t rows, int64_t cols,
+                             float *out, hipStream_t s);
+
+// Activation rows (bf16 [rows, cols], contiguous) -> fp16 MFMA operands.
+//  SHIFT: per row r, s_r = floor(log2 amax_r) - 15, out = x * 2^-s_r, shift[r] = s_r.
+//  QUANT: NVFP4-quantise with decode scale g (from amax_src/g_given as in
+//         launch_quantize) and write e2m1 * e4m3 (without g) in fp16.
+enum class PrepMode : int { SHIFT = 0, QUANT = 1 };
+hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols,
+                           PrepMode mode, _Float16 *out, int32_t *shift,
+                           const float *amax_src, int n_amax, const float *g_given,
+                           float *g_out, float *g_out2, hipStream_t s);
+
+// ---- routing (route.hip) -------------------------------------------------------
+
+hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
+                             int renormalize, int32_t *ids, float *weights,
+                             hipStream_t s);
+hipError_t launch_route_permute(const int32_t *ids, int64_t T, int E, int k,
+                                int32_t *offsets, int32_t *sorted_pairs,
+                                hipStream_t s);
+
+// ---- grouped GEMM and FFN glue (gemm.hip) ---------------------------------------
+
+enum class Epi : int { LINEAR = 0, SWIGLU = 1, DOWN = 2 };
+
+struct GemmArgs {
+  // A operand: fp16 rows.  Tile row `pos` reads A row
+  //   a_rowmap ? a_rowmap[pos] / a_rowdiv : pos
+  const _Float16 *A;
+  int64_t lda;
+  const int32_t *a_rowmap;
+  int a_rowdiv;
+  const int32_t *a_shift;   // per A row power-of-two exponent, or null
+  // B operand(s): NVFP4 [E][N][K]; matrix 1 is `up` for SWIGLU
+  const uint8_t *b_codes[2];
+  const uint8_t *b_scales[2];
+  const float *b_global[2];
+  int64_t b_codes_estride, b_scales_estride;
+  int N, K;
+  // work list: int4 {expert, first tile row, rows, 0}; null = dense mode,
+  // blocks of BM consecutive rows out of dense_rows, expert 0
+  const int4 *mblocks;
+  int64_t dense_rows;
+  const int32_t *n_mblocks_dev;   // device count, or null to use n_mblocks
+  int n_mblocks;                  // host count, or an upper bound when dev != null
+  // epilogue
+  const float *extra_scale;       // device scalar multiplier (W4A4 act scale) or null
+  void *out;
+  int64_t ldo;
+  OutType out_type;
+  uint32_t *amax_slot;            // SWIGLU: running max of |h| (float bits) or null
+  const float *pair_weights;      // DOWN: routing weight of pair p
+  const int32_t *sorted_pairs;    // DOWN: pair of each tile row
+};
+
+hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
+int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
+
+// FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.
+hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
+                           int32_t *n_mblocks, uint32_t *zero, int zero_words,
+                           hipStream_t s);
+
+// y[t] = sum_j Y[t*k + j], j ascending, fp32 -> out type.
+hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k,
+                          void *y, OutType t, hipStream_t s);
+
+}  // namespace nvfp4

@@ -1,0 +1,264 @@
+"""Thin Python binding of libnvfp4moe.so (include/nvfp4moe.h).
+
+Argument marshalling only: PyTorch allocates device memory and supplies the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no fallback: if the library is missing or cannot be
+loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libnvfp4moe.so")
+
+OK = 0
+DT_BF16, DT_F32 = 0, 1
+GLOBAL_COMPUTE, GLOBAL_GIVEN = 0, 1
+W4A16, W4A4 = 0, 1
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status, text, detail):
+        super().__init__(f"{text} ({status}): {detail}")
+        self.status = status
+
+
+class Matrix(ctypes.Structure):
+    _fields_ = [("codes", _vp), ("scales", _vp), ("global_scale", _vp),
+                ("rows", _i64), ("cols", _i64)]
+
+
+class ExpertWeightsC(ctypes.Structure):
+    _fields_ = [("gate_codes", _vp), ("up_codes", _vp), ("down_codes", _vp),
+                ("gate_scales", _vp), ("up_scales", _vp), ("down_scales", _vp),
+                ("gate_global", _vp), ("up_global", _vp), ("down_global", _vp)]
+
+
+_LIB = None
+
+
+def lib():
+    """Load the HIP library (once).  Raises if it is not built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m nvfp4_routed_expert_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        sigs = {
+            "nvfp4_quantize": (_i32, [_vp, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i32,
+                                      _vp, _sz, _vp]),
+            "nvfp4_quantize_workspace_size": (_sz, [_i64, _i64]),
+            "nvfp4_dequantize": (_i32, [ctypes.POINTER(Matrix), _vp, _vp]),
+            "nvfp4_linear": (_i32, [_vp, _i64, ctypes.POINTER(Matrix), _i32, _i32, _vp, _vp,
+                                    _i32, _vp, _sz, _vp]),
+            "nvfp4_linear_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
+            "moe_route_topk": (_i32, [_vp, _i64, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                      _vp, _sz, _vp]),
+            "moe_route_topk_workspace_size": (_sz, [_i64, _i32, _i32]),
+            "moe_grouped_nvfp4_ffn": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
+                                             ctypes.POINTER(ExpertWeightsC), _i32, _i32, _vp,
+                                             _vp, _i32, _vp, _sz, _vp]),
+            "moe_grouped_nvfp4_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+            "nvfp4_set_ffn_stage_events": (None, [_vp]),
+            "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
+            "nvfp4_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sigs.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+FFN_STAGES = ("plan", "x_prep", "gate_up", "h_prep", "down", "combine")
+
+
+def exported_symbols():
+    return ["nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_dequantize",
+            "nvfp4_linear", "nvfp4_linear_workspace_size", "moe_route_topk",
+            "moe_route_topk_workspace_size", "moe_grouped_nvfp4_ffn",
+            "moe_grouped_nvfp4_ffn_workspace_size", "nvfp4_set_ffn_stage_events",
+            "nvfp4_status_string", "nvfp4_last_error"]
+
+
+def _check(status):
+    if status != OK:
+        L = lib()
+        raise NVFP4Error(status, L.nvfp4_status_string(status).decode(),
+                         L.nvfp4_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _workspace(nbytes, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace needs {nbytes} bytes")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def _dt(dtype):
+    if dtype == torch.bfloat16:
+        return DT_BF16
+    if dtype == torch.float32:
+        return DT_F32
+    raise TypeError(f"unsupported dtype {dtype}")
+
+
+# ---------------------------------------------------------------------------
+
+
+def nvfp4_quantize(x, global_scale=None, workspace=None, out=None):
+    """Quantise x [rows, cols] (bf16/f32, cuda) to NVFP4.
+
+    global_scale: None computes g = amax/2688; a 1-element fp32 cuda tensor
+    is used as the given decode scale.  Returns (codes, scales, g).
+    """
+    rows, cols = x.shape
+    dev = x.device
+    if out is None:
+        codes = torch.empty((rows, cols // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 16), dtype=torch.uint8, device=dev)
+    else:
+        codes, scales = out
+    if global_scale is None:
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+        mode = GLOBAL_COMPUTE
+    else:
+        g, mode = global_scale, GLOBAL_GIVEN
+    L = lib()
+    nbytes = L.nvfp4_quantize_workspace_size(rows, cols)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(L.nvfp4_quantize(_ptr(x), _dt(x.dtype), rows, cols, x.stride(0), _ptr(codes),
+                            _ptr(scales), _ptr(g), mode, _ptr(ws), ws.numel(), _stream()))
+    return codes, scales, g
+
+
+def nvfp4_dequantize(codes, scales, g):
+    rows, half = codes.shape
+    out = torch.empty((rows, half * 2), dtype=torch.float32, device=codes.device)
+    m = Matrix(codes.data_ptr(), scales.data_ptr(), g.data_ptr(), rows, half * 2)
+    _check(lib().nvfp4_dequantize(ctypes.byref(m), _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_linear(x, codes, scales, g, act=W4A16, act_global=None,
+                 out_dtype=torch.bfloat16, workspace=None, out=None):
+    """y [M, N] = x [M, K] . deq(W [N, K])^T.  W4A4 quantises x first.
+
+    act_global (W4A4): None -> computed (returned); a tensor -> given.
+    Returns (y, act_global or None).
+    """
+    M, K = x.shape
+    N = codes.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((M, N), dtype=out_dtype, device=dev)
+    mode = GLOBAL_COMPUTE
+    ag = None
+    if act == W4A4:
+        if act_global is None:
+            ag = torch.empty(1, dtype=torch.float32, device=dev)
+        else:
+            ag, mode = act_global, GLOBAL_GIVEN
+    L = lib()
+    ws = _workspace(L.nvfp4_linear_workspace_size(M, N, K, act), dev, workspace)
+    m = Matrix(codes.data_ptr(), scales.data_ptr(), g.data_ptr(), N, K)
+    _check(L.nvfp4_linear(_ptr(x), M, ctypes.byref(m), act, mode, _ptr(ag), _ptr(y),
+                          _dt(y.dtype), _ptr(ws), ws.numel(), _stream()))
+    return y, ag
+
+
+def moe_route_topk(logits, k, renormalize=True, out=None):
+    """Returns (topk_ids [T,k] i32, topk_weights [T,k] f32, expert_offsets [E+1] i32,
+    sorted_pairs [T*k] i32)."""
+    T, E = logits.shape
+    dev = logits.device
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+    else:
+        ids, w, off, pairs = out
+    L = lib()
+    nbytes = L.moe_route_topk_workspace_size(T, E, k)
+    ws = _workspace(nbytes, dev)
+    _check(L.moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
+                            _ptr(off), _ptr(pairs), _ptr(ws), nbytes, _stream()))
+    return ids, w, off, pairs
+
+
+class ExpertWeights:
+    """Device tensors of E stacked NVFP4 experts (gate/up [E,I,H], down [E,H,I])."""
+
+    def __init__(self, gate_codes, gate_scales, gate_global, up_codes, up_scales,
+                 up_global, down_codes, down_scales, down_global):
+        self.gate_codes, self.gate_scales, self.gate_global = gate_codes, gate_scales, gate_global
+        self.up_codes, self.up_scales, self.up_global = up_codes, up_scales, up_global
+        self.down_codes, self.down_scales, self.down_global = down_codes, down_scales, down_global
+
+    @property
+    def num_experts(self):
+        return self.gate_codes.shape[0]
+
+    @property
+    def intermediate(self):
+        return self.gate_codes.shape[1]
+
+    @property
+    def hidden(self):
+        return self.down_codes.shape[1]
+
+    def c_struct(self):
+        return ExpertWeightsC(*(t.data_ptr() for t in (
+            self.gate_codes, self.up_codes, self.down_codes, self.gate_scales,
+            self.up_scales, self.down_scales, self.gate_global, self.up_global,
+            self.down_global)))
+
+
+def ffn_workspace_bytes(T, H, I, E, k, act=W4A16):
+    return lib().moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act)
+
+
+def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_weights, expert_offsets,
+                          sorted_pairs, k, act=W4A16, act_globals=None,
+                          out_dtype=torch.bfloat16, workspace=None, out=None):
+    """Routed-expert gated FFN.  Returns (y [T,H], act_globals or None)."""
+    T, H = x.shape
+    E, I = weights.num_experts, weights.intermediate
+    dev = x.device
+    y = out if out is not None else torch.empty((T, H), dtype=out_dtype, device=dev)
+    mode = GLOBAL_COMPUTE
+    ag = None
+    if act == W4A4:
+        if act_globals is None:
+            ag = torch.empty(2, dtype=torch.float32, device=dev)
+        else:
+            ag, mode = act_globals, GLOBAL_GIVEN
+    L = lib()
+    ws = _workspace(L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act), dev, workspace)
+    cw = weights.c_struct()
+    _check(L.moe_grouped_nvfp4_ffn(_ptr(x), T, H, I, E, k, _ptr(topk_weights),
+                                   _ptr(expert_offsets), _ptr(sorted_pairs), ctypes.byref(cw),
+                                   act, mode, _ptr(ag), _ptr(y), _dt(y.dtype), _ptr(ws),
+                                   ws.numel(), _stream()))
+    return y, ag

@@ -1,0 +1,78 @@
+"""Shared helpers for the parity tests: oracle-side weight preparation from
+the same seeded fp32 weights the GPU side quantises, and the error metrics."""
+from __future__ import annotations
+
+import concurrent.futures
+
+import numpy as np
+
+from nvfp4_routed_expert_amd import synth
+from oracle import nvfp4_oracle as O
+
+
+class LazyOracleExperts(O.ExpertWeights):
+    """Oracle ExpertWeights that quantises only the experts it is given."""
+
+    def __init__(self, E, H, I, experts, seed=0, workers=8):
+        experts = sorted(set(int(e) for e in experts))
+        z = lambda *s: np.zeros(s, np.uint8)
+        gc, gs, uc, us = z(E, I, H // 2), z(E, I, H // 16), z(E, I, H // 2), z(E, I, H // 16)
+        dc, ds = z(E, H, I // 2), z(E, H, I // 16)
+        gg, ug, dg = (np.ones(E, np.float32) for _ in range(3))
+
+        def prep(e):
+            g, u, d = synth.expert_weights_f32(e, H, I, seed)
+            return e, O.quantize(g), O.quantize(u), O.quantize(d)
+
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            for e, qg, qu, qd in ex.map(prep, experts):
+                gc[e], gs[e], gg[e] = qg
+                uc[e], us[e], ug[e] = qu
+                dc[e], ds[e], dg[e] = qd
+        super().__init__(gc, gs, gg, uc, us, ug, dc, ds, dg)
+        self.filled = experts
+
+
+def rel_frob(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-300))
+
+
+def max_abs_over_rms(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(got - ref)) / max(rms, 1e-300))
+
+
+# Output tolerance against the fp64 oracle (fp32 outputs): relative
+# Frobenius error <= 1e-3 and max |error| <= 1e-2 * RMS of the reference.
+REL_FROB_TOL = 1e-3
+MAX_ABS_RMS_TOL = 1e-2
+
+
+def assert_close_f32(got, ref, what=""):
+    rf, ma = rel_frob(got, ref), max_abs_over_rms(got, ref)
+    assert rf <= REL_FROB_TOL and ma <= MAX_ABS_RMS_TOL, \
+        f"{what}: rel_frob={rf:.3e} max_abs/rms={ma:.3e}"
+    return rf, ma
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 at each |v| (fp64)."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(np.where(v > 0, v, 1.0))
+    return np.exp2(np.maximum(e, -125) - 8.0)
+
+
+def assert_bf16_output(got_bf16, got_f32, ref64, what=""):
+    """bf16 output: exactly the RNE rounding of the same kernel's fp32
+    output, within one bf16 ulp of the rounded oracle value, and within the
+    Frobenius bound of the rounded oracle."""
+    g = np.asarray(got_bf16, np.float64)
+    assert np.array_equal(g, O.bf16_rne(np.asarray(got_f32, np.float64))), \
+        f"{what}: bf16 output is not the rounding of the fp32 output"
+    r = O.bf16_rne(ref64)
+    assert np.all(np.abs(g - r) <= bf16_ulp(r) * 1.0000001), f"{what}: more than 1 bf16 ulp off"
+    assert rel_frob(g, r) <= REL_FROB_TOL, f"{what}: rel_frob {rel_frob(g, r):.3e}"

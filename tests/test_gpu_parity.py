@@ -1,0 +1,301 @@
+"""GPU parity of the HIP library against the fp64 CPU oracle.
+
+Bit-exact: dequantisation, quantisation codes/scales/global, routing ids,
+offsets and permutation.  Tolerance (fp32 outputs): relative Frobenius
+error <= 1e-3 and max |error| <= 1e-2 * RMS against the fp64 oracle; bf16
+outputs must equal the RNE rounding of the same kernel's fp32 output and sit
+within one bf16 ulp of the rounded oracle.  Every call goes through the C ABI.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_routed_expert_amd import native, synth, weights
+from oracle import nvfp4_oracle as O
+from tests.helpers import LazyOracleExperts, assert_bf16_output, assert_close_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_np(t):
+    return t.detach().cpu().numpy()
+
+
+def bf16_np(t):
+    return t.detach().cpu().to(torch.float32).numpy()
+
+
+# ---------------------------------------------------------------------------
+# dequantisation and quantisation (bit-exact)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (37, 96), (256, 512)])
+def test_dequantize_bit_exact(rows, cols):
+    say("dequantize", rows, cols)
+    rng = np.random.default_rng(rows * 1000 + cols)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(rows, cols // 16), dtype=np.uint8)
+    scales.flat[: min(scales.size, 127)] = np.arange(min(scales.size, 127))  # every finite scale
+    g = np.float32(0.0371)
+    out = native.nvfp4_dequantize(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                                  torch.tensor([g], device=DEV))
+    ref = O.dequantize_f32(codes, scales, g)
+    assert np.array_equal(to_np(out).view(np.uint32), ref.view(np.uint32))
+
+
+def _quant_cases():
+    rng = np.random.default_rng(0)
+    cases = {}
+    cases["weights_512x256"] = (synth.weight(512, 256, synth.GATE, 0), torch.float32)
+    cases["wide_range"] = ((rng.standard_normal((33, 160)) *
+                            np.exp(rng.uniform(-12, 12, (33, 1)))).astype(np.float32), torch.float32)
+    # E2M1 half-way points (exact ties when g = 2^-8 is given, see below)
+    ties = np.tile(np.array([6, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, -0.25, -0.75, -1.25, -1.75,
+                             -2.5, -3.5, -5, 0], np.float32), (4, 2))
+    cases["ties"] = (ties, torch.float32)
+    z = rng.standard_normal((8, 64)).astype(np.float32)
+    z[2] = 0
+    z[5, 16:32] = 0
+    z[6, 0:16] *= 1e-9         # a block whose scale underflows
+    cases["zeros"] = (z, torch.float32)
+    cases["bf16_acts"] = (synth.activations(64, 2048).float().numpy(), torch.bfloat16)
+    return cases
+
+
+@pytest.mark.parametrize("name", list(_quant_cases().keys()))
+def test_quantize_bit_exact(name):
+    x, dt = _quant_cases()[name]
+    say("quantize", name, x.shape, dt)
+    xt = torch.from_numpy(x).to(DEV).to(dt)
+    codes, scales, g = native.nvfp4_quantize(xt)
+    rc, rs, rg = O.quantize(xt.float().cpu().numpy())
+    assert to_np(g)[0] == rg
+    assert np.array_equal(to_np(scales), rs)
+    assert np.array_equal(to_np(codes), rc)
+    # given-scale mode: for the tie block g = 2^-8 makes s = 256 and s*g = 1,
+    # so every listed element is an exact E2M1 half-way point
+    gg = np.float32(2.0 ** -8) if name == "ties" else np.float32(rg * 0.75)
+    codes2, scales2, _ = native.nvfp4_quantize(xt, global_scale=torch.tensor([gg], device=DEV))
+    rc2, rs2, _ = O.quantize(xt.float().cpu().numpy(), g=gg)
+    assert np.array_equal(to_np(scales2), rs2) and np.array_equal(to_np(codes2), rc2)
+
+
+def test_quantize_strided_rows():
+    say("quantize strided")
+    x = synth.weight(40, 128, synth.UP, 3)
+    big = torch.zeros((40, 192), dtype=torch.float32, device=DEV)
+    big[:, :128] = torch.from_numpy(x).to(DEV)
+    codes, scales, g = native.nvfp4_quantize(big[:, :128])
+    rc, rs, rg = O.quantize(x)
+    assert to_np(g)[0] == rg and np.array_equal(to_np(codes), rc) and np.array_equal(to_np(scales), rs)
+
+
+# ---------------------------------------------------------------------------
+# routing (bit-exact integers)
+# ---------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    ("decode_16x512_k8", 16, 512, 8, None, True),
+    ("prefill_512x512_k8_zipf", 512, 512, 8, 1.1, True),
+    ("w4a4_2048x128_k8", 2048, 128, 8, None, True),
+    ("ragged_37x20_k3", 37, 20, 3, None, True),
+    ("no_renorm_19x64_k6", 19, 64, 6, None, False),
+    ("k_eq_e_5x7", 5, 7, 7, None, True),
+    ("big_e_3x1024_k32", 3, 1024, 32, None, True),
+    ("long_9000x64_k2", 9000, 64, 2, None, True),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_topk_parity(case):
+    name, T, E, k, zipf, renorm = case
+    say("route", name)
+    logits = synth.router_logits(T, E, seed=1, zipf_s=zipf)
+    if name.startswith("ragged"):
+        logits = np.round(logits * 2) / 2      # plant many ties
+    ids, w, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k, renorm)
+    rids, rw = O.route_topk(logits, k, renorm)
+    roff, rpairs = O.permute(rids, E)
+    assert np.array_equal(to_np(ids), rids)
+    assert np.array_equal(to_np(off), roff)
+    assert np.array_equal(to_np(pairs), rpairs)
+    np.testing.assert_allclose(to_np(w), rw, rtol=5e-6, atol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# dense NVFP4 linear
+# ---------------------------------------------------------------------------
+
+def _linear_inputs(M, K, N, seed=0):
+    x = synth.activations(M, K, seed)
+    wf = synth.weight(N, K, synth.GATE, 0, seed)
+    return x, wf
+
+
+@pytest.mark.parametrize("M,K,N", [(4, 256, 512), (1, 32, 16), (5, 96, 40), (17, 160, 48),
+                                   (33, 256, 64), (130, 384, 96)])
+def test_linear_w4a16(M, K, N):
+    say("linear w4a16", M, K, N)
+    x, wf = _linear_inputs(M, K, N)
+    codes, scales, g = native.nvfp4_quantize(torch.from_numpy(wf).to(DEV))
+    rc, rs, rg = O.quantize(wf)
+    assert np.array_equal(to_np(codes), rc)
+    xd = x.to(DEV)
+    y32, _ = native.nvfp4_linear(xd, codes, scales, g, out_dtype=torch.float32)
+    yb, _ = native.nvfp4_linear(xd, codes, scales, g, out_dtype=torch.bfloat16)
+    ref, _ = O.linear(x.float().numpy(), rc, rs, rg)
+    assert_close_f32(to_np(y32), ref, "linear f32")
+    assert_bf16_output(bf16_np(yb), to_np(y32), ref, "linear bf16")
+
+
+@pytest.mark.parametrize("given", [False, True])
+def test_linear_w4a4(given):
+    M, K, N = 24, 256, 128
+    say("linear w4a4 given" if given else "linear w4a4 compute")
+    x, wf = _linear_inputs(M, K, N, seed=2)
+    codes, scales, g = native.nvfp4_quantize(torch.from_numpy(wf).to(DEV))
+    rc, rs, rg = O.quantize(wf)
+    xn = x.float().numpy()
+    gx_ref = O.tensor_global(xn) * (np.float32(1.5) if given else np.float32(1))
+    ag = torch.tensor([gx_ref], device=DEV) if given else None
+    y32, gx = native.nvfp4_linear(x.to(DEV), codes, scales, g, act=native.W4A4, act_global=ag,
+                                  out_dtype=torch.float32)
+    ref, rgx = O.linear(xn, rc, rs, rg, act_quant=True, act_global=gx_ref if given else None)
+    assert to_np(gx)[0] == rgx
+    assert_close_f32(to_np(y32), ref, "linear w4a4")
+
+
+# ---------------------------------------------------------------------------
+# routed-expert FFN
+# ---------------------------------------------------------------------------
+
+_ORACLE_CACHE = {}
+
+
+def oracle_experts(E, H, I, need, seed):
+    key = (E, H, I, seed, tuple(int(e) for e in need))
+    if key not in _ORACLE_CACHE:
+        _ORACLE_CACHE.clear()
+        _ORACLE_CACHE[key] = LazyOracleExperts(E, H, I, need, seed)
+    return _ORACLE_CACHE[key]
+
+
+def _moe_run(T, H, I, E, k, act=native.W4A16, zipf=None, seed=0, tokens=None,
+             given_globals=None, out_dtype=torch.float32, experts_needed=None):
+    x = synth.activations(T, H, seed)
+    logits = synth.router_logits(T, E, seed, zipf_s=zipf)
+    rids, rw = O.route_topk(logits, k)
+    sel = rids if tokens is None else rids[tokens]
+    need = np.unique(sel) if experts_needed is None else experts_needed
+    w_gpu = weights.synthetic_experts(E, H, I, seed, DEV, experts=np.unique(rids))
+    ids, wts, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k)
+    ag = None if given_globals is None else torch.tensor(given_globals, dtype=torch.float32,
+                                                         device=DEV)
+    y, g_out = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, wts, off, pairs, k, act=act,
+                                            act_globals=ag, out_dtype=out_dtype)
+    w_ref = oracle_experts(E, H, I, need, seed)
+    return x, rids, rw, y, g_out, w_ref, (ids, wts, off, pairs, w_gpu)
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (1, 64, 32, 4, 1), (12, 128, 96, 6, 6),
+                                       (40, 512, 256, 16, 4)])
+def test_moe_ffn_w4a16_small(T, H, I, E, k):
+    say("moe w4a16 small", T, H, I, E, k)
+    x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k)
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref)
+    assert_close_f32(to_np(y), ref, "moe w4a16")
+    # bf16 output: same kernels, rounded once
+    ids, wts, off, pairs, w_gpu = st
+    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, wts, off, pairs, k,
+                                         out_dtype=torch.bfloat16)
+    assert_bf16_output(bf16_np(yb), to_np(y), ref, "moe bf16")
+    # deterministic: a second run is bit-identical
+    y2, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, wts, off, pairs, k,
+                                         out_dtype=torch.float32)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (64, 512, 256, 16, 4)])
+def test_moe_ffn_w4a4_small(T, H, I, E, k):
+    say("moe w4a4 small", T, H, I, E, k)
+    x, rids, rw, y, g_out, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4)
+    ref, info = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True)
+    assert to_np(g_out)[0] == info["g_x"]
+    # g_h is the amax of the bf16 h, which can differ from the oracle's by a
+    # bf16 rounding flip of the largest element
+    assert abs(to_np(g_out)[1] / info["g_h"] - 1) <= 2 ** -7
+    assert_close_f32(to_np(y), ref, "moe w4a4")
+    # with the oracle's own globals given, the two runs agree as well
+    ids, wts, off, pairs, w_gpu = st
+    yg, _ = native.moe_grouped_nvfp4_ffn(
+        x.to(DEV), w_gpu, wts, off, pairs, k, act=native.W4A4,
+        act_globals=torch.tensor([info["g_x"], info["g_h"]], device=DEV), out_dtype=torch.float32)
+    refg, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True,
+                        act_globals=(info["g_x"], info["g_h"]))
+    assert_close_f32(to_np(yg), refg, "moe w4a4 given")
+
+
+def test_moe_single_expert_is_dense_mlp():
+    say("moe E=1 k=1")
+    T, H, I = 9, 256, 192
+    x, rids, rw, y, _, w_ref, _ = _moe_run(T, H, I, 1, 1)
+    ref = O.dense_mlp(x.float().numpy(), (w_ref.gate_codes[0], w_ref.gate_scales[0], w_ref.gate_global[0]),
+                      (w_ref.up_codes[0], w_ref.up_scales[0], w_ref.up_global[0]),
+                      (w_ref.down_codes[0], w_ref.down_scales[0], w_ref.down_global[0]))
+    assert_close_f32(to_np(y), ref, "dense mlp via moe")
+
+
+# ---- the full-size workloads, checked on sampled tokens ----------------------------
+
+def test_moe_decode_full_size_sampled():
+    wl = synth.MOE_DECODE
+    say("moe decode full size", wl)
+    tokens = [0, 7, 15]
+    x, rids, rw, y, _, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k, tokens=tokens)
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=tokens)
+    assert_close_f32(to_np(y)[tokens], ref, "moe decode")
+
+
+def test_moe_prefill_full_size_sampled():
+    wl = synth.MOE_PREFILL
+    say("moe prefill full size", wl)
+    tokens = [0, 1, 255, 511]
+    x, rids, rw, y, _, w_ref, st = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k, zipf=wl.zipf_s,
+                                            tokens=tokens)
+    off = to_np(st[2])
+    counts = np.diff(off)
+    say("active experts", int((counts > 0).sum()), "max tokens per expert", int(counts.max()))
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=tokens)
+    assert_close_f32(to_np(y)[tokens], ref, "moe prefill")
+
+
+def test_moe_w4a4_full_size_sampled_given_globals():
+    wl = synth.MOE_PREFILL_W4A4
+    say("moe w4a4 full size", wl)
+    x = synth.activations(wl.T, wl.H)
+    gx = O.tensor_global(x.float().numpy())
+    gh = np.float32(0.05 / 2688)       # a fixed static calibration scale for h
+    tokens = [5]
+    _, rids, rw, y, g_out, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k, act=native.W4A4,
+                                               tokens=tokens, given_globals=[gx, gh])
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True, act_globals=(gx, gh),
+                       tokens=tokens)
+    assert_close_f32(to_np(y)[tokens], ref, "moe w4a4 full")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_dense_mlp_decode_full_size(M):
+    wl = synth.WORKLOADS[f"mlp_decode_m{M}"]
+    say("dense mlp decode full size", M)
+    x, rids, rw, y, _, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, 1, 1)
+    rows = list(range(min(M, 4)))
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=rows)
+    assert_close_f32(to_np(y)[rows], ref, "dense mlp decode")

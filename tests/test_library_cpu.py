@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/nvfp4moe.h declares, and rejects bad arguments with
+the documented status before enqueuing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_routed_expert_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(native.LIB_PATH),
+                                reason="library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for call in ("nvfp4_quantize", "nvfp4_linear", "moe_route_topk", "moe_grouped_nvfp4_ffn"):
+        assert call in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(native.LIB_PATH)
+    names = declared_functions()
+    assert names and sorted(names) == sorted(native.exported_symbols())
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = native.lib()
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape"),
+                       (3, b"misaligned pointer"), (4, b"workspace too small"),
+                       (5, b"HIP error")]:
+        assert L.nvfp4_status_string(code) == text
+    assert L.nvfp4_status_string(99) == b"unknown status"
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+FAKE_MIS = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _last():
+    return native.lib().nvfp4_last_error().decode()
+
+
+def test_quantize_validation():
+    L = native.lib()
+    ws = L.nvfp4_quantize_workspace_size(4, 64)
+    assert ws > 0
+    q = lambda x, rows, cols, ld, codes, wsb, mode=0: L.nvfp4_quantize(
+        x, 0, rows, cols, ld, codes, FAKE, FAKE, mode, FAKE, wsb, None)
+    assert q(None, 4, 64, 64, FAKE, ws) == 1 and "x is NULL" in _last()
+    assert q(FAKE, 4, 48, 48, FAKE, ws) == 2 and "multiple of 32" in _last()
+    assert q(FAKE, 0, 64, 64, FAKE, ws) == 1
+    assert q(FAKE, 4, 64, 32, FAKE, ws) == 1 and "ld_x" in _last()
+    assert q(FAKE, 4, 64, 64, FAKE_MIS, ws) == 3 and "codes" in _last()
+    assert q(FAKE, 4, 64, 64, FAKE, ws - 1) == 4
+    assert q(FAKE, 4, 64, 64, FAKE, ws, mode=7) == 1
+
+
+def test_linear_validation():
+    L = native.lib()
+    m = native.Matrix(FAKE.value, FAKE.value, FAKE.value, 64, 96)   # K = 96 fine
+    ws = L.nvfp4_linear_workspace_size(4, 64, 96, 0)
+    lin = lambda M, mat, act=0, y=FAKE, wsb=ws: L.nvfp4_linear(
+        FAKE, M, ctypes.byref(mat), act, 0, None, y, 0, FAKE, wsb, None)
+    assert lin(0, m) == 1
+    bad = native.Matrix(FAKE.value, FAKE.value, FAKE.value, 64, 80)
+    assert lin(4, bad) == 2
+    assert lin(4, m, act=3) == 1
+    assert lin(4, m, y=None) == 1
+    assert lin(4, m, y=FAKE_MIS) == 3
+    assert lin(4, m, wsb=ws - 256) == 4
+    nullm = native.Matrix(None, FAKE.value, FAKE.value, 64, 96)
+    assert lin(4, nullm) == 1 and "codes" in _last()
+    # W4A4 with a given scale needs the pointer
+    assert L.nvfp4_linear(FAKE, 4, ctypes.byref(m), 1, 1, None, FAKE, 0, FAKE, ws, None) == 1
+
+
+def test_route_validation():
+    L = native.lib()
+    r = lambda T, E, k, logits=FAKE: L.moe_route_topk(logits, T, E, k, 1, FAKE, FAKE, FAKE,
+                                                      FAKE, None, 0, None)
+    assert r(16, 512, 0) == 2
+    assert r(16, 8, 9) == 2
+    assert r(16, 2048, 8) == 2
+    assert r(16, 64, 33) == 2
+    assert r(0, 64, 8) == 1
+    assert r(16, 64, 8, logits=None) == 1
+    assert r(16, 64, 8, logits=FAKE_MIS) == 3
+    assert r((1 << 22), 64, 8) == 2
+
+
+def test_ffn_validation():
+    L = native.lib()
+    w = native.ExpertWeightsC(*([FAKE.value] * 9))
+    T, H, I, E, k = 16, 256, 128, 8, 2
+    ws = L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, 0)
+    assert ws > 0
+    f = lambda T=T, H=H, I=I, E=E, k=k, wsb=ws, ww=w, act=0: L.moe_grouped_nvfp4_ffn(
+        FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, ctypes.byref(ww), act, 0, None, FAKE, 0,
+        FAKE, wsb, None)
+    assert f(H=250) == 2
+    assert f(I=100) == 2
+    assert f(k=9) == 2
+    assert f(T=0) == 1
+    assert f(wsb=ws - 1) == 4
+    assert f(act=5) == 1
+    bad = native.ExpertWeightsC(*([FAKE.value] * 8 + [None]))
+    assert f(ww=bad) == 1 and "down_global" in _last()
+    mis = native.ExpertWeightsC(*([FAKE_MIS.value] + [FAKE.value] * 8))
+    assert f(ww=mis) == 3
+    # a W4A4 call with given globals needs them
+    assert L.moe_grouped_nvfp4_ffn(FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, ctypes.byref(w), 1, 1,
+                                   None, FAKE, 0, FAKE, ws, None) == 1
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(native, "_LIB", None)
+    monkeypatch.setattr(native, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        native.lib()
