@@ -190,7 +190,8 @@ size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I,
  * events[2*s] on its stream just before stage s and events[2*s+1] just after
  * it, for the NVFP4_FFN_STAGES stages below; the caller creates the events
  * (hipEventCreate) and reads them with hipEventElapsedTime.  NULL disables
- * recording.  The setting is per thread and holds no other state.
+ * recording.  Nothing is recorded while the stream is being captured into a
+ * graph.  The setting is per thread and holds no other state.
  */
 enum {
   NVFP4_STAGE_PLAN = 0,     /* m-block list from the expert offsets              */

@@ -15,8 +15,12 @@ thread_local char g_last_error[512] = "";
 thread_local hipEvent_t *g_stage_events = nullptr;
 
 // Records the profiling event of stage s (before: 2s, after: 2s+1), if set.
+// Nothing is recorded while the stream is being captured into a graph.
 void mark(int s, bool after, hipStream_t stream) {
-  if (g_stage_events) (void)hipEventRecord(g_stage_events[2 * s + (after ? 1 : 0)], stream);
+  if (!g_stage_events) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  (void)hipEventRecord(g_stage_events[2 * s + (after ? 1 : 0)], stream);
 }
 
 nvfp4_status fail(nvfp4_status st, const char *fmt, ...) {
@@ -117,10 +121,12 @@ struct FfnWs {
   float *ypair;
   int4 *mblocks;
   int32_t *n_mblocks;
-  uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h
+  uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h, [3] -
   float *partials;
 };
-int ffn_bm(int64_t T, int64_t E, int64_t k) { return gemm_block_rows(2 * T * k / E); }
+int ffn_bm(int64_t T, int64_t E, int64_t k) {
+  return 2 * T * k <= 32 * E ? 16 : gemm_block_rows(2 * T * k / E);
+}
 int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) { return (P + bm - 1) / bm + E; }
 FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t P = T * k;
@@ -137,6 +143,9 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.partials = c.take<float>(kMaxPartials);
   return w;
 }
+// Small tiles (decode): experts average at most 16 pairs, so the small-M
+// GEMV with split K runs both projections.
+bool ffn_small(int64_t T, int64_t E, int64_t k) { return 2 * T * k <= 32 * E; }
 
 }  // namespace
 
@@ -418,30 +427,52 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   float *slot_gx = reinterpret_cast<float *>(ws.slots + 1);
   float *slot_gh = reinterpret_cast<float *>(ws.slots + 2);
 
-  // 1. plan (m-blocks per expert) and zeroed |h| maximum
-  mark(NVFP4_STAGE_PLAN, false, stream);
-  LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots, 1, stream),
-         "plan");
-  mark(NVFP4_STAGE_PLAN, true, stream);
-  // 2. activation rows -> fp16 operands
-  mark(NVFP4_STAGE_X_PREP, false, stream);
+  const bool small = ffn_small(T, E, k);
+  const OutType yt = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
   const uint16_t *xb = static_cast<const uint16_t *>(x);
-  if (!a4) {
-    LAUNCH(launch_row_prep(xb, T, H, PrepMode::SHIFT, ws.x16, ws.xshift, nullptr, 0, nullptr,
-                           nullptr, nullptr, stream),
-           "x prep");
-  } else if (given) {
-    LAUNCH(launch_row_prep(xb, T, H, PrepMode::QUANT, ws.x16, nullptr, nullptr, 0, act_globals,
-                           slot_gx, nullptr, stream),
-           "x quant");
+  const int64_t zero_words = 4;
+
+  // W4A16 decode: both projections stream whole weight rows against the bf16
+  // activations as given (no fp16 operand passes)
+  const bool rows = small && !a4 && row_gemv_supported((int)H) && row_gemv_supported((int)I);
+
+  // 1-2. plan (m-blocks per expert), zeroed scratch words and x -> fp16 rows
+  if (rows) {
+    mark(NVFP4_STAGE_PLAN, false, stream);
+    LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
+                           (int)zero_words, stream),
+           "plan");
+    mark(NVFP4_STAGE_PLAN, true, stream);
+    mark(NVFP4_STAGE_X_PREP, false, stream);
+    mark(NVFP4_STAGE_X_PREP, true, stream);
+  } else if (!a4) {
+    mark(NVFP4_STAGE_PLAN, false, stream);
+    mark(NVFP4_STAGE_PLAN, true, stream);
+    mark(NVFP4_STAGE_X_PREP, false, stream);
+    LAUNCH(launch_moe_prep(xb, T, H, ws.x16, ws.xshift, expert_offsets, E, bm, ws.mblocks,
+                           ws.n_mblocks, ws.slots, zero_words, stream),
+           "plan + x prep");
+    mark(NVFP4_STAGE_X_PREP, true, stream);
   } else {
-    const int n = amax_partials_grid(T, H);
-    LAUNCH(launch_amax_partials(x, InType::BF16, T, H, H, ws.partials, n, stream), "x amax");
-    LAUNCH(launch_row_prep(xb, T, H, PrepMode::QUANT, ws.x16, nullptr, ws.partials, n, nullptr,
-                           slot_gx, act_globals, stream),
-           "x quant");
+    mark(NVFP4_STAGE_PLAN, false, stream);
+    LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
+                           (int)zero_words, stream),
+           "plan");
+    mark(NVFP4_STAGE_PLAN, true, stream);
+    mark(NVFP4_STAGE_X_PREP, false, stream);
+    if (given) {
+      LAUNCH(launch_row_prep(xb, T, H, PrepMode::QUANT, ws.x16, nullptr, nullptr, 0, act_globals,
+                             slot_gx, nullptr, stream),
+             "x quant");
+    } else {
+      const int n = amax_partials_grid(T, H);
+      LAUNCH(launch_amax_partials(x, InType::BF16, T, H, H, ws.partials, n, stream), "x amax");
+      LAUNCH(launch_row_prep(xb, T, H, PrepMode::QUANT, ws.x16, nullptr, ws.partials, n, nullptr,
+                             slot_gx, act_globals, stream),
+             "x quant");
+    }
+    mark(NVFP4_STAGE_X_PREP, true, stream);
   }
-  mark(NVFP4_STAGE_X_PREP, true, stream);
   // 3. gate/up grouped GEMM with the SiLU * up epilogue -> h (bf16, expert-sorted rows)
   GemmArgs g = {};
   g.A = ws.x16;
@@ -467,15 +498,26 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.ldo = I;
   g.out_type = OutType::BF16;
   g.amax_slot = a4 ? ws.slots : nullptr;
+  if (rows) {
+    g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
+    g.a_shift = nullptr;
+  }
   mark(NVFP4_STAGE_GATE_UP, false, stream);
-  LAUNCH(launch_gemm(Epi::SWIGLU, g, bm, stream), "gate/up");
+  if (rows)
+    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, stream), "gate/up");
+  else if (small)
+    LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
+  else
+    LAUNCH(launch_gemm(Epi::SWIGLU, g, bm, stream), "gate/up");
   mark(NVFP4_STAGE_GATE_UP, true, stream);
-  // 4. h rows -> fp16 operands
+  // 4. h rows -> fp16 operands (W4A16 small tiles convert inside the down kernel)
   mark(NVFP4_STAGE_H_PREP, false, stream);
+  const bool h_inline = small && !a4;
   if (!a4) {
-    LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::SHIFT, ws.h16, ws.hshift, nullptr, 0, nullptr,
-                           nullptr, nullptr, stream),
-           "h prep");
+    if (!h_inline && !rows)
+      LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::SHIFT, ws.h16, ws.hshift, nullptr, 0, nullptr,
+                             nullptr, nullptr, stream),
+             "h prep");
   } else if (given) {
     LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::QUANT, ws.h16, nullptr, nullptr, 0,
                            act_globals + 1, slot_gh, nullptr, stream),
@@ -489,9 +531,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   mark(NVFP4_STAGE_H_PREP, true, stream);
   // 5. down grouped GEMM, weighted by the routing weight -> Y per pair (fp32)
   GemmArgs d = {};
-  d.A = ws.h16;
+  d.A = h_inline ? reinterpret_cast<const _Float16 *>(ws.h) : ws.h16;
   d.lda = I;
-  d.a_shift = a4 ? nullptr : ws.hshift;
+  d.a_shift = (a4 || h_inline) ? nullptr : ws.hshift;
   d.b_codes[0] = w->down_codes;
   d.b_scales[0] = w->down_scales;
   d.b_global[0] = w->down_global;
@@ -509,13 +551,18 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.pair_weights = topk_weights;
   d.sorted_pairs = sorted_pairs;
   mark(NVFP4_STAGE_DOWN, false, stream);
-  LAUNCH(launch_gemm(Epi::DOWN, d, bm, stream), "down");
+  if (rows) {
+    d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
+    d.a_shift = nullptr;
+    LAUNCH(launch_row_gemv(Epi::DOWN, d, stream), "down");
+  } else if (small)
+    LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
+  else
+    LAUNCH(launch_gemm(Epi::DOWN, d, bm, stream), "down");
   mark(NVFP4_STAGE_DOWN, true, stream);
   // 6. combine the k pairs of every token in slot order
   mark(NVFP4_STAGE_COMBINE, false, stream);
-  LAUNCH(launch_combine(ws.ypair, T, H, k, y,
-                        y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16, stream),
-         "combine");
+  LAUNCH(launch_combine(ws.ypair, T, H, k, y, yt, stream), "combine");
   mark(NVFP4_STAGE_COMBINE, true, stream);
   return NVFP4_OK;
 }

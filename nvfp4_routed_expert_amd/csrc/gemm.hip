@@ -209,15 +209,15 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// One workgroup: m-blocks of up to bm rows for every expert with pairs.
-__global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, int E, int bm,
-                                                        int4 *mblocks, int32_t *n_mblocks,
-                                                        uint32_t *zero, int zero_words) {
+// m-blocks of up to bm rows for every expert with pairs, built by one
+// workgroup of any size (multiple of 64, at most 1024 threads).
+__device__ void build_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
+                           int32_t *n_mblocks) {
   __shared__ int32_t wave_tot[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < zero_words; i += 1024) zero[i] = 0u;
+  const int nthreads = blockDim.x, nwaves = nthreads >> 6;
   int run = 0;   // m-blocks of experts handled by earlier passes
-  for (int e0 = 0; e0 < E; e0 += 1024) {
+  for (int e0 = 0; e0 < E; e0 += nthreads) {
     const int e = e0 + tid;
     int lo = 0, c = 0;
     if (e < E) {
@@ -235,17 +235,64 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, 
     __syncthreads();
     int wbase = run;
     for (int w = 0; w < wave; ++w) wbase += wave_tot[w];
-    int first = wbase + incl - nb;
+    const int first = wbase + incl - nb;
     for (int b = 0; b < nb; ++b) {
       const int r0 = b * bm;
       mblocks[first + b] = int4{e, lo + r0, (c - r0) < bm ? (c - r0) : bm, 0};
     }
     int total = 0;
-    for (int w = 0; w < 16; ++w) total += wave_tot[w];
+    for (int w = 0; w < nwaves; ++w) total += wave_tot[w];
     __syncthreads();
     run += total;
   }
   if (tid == 0) *n_mblocks = run;
+}
+
+__global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, int E, int bm,
+                                                        int4 *mblocks, int32_t *n_mblocks,
+                                                        uint32_t *zero, int zero_words) {
+  for (int i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
+  build_plan(offsets, E, bm, mblocks, n_mblocks);
+}
+
+// Blocks 0 .. ceil(T/4)-1: one wavefront per x row -> fp16 with its
+// power-of-two shift (as the row preparation kernel's SHIFT mode).  The last
+// block builds the plan and zeroes the scratch words.
+__global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_t T, int64_t H,
+                                                       _Float16 *x16, int32_t *xshift,
+                                                       const int32_t *offsets, int E, int bm,
+                                                       int4 *mblocks, int32_t *n_mblocks,
+                                                       uint32_t *zero, int64_t zero_words) {
+  if (blockIdx.x == gridDim.x - 1) {
+    for (int64_t i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
+    build_plan(offsets, E, bm, mblocks, n_mblocks);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= T) return;
+  const uint16_t *row = x + r * H;
+  float m = 0.0f;
+  for (int64_t c = lane * 8; c < H; c += 512) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      m = fmaxf(m, fmaxf(__builtin_fabsf(__uint_as_float(w[i] << 16)),
+                         __builtin_fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
+  }
+  m = wave_max(m);
+  const int s = m > 0.0f ? exponent_of(m) - 15 : 0;
+  for (int64_t c = lane * 8; c < H; c += 512) {
+    const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c);
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = (_Float16)__builtin_ldexpf(__uint_as_float(w[i] << 16), -s);
+      h[2 * i + 1] = (_Float16)__builtin_ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -s);
+    }
+    *reinterpret_cast<f16x8 *>(x16 + r * H + c) = h;
+  }
+  if (lane == 0) xshift[r] = s;
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *ypair, int64_t T, int64_t H,
@@ -293,6 +340,16 @@ hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
                            hipStream_t s) {
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, mblocks,
                      n_mblocks, zero, zero_words);
+  return hipGetLastError();
+}
+
+hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x16,
+                           int32_t *xshift, const int32_t *offsets, int E, int bm,
+                           int4 *mblocks, int32_t *n_mblocks, uint32_t *zero,
+                           int64_t zero_words, hipStream_t s) {
+  const int64_t blocks = (T + 3) / 4 + 1;
+  hipLaunchKernelGGL(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16,
+                     xshift, offsets, E, bm, mblocks, n_mblocks, zero, zero_words);
   return hipGetLastError();
 }
 

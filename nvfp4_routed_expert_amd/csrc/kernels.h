@@ -88,6 +88,26 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
+
+// Small-M grouped GEMV (tiles of 16 rows): waves of a workgroup split K and
+// keep several 128-wide chunks of weight loads in flight.  a_bf16: A rows are
+// bf16 and each workgroup derives their power-of-two shift from the row
+// maximum itself.  Output tiles are gemv_tile_cols(epi, N, K) columns wide.
+hipError_t launch_gemv(Epi epi, const GemmArgs &a, bool a_bf16, hipStream_t s);
+int gemv_tile_cols(Epi epi, int N, int K);
+
+// Row-streaming GEMV for W4A16 decode: A rows are bf16 (used as given), the
+// tile rows of each m-block are processed in small groups.  Supported K:
+// 256, 512, 1024 and 2048..8192 (multiples of 32).
+bool row_gemv_supported(int K);
+hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, hipStream_t s);
+
+// FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
+// workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.
+hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x16,
+                           int32_t *xshift, const int32_t *offsets, int E, int bm,
+                           int4 *mblocks, int32_t *n_mblocks, uint32_t *zero,
+                           int64_t zero_words, hipStream_t s);
 int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
 
 // FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.
