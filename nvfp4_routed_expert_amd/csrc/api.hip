@@ -120,6 +120,7 @@ struct FfnWs {
   int32_t *hshift;
   float *ypair;
   int4 *mblocks;
+  int4 *pair_info;      // per expert-sorted position: {expert, token, pair, 0}
   int32_t *n_mblocks;
   uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h, [3] -
   float *partials;
@@ -138,6 +139,7 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.hshift = c.take<int32_t>((size_t)P);
   w.ypair = c.take<float>((size_t)(P * H));
   w.mblocks = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
+  w.pair_info = c.take<int4>((size_t)P);
   w.n_mblocks = c.take<int32_t>(4);
   w.slots = c.take<uint32_t>(4);
   w.partials = c.take<float>(kMaxPartials);
@@ -280,6 +282,22 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   Carver c(workspace);
   const LinearWs ws = carve_linear(c, M, K);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
+  // decode-sized W4A16: stream the weight rows against the bf16 rows as given
+  if (act == NVFP4_W4A16 && M <= 16 && row_gemv_supported((int)K)) {
+    GemmArgs a = {};
+    a.A = static_cast<const _Float16 *>(x);
+    a.lda = K;
+    a.b_codes[0] = w->codes;
+    a.b_scales[0] = w->scales;
+    a.b_global[0] = w->global_scale;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.out = y;
+    a.ldo = N;
+    a.out_type = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
+    LAUNCH(launch_row_gemv(Epi::LINEAR, a, nullptr, (int)M, stream), "row gemv");
+    return NVFP4_OK;
+  }
   if (act == NVFP4_W4A16) {
     LAUNCH(launch_row_prep(xb, M, K, PrepMode::SHIFT, ws.x16, ws.shift, nullptr, 0, nullptr,
                            nullptr, nullptr, stream),
@@ -440,7 +458,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   if (rows) {
     mark(NVFP4_STAGE_PLAN, false, stream);
     LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
-                           (int)zero_words, stream),
+                           (int)zero_words, sorted_pairs, k, ws.pair_info, stream),
            "plan");
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
@@ -456,7 +474,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   } else {
     mark(NVFP4_STAGE_PLAN, false, stream);
     LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
-                           (int)zero_words, stream),
+                           (int)zero_words, nullptr, k, nullptr, stream),
            "plan");
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
@@ -504,7 +522,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   }
   mark(NVFP4_STAGE_GATE_UP, false, stream);
   if (rows)
-    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, stream), "gate/up");
+    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, ws.pair_info, (int)P, stream), "gate/up");
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
   else
@@ -554,7 +572,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   if (rows) {
     d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
     d.a_shift = nullptr;
-    LAUNCH(launch_row_gemv(Epi::DOWN, d, stream), "down");
+    LAUNCH(launch_row_gemv(Epi::DOWN, d, ws.pair_info, (int)P, stream), "down");
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else

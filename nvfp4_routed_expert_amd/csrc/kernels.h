@@ -96,11 +96,14 @@ hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
 hipError_t launch_gemv(Epi epi, const GemmArgs &a, bool a_bf16, hipStream_t s);
 int gemv_tile_cols(Epi epi, int N, int K);
 
-// Row-streaming GEMV for W4A16 decode: A rows are bf16 (used as given), the
-// tile rows of each m-block are processed in small groups.  Supported K:
-// 256, 512, 1024 and 2048..8192 (multiples of 32).
+// Row-streaming GEMV for W4A16 decode: A rows are bf16 (used as given).
+// Work items are (tile row, block of output rows); tile row pos has the
+// descriptor info[pos] = {expert, token, pair, 0} (info == null: a dense
+// matrix, all three equal pos).  n_pos tile rows.  Supported K: 256, 512,
+// 1024 and 2048..8192 (multiples of 32).
 bool row_gemv_supported(int K);
-hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, hipStream_t s);
+hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int4 *info, int n_pos,
+                           hipStream_t s);
 
 // FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
 // workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.
@@ -111,8 +114,12 @@ hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x1
 int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
 
 // FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.
+// With pair_info != null it also writes, for every expert-sorted position
+// pos < offsets[E], pair_info[pos] = {expert, token, pair, 0} (k slots per
+// token, pair = sorted_pairs[pos]).
 hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
                            int32_t *n_mblocks, uint32_t *zero, int zero_words,
+                           const int32_t *sorted_pairs, int k, int4 *pair_info,
                            hipStream_t s);
 
 // y[t] = sum_j Y[t*k + j], j ascending, fp32 -> out type.

@@ -8,20 +8,25 @@
 //
 //  * a wavefront reads whole weight rows: for K >= 2048 each of its 64 lanes
 //    takes 16 code bytes (32 elements) of a 2048-wide slice, so every load
-//    instruction moves one contiguous KiB; for K = 512 / 1024 / 256 a load
-//    covers 4 / 2 / 8 rows.  Workgroups of KS = ceil(K / 2048) waves split
+//    instruction moves one contiguous KiB; for K = 1024 / 512 / 256 a load
+//    covers 2 / 4 / 8 rows.  Workgroups of KS = ceil(K / 2048) waves split
 //    longer rows and add their partial sums in LDS in a fixed wave order.
 //  * each lane's activation slice (the same K positions for every row of the
 //    item) is loaded once per item and stays in registers, in bf16 as given;
 //  * codes become exact bf16 pairs (v_cvt_scalef32_pk_bf16_fp4, unit scale),
 //    multiply the activations in v_dot2_f32_bf16, and each 16-element block
 //    sum is scaled once by its E4M3 scale (v_cvt_scalef32_pk_f32_fp8);
-//  * D row steps of loads are kept in flight ahead of the arithmetic.
-// Row sums across lanes use a fixed butterfly, so results are deterministic.
+//  * eight load steps are kept in flight (a branch-free steady state, so the
+//    waits count outstanding loads exactly), and the eight steps' partial
+//    sums are reduced across lanes together by one butterfly built from
+//    gfx950's v_permlane32_swap / v_permlane16_swap and DPP row moves.
+// The butterfly's order is fixed, so results are deterministic.
 //
-// Items: (m-block of up to 16 tile rows of one expert, block of output rows).
-// Tile rows are processed in groups of TOK; a block with more rows streams
-// its weights once per group.
+// Each tile row (one token of one expert) is its own work item per block of
+// output rows, so an expert with several tokens streams its rows once per
+// token; the repeats are close in time and mostly hit L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -32,254 +37,317 @@ namespace nvfp4 {
 namespace {
 
 constexpr int kSlice = 2048;   // K elements covered by one wave (64 lanes x 32)
+constexpr int kBatch = 8;      // load steps in flight and reduced together
 
-// Dot product of the 8 E2M1 codes in `word` (as exact bf16 pairs) with
-// 8 bf16 activations (4 pairs), accumulated into acc.
-__device__ __forceinline__ float dot8(uint32_t word, const uint32_t *a, float acc) {
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 0),
-                                        __builtin_bit_cast(bf16x2_t, a[0]), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 1),
-                                        __builtin_bit_cast(bf16x2_t, a[1]), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 2),
-                                        __builtin_bit_cast(bf16x2_t, a[2]), acc, false);
-  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, 3),
-                                        __builtin_bit_cast(bf16x2_t, a[3]), acc, false);
-  return acc;
+// ---------------------------------------------------------------------------
+// arithmetic
+// ---------------------------------------------------------------------------
+
+// 32 codes of one lane -> 16 exact bf16 pairs
+__device__ __forceinline__ void decode32(const u32x4 codes, uint32_t (&w)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 0));
+    w[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 1));
+    w[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 2));
+    w[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 3));
+  }
 }
 
-// 32 codes (two 16-element blocks with decoded scales s0, s1) against 32
-// bf16 activations: each block sum is formed first, then scaled once.
-__device__ __forceinline__ float dot32(const u32x4 codes, const uint32_t (&a)[16], float s0,
+// sum over two 16-element blocks, each block sum scaled once by its scale
+__device__ __forceinline__ float dot32(const uint32_t (&w)[16], const uint32_t (&a)[16], float s0,
                                        float s1) {
-  const float b0 = dot8(codes[1], a + 4, dot8(codes[0], a + 0, 0.0f));
-  const float b1 = dot8(codes[3], a + 12, dot8(codes[2], a + 8, 0.0f));
+  float b0 = 0.0f, b1 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    b0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]),
+                                         __builtin_bit_cast(bf16x2_t, a[i]), b0, false);
+#pragma unroll
+  for (int i = 8; i < 16; ++i)
+    b1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]),
+                                         __builtin_bit_cast(bf16x2_t, a[i]), b1, false);
   return b0 * s0 + b1 * s1;
 }
 
-// Sum over each row of 16 lanes (or 8 when LPR == 8) with DPP moves; every
-// lane of the row ends with the row's sum.  Fixed order: deterministic.
+// ---------------------------------------------------------------------------
+// cross-lane butterfly over 8 values per lane
+// ---------------------------------------------------------------------------
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
                                                                0xF, 0xF, false));
 }
-
-template <int LPR>
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f32<0xB1>(v);                          // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp_f32<0x4E>(v);                          // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp_f32<0x141>(v);                         // row_half_mirror: the other quad of 8
-  if constexpr (LPR >= 16) v += dpp_f32<0x140>(v);   // row_mirror: the other 8 of 16
-  return v;
+__device__ __forceinline__ void swap32(float &a, float &b) {   // a=[a_lo,b_lo], b=[a_hi,b_hi]
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {   // odd 16-rows of a <-> even of b
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  a = __builtin_bit_cast(float, (uint32_t)r[0]);
+  b = __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+// One level of the butterfly at lane distance 8, 4 or 2 (the partner differs
+// in that lane bit): lanes with the bit set keep index hi, the others lo.
+template <int CTRL, int BIT>
+__device__ __forceinline__ float pair_level(float lo, float hi, int lane) {
+  const bool up = (lane >> BIT) & 1;
+  return (up ? hi : lo) + dpp_f32<CTRL>(up ? lo : hi);
 }
 
-__device__ __forceinline__ float lane_value(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-
-// The full sum of weight row u (0 <= u < 64/LPR) of a load step, wave-uniform:
-// per-16-lane sums combined in lane order.
-template <int LPR>
-__device__ __forceinline__ float row_total(float v16, int u) {
-  if constexpr (LPR == 64) {
-    return (lane_value(v16, 0) + lane_value(v16, 16)) + (lane_value(v16, 32) + lane_value(v16, 48));
-  } else if constexpr (LPR == 32) {
-    return lane_value(v16, 32 * u) + lane_value(v16, 32 * u + 16);
+// v[0..7]: per-lane partial sums of 8 values.  Returns, in every lane, the
+// total over the lane's aligned group of G lanes of value idx(lane):
+//   G = 64: idx = lane >> 3        G = 32: idx = (lane >> 2) & 7
+//   G = 16: idx = (lane >> 1) & 7  G = 8:  idx = lane & 7
+template <int G>
+__device__ __forceinline__ float reduce8(float (&v)[8], int lane) {
+  // 8 -> 4 values
+  if constexpr (G == 64) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { swap32(v[j], v[j + 4]); v[j] += v[j + 4]; }
+  } else if constexpr (G == 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { swap16(v[j], v[j + 4]); v[j] += v[j + 4]; }
+  } else if constexpr (G == 16) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = pair_level<0x128, 3>(v[j], v[j + 4], lane);   // row_ror:8
   } else {
-    return lane_value(v16, LPR * u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = pair_level<0x141, 2>(v[j], v[j + 4], lane);   // half mirror
   }
+  // 4 -> 2 values
+  if constexpr (G == 64) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) { swap16(v[j], v[j + 2]); v[j] += v[j + 2]; }
+  } else if constexpr (G == 32) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) v[j] = pair_level<0x128, 3>(v[j], v[j + 2], lane);
+  } else if constexpr (G == 16) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) v[j] = pair_level<0x141, 2>(v[j], v[j + 2], lane);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) v[j] = pair_level<0x4E, 1>(v[j], v[j + 2], lane);    // lane ^ 2
+  }
+  // 2 -> 1 value
+  float r;
+  if constexpr (G == 64) r = pair_level<0x128, 3>(v[0], v[1], lane);
+  else if constexpr (G == 32) r = pair_level<0x141, 2>(v[0], v[1], lane);
+  else if constexpr (G == 16) r = pair_level<0x4E, 1>(v[0], v[1], lane);
+  else r = pair_level<0xB1, 0>(v[0], v[1], lane);                                     // lane ^ 1
+  // plain sums over the lanes still holding the same value
+  if constexpr (G == 64) r += dpp_f32<0x141>(r);
+  if constexpr (G == 64 || G == 32) r += dpp_f32<0x4E>(r);
+  if constexpr (G >= 16) r += dpp_f32<0xB1>(r);
+  return r;
 }
 
-// LPR: lanes per weight row (64, 32, 16 or 8); TOK: tile rows per pass;
-// D: load steps in flight; NMAT: 2 for gate/up (SWIGLU), else 1.
-// rows_per_item must be a multiple of D * (64 / LPR) and at most 64.
-template <int LPR, int TOK, int D, Epi EPI>
-__global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, int rows_per_item) {
-  constexpr int NMAT = EPI == Epi::SWIGLU ? 2 : 1;
-  constexpr int RPL = 64 / LPR;                     // rows per load instruction
-  __shared__ float red[3][NMAT * TOK * 64];         // partial row sums of waves 1..3
+// ---------------------------------------------------------------------------
+// the kernel
+// ---------------------------------------------------------------------------
+//
+// Work is a flat list of items: item i = (tile row pos = i / groups, group g
+// = i % groups of rows_per_item consecutive output rows).  A tile row's
+// expert, token and pair come from one 16-byte descriptor (built by the FFN
+// plan; absent for a dense matrix, where all three are pos).  Each unit of KS
+// waves walks items u, u + U, u + 2U, ... (U units in the grid) and keeps the
+// next item's weight loads in flight while it computes the current one; the
+// descriptor is fetched two items ahead and the activation slice one ahead.
+// Consecutive units take consecutive row groups, so concurrently running
+// waves read neighbouring rows of the same expert.
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, ks = blockDim.x >> 6;
+template <int LPR, Epi EPI>
+struct RowCfg {
+  static constexpr int NMAT = EPI == Epi::SWIGLU ? 2 : 1;
+  static constexpr int RPL = 64 / LPR;             // weight rows per load step
+  static constexpr int G = LPR;                    // lanes reduced together
+  static constexpr int DUP = LPR / kBatch;         // lanes holding the same result
+  static constexpr int ROWS = kBatch * RPL;        // output rows per item
+};
+
+__device__ __forceinline__ int4 item_info(const int4 *info, int pos) {
+  return info ? info[pos] : int4{0, pos, pos, 0};
+}
+
+template <int LPR, Epi EPI>
+__global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const int4 *info,
+                                                       int n_pos) {
+  using C = RowCfg<LPR, EPI>;
+  constexpr int NMAT = C::NMAT;
+  __shared__ float red[3 * NMAT * 64];   // partial row sums of waves 1..3 of a unit
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = p.K, N = p.N;
-  const int sub = lane / LPR, seg = lane % LPR;     // row within a step, 32-element segment
-  const int kseg = wave * kSlice + 32 * seg;        // first K element of this lane
+  const int ks = (K + kSlice - 1) / kSlice;               // waves per unit (K slices)
+  const int units_per_wg = (int)(blockDim.x >> 6) / ks;
+  const int kw = wave % ks;                               // this wave's K slice
+  const int unit = blockIdx.x * units_per_wg + wave / ks;
+  const int n_units = gridDim.x * units_per_wg;
+  const int sub = lane / LPR, seg = lane % LPR;
+  const int kseg = kw * kSlice + 32 * seg;
   const bool kval = kseg < K;
+  const uint32_t kc = (uint32_t)min(kseg, K - 32);        // clamped: masked lanes read valid bytes
   const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
-  const uint32_t kc = (uint32_t)min(kseg, K - 32);  // clamped: masked lanes read valid bytes
-  const int row_blocks = (N + rows_per_item - 1) / rows_per_item;
-  const int n_mb = p.n_mblocks_dev ? *p.n_mblocks_dev : p.n_mblocks;
-  const int n_items = n_mb * row_blocks;
-  const int steps = rows_per_item / RPL;            // a multiple of D
+  const int groups = (N + C::ROWS - 1) / C::ROWS;
+  const int n_items = n_pos * groups;
+  if (unit >= n_items) return;                            // whole unit idle (uniform)
 
-  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int mb = item / row_blocks, rb = item - mb * row_blocks;
-    int e = 0, pos0, nrows;
-    if (p.mblocks) {
-      const int4 blk = p.mblocks[mb];
-      e = blk.x;
-      pos0 = blk.y;
-      nrows = blk.z;
-    } else {
-      pos0 = mb * 16;
-      nrows = (int)(p.dense_rows - pos0 < 16 ? p.dense_rows - pos0 : 16);
-    }
-    const int r0 = rb * rows_per_item;
-    const uint8_t *cbase[2], *sbase[2];
+  const uint8_t *cbase[2] = {p.b_codes[0], p.b_codes[NMAT - 1]};
+  const uint8_t *sbase[2] = {p.b_scales[0], p.b_scales[NMAT - 1]};
+  const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
+
+  // item geometry: byte offsets of this lane's first row
+  struct Geo {
+    uint32_t code, scale;   // within the expert's matrix
+    int64_t ecode, escale;  // expert base offsets
+    int e, r0, pos;
+    int4 inf;
+  };
+  auto geo = [&](int item, int4 inf) {
+    Geo gm;
+    gm.pos = item / groups;
+    gm.r0 = (item - gm.pos * groups) * C::ROWS;
+    gm.inf = inf;
+    gm.e = inf.x;
+    gm.ecode = (int64_t)gm.e * p.b_codes_estride;
+    gm.escale = (int64_t)gm.e * p.b_scales_estride;
+    gm.code = (uint32_t)(gm.r0 + sub) * code_row + kc / 2;
+    gm.scale = (uint32_t)(gm.r0 + sub) * scale_row + kc / 16;
+    return gm;
+  };
+  const uint32_t last_code = (uint32_t)(N - 1) * code_row + kc / 2;
+  const uint32_t last_scale = (uint32_t)(N - 1) * scale_row + kc / 16;
+  const uint32_t step_code = (uint32_t)C::RPL * code_row, step_scale = (uint32_t)C::RPL * scale_row;
+
+  u32x4 bq[kBatch][NMAT];
+  uint32_t sq[kBatch][NMAT];
+  auto load_step = [&](const Geo &gm, int d) {
+    const uint32_t oc = min(gm.code + (uint32_t)d * step_code, last_code);
+    const uint32_t os = min(gm.scale + (uint32_t)d * step_scale, last_scale);
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
-      cbase[m] = p.b_codes[m] + (int64_t)e * p.b_codes_estride;
-      sbase[m] = p.b_scales[m] + (int64_t)e * p.b_scales_estride;
+      bq[d][m] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(cbase[m] + gm.ecode + oc));
+      sq[d][m] = *reinterpret_cast<const uint16_t *>(sbase[m] + gm.escale + os);
     }
-    float gsc[2];
+  };
+  auto load_a = [&](const Geo &gm, uint32_t (&a)[16]) {
+    const int arow = EPI == Epi::SWIGLU ? gm.inf.y : gm.pos;
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(p.A) + (int64_t)arow * p.lda + kc;
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m) gsc[m] = p.b_global[m][e];
-    const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
-    // per-lane byte offsets of this lane's first row (steps add RPL rows)
-    const uint32_t lane_code = (uint32_t)(r0 + sub) * code_row + kc / 2;
-    const uint32_t lane_scale = (uint32_t)(r0 + sub) * scale_row + kc / 16;
-    const uint32_t last_code = (uint32_t)(N - 1) * code_row + kc / 2;
-    const uint32_t last_scale = (uint32_t)(N - 1) * scale_row + kc / 16;
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 8 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[4 * q + j] = v[j];
+    }
+  };
+  // later items than the last are clamped to the last (valid, never written)
+  auto clamp = [&](int item) { return item < n_items ? item : n_items - 1; };
 
-    for (int t0 = 0; t0 < nrows; t0 += TOK) {
-      // ---- activation slices of this group's tile rows (bf16, zero if absent)
-      uint32_t a[TOK][16];
+  // prologue: item i0 loaded, descriptor of i0 + U known
+  int item = unit;
+  Geo cur = geo(item, item_info(info, item / groups));
+  const int i1 = clamp(item + n_units);
+  int4 inf_next = item_info(info, i1 / groups);
+  uint32_t a_cur[16];
+  load_a(cur, a_cur);
 #pragma unroll
-      for (int t = 0; t < TOK; ++t) {
-        const bool tv = t0 + t < nrows;
-        const int arow = tv ? (p.a_rowmap ? p.a_rowmap[pos0 + t0 + t] / p.a_rowdiv : pos0 + t0 + t) : 0;
-        const uint16_t *src = reinterpret_cast<const uint16_t *>(p.A) + (int64_t)arow * p.lda + kc;
+  for (int d = 0; d < kBatch; ++d) load_step(cur, d);
+
+  for (; item < n_items; item += n_units) {
+    // descriptor two items ahead, activation slice and weights one item ahead
+    const int inx = clamp(item + n_units);
+    const int4 inf_after = item_info(info, clamp(item + 2 * n_units) / groups);
+    const Geo nxt = geo(inx, inf_next);
+    uint32_t a_nxt[16];
+    load_a(nxt, a_nxt);
+
+    float part[NMAT][kBatch];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          u32x4 v = u32x4{0u, 0u, 0u, 0u};
-          if (tv && kval) v = *reinterpret_cast<const u32x4 *>(src + 8 * q);
+    for (int d = 0; d < kBatch; ++d) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) a[t][4 * q + j] = v[j];
+      for (int m = 0; m < NMAT; ++m) {
+        const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sq[d][m], 1.0f, false);
+        uint32_t w[16];
+        decode32(bq[d][m], w);
+        part[m][d] = kval ? dot32(w, a_cur, sc[0], sc[1]) : 0.0f;
+      }
+      load_step(nxt, d);
+    }
+    float r[NMAT];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) r[m] = reduce8<C::G>(part[m], lane);
+    if (ks > 1) {   // partial sums of the K slices, added in wave order
+      if (kw > 0) {
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) red[((kw - 1) * NMAT + m) * 64 + lane] = r[m];
+      }
+      __syncthreads();
+      if (kw == 0) {
+        for (int wv = 1; wv < ks; ++wv) {
+#pragma unroll
+          for (int m = 0; m < NMAT; ++m) r[m] += red[((wv - 1) * NMAT + m) * 64 + lane];
         }
       }
-
-      // ---- stream the load steps with D of them in flight (branch-free
-      //      steady state, so the waits count outstanding loads exactly)
-      u32x4 bq[D][NMAT];
-      uint32_t sq[D][NMAT];
-      float outv[NMAT][TOK];          // lane (row - r0) keeps that row's result
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int t = 0; t < TOK; ++t) outv[m][t] = 0.0f;
-
-#define NVFP4_ROW_LOAD(d, step)                                                           \
-      do {                                                                                \
-        const uint32_t oc_ = min(lane_code + (uint32_t)(step) * RPL * code_row, last_code);   \
-        const uint32_t os_ = min(lane_scale + (uint32_t)(step) * RPL * scale_row, last_scale); \
-        _Pragma("unroll") for (int m = 0; m < NMAT; ++m) {                                \
-          bq[d][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cbase[m] + oc_)); \
-          sq[d][m] = *reinterpret_cast<const uint16_t *>(sbase[m] + os_);                 \
-        }                                                                                 \
-      } while (0)
-
-#define NVFP4_ROW_STEP(d, step)                                                           \
-      do {                                                                                \
-        float part_[NMAT][TOK];                                                           \
-        _Pragma("unroll") for (int m = 0; m < NMAT; ++m) {                                \
-          const f32x2_t sc_ = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sq[d][m], 1.0f, false); \
-          _Pragma("unroll") for (int t = 0; t < TOK; ++t)                                 \
-            part_[m][t] = row16_sum<LPR>(kval ? dot32(bq[d][m], a[t], sc_[0], sc_[1]) : 0.0f); \
-        }                                                                                 \
-        _Pragma("unroll") for (int u = 0; u < RPL; ++u) {                                 \
-          const int lr_ = (step) * RPL + u;                                               \
-          _Pragma("unroll") for (int m = 0; m < NMAT; ++m)                                \
-            _Pragma("unroll") for (int t = 0; t < TOK; ++t) {                             \
-              const float tot_ = row_total<LPR>(part_[m][t], u);                          \
-              outv[m][t] = lane == lr_ ? tot_ : outv[m][t];                               \
-            }                                                                             \
-        }                                                                                 \
-      } while (0)
-
-#pragma unroll
-      for (int d = 0; d < D; ++d) NVFP4_ROW_LOAD(d, d);
-      int s0 = 0;
-      for (; s0 + D < steps; s0 += D) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-          NVFP4_ROW_STEP(d, s0 + d);
-          NVFP4_ROW_LOAD(d, s0 + d + D);
+      __syncthreads();
+    }
+    // epilogue: the first lane of each duplicate set writes its row
+    int idx;
+    if constexpr (C::G == 64) idx = lane >> 3;
+    else if constexpr (C::G == 32) idx = (lane >> 2) & 7;
+    else if constexpr (C::G == 16) idx = (lane >> 1) & 7;
+    else idx = lane & 7;
+    const int row = cur.r0 + idx * C::RPL + lane / LPR;
+    if (kw == 0 && (lane % C::DUP) == 0 && row < N) {
+      if constexpr (EPI == Epi::SWIGLU) {
+        const float G = r[0] * p.b_global[0][cur.e] * extra;
+        const float U = r[1] * p.b_global[1][cur.e] * extra;
+        const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
+        static_cast<uint16_t *>(p.out)[(int64_t)cur.pos * p.ldo + row] = (uint16_t)hb;
+      } else {
+        float v = r[0] * p.b_global[0][cur.e] * extra;
+        int64_t orow = cur.pos;
+        if constexpr (EPI == Epi::DOWN) {
+          orow = cur.inf.z;
+          v *= p.pair_weights[orow];
         }
-      }
-#pragma unroll
-      for (int d = 0; d < D; ++d) NVFP4_ROW_STEP(d, s0 + d);
-#undef NVFP4_ROW_LOAD
-#undef NVFP4_ROW_STEP
-
-      // ---- the KS waves' partial sums, added in wave order
-      if (ks > 1) {
-        if (wave > 0) {
-#pragma unroll
-          for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-            for (int t = 0; t < TOK; ++t) red[wave - 1][(m * TOK + t) * 64 + lane] = outv[m][t];
-        }
-        __syncthreads();
-        if (wave == 0) {
-          for (int w = 1; w < ks; ++w) {
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-              for (int t = 0; t < TOK; ++t) outv[m][t] += red[w - 1][(m * TOK + t) * 64 + lane];
-          }
-        }
-        __syncthreads();
-      }
-
-      // ---- epilogue: lane i writes row r0 + i
-      const int row = r0 + lane;
-      if (wave == 0 && lane < rows_per_item && row < N) {
-#pragma unroll
-        for (int t = 0; t < TOK; ++t) {
-          if (t0 + t >= nrows) break;
-          const int pos = pos0 + t0 + t;
-          if constexpr (EPI == Epi::SWIGLU) {
-            const float G = outv[0][t] * gsc[0] * extra;
-            const float U = outv[1][t] * gsc[1] * extra;
-            const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
-            static_cast<uint16_t *>(p.out)[(int64_t)pos * p.ldo + row] = (uint16_t)hb;
-          } else {
-            float v = outv[0][t] * gsc[0] * extra;
-            int64_t orow = pos;
-            if constexpr (EPI == Epi::DOWN) {
-              orow = p.sorted_pairs[pos];
-              v *= p.pair_weights[orow];
-            }
-            if (p.out_type == OutType::F32)
-              static_cast<float *>(p.out)[orow * p.ldo + row] = v;
-            else
-              static_cast<uint16_t *>(p.out)[orow * p.ldo + row] = (uint16_t)f32_to_bf16_bits(v);
-          }
-        }
+        if (p.out_type == OutType::F32)
+          static_cast<float *>(p.out)[orow * p.ldo + row] = v;
+        else
+          static_cast<uint16_t *>(p.out)[orow * p.ldo + row] = (uint16_t)f32_to_bf16_bits(v);
       }
     }
+    cur = nxt;
+    inf_next = inf_after;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a_cur[j] = a_nxt[j];
   }
 }
 
-template <int LPR, int TOK, int D>
-hipError_t launch_cfg(Epi epi, const GemmArgs &a, int ks, int rows_per_item, hipStream_t s) {
-  const int64_t row_blocks = (a.N + rows_per_item - 1) / rows_per_item;
-  int64_t items = row_blocks * (int64_t)a.n_mblocks;
-  const int64_t cap = 4096;
-  if (items > cap) items = cap;
-  if (items < 1) items = 1;
-  const dim3 grid((unsigned)items), block(64 * ks);
+template <int LPR>
+hipError_t launch_cfg(Epi epi, const GemmArgs &a, const int4 *info, int n_pos, hipStream_t s) {
+  const int ks = (a.K + kSlice - 1) / kSlice;
+  const int units_per_wg = ks == 1 ? 4 : 1;
+  constexpr int rows = kBatch * (64 / LPR);
+  const int64_t groups = (a.N + rows - 1) / rows;
+  const int64_t items = groups * (int64_t)n_pos;
+  // persistent units: enough to fill every SIMD a few times, never more than items
+  int64_t units = 4096 / ks;
+  if (units > items) units = items;
+  const int64_t blocks = (units + units_per_wg - 1) / units_per_wg;
+  const dim3 grid((unsigned)(blocks < 1 ? 1 : blocks)), block(64 * ks * units_per_wg);
   switch (epi) {
     case Epi::LINEAR:
-      hipLaunchKernelGGL((row_gemv_kernel<LPR, TOK, D, Epi::LINEAR>), grid, block, 0, s, a,
-                         rows_per_item);
+      hipLaunchKernelGGL((row_gemv_kernel<LPR, Epi::LINEAR>), grid, block, 0, s, a, info, n_pos);
       break;
     case Epi::SWIGLU:
-      hipLaunchKernelGGL((row_gemv_kernel<LPR, TOK, D, Epi::SWIGLU>), grid, block, 0, s, a,
-                         rows_per_item);
+      hipLaunchKernelGGL((row_gemv_kernel<LPR, Epi::SWIGLU>), grid, block, 0, s, a, info, n_pos);
       break;
     case Epi::DOWN:
-      hipLaunchKernelGGL((row_gemv_kernel<LPR, TOK, D, Epi::DOWN>), grid, block, 0, s, a,
-                         rows_per_item);
+      hipLaunchKernelGGL((row_gemv_kernel<LPR, Epi::DOWN>), grid, block, 0, s, a, info, n_pos);
       break;
   }
   return hipGetLastError();
@@ -293,13 +361,13 @@ bool row_gemv_supported(int K) {
   return K >= kSlice && K <= 4 * kSlice;
 }
 
-hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, hipStream_t s) {
+hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int4 *info, int n_pos,
+                           hipStream_t s) {
   const int K = a.K;
-  if (K == 512) return launch_cfg<16, 2, 8>(epi, a, 1, 64, s);    // 16 steps of 4 rows
-  if (K == 256) return launch_cfg<8, 2, 4>(epi, a, 1, 64, s);     // 8 steps of 8 rows
-  if (K == 1024) return launch_cfg<32, 2, 8>(epi, a, 1, 32, s);   // 16 steps of 2 rows
-  const int ks = (K + kSlice - 1) / kSlice;
-  return launch_cfg<64, 2, 8>(epi, a, ks, 32, s);                 // 32 steps of 1 row
+  if (K == 512) return launch_cfg<16>(epi, a, info, n_pos, s);    // items of 32 rows
+  if (K == 256) return launch_cfg<8>(epi, a, info, n_pos, s);     // items of 64 rows
+  if (K == 1024) return launch_cfg<32>(epi, a, info, n_pos, s);   // items of 16 rows
+  return launch_cfg<64>(epi, a, info, n_pos, s);                  // items of 8 rows
 }
 
 }  // namespace nvfp4

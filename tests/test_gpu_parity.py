@@ -140,8 +140,11 @@ def _linear_inputs(M, K, N, seed=0):
     return x, wf
 
 
+# M <= 16 with K in {256, 512, 1024, 2048..8192} takes the row-streaming
+# kernel (N need not fill its 8/16/32/64-row items); the rest the MFMA kernel
 @pytest.mark.parametrize("M,K,N", [(4, 256, 512), (1, 32, 16), (5, 96, 40), (17, 160, 48),
-                                   (33, 256, 64), (130, 384, 96)])
+                                   (33, 256, 64), (130, 384, 96), (3, 2048, 40), (16, 5120, 24),
+                                   (2, 1024, 100), (7, 512, 64), (1, 8192, 13)])
 def test_linear_w4a16(M, K, N):
     say("linear w4a16", M, K, N)
     x, wf = _linear_inputs(M, K, N)
