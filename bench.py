@@ -130,7 +130,7 @@ def main():
     def step(c):
         if route:
             native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs))
-        native.moe_grouped_nvfp4_ffn(x, wcopies[c], wts, off, pairs, k, act=act,
+        native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
                                      act_globals=None, out_dtype=torch.bfloat16,
                                      workspace=ws, out=y)
 
@@ -189,29 +189,24 @@ def main():
     wall_ms = (time.perf_counter() - wall0) * 1e3
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # ---- stage timing: library stage events inside captured steps -----------------
+    # ---- stage timing: the library's stage events around each kernel ------------
+    # Eager steps (events are not recorded inside graphs).  A GPU sleep kernel
+    # first keeps the stream busy while the host enqueues every step, so the
+    # steps then run back to back with no host-side gaps inside the events.
     nst = len(native.FFN_STAGES)
     reps = min(args.steps, 64)
     ev = HipEvents(2 * nst * reps)
     L = native.lib()
     stage_ms = {n: [] for n in native.FFN_STAGES}
-    sgraphs = []
     try:
+        torch.cuda.synchronize()
+        torch.cuda._sleep(400_000_000)
         for r in range(reps):
             base = ctypes.c_void_p(ctypes.addressof(ev.arr) +
                                    2 * nst * r * ctypes.sizeof(ctypes.c_void_p))
             L.nvfp4_set_ffn_stage_events(base)
-            if use_graph:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    step(r % copies)
-                sgraphs.append(g)
-            else:
-                step(r % copies)
+            step(r % copies)
         L.nvfp4_set_ffn_stage_events(None)
-        torch.cuda.synchronize()
-        for g in sgraphs:
-            g.replay()
         torch.cuda.synchronize()
         for r in range(reps):
             for si, n in enumerate(native.FFN_STAGES):

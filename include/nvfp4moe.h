@@ -159,7 +159,8 @@ size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k);
 
 /*
  * moe_grouped_nvfp4_ffn: routed-expert gated FFN.  For each pair p = t*k + j
- * routed to expert e (from moe_route_topk's offsets / sorted_pairs / weights):
+ * routed to expert e = topk_ids[p] (moe_route_topk's ids / weights / offsets /
+ * sorted_pairs, which must be consistent with each other):
  *   h_p = bf16_rne( silu(g_gate[e] x_t D_gate[e]^T) * (g_up[e] x_t D_up[e]^T) )
  *   y_t = sum_j topk_weights[p] * g_down[e] h_p D_down[e]^T   (j ascending)
  * with D the e2m1*e4m3 part of each NVFP4 matrix and fp32 accumulation.
@@ -171,6 +172,7 @@ size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k);
  */
 nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H,
                                    int64_t I, int32_t E, int32_t k,
+                                   const int32_t *topk_ids,
                                    const float *topk_weights,
                                    const int32_t *expert_offsets,
                                    const int32_t *sorted_pairs,

@@ -120,7 +120,6 @@ struct FfnWs {
   int32_t *hshift;
   float *ypair;
   int4 *mblocks;
-  int4 *pair_info;      // per expert-sorted position: {expert, token, pair, 0}
   int32_t *n_mblocks;
   uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h, [3] -
   float *partials;
@@ -139,7 +138,6 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.hshift = c.take<int32_t>((size_t)P);
   w.ypair = c.take<float>((size_t)(P * H));
   w.mblocks = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
-  w.pair_info = c.take<int4>((size_t)P);
   w.n_mblocks = c.take<int32_t>(4);
   w.slots = c.take<uint32_t>(4);
   w.partials = c.take<float>(kMaxPartials);
@@ -295,7 +293,7 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
     a.out = y;
     a.ldo = N;
     a.out_type = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
-    LAUNCH(launch_row_gemv(Epi::LINEAR, a, nullptr, (int)M, stream), "row gemv");
+    LAUNCH(launch_row_gemv(Epi::LINEAR, a, nullptr, nullptr, 1, (int)M, stream), "row gemv");
     return NVFP4_OK;
   }
   if (act == NVFP4_W4A16) {
@@ -367,8 +365,9 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
   CHECK_ALIGN(topk_weights);
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
-  LAUNCH(launch_route_topk(logits, T, E, k, renormalize, topk_ids, topk_weights, stream), "topk");
-  LAUNCH(launch_route_permute(topk_ids, T, E, k, expert_offsets, sorted_pairs, stream), "permute");
+  LAUNCH(launch_route(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets,
+                      sorted_pairs, stream),
+         "route");
   return NVFP4_OK;
 }
 
@@ -384,7 +383,7 @@ size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int
 }
 
 nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t I, int32_t E,
-                                   int32_t k, const float *topk_weights,
+                                   int32_t k, const int32_t *topk_ids, const float *topk_weights,
                                    const int32_t *expert_offsets, const int32_t *sorted_pairs,
                                    const nvfp4_expert_weights *w, nvfp4_act_mode act,
                                    nvfp4_global_mode act_global_mode, float *act_globals,
@@ -392,6 +391,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
                                    size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
   CHECK_NULL(x);
+  CHECK_NULL(topk_ids);
   CHECK_NULL(topk_weights);
   CHECK_NULL(expert_offsets);
   CHECK_NULL(sorted_pairs);
@@ -425,6 +425,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   }
   CHECK_ALIGN(x);
   CHECK_ALIGN(y);
+  CHECK_ALIGN(topk_ids);
   CHECK_ALIGN(topk_weights);
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
@@ -455,11 +456,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   const bool rows = small && !a4 && row_gemv_supported((int)H) && row_gemv_supported((int)I);
 
   // 1-2. plan (m-blocks per expert), zeroed scratch words and x -> fp16 rows
-  if (rows) {
+  if (rows) {   // no plan: the stream kernels read the routing directly
     mark(NVFP4_STAGE_PLAN, false, stream);
-    LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
-                           (int)zero_words, sorted_pairs, k, ws.pair_info, stream),
-           "plan");
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
     mark(NVFP4_STAGE_X_PREP, true, stream);
@@ -474,7 +472,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   } else {
     mark(NVFP4_STAGE_PLAN, false, stream);
     LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
-                           (int)zero_words, nullptr, k, nullptr, stream),
+                           (int)zero_words, stream),
            "plan");
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
@@ -522,7 +520,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   }
   mark(NVFP4_STAGE_GATE_UP, false, stream);
   if (rows)
-    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, ws.pair_info, (int)P, stream), "gate/up");
+    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, sorted_pairs, topk_ids, k, (int)P, stream), "gate/up");
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
   else
@@ -572,7 +570,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   if (rows) {
     d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
     d.a_shift = nullptr;
-    LAUNCH(launch_row_gemv(Epi::DOWN, d, ws.pair_info, (int)P, stream), "down");
+    LAUNCH(launch_row_gemv(Epi::DOWN, d, sorted_pairs, topk_ids, k, (int)P, stream), "down");
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else

@@ -250,19 +250,8 @@ __device__ void build_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
 
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, int E, int bm,
                                                         int4 *mblocks, int32_t *n_mblocks,
-                                                        uint32_t *zero, int zero_words,
-                                                        const int32_t *sorted_pairs, int k,
-                                                        int4 *pair_info) {
+                                                        uint32_t *zero, int zero_words) {
   for (int i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
-  if (pair_info) {
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-      const int hi = offsets[e + 1];
-      for (int pos = offsets[e]; pos < hi; ++pos) {
-        const int pair = sorted_pairs[pos];
-        pair_info[pos] = int4{e, pair / k, pair, 0};
-      }
-    }
-  }
   build_plan(offsets, E, bm, mblocks, n_mblocks);
 }
 
@@ -348,10 +337,9 @@ hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s) {
 
 hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
                            int32_t *n_mblocks, uint32_t *zero, int zero_words,
-                           const int32_t *sorted_pairs, int k, int4 *pair_info,
                            hipStream_t s) {
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, mblocks,
-                     n_mblocks, zero, zero_words, sorted_pairs, k, pair_info);
+                     n_mblocks, zero, zero_words);
   return hipGetLastError();
 }
 

@@ -46,12 +46,11 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols,
 
 // ---- routing (route.hip) -------------------------------------------------------
 
-hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
-                             int renormalize, int32_t *ids, float *weights,
-                             hipStream_t s);
-hipError_t launch_route_permute(const int32_t *ids, int64_t T, int E, int k,
-                                int32_t *offsets, int32_t *sorted_pairs,
-                                hipStream_t s);
+// Top-k ids/weights and the expert-sorted permutation (one workgroup for
+// T <= 32 tokens, else a top-k grid followed by a one-workgroup permutation).
+hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
+                        int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
+                        hipStream_t s);
 
 // ---- grouped GEMM and FFN glue (gemm.hip) ---------------------------------------
 
@@ -97,13 +96,15 @@ hipError_t launch_gemv(Epi epi, const GemmArgs &a, bool a_bf16, hipStream_t s);
 int gemv_tile_cols(Epi epi, int N, int K);
 
 // Row-streaming GEMV for W4A16 decode: A rows are bf16 (used as given).
-// Work items are (tile row, block of output rows); tile row pos has the
-// descriptor info[pos] = {expert, token, pair, 0} (info == null: a dense
-// matrix, all three equal pos).  n_pos tile rows.  Supported K: 256, 512,
-// 1024 and 2048..8192 (multiples of 32).
+// Work items are (tile row, block of output rows); tile row pos is the pair
+// sorted_pairs[pos] of expert ids[pair] and token pair / k (sorted_pairs ==
+// null: a dense matrix, pair = token = pos, expert 0).  SWIGLU reads A row
+// token and writes row pos; DOWN reads A row pos and writes row pair; LINEAR
+// reads and writes row pos.  n_pos tile rows.  Supported K: 256, 512, 1024
+// and 2048..8192 (multiples of 32).
 bool row_gemv_supported(int K);
-hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int4 *info, int n_pos,
-                           hipStream_t s);
+hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pairs,
+                           const int32_t *ids, int k, int n_pos, hipStream_t s);
 
 // FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
 // workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.
@@ -114,12 +115,8 @@ hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x1
 int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
 
 // FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.
-// With pair_info != null it also writes, for every expert-sorted position
-// pos < offsets[E], pair_info[pos] = {expert, token, pair, 0} (k slots per
-// token, pair = sorted_pairs[pos]).
 hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
                            int32_t *n_mblocks, uint32_t *zero, int zero_words,
-                           const int32_t *sorted_pairs, int k, int4 *pair_info,
                            hipStream_t s);
 
 // y[t] = sum_j Y[t*k + j], j ascending, fp32 -> out type.

@@ -17,20 +17,43 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxPerLane = kMaxExperts / kWave;  // 16 logits per lane
 constexpr int kTopkThreads = 256;
 
-// a beats b: larger logit, or equal logit and lower index
+// a beats b: larger logit, or equal logit and lower index (branch-free)
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+  return (av > bv) | ((av == bv) & (ai < bi));
 }
 
-// One wavefront per token.  Lane l holds logits l, l+64, ...; k rounds of a
-// wave-wide argmax pick the experts in descending order.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const float *logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
-    float *weights) {
+// Takes the partner lane's (value, index) when it beats this lane's.  Lanes
+// of rows outside ROW_MASK keep theirs.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_best(float &v, int &i) {
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+      __builtin_bit_cast(int, v), __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xF, false);
+  const bool t = beats(ov, oi, v, i);
+  v = t ? ov : v;
+  i = t ? oi : i;
+}
+
+// Wave-wide best (value, index) with DPP: within rows of 16 lanes, then
+// row_bcast15 / row_bcast31 carry the row winners up to lane 63, whose result
+// is broadcast.  Every lane gets the result.
+__device__ __forceinline__ void wave_best(float &v, int &i) {
+  dpp_best<0xB1, 0xF>(v, i);    // lane ^ 1
+  dpp_best<0x4E, 0xF>(v, i);    // lane ^ 2
+  dpp_best<0x141, 0xF>(v, i);   // the other quad of 8
+  dpp_best<0x140, 0xF>(v, i);   // the other 8 of 16
+  dpp_best<0x142, 0xA>(v, i);   // rows 1, 3 take lane 15 of the row below
+  dpp_best<0x143, 0xC>(v, i);   // rows 2, 3 take lane 31
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// Top-k of one token's logits by one wavefront.  Lane l holds logits
+// l, l+64, ...; k rounds of a wave-wide argmax pick the experts in
+// descending order.  Lane j < k writes the j-th id and weight.
+__device__ void wave_topk(const float *row, int E, int k, int renormalize, int32_t *ids,
+                          float *weights, int32_t *ids_copy) {
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * (kTopkThreads / 64) + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const float *row = logits + t * E;
   float v[kMaxPerLane];
   const int per_lane = (E + 63) / 64;
 #pragma unroll
@@ -42,26 +65,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
   float my_val = 0.0f;   // lane j < k keeps the j-th selected logit
   int my_idx = 0;
   for (int r = 0; r < k; ++r) {
+    // this lane's best untaken candidate; indices rise with i, so a strict
+    // comparison keeps the lower index on ties (branch-free selects)
     float bv = -__builtin_inff();
     int bi = 0x7FFFFFFF;
 #pragma unroll
     for (int i = 0; i < kMaxPerLane; ++i) {
       const int e = lane + 64 * i;
-      if (i < per_lane && e < E && !((taken >> i) & 1u) && beats(v[i], e, bv, bi)) {
-        bv = v[i];
-        bi = e;
-      }
+      const bool ok = (i < per_lane) & (e < E) & !((taken >> i) & 1u) & (v[i] > bv);
+      bv = ok ? v[i] : bv;
+      bi = ok ? e : bi;
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (beats(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
+    wave_best(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == r) { my_val = bv; my_idx = bi; }
   }
-  const float lmax = __shfl(my_val, 0, kWave);
+  const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
   const float ex = lane < k ? expf(my_val - lmax) : 0.0f;
   float denom;
   if (renormalize) {
@@ -76,9 +95,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     denom = wave_sum(s);
   }
   if (lane < k) {
-    ids[t * k + lane] = my_idx;
-    weights[t * k + lane] = ex / denom;
+    ids[lane] = my_idx;
+    weights[lane] = ex / denom;
+    if (ids_copy) ids_copy[lane] = my_idx;
   }
+}
+
+// One wavefront per token.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+    const float *logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
+    float *weights) {
+  const int64_t t = (int64_t)blockIdx.x * (kTopkThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  wave_topk(logits + t * E, E, k, renormalize, ids + t * k, weights + t * k, nullptr);
 }
 
 // Single workgroup.  Pass 1 counts pairs per expert and writes the offsets.
@@ -88,16 +117,23 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 constexpr int kPermThreads = 1024;
 constexpr int kBitmapWords = 16384;   // experts * words-per-expert per chunk
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(
-    const int32_t *ids, int64_t T, int E, int k, int W, int32_t *offsets,
-    int32_t *sorted_pairs) {
-  __shared__ uint32_t bitmap[kBitmapWords];
-  __shared__ uint16_t prefix[kBitmapWords];
-  __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t off[kMaxExperts];
-  __shared__ int32_t base[kMaxExperts];
-  __shared__ int32_t chunk_cnt[kMaxExperts];
-  __shared__ int32_t wave_tot[kPermThreads / 64];
+struct PermuteLds {
+  uint32_t bitmap[kBitmapWords];
+  uint16_t prefix[kBitmapWords];
+  int32_t cnt[kMaxExperts];
+  int32_t off[kMaxExperts];
+  int32_t base[kMaxExperts];
+  int32_t chunk_cnt[kMaxExperts];
+  int32_t wave_tot[kPermThreads / 64];
+};
+
+// ids: the [T, k] expert ids (global or LDS).  One workgroup of kPermThreads.
+__device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W,
+                              int32_t *offsets, int32_t *sorted_pairs, PermuteLds &L) {
+  uint32_t *bitmap = L.bitmap;
+  uint16_t *prefix = L.prefix;
+  int32_t *cnt = L.cnt, *off = L.off, *base = L.base, *chunk_cnt = L.chunk_cnt;
+  int32_t *wave_tot = L.wave_tot;
   const int tid = threadIdx.x;
   const int64_t P = T * k;
 
@@ -161,20 +197,30 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   }
 }
 
-}  // namespace
 
-hipError_t launch_route_topk(const float *logits, int64_t T, int E, int k,
-                             int renormalize, int32_t *ids, float *weights,
-                             hipStream_t s) {
-  const int64_t blocks = (T + 3) / 4;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s,
-                     logits, T, E, k, renormalize, ids, weights);
-  return hipGetLastError();
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(
+    const int32_t *ids, int64_t T, int E, int k, int W, int32_t *offsets,
+    int32_t *sorted_pairs) {
+  __shared__ PermuteLds L;
+  permute_block(ids, T, E, k, W, offsets, sorted_pairs, L);
 }
 
-hipError_t launch_route_permute(const int32_t *ids, int64_t T, int E, int k,
-                                int32_t *offsets, int32_t *sorted_pairs,
-                                hipStream_t s) {
+// Small T: one workgroup does the top-k of every token (waves take tokens
+// t, t + 16, ...) and then the permutation, from a copy of the ids in LDS.
+constexpr int kSmallT = 32;
+__global__ __launch_bounds__(kPermThreads) void route_small_kernel(
+    const float *logits, int64_t T, int E, int k, int renormalize, int W, int32_t *ids,
+    float *weights, int32_t *offsets, int32_t *sorted_pairs) {
+  __shared__ PermuteLds L;
+  __shared__ int32_t ids_lds[kSmallT * 32];
+  const int wave = threadIdx.x >> 6;
+  for (int64_t t = wave; t < T; t += kPermThreads / 64)
+    wave_topk(logits + t * E, E, k, renormalize, ids + t * k, weights + t * k, ids_lds + t * k);
+  __syncthreads();
+  permute_block(ids_lds, T, E, k, W, offsets, sorted_pairs, L);
+}
+
+int permute_words(int64_t T, int E) {
   // words per expert per chunk: E * W <= kBitmapWords, and W * 32 tokens
   // per chunk keep every per-word prefix below 2^16
   int W = kBitmapWords / E;
@@ -182,6 +228,25 @@ hipError_t launch_route_permute(const int32_t *ids, int64_t T, int E, int k,
   const int64_t need = (T + 31) / 32;
   if (W > need) W = (int)need;
   if (W < 1) W = 1;
+  return W;
+}
+
+}  // namespace
+
+hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
+                        int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
+                        hipStream_t s) {
+  const int W = permute_words(T, E);
+  if (T <= kSmallT) {
+    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kPermThreads), 0, s, logits, T, E, k,
+                       renormalize, W, ids, weights, offsets, sorted_pairs);
+    return hipGetLastError();
+  }
+  const int64_t blocks = (T + 3) / 4;
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
+                     E, k, renormalize, ids, weights);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, T, E, k, W,
                      offsets, sorted_pairs);
   return hipGetLastError();

@@ -150,14 +150,17 @@ __device__ __forceinline__ float reduce8(float (&v)[8], int lane) {
 // ---------------------------------------------------------------------------
 //
 // Work is a flat list of items: item i = (tile row pos = i / groups, group g
-// = i % groups of rows_per_item consecutive output rows).  A tile row's
-// expert, token and pair come from one 16-byte descriptor (built by the FFN
-// plan; absent for a dense matrix, where all three are pos).  Each unit of KS
-// waves walks items u, u + U, u + 2U, ... (U units in the grid) and keeps the
-// next item's weight loads in flight while it computes the current one; the
-// descriptor is fetched two items ahead and the activation slice one ahead.
-// Consecutive units take consecutive row groups, so concurrently running
-// waves read neighbouring rows of the same expert.
+// = i % groups of ROWS consecutive output rows).  Tile row pos is the pos-th
+// (token, slot) pair in expert order: pair = sorted_pairs[pos], expert =
+// topk_ids[pair], token = pair / k (a dense matrix has no routing: pair =
+// token = pos, expert 0).  Each unit of KS waves walks items u, u + U, ...
+// (U units in the grid) and keeps the next item's weight loads in flight
+// while it computes the current one; the routing loads run further ahead
+// (pair three items ahead, expert two) so no item waits on a dependent
+// chain.  Consecutive units take consecutive row groups, so concurrently
+// running waves read neighbouring rows of the same expert, and the tile rows
+// of one expert (adjacent positions) share the same XCD, where repeated
+// reads of its rows hit L2.
 
 template <int LPR, Epi EPI>
 struct RowCfg {
@@ -168,12 +171,14 @@ struct RowCfg {
   static constexpr int ROWS = kBatch * RPL;        // output rows per item
 };
 
-__device__ __forceinline__ int4 item_info(const int4 *info, int pos) {
-  return info ? info[pos] : int4{0, pos, pos, 0};
-}
+struct Routing {
+  const int32_t *sorted_pairs;   // null: dense
+  const int32_t *ids;
+  int k;
+};
 
 template <int LPR, Epi EPI>
-__global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const int4 *info,
+__global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const Routing rt,
                                                        int n_pos) {
   using C = RowCfg<LPR, EPI>;
   constexpr int NMAT = C::NMAT;
@@ -203,17 +208,16 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const i
   struct Geo {
     uint32_t code, scale;   // within the expert's matrix
     int64_t ecode, escale;  // expert base offsets
-    int e, r0, pos;
-    int4 inf;
+    int e, r0, pos, pair;
   };
-  auto geo = [&](int item, int4 inf) {
+  auto geo = [&](int item, int e, int pair) {
     Geo gm;
     gm.pos = item / groups;
     gm.r0 = (item - gm.pos * groups) * C::ROWS;
-    gm.inf = inf;
-    gm.e = inf.x;
-    gm.ecode = (int64_t)gm.e * p.b_codes_estride;
-    gm.escale = (int64_t)gm.e * p.b_scales_estride;
+    gm.e = e;
+    gm.pair = pair;
+    gm.ecode = (int64_t)e * p.b_codes_estride;
+    gm.escale = (int64_t)e * p.b_scales_estride;
     gm.code = (uint32_t)(gm.r0 + sub) * code_row + kc / 2;
     gm.scale = (uint32_t)(gm.r0 + sub) * scale_row + kc / 16;
     return gm;
@@ -235,7 +239,7 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const i
     }
   };
   auto load_a = [&](const Geo &gm, uint32_t (&a)[16]) {
-    const int arow = EPI == Epi::SWIGLU ? gm.inf.y : gm.pos;
+    const int arow = EPI == Epi::SWIGLU ? gm.pair / rt.k : gm.pos;
     const uint16_t *src = reinterpret_cast<const uint16_t *>(p.A) + (int64_t)arow * p.lda + kc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -246,22 +250,29 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const i
   };
   // later items than the last are clamped to the last (valid, never written)
   auto clamp = [&](int item) { return item < n_items ? item : n_items - 1; };
+  auto pair_of = [&](int item) {
+    const int pos = clamp(item) / groups;
+    return rt.sorted_pairs ? rt.sorted_pairs[pos] : pos;
+  };
+  auto expert_of = [&](int pair) { return rt.sorted_pairs ? rt.ids[pair] : 0; };
 
-  // prologue: item i0 loaded, descriptor of i0 + U known
+  // prologue: item u loaded; routing of u + U known, pair of u + 2U known
   int item = unit;
-  Geo cur = geo(item, item_info(info, item / groups));
-  const int i1 = clamp(item + n_units);
-  int4 inf_next = item_info(info, i1 / groups);
+  const int pair0 = pair_of(item);
+  Geo cur = geo(item, expert_of(pair0), pair0);
+  int pair_next = pair_of(item + n_units);
+  int e_next = expert_of(pair_next);
+  int pair_after = pair_of(item + 2 * n_units);
   uint32_t a_cur[16];
   load_a(cur, a_cur);
 #pragma unroll
   for (int d = 0; d < kBatch; ++d) load_step(cur, d);
 
   for (; item < n_items; item += n_units) {
-    // descriptor two items ahead, activation slice and weights one item ahead
-    const int inx = clamp(item + n_units);
-    const int4 inf_after = item_info(info, clamp(item + 2 * n_units) / groups);
-    const Geo nxt = geo(inx, inf_next);
+    // routing two and three items ahead, activations and weights one ahead
+    const int e_after = expert_of(pair_after);
+    const int pair_after2 = pair_of(item + 3 * n_units);
+    const Geo nxt = geo(clamp(item + n_units), e_next, pair_next);
     uint32_t a_nxt[16];
     load_a(nxt, a_nxt);
 
@@ -304,14 +315,14 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const i
     if (kw == 0 && (lane % C::DUP) == 0 && row < N) {
       if constexpr (EPI == Epi::SWIGLU) {
         const float G = r[0] * p.b_global[0][cur.e] * extra;
-        const float U = r[1] * p.b_global[1][cur.e] * extra;
+        const float U = r[1] * p.b_global[NMAT - 1][cur.e] * extra;
         const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
         static_cast<uint16_t *>(p.out)[(int64_t)cur.pos * p.ldo + row] = (uint16_t)hb;
       } else {
         float v = r[0] * p.b_global[0][cur.e] * extra;
         int64_t orow = cur.pos;
         if constexpr (EPI == Epi::DOWN) {
-          orow = cur.inf.z;
+          orow = cur.pair;
           v *= p.pair_weights[orow];
         }
         if (p.out_type == OutType::F32)
@@ -321,14 +332,16 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const i
       }
     }
     cur = nxt;
-    inf_next = inf_after;
+    pair_next = pair_after;
+    e_next = e_after;
+    pair_after = pair_after2;
 #pragma unroll
     for (int j = 0; j < 16; ++j) a_cur[j] = a_nxt[j];
   }
 }
 
 template <int LPR>
-hipError_t launch_cfg(Epi epi, const GemmArgs &a, const int4 *info, int n_pos, hipStream_t s) {
+hipError_t launch_cfg(Epi epi, const GemmArgs &a, const Routing &info, int n_pos, hipStream_t s) {
   const int ks = (a.K + kSlice - 1) / kSlice;
   const int units_per_wg = ks == 1 ? 4 : 1;
   constexpr int rows = kBatch * (64 / LPR);
@@ -361,9 +374,10 @@ bool row_gemv_supported(int K) {
   return K >= kSlice && K <= 4 * kSlice;
 }
 
-hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int4 *info, int n_pos,
-                           hipStream_t s) {
+hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pairs,
+                           const int32_t *ids, int k, int n_pos, hipStream_t s) {
   const int K = a.K;
+  const Routing info{sorted_pairs, ids, k < 1 ? 1 : k};
   if (K == 512) return launch_cfg<16>(epi, a, info, n_pos, s);    // items of 32 rows
   if (K == 256) return launch_cfg<8>(epi, a, info, n_pos, s);     // items of 64 rows
   if (K == 1024) return launch_cfg<32>(epi, a, info, n_pos, s);   // items of 16 rows

@@ -67,8 +67,8 @@ def lib():
                                       _vp, _sz, _vp]),
             "moe_route_topk_workspace_size": (_sz, [_i64, _i32, _i32]),
             "moe_grouped_nvfp4_ffn": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
-                                             ctypes.POINTER(ExpertWeightsC), _i32, _i32, _vp,
-                                             _vp, _i32, _vp, _sz, _vp]),
+                                             _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
+                                             _vp, _vp, _i32, _vp, _sz, _vp]),
             "moe_grouped_nvfp4_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
             "nvfp4_set_ffn_stage_events": (None, [_vp]),
             "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
@@ -239,10 +239,11 @@ def ffn_workspace_bytes(T, H, I, E, k, act=W4A16):
     return lib().moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act)
 
 
-def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_weights, expert_offsets,
+def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_ids, topk_weights, expert_offsets,
                           sorted_pairs, k, act=W4A16, act_globals=None,
                           out_dtype=torch.bfloat16, workspace=None, out=None):
-    """Routed-expert gated FFN.  Returns (y [T,H], act_globals or None)."""
+    """Routed-expert gated FFN over moe_route_topk's outputs.
+    Returns (y [T,H], act_globals or None)."""
     T, H = x.shape
     E, I = weights.num_experts, weights.intermediate
     dev = x.device
@@ -257,7 +258,7 @@ def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_weights, expert_offset
     L = lib()
     ws = _workspace(L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act), dev, workspace)
     cw = weights.c_struct()
-    _check(L.moe_grouped_nvfp4_ffn(_ptr(x), T, H, I, E, k, _ptr(topk_weights),
+    _check(L.moe_grouped_nvfp4_ffn(_ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights),
                                    _ptr(expert_offsets), _ptr(sorted_pairs), ctypes.byref(cw),
                                    act, mode, _ptr(ag), _ptr(y), _dt(y.dtype), _ptr(ws),
                                    ws.numel(), _stream()))

@@ -202,7 +202,7 @@ def _moe_run(T, H, I, E, k, act=native.W4A16, zipf=None, seed=0, tokens=None,
     ids, wts, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k)
     ag = None if given_globals is None else torch.tensor(given_globals, dtype=torch.float32,
                                                          device=DEV)
-    y, g_out = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, wts, off, pairs, k, act=act,
+    y, g_out = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k, act=act,
                                             act_globals=ag, out_dtype=out_dtype)
     w_ref = oracle_experts(E, H, I, need, seed)
     return x, rids, rw, y, g_out, w_ref, (ids, wts, off, pairs, w_gpu)
@@ -222,11 +222,11 @@ def test_moe_ffn_w4a16_small(T, H, I, E, k):
     assert_close_f32(to_np(y), ref, "moe w4a16")
     # bf16 output: same kernels, rounded once
     ids, wts, off, pairs, w_gpu = st
-    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, wts, off, pairs, k,
+    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
                                          out_dtype=torch.bfloat16)
     assert_bf16_output(bf16_np(yb), to_np(y), ref, "moe bf16")
     # deterministic: a second run is bit-identical
-    y2, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, wts, off, pairs, k,
+    y2, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
                                          out_dtype=torch.float32)
     assert torch.equal(y, y2)
 
@@ -244,7 +244,7 @@ def test_moe_ffn_w4a4_small(T, H, I, E, k):
     # with the oracle's own globals given, the two runs agree as well
     ids, wts, off, pairs, w_gpu = st
     yg, _ = native.moe_grouped_nvfp4_ffn(
-        x.to(DEV), w_gpu, wts, off, pairs, k, act=native.W4A4,
+        x.to(DEV), w_gpu, ids, wts, off, pairs, k, act=native.W4A4,
         act_globals=torch.tensor([info["g_x"], info["g_h"]], device=DEV), out_dtype=torch.float32)
     refg, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True,
                         act_globals=(info["g_x"], info["g_h"]))

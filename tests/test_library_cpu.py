@@ -108,8 +108,8 @@ def test_ffn_validation():
     T, H, I, E, k = 16, 256, 128, 8, 2
     ws = L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, 0)
     assert ws > 0
-    f = lambda T=T, H=H, I=I, E=E, k=k, wsb=ws, ww=w, act=0: L.moe_grouped_nvfp4_ffn(
-        FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, ctypes.byref(ww), act, 0, None, FAKE, 0,
+    f = lambda T=T, H=H, I=I, E=E, k=k, wsb=ws, ww=w, act=0, ids=FAKE: L.moe_grouped_nvfp4_ffn(
+        FAKE, T, H, I, E, k, ids, FAKE, FAKE, FAKE, ctypes.byref(ww), act, 0, None, FAKE, 0,
         FAKE, wsb, None)
     assert f(H=250) == 2
     assert f(I=100) == 2
@@ -117,13 +117,15 @@ def test_ffn_validation():
     assert f(T=0) == 1
     assert f(wsb=ws - 1) == 4
     assert f(act=5) == 1
+    assert f(ids=None) == 1 and "topk_ids" in _last()
+    assert f(ids=FAKE_MIS) == 3
     bad = native.ExpertWeightsC(*([FAKE.value] * 8 + [None]))
     assert f(ww=bad) == 1 and "down_global" in _last()
     mis = native.ExpertWeightsC(*([FAKE_MIS.value] + [FAKE.value] * 8))
     assert f(ww=mis) == 3
     # a W4A4 call with given globals needs them
-    assert L.moe_grouped_nvfp4_ffn(FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, ctypes.byref(w), 1, 1,
-                                   None, FAKE, 0, FAKE, ws, None) == 1
+    assert L.moe_grouped_nvfp4_ffn(FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, FAKE, ctypes.byref(w), 1,
+                                   1, None, FAKE, 0, FAKE, ws, None) == 1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
