@@ -9,6 +9,10 @@
 
 using namespace nvfp4;
 
+namespace nvfp4 {
+thread_local TimedLaunch g_timed_launch = {nullptr, nullptr};
+}
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -21,6 +25,15 @@ void mark(int s, bool after, hipStream_t stream) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
   (void)hipEventRecord(g_stage_events[2 * s + (after ? 1 : 0)], stream);
+}
+
+// For a stage that is exactly one kernel: its events ride on that kernel's
+// dispatch (see launch_kernel), so the stage time is the kernel's own.
+void mark_kernel(int s, hipStream_t stream) {
+  if (!g_stage_events) return;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
+  g_timed_launch = TimedLaunch{g_stage_events[2 * s], g_stage_events[2 * s + 1]};
 }
 
 nvfp4_status fail(nvfp4_status st, const char *fmt, ...) {
@@ -518,14 +531,14 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
     g.a_shift = nullptr;
   }
-  mark(NVFP4_STAGE_GATE_UP, false, stream);
+  mark_kernel(NVFP4_STAGE_GATE_UP, stream);
   if (rows)
     LAUNCH(launch_row_gemv(Epi::SWIGLU, g, sorted_pairs, topk_ids, k, (int)P, stream), "gate/up");
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
   else
     LAUNCH(launch_gemm(Epi::SWIGLU, g, bm, stream), "gate/up");
-  mark(NVFP4_STAGE_GATE_UP, true, stream);
+  g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 4. h rows -> fp16 operands (W4A16 small tiles convert inside the down kernel)
   mark(NVFP4_STAGE_H_PREP, false, stream);
   const bool h_inline = small && !a4;
@@ -566,7 +579,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.out_type = OutType::F32;
   d.pair_weights = topk_weights;
   d.sorted_pairs = sorted_pairs;
-  mark(NVFP4_STAGE_DOWN, false, stream);
+  mark_kernel(NVFP4_STAGE_DOWN, stream);
   if (rows) {
     d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
     d.a_shift = nullptr;
@@ -575,11 +588,11 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else
     LAUNCH(launch_gemm(Epi::DOWN, d, bm, stream), "down");
-  mark(NVFP4_STAGE_DOWN, true, stream);
+  g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order
-  mark(NVFP4_STAGE_COMBINE, false, stream);
+  mark_kernel(NVFP4_STAGE_COMBINE, stream);
   LAUNCH(launch_combine(ws.ypair, T, H, k, y, yt, stream), "combine");
-  mark(NVFP4_STAGE_COMBINE, true, stream);
+  g_timed_launch = TimedLaunch{nullptr, nullptr};
   return NVFP4_OK;
 }
 

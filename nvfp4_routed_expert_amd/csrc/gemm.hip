@@ -197,13 +197,13 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)items), block(NW * 64);
   switch (epi) {
     case Epi::LINEAR:
-      hipLaunchKernelGGL((grouped_gemm_kernel<NW, NF, MS, Epi::LINEAR>), grid, block, 0, s, a);
+      launch_kernel((grouped_gemm_kernel<NW, NF, MS, Epi::LINEAR>), grid, block, 0, s, a);
       break;
     case Epi::SWIGLU:
-      hipLaunchKernelGGL((grouped_gemm_kernel<NW, NF, MS, Epi::SWIGLU>), grid, block, 0, s, a);
+      launch_kernel((grouped_gemm_kernel<NW, NF, MS, Epi::SWIGLU>), grid, block, 0, s, a);
       break;
     case Epi::DOWN:
-      hipLaunchKernelGGL((grouped_gemm_kernel<NW, NF, MS, Epi::DOWN>), grid, block, 0, s, a);
+      launch_kernel((grouped_gemm_kernel<NW, NF, MS, Epi::DOWN>), grid, block, 0, s, a);
       break;
   }
   return hipGetLastError();
@@ -338,7 +338,7 @@ hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s) {
 hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
                            int32_t *n_mblocks, uint32_t *zero, int zero_words,
                            hipStream_t s) {
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, mblocks,
+  launch_kernel(moe_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, mblocks,
                      n_mblocks, zero, zero_words);
   return hipGetLastError();
 }
@@ -348,7 +348,7 @@ hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x1
                            int4 *mblocks, int32_t *n_mblocks, uint32_t *zero,
                            int64_t zero_words, hipStream_t s) {
   const int64_t blocks = (T + 3) / 4 + 1;
-  hipLaunchKernelGGL(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16,
+  launch_kernel(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16,
                      xshift, offsets, E, bm, mblocks, n_mblocks, zero, zero_words);
   return hipGetLastError();
 }
@@ -358,7 +358,7 @@ hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k, void 
   int64_t blocks = (T * (H / 4) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ypair, T, H, k,
+  launch_kernel(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ypair, T, H, k,
                      y, t);
   return hipGetLastError();
 }

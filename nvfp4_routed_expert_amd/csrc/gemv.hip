@@ -276,9 +276,9 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, bool a_bf16, hipStream_t s) {
   const dim3 grid((unsigned)items), block(KS * 64);
 #define NVFP4_GEMV_CASE(EPIV)                                                               \
   if (a_bf16)                                                                               \
-    hipLaunchKernelGGL((grouped_gemv_kernel<KS, NF, D, EPIV, true>), grid, block, 0, s, a);  \
+    launch_kernel((grouped_gemv_kernel<KS, NF, D, EPIV, true>), grid, block, 0, s, a);  \
   else                                                                                      \
-    hipLaunchKernelGGL((grouped_gemv_kernel<KS, NF, D, EPIV, false>), grid, block, 0, s, a);
+    launch_kernel((grouped_gemv_kernel<KS, NF, D, EPIV, false>), grid, block, 0, s, a);
   switch (epi) {
     case Epi::LINEAR: NVFP4_GEMV_CASE(Epi::LINEAR) break;
     case Epi::SWIGLU: NVFP4_GEMV_CASE(Epi::SWIGLU) break;

@@ -4,9 +4,30 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 namespace nvfp4 {
+
+// Timing hook.  When a pair of events is attached, the next kernel launched
+// through launch_kernel on this thread carries them in its own dispatch
+// (start and end timestamps of that kernel), so their span is the kernel
+// alone, without separate event packets around it.  The pair is used once.
+struct TimedLaunch {
+  hipEvent_t start, stop;
+};
+extern thread_local TimedLaunch g_timed_launch;
+
+template <typename F, typename... Args>
+void launch_kernel(F kernel, dim3 grid, dim3 block, uint32_t shm, hipStream_t s, Args... args) {
+  const TimedLaunch t = g_timed_launch;
+  if (t.start) {
+    g_timed_launch = TimedLaunch{nullptr, nullptr};
+    hipExtLaunchKernelGGL(kernel, grid, block, shm, s, t.start, t.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, shm, s, args...);
+  }
+}
 
 enum class InType : int { BF16 = 0, F32 = 1 };
 enum class OutType : int { BF16 = 0, F32 = 1 };

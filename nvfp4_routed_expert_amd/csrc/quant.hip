@@ -199,7 +199,7 @@ int amax_partials_grid(int64_t rows, int64_t cols) {
 hipError_t launch_amax_partials(const void *x, InType t, int64_t rows, int64_t cols,
                                 int64_t ld, float *partials, int n_partials,
                                 hipStream_t s) {
-  hipLaunchKernelGGL(amax_partials_kernel, dim3(n_partials), dim3(kThreads), 0, s, x, t,
+  launch_kernel(amax_partials_kernel, dim3(n_partials), dim3(kThreads), 0, s, x, t,
                      rows, cols, ld, partials);
   return hipGetLastError();
 }
@@ -208,7 +208,7 @@ hipError_t launch_quantize(const void *x, InType t, int64_t rows, int64_t cols,
                            int64_t ld, uint8_t *codes, uint8_t *scales,
                            const float *amax_src, int n_amax, const float *g_given,
                            float *g_out, hipStream_t s) {
-  hipLaunchKernelGGL(quantize_kernel, dim3(grid_for(rows * (cols / 16), kThreads)),
+  launch_kernel(quantize_kernel, dim3(grid_for(rows * (cols / 16), kThreads)),
                      dim3(kThreads), 0, s, x, t, rows, cols, ld, codes, scales, amax_src,
                      n_amax, g_given, g_out);
   return hipGetLastError();
@@ -216,7 +216,7 @@ hipError_t launch_quantize(const void *x, InType t, int64_t rows, int64_t cols,
 
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const float *g,
                              int64_t rows, int64_t cols, float *out, hipStream_t s) {
-  hipLaunchKernelGGL(dequantize_kernel, dim3(grid_for(rows * (cols / 8), kThreads)),
+  launch_kernel(dequantize_kernel, dim3(grid_for(rows * (cols / 8), kThreads)),
                      dim3(kThreads), 0, s, codes, scales, g, rows, cols, out);
   return hipGetLastError();
 }
@@ -226,7 +226,7 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols, PrepMo
                            int n_amax, const float *g_given, float *g_out,
                            float *g_out2, hipStream_t s) {
   const int64_t blocks = (rows + 3) / 4;
-  hipLaunchKernelGGL(row_prep_kernel, dim3((unsigned)(blocks < 1 ? 1 : blocks)),
+  launch_kernel(row_prep_kernel, dim3((unsigned)(blocks < 1 ? 1 : blocks)),
                      dim3(kThreads), 0, s, x, rows, cols, mode, out, shift, amax_src,
                      n_amax, g_given, g_out, g_out2);
   return hipGetLastError();

@@ -238,16 +238,16 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renorm
                         hipStream_t s) {
   const int W = permute_words(T, E);
   if (T <= kSmallT) {
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kPermThreads), 0, s, logits, T, E, k,
+    launch_kernel(route_small_kernel, dim3(1), dim3(kPermThreads), 0, s, logits, T, E, k,
                        renormalize, W, ids, weights, offsets, sorted_pairs);
     return hipGetLastError();
   }
   const int64_t blocks = (T + 3) / 4;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
+  launch_kernel(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
                      E, k, renormalize, ids, weights);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, T, E, k, W,
+  launch_kernel(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, T, E, k, W,
                      offsets, sorted_pairs);
   return hipGetLastError();
 }

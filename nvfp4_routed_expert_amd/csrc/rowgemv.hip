@@ -354,13 +354,13 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, const Routing &info, int n_pos
   const dim3 grid((unsigned)(blocks < 1 ? 1 : blocks)), block(64 * ks * units_per_wg);
   switch (epi) {
     case Epi::LINEAR:
-      hipLaunchKernelGGL((row_gemv_kernel<LPR, Epi::LINEAR>), grid, block, 0, s, a, info, n_pos);
+      launch_kernel((row_gemv_kernel<LPR, Epi::LINEAR>), grid, block, 0, s, a, info, n_pos);
       break;
     case Epi::SWIGLU:
-      hipLaunchKernelGGL((row_gemv_kernel<LPR, Epi::SWIGLU>), grid, block, 0, s, a, info, n_pos);
+      launch_kernel((row_gemv_kernel<LPR, Epi::SWIGLU>), grid, block, 0, s, a, info, n_pos);
       break;
     case Epi::DOWN:
-      hipLaunchKernelGGL((row_gemv_kernel<LPR, Epi::DOWN>), grid, block, 0, s, a, info, n_pos);
+      launch_kernel((row_gemv_kernel<LPR, Epi::DOWN>), grid, block, 0, s, a, info, n_pos);
       break;
   }
   return hipGetLastError();
