@@ -138,7 +138,7 @@ struct FfnWs {
   float *partials;
 };
 int ffn_bm(int64_t T, int64_t E, int64_t k) {
-  return 2 * T * k <= 32 * E ? 16 : gemm_block_rows(2 * T * k / E);
+  return 2 * T * k <= 32 * E ? 16 : 128;
 }
 int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) { return (P + bm - 1) / bm + E; }
 FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
@@ -156,9 +156,13 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.partials = c.take<float>(kMaxPartials);
   return w;
 }
-// Small tiles (decode): experts average at most 16 pairs, so the small-M
-// GEMV with split K runs both projections.
-bool ffn_small(int64_t T, int64_t E, int64_t k) { return 2 * T * k <= 32 * E; }
+// Decode-sized batches: at most 256 (token, expert) pairs that average at
+// most 16 per expert run as GEMVs over the pairs.  Anything larger runs as a
+// grouped GEMM over m-blocks of 128 rows, which streams every active
+// expert's weights once per block however skewed the routing is (one expert
+// holding almost every token of a prefill chunk costs a few blocks, not one
+// weight stream per token).
+bool ffn_small(int64_t T, int64_t E, int64_t k) { return T * k <= 256 && 2 * T * k <= 32 * E; }
 
 }  // namespace
 
@@ -341,7 +345,9 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   a.out = y;
   a.ldo = N;
   a.out_type = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
-  LAUNCH(launch_gemm(Epi::LINEAR, a, bm, stream), "gemm");
+  LAUNCH(tile_gemm_supported((int)K) ? launch_tile_gemm(Epi::LINEAR, a, bm, stream)
+                                        : launch_gemm(Epi::LINEAR, a, bm, stream),
+         "gemm");
   return NVFP4_OK;
 }
 
@@ -537,7 +543,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
   else
-    LAUNCH(launch_gemm(Epi::SWIGLU, g, bm, stream), "gate/up");
+    LAUNCH(tile_gemm_supported((int)H) ? launch_tile_gemm(Epi::SWIGLU, g, bm, stream)
+                                         : launch_gemm(Epi::SWIGLU, g, bm, stream),
+           "gate/up");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 4. h rows -> fp16 operands (W4A16 small tiles convert inside the down kernel)
   mark(NVFP4_STAGE_H_PREP, false, stream);
@@ -587,7 +595,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else
-    LAUNCH(launch_gemm(Epi::DOWN, d, bm, stream), "down");
+    LAUNCH(tile_gemm_supported((int)I) ? launch_tile_gemm(Epi::DOWN, d, bm, stream)
+                                         : launch_gemm(Epi::DOWN, d, bm, stream),
+           "down");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order
   mark_kernel(NVFP4_STAGE_COMBINE, stream);

@@ -109,6 +109,12 @@ struct GemmArgs {
 
 hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
 
+// Grouped GEMM with both operands staged through an LDS ring (tile_gemm.hip):
+// m-blocks of bm (16, 32, 64 or 128) rows, 256 weight rows per workgroup.
+// Needs K % 64 == 0 (tile_gemm_supported); other K use launch_gemm.
+bool tile_gemm_supported(int K);
+hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
+
 // Small-M grouped GEMV (tiles of 16 rows): waves of a workgroup split K and
 // keep several 128-wide chunks of weight loads in flight.  a_bf16: A rows are
 // bf16 and each workgroup derives their power-of-two shift from the row

@@ -1,0 +1,311 @@
+// Expert-grouped NVFP4 GEMM with LDS-staged activations (gfx950 MFMA).
+//
+// The prefill form of the routed-expert FFN: the tokens routed to one expert
+// form a block of rows that reuses that expert's weights, up to 512 prompt
+// tokens per chunk (Eider page, "Performance"); the W4A4 experts of the
+// Flash-Next checkpoint (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card,
+// "What this model is") arrive here as exact fp16 rows of their quantised
+// activations.
+//
+// A work item is (m-block of up to BM = 16*MS expert-sorted rows, tile of
+// 256 weight rows).  The four waves of a workgroup split the weight rows (64
+// each; for the gate/up pair 32 gate and the same 32 up rows) and share the
+// activation rows.  Both operands pass through a three-stage LDS ring of
+// 64-wide K chunks, filled by direct global-to-LDS loads (no registers), so
+// two chunks are in flight while one is multiplied and two workgroups fit
+// on a CU.  A wave reads its weight codes from LDS, dequantises them in
+// registers (E2M1 -> fp16 by the packed converter, times the E4M3 block
+// scale in packed fp16: exact) and issues 4 * MS v_mfma_f32_16x16x32_f16 per
+// 32-wide step.  Subtiles of 16 rows beyond the block's row count are
+// skipped, so a block of an expert with few tokens costs its weight stream
+// and little else.
+//
+// K permutation: in a 64-wide chunk lane group g = lane / 16 supplies
+// k = 16 g + 8 i .. +8 at step i (0, 1) for both operands, so a lane needs
+// one 8-byte unit of codes and one scale byte per weight row and chunk.
+//
+// Work order is XCD-aware: consecutive workgroup ids land on different XCDs
+// (round robin over 8), so the item space is cut into 8 contiguous ranges
+// and XCD x walks range x; the weight tiles of one m-block then run next to
+// each other on one XCD and share its L2 copy of the activation rows.
+#include "common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 64;             // K per pipeline stage
+constexpr int kStages = 3;
+constexpr int kARow = kChunk * 2;      // bytes of one fp16 activation row per chunk
+constexpr int kBRows = 256;            // weight rows per workgroup
+constexpr int kBRow = kChunk / 2;      // code bytes of one weight row per chunk
+constexpr int kXcds = 8;
+
+template <int MS>
+struct TileCfg {
+  static constexpr int BM = MS * 16;
+  static constexpr int A_BYTES = BM * kARow;
+  static constexpr int B_BYTES = kBRows * kBRow;
+  static constexpr int S_BYTES = kBRows * (kChunk / 16);
+  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 1 KB direct loads per wave
+  static constexpr int LOADS = A_LOADS + 2 + 1;        // per lane and chunk (A, codes, scales)
+  static_assert(A_BYTES % 4096 == 0, "activation stage splits over four waves");
+};
+
+template <Epi EPI>
+constexpr int cols_per_wave() { return EPI == Epi::SWIGLU ? 32 : 64; }
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+template <int MS, Epi EPI>
+__global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p) {
+  using C = TileCfg<MS>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = p.K, N = p.N;
+  constexpr int kCols = cols_per_wave<EPI>();
+  const int n_tiles = (N + 4 * kCols - 1) / (4 * kCols);
+  const int n_mb = p.n_mblocks_dev ? *p.n_mblocks_dev : p.n_mblocks;
+  const int n_items = n_mb * n_tiles;
+  const int per = (n_items + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per + slot;
+  if (slot >= per || item >= n_items) return;
+  const int mb = item / n_tiles, nt = item - mb * n_tiles;
+
+  int e = 0, pos0, nrows;
+  if (p.mblocks) {
+    const int4 blk = p.mblocks[mb];
+    e = blk.x;
+    pos0 = blk.y;
+    nrows = blk.z;
+  } else {
+    pos0 = mb * C::BM;
+    nrows = (int)(p.dense_rows - pos0 < C::BM ? p.dense_rows - pos0 : C::BM);
+  }
+  const int col0 = (nt * 4 + wave) * kCols;
+
+  // ---- loader state.  Workgroup-local weight row R = 64 w + 16 f + r is row
+  // r of fragment f of wave w (SWIGLU: fragments 2, 3 are the up rows of the
+  // gate rows in fragments 0, 1).  Rows past N reread row N - 1.
+  auto weight_row = [&](int R, int &mat) {
+    const int w = R >> 6, f = (R >> 4) & 3, r = R & 15;
+    mat = (EPI == Epi::SWIGLU && f >= 2) ? 1 : 0;
+    const int fr = EPI == Epi::SWIGLU ? (f & 1) : f;
+    const int row = (nt * 4 + w) * kCols + fr * 16 + r;
+    return row < N ? row : N - 1;
+  };
+  // Codes: LDS row R holds 32 bytes as two 16-byte halves, half h at
+  // position h ^ ((R >> 3) & 1).  Direct load j of wave w is instruction
+  // q = 2 w + j (0..7); it fills 1 KB = rows 32 q .. 32 q + 31, lane l
+  // writing position l % 2 of row 32 q + l / 2.
+  const uint8_t *csrc[2];
+  int cdst[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int q = 2 * wave + j, R = 32 * q + (lane >> 1);
+    int mat;
+    const int row = weight_row(R, mat);
+    const int h = (lane & 1) ^ ((R >> 3) & 1);
+    csrc[j] = p.b_codes[mat] + (int64_t)e * p.b_codes_estride + (int64_t)row * (K / 2) + h * 16;
+    cdst[j] = q * 1024;
+  }
+  // Scales: 4 bytes (one chunk) per row, wave w loads rows 64 w .. 64 w + 63.
+  const uint8_t *ssrc;
+  {
+    int mat;
+    const int row = weight_row(64 * wave + lane, mat);
+    ssrc = p.b_scales[mat] + (int64_t)e * p.b_scales_estride + (int64_t)row * (K / 16);
+  }
+  // Activations: LDS row r holds 128 bytes as eight 16-byte granules, granule
+  // c at position c ^ ((r >> 1) & 7); instruction q = wave + 4 j fills rows
+  // 8 q .. 8 q + 7, lane l writing position l % 8 of row 8 q + l / 8.  Rows
+  // past the block reread row 0 (finite data, results discarded).
+  int arow[C::A_LOADS];
+  // (row >> 1) & 7 = (4 q + l / 16) & 7 = (4 w + l / 16) & 7 for every j
+  const int agran = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) {
+    const int r = 8 * (wave + 4 * j) + (lane >> 3);
+    const int rr = r < nrows ? r : 0;
+    arow[j] = p.a_rowmap ? p.a_rowmap[pos0 + rr] / p.a_rowdiv : pos0 + rr;
+  }
+
+  f32x4 acc[MS][4];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[ms][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nchunks = K / kChunk;
+  const int last = nchunks - 1;
+
+  // Issue the loads of chunk c (K is a multiple of 64) into ring slot c % 3.
+  auto load_chunk = [&](int c) {
+    uint8_t *st = lds + (c % kStages) * C::STAGE;
+    const int k0 = c * kChunk;
+#pragma unroll
+    for (int j = 0; j < C::A_LOADS; ++j)
+      __builtin_amdgcn_global_load_lds(p.A + (int64_t)arow[j] * p.lda + k0 + agran * 8,
+                                       (lds_ptr_t)(st + (wave + 4 * j) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(csrc[j] + k0 / 2, (lds_ptr_t)(st + C::A_BYTES + cdst[j]),
+                                       16, 0, 0);
+    __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
+                                     (lds_ptr_t)(st + C::A_BYTES + C::B_BYTES + wave * 256), 4,
+                                     0, 0);
+  };
+
+  auto compute = [&](int c) {
+    const uint8_t *st = lds + (c % kStages) * C::STAGE;
+    f16x8 bf[2][4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int R = 64 * wave + 16 * f + lr;
+      const int pos = (((lg >> 1) ^ ((R >> 3) & 1)) << 4) + ((lg & 1) << 3);
+      const u32x2 w = *reinterpret_cast<const u32x2 *>(st + C::A_BYTES + R * kBRow + pos);
+      const uint32_t sb = st[C::A_BYTES + C::B_BYTES + R * 4 + lg];
+      f16x2 s0, s1;
+      e4m3x2_to_f16_pairs(sb, s0, s1);
+      bf[0][f] = dequant8_f16(w[0], s0);
+      bf[1][f] = dequant8_f16(w[1], s0);
+    }
+    const uint8_t *abase = st + lr * kARow;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int gran = ((2 * lg + i) ^ ((lr >> 1) & 7)) * 16;
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) {
+        if (ms * 16 >= nrows) break;   // wave-uniform: skip empty subtiles
+        const f16x8 a = *reinterpret_cast<const f16x8 *>(abase + ms * 16 * kARow + gran);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[ms][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bf[i][f], acc[ms][f], 0, 0, 0);
+      }
+    }
+  };
+
+  // Ring: chunks c + 1 and c + 2 are in flight while chunk c is multiplied.
+  // The wait before each barrier leaves only the newest chunk's loads
+  // outstanding; the barrier then also guarantees every wave is done with
+  // the slot the next loads overwrite.  Past the end the last chunk is
+  // requested again (a cache hit into a slot nobody reads).
+  load_chunk(0);
+  load_chunk(last < 1 ? last : 1);
+  for (int c = 0; c <= last; ++c) {
+    // (a plain barrier: __syncthreads would also wait for the newest loads)
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::LOADS) : "memory");
+    load_chunk(c + 2 <= last ? c + 2 : last);
+    compute(c);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: lane holds rows 4*lg + j (j = 0..3) of each subtile and
+  //      column lr of each fragment.
+  const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
+  if constexpr (EPI == Epi::SWIGLU) {
+    float amax = 0.0f;
+    const float gg = p.b_global[0][e] * extra, gu = p.b_global[1][e] * extra;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = ms * 16 + 4 * lg + j;
+        if (r >= nrows) continue;
+        const int pos = pos0 + r;
+        const int arow = p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
+        const int sh = p.a_shift ? p.a_shift[arow] : 0;
+        uint16_t *hrow = static_cast<uint16_t *>(p.out) + (int64_t)pos * p.ldo;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int col = col0 + f * 16 + lr;
+          if (col >= N) continue;
+          const float G = __builtin_ldexpf(acc[ms][f][j], sh) * gg;
+          const float U = __builtin_ldexpf(acc[ms][f + 2][j], sh) * gu;
+          const float hv = G / (1.0f + expf(-G)) * U;
+          const uint32_t hb = f32_to_bf16_bits(hv);
+          hrow[col] = (uint16_t)hb;
+          amax = fmaxf(amax, __builtin_fabsf(bf16_bits_to_f32(hb)));
+        }
+      }
+    }
+    if (p.amax_slot) {
+      amax = wave_max(amax);
+      if (lane == 0 && amax > 0.0f) atomicMax(p.amax_slot, __float_as_uint(amax));
+    }
+  } else {
+    const float gw = p.b_global[0][e] * extra;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = ms * 16 + 4 * lg + j;
+        if (r >= nrows) continue;
+        const int pos = pos0 + r;
+        const int arow = p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
+        const int sh = p.a_shift ? p.a_shift[arow] : 0;
+        int64_t orow = pos;
+        float w = 1.0f;
+        if constexpr (EPI == Epi::DOWN) {
+          const int pair = p.sorted_pairs[pos];
+          orow = pair;
+          w = p.pair_weights[pair];
+        }
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int col = col0 + f * 16 + lr;
+          if (col >= N) continue;
+          float v = __builtin_ldexpf(acc[ms][f][j], sh) * gw;
+          if constexpr (EPI == Epi::DOWN) v *= w;
+          if (p.out_type == OutType::F32)
+            static_cast<float *>(p.out)[orow * p.ldo + col] = v;
+          else
+            static_cast<uint16_t *>(p.out)[orow * p.ldo + col] = (uint16_t)f32_to_bf16_bits(v);
+        }
+      }
+    }
+  }
+}
+
+template <int MS>
+hipError_t launch_ms(Epi epi, const GemmArgs &a, hipStream_t s) {
+  const int cols = epi == Epi::SWIGLU ? 4 * cols_per_wave<Epi::SWIGLU>()
+                                      : 4 * cols_per_wave<Epi::LINEAR>();
+  const int64_t n_tiles = (a.N + cols - 1) / cols;
+  int64_t items = n_tiles * (int64_t)a.n_mblocks;
+  items = (items + kXcds - 1) / kXcds * kXcds;
+  if (items < kXcds) items = kXcds;
+  const dim3 grid((unsigned)items), block(kThreads);
+  switch (epi) {
+    case Epi::LINEAR:
+      launch_kernel((tile_gemm_kernel<MS, Epi::LINEAR>), grid, block, 0, s, a);
+      break;
+    case Epi::SWIGLU:
+      launch_kernel((tile_gemm_kernel<MS, Epi::SWIGLU>), grid, block, 0, s, a);
+      break;
+    case Epi::DOWN:
+      launch_kernel((tile_gemm_kernel<MS, Epi::DOWN>), grid, block, 0, s, a);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool tile_gemm_supported(int K) { return K % kChunk == 0; }
+
+hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s) {
+  if (!tile_gemm_supported(a.K)) return hipErrorInvalidValue;
+  switch (bm) {
+    case 16:
+    case 32: return launch_ms<2>(epi, a, s);
+    case 64: return launch_ms<4>(epi, a, s);
+    default: return launch_ms<8>(epi, a, s);
+  }
+}
+
+}  // namespace nvfp4

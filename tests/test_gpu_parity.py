@@ -231,7 +231,29 @@ def test_moe_ffn_w4a16_small(T, H, I, E, k):
     assert torch.equal(y, y2)
 
 
-@pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (64, 512, 256, 16, 4)])
+# prefill-shaped cases (more than 256 pairs) take the grouped GEMM over
+# m-blocks of 128 rows; H or I not a multiple of 64 takes its fallback kernel.
+# zipf: one expert takes most tokens (several m-blocks, a ragged last one).
+@pytest.mark.parametrize("T,H,I,E,k,zipf", [(80, 256, 192, 8, 4, None), (129, 128, 128, 3, 2, None),
+                                            (300, 512, 256, 16, 2, None), (70, 320, 96, 5, 4, None),
+                                            (333, 256, 128, 32, 2, 3.0), (600, 192, 64, 64, 1, 2.0)])
+def test_moe_ffn_w4a16_tiles(T, H, I, E, k, zipf):
+    say("moe w4a16 tiles", T, H, I, E, k, zipf)
+    x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k, zipf=zipf)
+    counts = np.bincount(rids.ravel(), minlength=E)
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref)
+    assert_close_f32(to_np(y), ref, f"moe tiles (max rows per expert {counts.max()})")
+    ids, wts, off, pairs, w_gpu = st
+    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                         out_dtype=torch.bfloat16)
+    assert_bf16_output(bf16_np(yb), to_np(y), ref, "moe tiles bf16")
+    y2, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                         out_dtype=torch.float32)
+    assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (64, 512, 256, 16, 4),
+                                       (96, 256, 128, 8, 4)])
 def test_moe_ffn_w4a4_small(T, H, I, E, k):
     say("moe w4a4 small", T, H, I, E, k)
     x, rids, rw, y, g_out, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4)
