@@ -473,6 +473,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   // W4A16 decode: both projections stream whole weight rows against the bf16
   // activations as given (no fp16 operand passes)
   const bool rows = small && !a4 && row_gemv_supported((int)H) && row_gemv_supported((int)I);
+  // ... and the down projection sums each token's slots itself (no combine)
+  const bool fused_sum = rows && row_down_sum_supported((int)I, k);
 
   // 1-2. plan (m-blocks per expert), zeroed scratch words and x -> fp16 rows
   if (rows) {   // no plan: the stream kernels read the routing directly
@@ -539,7 +541,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   }
   mark_kernel(NVFP4_STAGE_GATE_UP, stream);
   if (rows)
-    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, sorted_pairs, topk_ids, k, (int)P, stream), "gate/up");
+    LAUNCH(launch_row_gemv(Epi::SWIGLU, g, sorted_pairs, topk_ids, k, (int)P, stream, fused_sum),
+           "gate/up");
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
   else
@@ -591,7 +594,14 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   if (rows) {
     d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
     d.a_shift = nullptr;
-    LAUNCH(launch_row_gemv(Epi::DOWN, d, sorted_pairs, topk_ids, k, (int)P, stream), "down");
+    if (fused_sum) {
+      d.out = y;
+      d.ldo = H;
+      d.out_type = yt;
+      LAUNCH(launch_row_down_sum(d, topk_ids, k, (int)T, stream), "down + combine");
+    } else {
+      LAUNCH(launch_row_gemv(Epi::DOWN, d, sorted_pairs, topk_ids, k, (int)P, stream), "down");
+    }
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else
@@ -600,6 +610,11 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
            "down");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order
+  if (fused_sum) {   // done by the down kernel: an empty stage
+    mark(NVFP4_STAGE_COMBINE, false, stream);
+    mark(NVFP4_STAGE_COMBINE, true, stream);
+    return NVFP4_OK;
+  }
   mark_kernel(NVFP4_STAGE_COMBINE, stream);
   LAUNCH(launch_combine(ws.ypair, T, H, k, y, yt, stream), "combine");
   g_timed_launch = TimedLaunch{nullptr, nullptr};

@@ -131,7 +131,16 @@ int gemv_tile_cols(Epi epi, int N, int K);
 // and 2048..8192 (multiples of 32).
 bool row_gemv_supported(int K);
 hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pairs,
-                           const int32_t *ids, int k, int n_pos, hipStream_t s);
+                           const int32_t *ids, int k, int n_pos, hipStream_t s,
+                           bool h_by_pair = false);
+
+// Token-major down projection for decode with the combine folded in: y[t] =
+// sum over slots j (in order) of w[t k + j] * g * (h[t k + j] . W_down[e]);
+// A = h rows in pair order (bf16), out = y.  Supported for K (= I) in
+// {256, 512, 1024, 2048} and k <= 32.
+bool row_down_sum_supported(int K, int k);
+hipError_t launch_row_down_sum(const GemmArgs &a, const int32_t *ids, int k, int T,
+                               hipStream_t s);
 
 // FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
 // workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.

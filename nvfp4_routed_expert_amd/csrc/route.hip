@@ -127,24 +127,30 @@ struct PermuteLds {
   int32_t wave_tot[kPermThreads / 64];
 };
 
-// ids: the [T, k] expert ids (global or LDS).  One workgroup of kPermThreads.
+// ids: the [T, k] expert ids (global or LDS).  One workgroup of any
+// multiple of 64 threads up to kPermThreads.
 __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W,
                               int32_t *offsets, int32_t *sorted_pairs, PermuteLds &L) {
   uint32_t *bitmap = L.bitmap;
   uint16_t *prefix = L.prefix;
   int32_t *cnt = L.cnt, *off = L.off, *base = L.base, *chunk_cnt = L.chunk_cnt;
   int32_t *wave_tot = L.wave_tot;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, nthr = blockDim.x;
   const int64_t P = T * k;
 
-  for (int e = tid; e < E; e += kPermThreads) { cnt[e] = 0; base[e] = 0; }
+  for (int e = tid; e < E; e += nthr) { cnt[e] = 0; base[e] = 0; }
   __syncthreads();
-  for (int64_t p = tid; p < P; p += kPermThreads) atomicAdd(&cnt[ids[p]], 1);
+  for (int64_t p = tid; p < P; p += nthr) atomicAdd(&cnt[ids[p]], 1);
   __syncthreads();
 
-  // exclusive scan of cnt over E <= 1024 experts (one per thread)
+  // exclusive scan of cnt over E <= 1024 experts: thread tid owns the ept
+  // consecutive experts tid * ept ..
   {
-    const int c = tid < E ? cnt[tid] : 0;
+    const int ept = (E + nthr - 1) / nthr;
+    const int e0 = tid * ept;
+    int c = 0;
+    for (int i = 0; i < ept; ++i)
+      if (e0 + i < E) c += cnt[e0 + i];
     int incl = c;
     const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
@@ -154,11 +160,15 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
     }
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += wave_tot[w];
-    if (tid < E) {
-      off[tid] = wbase + incl - c;
-      offsets[tid] = wbase + incl - c;
+    int run = incl - c;
+    for (int w = 0; w < wave; ++w) run += wave_tot[w];
+    for (int i = 0; i < ept; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        off[e] = run;
+        offsets[e] = run;
+        run += cnt[e];
+      }
     }
     if (tid == 0) offsets[E] = (int32_t)P;
   }
@@ -167,14 +177,14 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
   const int64_t chunk_tokens = (int64_t)W * 32;
   for (int64_t t0 = 0; t0 < T; t0 += chunk_tokens) {
     const int64_t t1 = t0 + chunk_tokens < T ? t0 + chunk_tokens : T;
-    for (int i = tid; i < E * W; i += kPermThreads) bitmap[i] = 0u;
+    for (int i = tid; i < E * W; i += nthr) bitmap[i] = 0u;
     __syncthreads();
-    for (int64_t p = t0 * k + tid; p < t1 * k; p += kPermThreads) {
+    for (int64_t p = t0 * k + tid; p < t1 * k; p += nthr) {
       const int64_t tl = p / k - t0;
       atomicOr(&bitmap[ids[p] * W + (int)(tl >> 5)], 1u << (tl & 31));
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kPermThreads) {
+    for (int e = tid; e < E; e += nthr) {
       int run = 0;
       for (int w = 0; w < W; ++w) {
         prefix[e * W + w] = (uint16_t)run;
@@ -183,7 +193,7 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
       chunk_cnt[e] = run;
     }
     __syncthreads();
-    for (int64_t p = t0 * k + tid; p < t1 * k; p += kPermThreads) {
+    for (int64_t p = t0 * k + tid; p < t1 * k; p += nthr) {
       const int e = ids[p];
       const int64_t tl = p / k - t0;
       const int w = (int)(tl >> 5);
@@ -192,7 +202,7 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
       sorted_pairs[off[e] + rank] = (int32_t)p;
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kPermThreads) base[e] += chunk_cnt[e];
+    for (int e = tid; e < E; e += nthr) base[e] += chunk_cnt[e];
     __syncthreads();
   }
 }
@@ -203,21 +213,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
     int32_t *sorted_pairs) {
   __shared__ PermuteLds L;
   permute_block(ids, T, E, k, W, offsets, sorted_pairs, L);
-}
-
-// Small T: one workgroup does the top-k of every token (waves take tokens
-// t, t + 16, ...) and then the permutation, from a copy of the ids in LDS.
-constexpr int kSmallT = 32;
-__global__ __launch_bounds__(kPermThreads) void route_small_kernel(
-    const float *logits, int64_t T, int E, int k, int renormalize, int W, int32_t *ids,
-    float *weights, int32_t *offsets, int32_t *sorted_pairs) {
-  __shared__ PermuteLds L;
-  __shared__ int32_t ids_lds[kSmallT * 32];
-  const int wave = threadIdx.x >> 6;
-  for (int64_t t = wave; t < T; t += kPermThreads / 64)
-    wave_topk(logits + t * E, E, k, renormalize, ids + t * k, weights + t * k, ids_lds + t * k);
-  __syncthreads();
-  permute_block(ids_lds, T, E, k, W, offsets, sorted_pairs, L);
 }
 
 int permute_words(int64_t T, int E) {
@@ -236,19 +231,19 @@ int permute_words(int64_t T, int E) {
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         hipStream_t s) {
+  // top-k: one wavefront per token, four per workgroup, so a decode batch
+  // spreads over several CUs (one wave per SIMD) instead of sharing one
   const int W = permute_words(T, E);
-  if (T <= kSmallT) {
-    launch_kernel(route_small_kernel, dim3(1), dim3(kPermThreads), 0, s, logits, T, E, k,
-                       renormalize, W, ids, weights, offsets, sorted_pairs);
-    return hipGetLastError();
-  }
   const int64_t blocks = (T + 3) / 4;
-  launch_kernel(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
-                     E, k, renormalize, ids, weights);
+  launch_kernel(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T, E, k,
+                renormalize, ids, weights);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  launch_kernel(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, T, E, k, W,
-                     offsets, sorted_pairs);
+  // permutation: one workgroup, small for decode-sized batches (fewer
+  // waves make its barriers cheaper)
+  const int threads = T * k <= 1024 ? 256 : kPermThreads;
+  launch_kernel(permute_kernel, dim3(1), dim3(threads), 0, s, ids, T, E, k, W, offsets,
+                sorted_pairs);
   return hipGetLastError();
 }
 

@@ -38,6 +38,7 @@ namespace {
 
 constexpr int kSlice = 2048;   // K elements covered by one wave (64 lanes x 32)
 constexpr int kBatch = 8;      // load steps in flight and reduced together
+constexpr int kMaxSlots = 32;  // top-k slots a token-major down item sums
 
 // ---------------------------------------------------------------------------
 // arithmetic
@@ -175,6 +176,7 @@ struct Routing {
   const int32_t *sorted_pairs;   // null: dense
   const int32_t *ids;
   int k;
+  bool h_by_pair;                // SWIGLU: write h row `pair` instead of `pos`
 };
 
 template <int LPR, Epi EPI>
@@ -317,7 +319,8 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const R
         const float G = r[0] * p.b_global[0][cur.e] * extra;
         const float U = r[1] * p.b_global[NMAT - 1][cur.e] * extra;
         const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
-        static_cast<uint16_t *>(p.out)[(int64_t)cur.pos * p.ldo + row] = (uint16_t)hb;
+        const int64_t hrow = rt.h_by_pair ? cur.pair : cur.pos;
+        static_cast<uint16_t *>(p.out)[hrow * p.ldo + row] = (uint16_t)hb;
       } else {
         float v = r[0] * p.b_global[0][cur.e] * extra;
         int64_t orow = cur.pos;
@@ -337,6 +340,98 @@ __global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const R
     pair_after = pair_after2;
 #pragma unroll
     for (int j = 0; j < 16; ++j) a_cur[j] = a_nxt[j];
+  }
+}
+
+// Token-major down projection with the combine folded in (decode).  A
+// workgroup owns (token t, ROWS consecutive output rows); wave w takes the
+// token's slots j = w, w + 4, ... and streams the rows of expert ids[t k + j]
+// against h of pair t k + j (h is pair-major), scaled by the expert's global
+// and the routing weight.  Wave 0 then adds the slots in order j = 0 .. k-1,
+// the same fp32 sum the separate combine would form, and writes y[t].  Only
+// for K <= 2048 (one wave per row slice).
+template <int LPR>
+__global__ __launch_bounds__(256) void row_down_sum_kernel(const GemmArgs p, const int32_t *ids,
+                                                           int k) {
+  using C = RowCfg<LPR, Epi::DOWN>;
+  __shared__ float slot_val[kMaxSlots * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int K = p.K, N = p.N;
+  const int sub = lane / LPR, seg = lane % LPR;
+  const int kseg = 32 * seg;
+  const bool kval = kseg < K;
+  const uint32_t kc = (uint32_t)min(kseg, K - 32);
+  const uint32_t code_row = (uint32_t)K / 2, scale_row = (uint32_t)K / 16;
+  const int groups = (N + C::ROWS - 1) / C::ROWS;
+  const int t = blockIdx.x / groups;
+  const int r0 = (blockIdx.x - t * groups) * C::ROWS;
+  const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
+
+  // the token's experts and routing weights, lane j holding slot j
+  const int my_e = lane < k ? ids[t * k + lane] : 0;
+  const float my_w = lane < k ? p.pair_weights[t * k + lane] : 0.0f;
+
+  const uint32_t last_code = (uint32_t)(N - 1) * code_row + kc / 2;
+  const uint32_t last_scale = (uint32_t)(N - 1) * scale_row + kc / 16;
+  const uint32_t step_code = (uint32_t)C::RPL * code_row, step_scale = (uint32_t)C::RPL * scale_row;
+  const uint32_t code0 = (uint32_t)(r0 + sub) * code_row + kc / 2;
+  const uint32_t scale0 = (uint32_t)(r0 + sub) * scale_row + kc / 16;
+
+  u32x4 bq[kBatch];
+  uint32_t sq[kBatch];
+  uint32_t a[16];
+  auto load = [&](int j) {
+    const int e = __builtin_amdgcn_readlane(my_e, j);
+    const uint8_t *cb = p.b_codes[0] + (int64_t)e * p.b_codes_estride;
+    const uint8_t *sb = p.b_scales[0] + (int64_t)e * p.b_scales_estride;
+#pragma unroll
+    for (int d = 0; d < kBatch; ++d) {
+      const uint32_t oc = min(code0 + (uint32_t)d * step_code, last_code);
+      const uint32_t os = min(scale0 + (uint32_t)d * step_scale, last_scale);
+      bq[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cb + oc));
+      sq[d] = *reinterpret_cast<const uint16_t *>(sb + os);
+    }
+    const uint16_t *src =
+        reinterpret_cast<const uint16_t *>(p.A) + (int64_t)(t * k + j) * p.lda + kc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 8 * q);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[4 * q + i] = v[i];
+    }
+  };
+
+  for (int j = wave; j < k; j += 4) {
+    load(j);
+    float part[kBatch];
+#pragma unroll
+    for (int d = 0; d < kBatch; ++d) {
+      const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sq[d], 1.0f, false);
+      uint32_t w[16];
+      decode32(bq[d], w);
+      part[d] = kval ? dot32(w, a, sc[0], sc[1]) : 0.0f;
+    }
+    const float r = reduce8<C::G>(part, lane);
+    const int e = __builtin_amdgcn_readlane(my_e, j);
+    const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_w), j));
+    slot_val[j * 64 + lane] = r * p.b_global[0][e] * extra * wj;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float acc = slot_val[lane];
+    for (int j = 1; j < k; ++j) acc += slot_val[j * 64 + lane];
+    int idx;
+    if constexpr (C::G == 64) idx = lane >> 3;
+    else if constexpr (C::G == 32) idx = (lane >> 2) & 7;
+    else if constexpr (C::G == 16) idx = (lane >> 1) & 7;
+    else idx = lane & 7;
+    const int row = r0 + idx * C::RPL + lane / LPR;
+    if ((lane % C::DUP) == 0 && row < N) {
+      if (p.out_type == OutType::F32)
+        static_cast<float *>(p.out)[(int64_t)t * p.ldo + row] = acc;
+      else
+        static_cast<uint16_t *>(p.out)[(int64_t)t * p.ldo + row] = (uint16_t)f32_to_bf16_bits(acc);
+    }
   }
 }
 
@@ -366,7 +461,29 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, const Routing &info, int n_pos
   return hipGetLastError();
 }
 
+template <int LPR>
+hipError_t launch_down_sum(const GemmArgs &a, const int32_t *ids, int k, int T, hipStream_t s) {
+  constexpr int rows = kBatch * (64 / LPR);
+  const int64_t groups = (a.N + rows - 1) / rows;
+  const dim3 grid((unsigned)(groups * T)), block(256);
+  launch_kernel((row_down_sum_kernel<LPR>), grid, block, 0, s, a, ids, k);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool row_down_sum_supported(int K, int k) {
+  return (K == 256 || K == 512 || K == 1024 || K == kSlice) && k >= 1 && k <= kMaxSlots;
+}
+
+hipError_t launch_row_down_sum(const GemmArgs &a, const int32_t *ids, int k, int T,
+                               hipStream_t s) {
+  if (!row_down_sum_supported(a.K, k)) return hipErrorInvalidValue;
+  if (a.K == 512) return launch_down_sum<16>(a, ids, k, T, s);
+  if (a.K == 256) return launch_down_sum<8>(a, ids, k, T, s);
+  if (a.K == 1024) return launch_down_sum<32>(a, ids, k, T, s);
+  return launch_down_sum<64>(a, ids, k, T, s);
+}
 
 bool row_gemv_supported(int K) {
   if (K % 32 != 0) return false;
@@ -375,9 +492,9 @@ bool row_gemv_supported(int K) {
 }
 
 hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pairs,
-                           const int32_t *ids, int k, int n_pos, hipStream_t s) {
+                           const int32_t *ids, int k, int n_pos, hipStream_t s, bool h_by_pair) {
   const int K = a.K;
-  const Routing info{sorted_pairs, ids, k < 1 ? 1 : k};
+  const Routing info{sorted_pairs, ids, k < 1 ? 1 : k, h_by_pair};
   if (K == 512) return launch_cfg<16>(epi, a, info, n_pos, s);    // items of 32 rows
   if (K == 256) return launch_cfg<8>(epi, a, info, n_pos, s);     // items of 64 rows
   if (K == 1024) return launch_cfg<32>(epi, a, info, n_pos, s);   // items of 16 rows
