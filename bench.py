@@ -175,17 +175,18 @@ def main():
     ws = torch.empty(native.ffn_workspace_bytes(T, H, I, E, k, act), dtype=torch.uint8,
                      device=dev)
     ag = torch.empty(2, dtype=torch.float32, device=dev) if act == native.W4A4 else None
+    rws = native.route_workspace(T, E, k, dev)
     route = E > 1
 
     def step(c):
         if route:
-            native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs))
+            native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
         native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
                                      act_globals=None, out_dtype=torch.bfloat16,
                                      workspace=ws, out=y)
 
     if not route:   # one expert: the routing is fixed (all rows to expert 0)
-        native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs))
+        native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
     step(0)
     torch.cuda.synchronize()
 

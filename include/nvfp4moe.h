@@ -149,6 +149,12 @@ size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K,
  * offsets[e] .. offsets[e+1]-1), sorted_pairs [T*k] int32.
  * The ids, offsets and permutation are exact integers; the weights are fp32.
  * Requires 1 <= k <= E <= 1024, k <= 32, 1 <= T <= 2^24 / k.
+ * workspace (moe_route_topk_workspace_size bytes, device, 16-byte aligned):
+ * its first 32-bit word must be zero when the call runs, and every call
+ * leaves it zero, so a workspace zeroed once serves successive calls on one
+ * stream; calls that may run at the same time need separate workspaces.
+ * (Decode-sized batches route in one launch whose last finishing wavefront
+ * builds the permutation; the word counts finished wavefronts.)
  */
 nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E,
                             int32_t k, int renormalize, int32_t *topk_ids,

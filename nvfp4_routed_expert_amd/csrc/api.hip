@@ -357,7 +357,7 @@ size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k) {
   (void)T;
   (void)E;
   (void)k;
-  return 0;
+  return 256;   // word 0: the ticket counter of the one-launch decode routing
 }
 
 nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
@@ -365,8 +365,6 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
                             int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  (void)workspace;
-  (void)workspace_bytes;
   CHECK_NULL(logits);
   CHECK_NULL(topk_ids);
   CHECK_NULL(topk_weights);
@@ -384,8 +382,9 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
   CHECK_ALIGN(topk_weights);
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
+  TRY(check_workspace(workspace, workspace_bytes, moe_route_topk_workspace_size(T, E, k)));
   LAUNCH(launch_route(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets,
-                      sorted_pairs, stream),
+                      sorted_pairs, static_cast<uint32_t *>(workspace), stream),
          "route");
   return NVFP4_OK;
 }

@@ -69,9 +69,12 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols,
 
 // Top-k ids/weights and the expert-sorted permutation (one workgroup for
 // T <= 32 tokens, else a top-k grid followed by a one-workgroup permutation).
+// ticket: a zero uint32 in the caller's workspace (left zero on return); with
+// it, decode-sized batches (route_decode_supported) route in one launch.
+bool route_decode_supported(int64_t T, int E, int k);
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
-                        hipStream_t s);
+                        uint32_t *ticket, hipStream_t s);
 
 // ---- grouped GEMM and FFN glue (gemm.hip) ---------------------------------------
 

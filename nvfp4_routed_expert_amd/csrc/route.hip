@@ -101,6 +101,133 @@ __device__ void wave_topk(const float *row, int E, int k, int renormalize, int32
   }
 }
 
+// ---- merge-network top-k (E <= 512, k <= 8) -------------------------------
+//
+// The round-by-round argmax above is a long dependent chain (k rounds of a
+// six-level reduction).  For the common decode shapes this variant orders
+// 64-bit keys instead: key = (order-preserving bits of the logit, complement
+// of the index), so a larger key is a larger logit or, on equal logits, a
+// lower index (the same order as `beats`; -0 is folded into +0 first).  Each
+// lane sorts its 8 keys with a 19-comparator network, then six merge levels
+// pair lanes (xor 1, xor 2, the mirrored lane in 8 and in 16 through DPP,
+// then the other row and the other half through permlane swaps); a merge
+// keeps the top 8 of both sorted lists (elementwise max against the
+// partner's reversed list, then a bitonic clean-up).  Both partners compute
+// the same list, so after the last level every lane holds the sorted top 8.
+
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+  const uint32_t b = __float_as_uint(v + 0.0f);   // -0 -> +0
+  const uint32_t m = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)m << 32) | (uint32_t)~(uint32_t)e;
+}
+
+// keep the larger key in x, the smaller in y
+__device__ __forceinline__ void cas(uint64_t &x, uint64_t &y) {
+  const bool sw = y > x;
+  const uint64_t hi = sw ? y : x, lo = sw ? x : y;
+  x = hi;
+  y = lo;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint32_t swap16_partner(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return ((lane >> 4) & 1) ? (uint32_t)r[0] : (uint32_t)r[1];
+}
+__device__ __forceinline__ uint32_t swap32_partner(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return lane >= 32 ? (uint32_t)r[0] : (uint32_t)r[1];
+}
+
+template <int LEVEL>
+__device__ __forceinline__ uint64_t partner_key(uint64_t v, int lane) {
+  if constexpr (LEVEL == 0) return dpp_u64<0xB1>(v);    // lane ^ 1
+  if constexpr (LEVEL == 1) return dpp_u64<0x4E>(v);    // lane ^ 2
+  if constexpr (LEVEL == 2) return dpp_u64<0x141>(v);   // 7 - i within 8
+  if constexpr (LEVEL == 3) return dpp_u64<0x140>(v);   // 15 - i within 16
+  if constexpr (LEVEL == 4)
+    return ((uint64_t)swap16_partner((uint32_t)(v >> 32), lane) << 32) |
+           swap16_partner((uint32_t)v, lane);
+  return ((uint64_t)swap32_partner((uint32_t)(v >> 32), lane) << 32) |
+         swap32_partner((uint32_t)v, lane);
+}
+
+template <int LEVEL>
+__device__ __forceinline__ void merge_level(uint64_t (&c)[8], int lane) {
+  uint64_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) b[i] = partner_key<LEVEL>(c[i], lane);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = c[i] > b[7 - i] ? c[i] : b[7 - i];
+#pragma unroll
+  for (int d = 4; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((i & d) == 0) cas(c[i], c[i + d]);
+}
+
+__device__ void wave_topk_merge(const float *row, int E, int k, int renormalize, int32_t *ids,
+                                float *weights, int32_t *ids_copy) {
+  const int lane = threadIdx.x & 63;
+  float v[8];
+  uint64_t c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : 0.0f;
+    c[i] = e < E ? topk_key(v[i], e) : 0ull;
+  }
+  constexpr int kNet[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6},
+                               {3, 7}, {0, 1}, {2, 3}, {4, 5}, {6, 7}, {2, 4}, {3, 5},
+                               {1, 4}, {3, 6}, {1, 2}, {3, 4}, {5, 6}};
+#pragma unroll
+  for (int n = 0; n < 19; ++n) cas(c[kNet[n][0]], c[kNet[n][1]]);
+  merge_level<0>(c, lane);
+  merge_level<1>(c, lane);
+  merge_level<2>(c, lane);
+  merge_level<3>(c, lane);
+  merge_level<4>(c, lane);
+  merge_level<5>(c, lane);
+  // lane j < k takes the j-th key
+  uint64_t mine = c[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mine = lane == i ? c[i] : mine;
+  const int my_idx = (int)~(uint32_t)mine;
+  const uint32_t m = (uint32_t)(mine >> 32);
+  const float my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+  const float lmax = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
+  const float ex = lane < k ? expf(my_val - lmax) : 0.0f;
+  float denom;
+  if (renormalize) {
+    denom = wave_sum(ex);
+  } else {
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (lane + 64 * i < E) s += expf(v[i] - lmax);
+    denom = wave_sum(s);
+  }
+  if (lane < k) {
+    ids[lane] = my_idx;
+    weights[lane] = ex / denom;
+    if (ids_copy) ids_copy[lane] = my_idx;
+  }
+}
+
+// One wavefront per token.
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
+    const float *logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
+    float *weights) {
+  const int64_t t = (int64_t)blockIdx.x * (kTopkThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  wave_topk_merge(logits + t * E, E, k, renormalize, ids + t * k, weights + t * k, nullptr);
+}
+
 // One wavefront per token.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
     const float *logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
@@ -215,6 +342,144 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   permute_block(ids, T, E, k, W, offsets, sorted_pairs, L);
 }
 
+// Permutation of a decode-sized batch (T k <= 256 pairs, E <= 1024), one
+// workgroup of 256 threads: expert counts by LDS atomics, one wave scans
+// them into the offsets, and pair p (expert e) goes to offsets[e] plus the
+// number of earlier pairs with expert e, counted directly from the ids in
+// LDS: the stable counting-sort result in three barriers.
+constexpr int kSmallPairs = 256;
+__global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, int64_t T, int E,
+                                                            int k, int32_t *offsets,
+                                                            int32_t *sorted_pairs) {
+  __shared__ int32_t ids_lds[kSmallPairs];
+  __shared__ int32_t cnt[kMaxExperts];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int P = (int)T * k;
+  for (int e = tid; e < E; e += 256) cnt[e] = 0;
+  int my_e = 0;
+  if (tid < P) {
+    my_e = ids[tid];
+    ids_lds[tid] = my_e;
+  }
+  __syncthreads();
+  if (tid < P) atomicAdd(&cnt[my_e], 1);
+  __syncthreads();
+  if (tid < 64) {   // exclusive scan: lane l owns experts l * per .. (l + 1) * per - 1
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    int local = 0;
+    for (int i = 0; i < per; ++i)
+      if (e0 + i < E) local += cnt[e0 + i];
+    int incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - local;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        const int c = cnt[e];
+        cnt[e] = run;   // now the expert's first position
+        offsets[e] = run;
+        run += c;
+      }
+    }
+    if (lane == 0) offsets[E] = P;
+  }
+  __syncthreads();
+  if (tid < P) {
+    int before = 0;
+    for (int q = 0; q < tid; ++q) before += ids_lds[q] == my_e;
+    sorted_pairs[cnt[my_e] + before] = tid;
+  }
+}
+
+// Decode-sized routing in one launch (T k <= 256 pairs, E <= 512, k <= 8):
+// one wavefront per token (own workgroup, so tokens spread over CUs) takes
+// the top-k with the merge network and publishes ids and weights; each wave
+// then takes a ticket from a counter in the caller's workspace
+// (acquire-release at device scope), and the wave holding the last ticket,
+// which therefore sees every token's ids, resets the counter and builds the
+// permutation alone: expert counts by LDS atomics, a DPP scan into the
+// offsets, and for pair p (expert e) the position offsets[e] + (earlier
+// pairs with expert e), counted 16 ids per step from LDS.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  // inclusive prefix sum over the 64 lanes (row shifts, then row broadcasts)
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  (void)lane;
+  return x;
+}
+
+__global__ __launch_bounds__(64) void route_decode_kernel(const float *logits, int64_t T, int E,
+                                                          int k, int renormalize, int32_t *ids,
+                                                          float *weights, int32_t *offsets,
+                                                          int32_t *sorted_pairs,
+                                                          uint32_t *ticket) {
+  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kSmallPairs];
+  __shared__ __attribute__((aligned(16))) int32_t cnt[512];
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  wave_topk_merge(logits + (int64_t)t * E, E, k, renormalize, ids + (int64_t)t * k,
+                  weights + (int64_t)t * k, nullptr);
+  uint32_t mine = 0;
+  if (lane == 0)
+    mine = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  mine = __builtin_amdgcn_readfirstlane(mine);
+  if (mine != (uint32_t)T - 1) return;
+  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  const int P = (int)T * k;
+  for (int e = lane; e < E; e += 64) cnt[e] = 0;
+  for (int p = lane; p < P; p += 64) ids_lds[p] = ids[p];
+  __syncthreads();
+  for (int p = lane; p < P; p += 64) atomicAdd(&cnt[ids_lds[p]], 1);
+  __syncthreads();
+  // lane l owns experts 8 l .. 8 l + 7
+  int c8[8], local = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = 8 * lane + i;
+    c8[i] = e < E ? cnt[e] : 0;
+    local += c8[i];
+  }
+  int run = wave_incl_scan(local, lane) - local;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = 8 * lane + i;
+    if (e < E) {
+      cnt[e] = run;
+      offsets[e] = run;
+    }
+    run += c8[i];
+  }
+  if (lane == 0) offsets[E] = P;
+  __syncthreads();
+  for (int p = lane; p < P; p += 64) {
+    const int e = ids_lds[p];
+    int before = 0;
+    for (int q0 = 0; q0 < p; q0 += 16) {
+      const int4 *v = reinterpret_cast<const int4 *>(ids_lds + q0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int4 w = v[u];
+        const int q = q0 + 4 * u;
+        before += (w.x == e) & (q < p);
+        before += (w.y == e) & (q + 1 < p);
+        before += (w.z == e) & (q + 2 < p);
+        before += (w.w == e) & (q + 3 < p);
+      }
+    }
+    sorted_pairs[cnt[e] + before] = p;
+  }
+}
+
 int permute_words(int64_t T, int E) {
   // words per expert per chunk: E * W <= kBitmapWords, and W * 32 tokens
   // per chunk keep every per-word prefix below 2^16
@@ -228,21 +493,37 @@ int permute_words(int64_t T, int E) {
 
 }  // namespace
 
+bool route_decode_supported(int64_t T, int E, int k) {
+  return T * k <= kSmallPairs && E <= 512 && k <= 8;
+}
+
 hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
-                        hipStream_t s) {
+                        uint32_t *ticket, hipStream_t s) {
+  if (ticket && route_decode_supported(T, E, k)) {
+    launch_kernel(route_decode_kernel, dim3((unsigned)T), dim3(64), 0, s, logits, T, E, k,
+                  renormalize, ids, weights, offsets, sorted_pairs, ticket);
+    return hipGetLastError();
+  }
   // top-k: one wavefront per token, four per workgroup, so a decode batch
   // spreads over several CUs (one wave per SIMD) instead of sharing one
   const int W = permute_words(T, E);
   const int64_t blocks = (T + 3) / 4;
-  launch_kernel(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T, E, k,
-                renormalize, ids, weights);
+  if (E <= 512 && k <= 8)
+    launch_kernel(topk_merge_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
+                  E, k, renormalize, ids, weights);
+  else
+    launch_kernel(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T, E, k,
+                  renormalize, ids, weights);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // permutation: one workgroup, small for decode-sized batches (fewer
-  // waves make its barriers cheaper)
-  const int threads = T * k <= 1024 ? 256 : kPermThreads;
-  launch_kernel(permute_kernel, dim3(1), dim3(threads), 0, s, ids, T, E, k, W, offsets,
+  // permutation: one workgroup
+  if (T * k <= kSmallPairs) {
+    launch_kernel(permute_small_kernel, dim3(1), dim3(256), 0, s, ids, T, E, k, offsets,
+                  sorted_pairs);
+    return hipGetLastError();
+  }
+  launch_kernel(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, T, E, k, W, offsets,
                 sorted_pairs);
   return hipGetLastError();
 }

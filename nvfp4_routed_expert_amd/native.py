@@ -187,9 +187,17 @@ def nvfp4_linear(x, codes, scales, g, act=W4A16, act_global=None,
     return y, ag
 
 
-def moe_route_topk(logits, k, renormalize=True, out=None):
+def route_workspace(T, E, k, device):
+    """A zeroed routing workspace; every call leaves it zeroed again, so one
+    workspace serves successive (not overlapping) calls on a stream."""
+    return torch.zeros(max(lib().moe_route_topk_workspace_size(T, E, k), 1), dtype=torch.uint8,
+                       device=device)
+
+
+def moe_route_topk(logits, k, renormalize=True, out=None, workspace=None):
     """Returns (topk_ids [T,k] i32, topk_weights [T,k] f32, expert_offsets [E+1] i32,
-    sorted_pairs [T*k] i32)."""
+    sorted_pairs [T*k] i32).  workspace: from route_workspace (a fresh zeroed
+    one is made when omitted)."""
     T, E = logits.shape
     dev = logits.device
     if out is None:
@@ -201,7 +209,8 @@ def moe_route_topk(logits, k, renormalize=True, out=None):
         ids, w, off, pairs = out
     L = lib()
     nbytes = L.moe_route_topk_workspace_size(T, E, k)
-    ws = _workspace(nbytes, dev)
+    ws = _workspace(nbytes, dev, workspace) if workspace is not None else \
+        route_workspace(T, E, k, dev)
     _check(L.moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
                             _ptr(off), _ptr(pairs), _ptr(ws), nbytes, _stream()))
     return ids, w, off, pairs

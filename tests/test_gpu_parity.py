@@ -111,6 +111,8 @@ ROUTE_CASES = [
     ("k_eq_e_5x7", 5, 7, 7, None, True),
     ("big_e_3x1024_k32", 3, 1024, 32, None, True),
     ("long_9000x64_k2", 9000, 64, 2, None, True),
+    ("decode_ties_32x256_k8", 32, 256, 8, None, True),
+    ("one_token_1x512_k8", 1, 512, 8, None, True),
 ]
 
 
@@ -119,7 +121,7 @@ def test_route_topk_parity(case):
     name, T, E, k, zipf, renorm = case
     say("route", name)
     logits = synth.router_logits(T, E, seed=1, zipf_s=zipf)
-    if name.startswith("ragged"):
+    if name.startswith("ragged") or "ties" in name:
         logits = np.round(logits * 2) / 2      # plant many ties
     ids, w, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k, renorm)
     rids, rw = O.route_topk(logits, k, renorm)
@@ -128,6 +130,26 @@ def test_route_topk_parity(case):
     assert np.array_equal(to_np(off), roff)
     assert np.array_equal(to_np(pairs), rpairs)
     np.testing.assert_allclose(to_np(w), rw, rtol=5e-6, atol=1e-7)
+
+
+def test_route_workspace_reused_across_calls():
+    """One zeroed workspace serves successive decode-sized calls: each call's
+    last wavefront resets the counter, and every call is exact."""
+    T, E, k = 16, 512, 8
+    say("route workspace reuse")
+    ws = native.route_workspace(T, E, k, DEV)
+    for seed in (3, 4, 5, 6):
+        logits = synth.router_logits(T, E, seed=seed)
+        if seed == 5:
+            logits = np.round(logits)   # ties
+        ids, w, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k,
+                                                   workspace=ws)
+        rids, rw = O.route_topk(logits, k)
+        roff, rpairs = O.permute(rids, E)
+        assert np.array_equal(to_np(ids), rids)
+        assert np.array_equal(to_np(off), roff)
+        assert np.array_equal(to_np(pairs), rpairs)
+        assert int(to_np(ws[:4].view(torch.int32))[0]) == 0
 
 
 # ---------------------------------------------------------------------------

@@ -100,6 +100,7 @@ def test_route_validation():
     assert r(16, 64, 8, logits=None) == 1
     assert r(16, 64, 8, logits=FAKE_MIS) == 3
     assert r((1 << 22), 64, 8) == 2
+    assert r(16, 64, 8) == 4 and "workspace" in _last()
 
 
 def test_ffn_validation():
