@@ -92,7 +92,7 @@ def stored_traffic(kernel, workload):
 def gate_up_kernel(T, H, I, E, k, act):
     """Which kernel runs the gate/up projection (mirrors the library's dispatch)."""
     small = 2 * T * k <= 32 * E
-    row_ok = lambda K: K in (256, 512, 1024) or (K % 32 == 0 and 2048 <= K <= 8192)
+    row_ok = lambda K: K in (256, 512, 1024) or (K % 32 == 0 and 2048 <= K <= 32768)
     if small and act == "w4a16" and row_ok(H) and row_ok(I):
         return "row_gemv_kernel"
     return "grouped_gemv_kernel" if small else "grouped_gemm_kernel"

@@ -115,13 +115,24 @@ struct LinearWs {
   int32_t *shift;
   float *partials;
   float *g_x;
+  float *split;   // partial sums of a K-split GEMM
 };
-LinearWs carve_linear(Carver &c, int64_t M, int64_t K) {
+// the dense row-streaming GEMV serves one or two rows (more would stream
+// the weights once per row); larger M runs the tile GEMM
+bool linear_rows(int64_t M, int64_t K, nvfp4_act_mode act) {
+  return act == NVFP4_W4A16 && M <= 2 && row_gemv_supported((int)K);
+}
+TilePlan linear_plan(int64_t M, int64_t N, int64_t K) {
+  const int bm = gemm_block_rows(M);
+  return tile_gemm_plan(Epi::LINEAR, N, K, (M + bm - 1) / bm, M);
+}
+LinearWs carve_linear(Carver &c, int64_t M, int64_t N, int64_t K) {
   LinearWs w;
   w.x16 = c.take<_Float16>((size_t)(M * K));
   w.shift = c.take<int32_t>((size_t)M);
   w.partials = c.take<float>(kMaxPartials);
   w.g_x = c.take<float>(4);
+  w.split = c.take<float>(tile_gemm_supported((int)K) ? linear_plan(M, N, K).partial_floats : 0);
   return w;
 }
 
@@ -136,11 +147,41 @@ struct FfnWs {
   int32_t *n_mblocks;
   uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h, [3] -
   float *partials;
+  float *split;         // partial sums of a K-split GEMM
 };
-int ffn_bm(int64_t T, int64_t E, int64_t k) {
-  return 2 * T * k <= 32 * E ? 16 : 128;
+// Decode-sized batches: at most 256 (token, expert) pairs that average at
+// most 16 per expert run as GEMVs over the pairs (a single expert, the dense
+// MLP, only for one or two tokens, since the GEMVs stream an expert's rows
+// once per pair).  Anything larger runs as a grouped GEMM over m-blocks of
+// up to 128 rows, which streams every active expert's weights once per block
+// however skewed the routing is (one expert holding almost every token of a
+// prefill chunk costs a few blocks, not one weight stream per token).
+bool ffn_small(int64_t T, int64_t E, int64_t k) {
+  if (E == 1) return T * k <= 2;
+  return T * k <= 256 && 2 * T * k <= 32 * E;
 }
-int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) { return (P + bm - 1) / bm + E; }
+int ffn_bm(int64_t T, int64_t E, int64_t k) {
+  if (ffn_small(T, E, k)) return 16;
+  return E == 1 ? gemm_block_rows(T * k) : 128;
+}
+// m-blocks of up to bm rows over P pairs: each expert rounds up once (a
+// single expert, the dense MLP, has exactly ceil(P / bm))
+int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) {
+  return (P + bm - 1) / bm + (E > 1 ? (E < P ? E : P) : 0);
+}
+struct FfnPlans {
+  TilePlan gate_up, down;
+};
+FfnPlans ffn_plans(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  FfnPlans f;
+  const int64_t P = T * k;
+  const int64_t mb = ffn_max_mblocks(P, E, ffn_bm(T, E, k));
+  if (!ffn_small(T, E, k)) {
+    if (tile_gemm_supported((int)H)) f.gate_up = tile_gemm_plan(Epi::SWIGLU, I, H, mb, P);
+    if (tile_gemm_supported((int)I)) f.down = tile_gemm_plan(Epi::DOWN, H, I, mb, P);
+  }
+  return f;
+}
 FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t P = T * k;
   FfnWs w;
@@ -154,15 +195,12 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.n_mblocks = c.take<int32_t>(4);
   w.slots = c.take<uint32_t>(4);
   w.partials = c.take<float>(kMaxPartials);
+  const FfnPlans pl = ffn_plans(T, H, I, E, k);
+  w.split = c.take<float>(pl.gate_up.partial_floats > pl.down.partial_floats
+                              ? pl.gate_up.partial_floats
+                              : pl.down.partial_floats);
   return w;
 }
-// Decode-sized batches: at most 256 (token, expert) pairs that average at
-// most 16 per expert run as GEMVs over the pairs.  Anything larger runs as a
-// grouped GEMM over m-blocks of 128 rows, which streams every active
-// expert's weights once per block however skewed the routing is (one expert
-// holding almost every token of a prefill chunk costs a few blocks, not one
-// weight stream per token).
-bool ffn_small(int64_t T, int64_t E, int64_t k) { return T * k <= 256 && 2 * T * k <= 32 * E; }
 
 }  // namespace
 
@@ -262,11 +300,10 @@ nvfp4_status nvfp4_dequantize(const nvfp4_matrix *w, float *out, hipStream_t str
 // ---- nvfp4_linear -------------------------------------------------------------------
 
 size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, nvfp4_act_mode act) {
-  (void)N;
   (void)act;
-  if (M < 1 || K < 1) return 0;
+  if (M < 1 || K < 1 || N < 1) return 0;
   Carver c(nullptr);
-  carve_linear(c, M, K);
+  carve_linear(c, M, N, K);
   return c.used;
 }
 
@@ -295,10 +332,10 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   const int64_t K = w->cols, N = w->rows;
   TRY(check_workspace(workspace, workspace_bytes, nvfp4_linear_workspace_size(M, N, K, act)));
   Carver c(workspace);
-  const LinearWs ws = carve_linear(c, M, K);
+  const LinearWs ws = carve_linear(c, M, N, K);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   // decode-sized W4A16: stream the weight rows against the bf16 rows as given
-  if (act == NVFP4_W4A16 && M <= 16 && row_gemv_supported((int)K)) {
+  if (linear_rows(M, K, act)) {
     GemmArgs a = {};
     a.A = static_cast<const _Float16 *>(x);
     a.lda = K;
@@ -345,9 +382,14 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   a.out = y;
   a.ldo = N;
   a.out_type = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
-  LAUNCH(tile_gemm_supported((int)K) ? launch_tile_gemm(Epi::LINEAR, a, bm, stream)
-                                        : launch_gemm(Epi::LINEAR, a, bm, stream),
-         "gemm");
+  if (tile_gemm_supported((int)K)) {
+    const TilePlan plan = linear_plan(M, N, K);
+    a.partial = ws.split;
+    a.partial_rows = M;
+    LAUNCH(launch_tile_gemm(Epi::LINEAR, a, bm, plan, nullptr, (int)M, stream), "gemm");
+  } else {
+    LAUNCH(launch_gemm(Epi::LINEAR, a, bm, stream), "gemm");
+  }
   return NVFP4_OK;
 }
 
@@ -459,6 +501,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   const FfnWs ws = carve_ffn(c, T, H, I, E, k);
   const int64_t P = T * k;
   const int bm = ffn_bm(T, E, k);
+  const FfnPlans plans = ffn_plans(T, H, I, E, k);
   const bool a4 = act == NVFP4_W4A4;
   const bool given = a4 && act_global_mode == NVFP4_GLOBAL_GIVEN;
   float *slot_gx = reinterpret_cast<float *>(ws.slots + 1);
@@ -534,6 +577,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.ldo = I;
   g.out_type = OutType::BF16;
   g.amax_slot = a4 ? ws.slots : nullptr;
+  g.sorted_pairs = sorted_pairs;   // (split-K reduce: expert of each tile row)
+  g.partial = ws.split;
+  g.partial_rows = P;
   if (rows) {
     g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
     g.a_shift = nullptr;
@@ -545,8 +591,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
   else
-    LAUNCH(tile_gemm_supported((int)H) ? launch_tile_gemm(Epi::SWIGLU, g, bm, stream)
-                                         : launch_gemm(Epi::SWIGLU, g, bm, stream),
+    LAUNCH(tile_gemm_supported((int)H)
+               ? launch_tile_gemm(Epi::SWIGLU, g, bm, plans.gate_up, topk_ids, (int)P, stream)
+               : launch_gemm(Epi::SWIGLU, g, bm, stream),
            "gate/up");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 4. h rows -> fp16 operands (W4A16 small tiles convert inside the down kernel)
@@ -589,6 +636,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.out_type = OutType::F32;
   d.pair_weights = topk_weights;
   d.sorted_pairs = sorted_pairs;
+  d.partial = ws.split;
+  d.partial_rows = P;
   mark_kernel(NVFP4_STAGE_DOWN, stream);
   if (rows) {
     d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
@@ -604,8 +653,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else
-    LAUNCH(tile_gemm_supported((int)I) ? launch_tile_gemm(Epi::DOWN, d, bm, stream)
-                                         : launch_gemm(Epi::DOWN, d, bm, stream),
+    LAUNCH(tile_gemm_supported((int)I)
+               ? launch_tile_gemm(Epi::DOWN, d, bm, plans.down, topk_ids, (int)P, stream)
+               : launch_gemm(Epi::DOWN, d, bm, stream),
            "down");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order

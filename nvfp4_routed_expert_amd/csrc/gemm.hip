@@ -255,25 +255,30 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, 
   build_plan(offsets, E, bm, mblocks, n_mblocks);
 }
 
-// Blocks 0 .. ceil(T/4)-1: one wavefront per x row -> fp16 with its
-// power-of-two shift (as the row preparation kernel's SHIFT mode).  The last
-// block builds the plan and zeroes the scratch words.
+// Blocks before the last: x rows -> fp16 with their power-of-two shift (as
+// the row preparation kernel's SHIFT mode), one wavefront per row, or for
+// few rows (wide) one workgroup per row.  The last block builds the plan and
+// zeroes the scratch words.
 __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_t T, int64_t H,
                                                        _Float16 *x16, int32_t *xshift,
                                                        const int32_t *offsets, int E, int bm,
                                                        int4 *mblocks, int32_t *n_mblocks,
-                                                       uint32_t *zero, int64_t zero_words) {
+                                                       uint32_t *zero, int64_t zero_words,
+                                                       int wide) {
   if (blockIdx.x == gridDim.x - 1) {
     for (int64_t i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
     build_plan(offsets, E, bm, mblocks, n_mblocks);
     return;
   }
+  __shared__ float wmax[4];
   const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t r = wide ? (int64_t)blockIdx.x : (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= T) return;
+  const int t0 = wide ? threadIdx.x : lane;
+  const int step = wide ? 256 * 8 : 512;
   const uint16_t *row = x + r * H;
   float m = 0.0f;
-  for (int64_t c = lane * 8; c < H; c += 512) {
+  for (int64_t c = t0 * 8; c < H; c += step) {
     const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -281,8 +286,13 @@ __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_
                          __builtin_fabsf(__uint_as_float(w[i] & 0xFFFF0000u))));
   }
   m = wave_max(m);
+  if (wide) {   // every wave of the block is in this branch (wide is uniform)
+    if (lane == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  }
   const int s = m > 0.0f ? exponent_of(m) - 15 : 0;
-  for (int64_t c = lane * 8; c < H; c += 512) {
+  for (int64_t c = t0 * 8; c < H; c += step) {
     const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c);
     f16x8 h;
 #pragma unroll
@@ -292,7 +302,7 @@ __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_
     }
     *reinterpret_cast<f16x8 *>(x16 + r * H + c) = h;
   }
-  if (lane == 0) xshift[r] = s;
+  if (t0 == 0) xshift[r] = s;
 }
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *ypair, int64_t T, int64_t H,
@@ -347,9 +357,10 @@ hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x1
                            int32_t *xshift, const int32_t *offsets, int E, int bm,
                            int4 *mblocks, int32_t *n_mblocks, uint32_t *zero,
                            int64_t zero_words, hipStream_t s) {
-  const int64_t blocks = (T + 3) / 4 + 1;
-  launch_kernel(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16,
-                     xshift, offsets, E, bm, mblocks, n_mblocks, zero, zero_words);
+  const int wide = T <= 1024;
+  const int64_t blocks = (wide ? T : (T + 3) / 4) + 1;
+  launch_kernel(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16, xshift,
+                offsets, E, bm, mblocks, n_mblocks, zero, zero_words, wide);
   return hipGetLastError();
 }
 

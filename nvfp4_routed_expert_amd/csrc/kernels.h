@@ -108,15 +108,33 @@ struct GemmArgs {
   uint32_t *amax_slot;            // SWIGLU: running max of |h| (float bits) or null
   const float *pair_weights;      // DOWN: routing weight of pair p
   const int32_t *sorted_pairs;    // DOWN: pair of each tile row
+  // split K (tile GEMM): raw fp32 sums of part kz at partial[kz][pos][col]
+  // (SWIGLU: gate columns 0..N-1, up columns N..2N-1); partial_rows = rows
+  // per part
+  int ksplit;
+  float *partial;
+  int64_t partial_rows;
 };
 
 hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
 
 // Grouped GEMM with both operands staged through an LDS ring (tile_gemm.hip):
-// m-blocks of bm (16, 32, 64 or 128) rows, 256 weight rows per workgroup.
-// Needs K % 64 == 0 (tile_gemm_supported); other K use launch_gemm.
+// m-blocks of bm (16, 32, 64 or 128) rows, 256 (or 64) weight rows per
+// workgroup.  Needs K % 64 == 0 (tile_gemm_supported); other K use
+// launch_gemm.  tile_gemm_plan picks the workgroup width and the K split for
+// a problem (n_mblocks_bound: the m-block count or a bound on it; rows: tile
+// rows, the partial buffer's rows); a split needs partial_floats floats of
+// workspace in GemmArgs::partial (partial_rows >= rows).  ids (grouped mode,
+// with a K split): expert of tile row pos is ids[sorted_pairs[pos]].
+struct TilePlan {
+  int waves = 4;
+  int ksplit = 1;
+  size_t partial_floats = 0;
+};
 bool tile_gemm_supported(int K);
-hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
+TilePlan tile_gemm_plan(Epi epi, int64_t N, int64_t K, int64_t n_mblocks_bound, int64_t rows);
+hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, const TilePlan &plan,
+                            const int32_t *ids, int rows, hipStream_t s);
 
 // Small-M grouped GEMV (tiles of 16 rows): waves of a workgroup split K and
 // keep several 128-wide chunks of weight loads in flight.  a_bf16: A rows are
@@ -131,7 +149,7 @@ int gemv_tile_cols(Epi epi, int N, int K);
 // null: a dense matrix, pair = token = pos, expert 0).  SWIGLU reads A row
 // token and writes row pos; DOWN reads A row pos and writes row pair; LINEAR
 // reads and writes row pos.  n_pos tile rows.  Supported K: 256, 512, 1024
-// and 2048..8192 (multiples of 32).
+// and 2048..32768 (multiples of 32).
 bool row_gemv_supported(int K);
 hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pairs,
                            const int32_t *ids, int k, int n_pos, hipStream_t s,

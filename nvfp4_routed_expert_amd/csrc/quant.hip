@@ -121,6 +121,37 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(
   }
 }
 
+// SHIFT mode for few rows: one workgroup per row (the row maximum reduced
+// over its four waves), so a long row is not one wavefront's serial loop.
+__global__ __launch_bounds__(kThreads) void row_shift_wide_kernel(const uint16_t *x, int64_t cols,
+                                                                 _Float16 *out, int32_t *shift) {
+  __shared__ float wmax[kThreads / 64];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint16_t *row = x + r * cols;
+  float m = 0.0f;
+  for (int64_t c = tid * 8; c < cols; c += kThreads * 8) {
+    float v[8];
+    load8(row, InType::BF16, c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) wmax[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const int s = m > 0.0f ? exponent_of(m) - 15 : 0;
+  for (int64_t c = tid * 8; c < cols; c += kThreads * 8) {
+    float v[8];
+    load8(row, InType::BF16, c, v);
+    f16x8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)__builtin_ldexpf(v[i], -s);
+    *reinterpret_cast<f16x8 *>(out + r * cols + c) = h;
+  }
+  if (tid == 0) shift[r] = s;
+}
+
 // One wavefront per row.
 __global__ __launch_bounds__(kThreads) void row_prep_kernel(
     const uint16_t *x, int64_t rows, int64_t cols, PrepMode mode, _Float16 *out,
@@ -225,6 +256,12 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols, PrepMo
                            _Float16 *out, int32_t *shift, const float *amax_src,
                            int n_amax, const float *g_given, float *g_out,
                            float *g_out2, hipStream_t s) {
+  static_assert(kThreads == 256, "row_shift_wide_kernel reduces four waves");
+  if (mode == PrepMode::SHIFT && rows <= 1024) {   // few rows: a workgroup each
+    launch_kernel(row_shift_wide_kernel, dim3((unsigned)rows), dim3(kThreads), 0, s, x, cols, out,
+                  shift);
+    return hipGetLastError();
+  }
   const int64_t blocks = (rows + 3) / 4;
   launch_kernel(row_prep_kernel, dim3((unsigned)(blocks < 1 ? 1 : blocks)),
                      dim3(kThreads), 0, s, x, rows, cols, mode, out, shift, amax_src,

@@ -39,6 +39,7 @@ namespace {
 constexpr int kSlice = 2048;   // K elements covered by one wave (64 lanes x 32)
 constexpr int kBatch = 8;      // load steps in flight and reduced together
 constexpr int kMaxSlots = 32;  // top-k slots a token-major down item sums
+constexpr int kMaxKs = 16;     // K slices (waves) of one unit: K <= 16 * 2048
 
 // ---------------------------------------------------------------------------
 // arithmetic
@@ -179,12 +180,14 @@ struct Routing {
   bool h_by_pair;                // SWIGLU: write h row `pair` instead of `pos`
 };
 
-template <int LPR, Epi EPI>
-__global__ __launch_bounds__(256) void row_gemv_kernel(const GemmArgs p, const Routing rt,
-                                                       int n_pos) {
+// WIDE: units of up to 16 waves (K > 4 * 2048) in workgroups of up to 1024
+// threads; otherwise at most 4 waves, which leaves the compiler more registers.
+template <int LPR, Epi EPI, bool WIDE>
+__global__ __launch_bounds__(WIDE ? 1024 : 256) void row_gemv_kernel(const GemmArgs p,
+                                                                     const Routing rt, int n_pos) {
   using C = RowCfg<LPR, EPI>;
   constexpr int NMAT = C::NMAT;
-  __shared__ float red[3 * NMAT * 64];   // partial row sums of waves 1..3 of a unit
+  __shared__ float red[((WIDE ? kMaxKs : 4) - 1) * NMAT * 64];   // partial sums of waves 1..
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int K = p.K, N = p.N;
@@ -435,6 +438,23 @@ __global__ __launch_bounds__(256) void row_down_sum_kernel(const GemmArgs p, con
   }
 }
 
+template <int LPR, bool WIDE>
+hipError_t launch_cfg_w(Epi epi, const GemmArgs &a, const Routing &info, int n_pos, dim3 grid,
+                        dim3 block, hipStream_t s) {
+  switch (epi) {
+    case Epi::LINEAR:
+      launch_kernel((row_gemv_kernel<LPR, Epi::LINEAR, WIDE>), grid, block, 0, s, a, info, n_pos);
+      break;
+    case Epi::SWIGLU:
+      launch_kernel((row_gemv_kernel<LPR, Epi::SWIGLU, WIDE>), grid, block, 0, s, a, info, n_pos);
+      break;
+    case Epi::DOWN:
+      launch_kernel((row_gemv_kernel<LPR, Epi::DOWN, WIDE>), grid, block, 0, s, a, info, n_pos);
+      break;
+  }
+  return hipGetLastError();
+}
+
 template <int LPR>
 hipError_t launch_cfg(Epi epi, const GemmArgs &a, const Routing &info, int n_pos, hipStream_t s) {
   const int ks = (a.K + kSlice - 1) / kSlice;
@@ -447,18 +467,10 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, const Routing &info, int n_pos
   if (units > items) units = items;
   const int64_t blocks = (units + units_per_wg - 1) / units_per_wg;
   const dim3 grid((unsigned)(blocks < 1 ? 1 : blocks)), block(64 * ks * units_per_wg);
-  switch (epi) {
-    case Epi::LINEAR:
-      launch_kernel((row_gemv_kernel<LPR, Epi::LINEAR>), grid, block, 0, s, a, info, n_pos);
-      break;
-    case Epi::SWIGLU:
-      launch_kernel((row_gemv_kernel<LPR, Epi::SWIGLU>), grid, block, 0, s, a, info, n_pos);
-      break;
-    case Epi::DOWN:
-      launch_kernel((row_gemv_kernel<LPR, Epi::DOWN>), grid, block, 0, s, a, info, n_pos);
-      break;
+  if constexpr (LPR == 64) {
+    if (ks > 4) return launch_cfg_w<LPR, true>(epi, a, info, n_pos, grid, block, s);
   }
-  return hipGetLastError();
+  return launch_cfg_w<LPR, false>(epi, a, info, n_pos, grid, block, s);
 }
 
 template <int LPR>
@@ -488,7 +500,7 @@ hipError_t launch_row_down_sum(const GemmArgs &a, const int32_t *ids, int k, int
 bool row_gemv_supported(int K) {
   if (K % 32 != 0) return false;
   if (K == 256 || K == 512 || K == 1024) return true;
-  return K >= kSlice && K <= 4 * kSlice;
+  return K >= kSlice && K <= kMaxKs * kSlice;
 }
 
 hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pairs,

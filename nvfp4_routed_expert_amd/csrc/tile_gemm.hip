@@ -8,9 +8,10 @@
 // activations.
 //
 // A work item is (m-block of up to BM = 16*MS expert-sorted rows, tile of
-// 256 weight rows).  The four waves of a workgroup split the weight rows (64
-// each; for the gate/up pair 32 gate and the same 32 up rows) and share the
-// activation rows.  Both operands pass through a three-stage LDS ring of
+// 64 NW weight rows, K range).  The NW waves (4, or 1 for skinny problems
+// that would otherwise leave CUs idle) of a workgroup split the weight rows
+// (64 each; for the gate/up pair 32 gate and the same 32 up rows) and share
+// the activation rows.  Both operands pass through a three-stage LDS ring of
 // 64-wide K chunks, filled by direct global-to-LDS loads (no registers), so
 // two chunks are in flight while one is multiplied and two workgroups fit
 // on a CU.  A wave reads its weight codes from LDS, dequantises them in
@@ -28,30 +29,36 @@
 // (round robin over 8), so the item space is cut into 8 contiguous ranges
 // and XCD x walks range x; the weight tiles of one m-block then run next to
 // each other on one XCD and share its L2 copy of the activation rows.
+// Split K: when even one-wave tiles are too few to fill the GPU (a dense
+// decode-sized down projection has 80 of them), each tile's K range is cut
+// into KS parts; the parts write raw fp32 sums to a workspace and a reduce
+// kernel adds them in part order and applies the epilogue, so results stay
+// deterministic.
 #include "common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kThreads = 256;
 constexpr int kChunk = 64;             // K per pipeline stage
 constexpr int kStages = 3;
 constexpr int kARow = kChunk * 2;      // bytes of one fp16 activation row per chunk
-constexpr int kBRows = 256;            // weight rows per workgroup
 constexpr int kBRow = kChunk / 2;      // code bytes of one weight row per chunk
 constexpr int kXcds = 8;
+constexpr int kFillGroups = 512;       // four-wave workgroups that keep every CU busy (2 per CU)
+constexpr int kSkinnyGroups = 2048;    // one-wave workgroups for the same (2 per SIMD)
 
-template <int MS>
+template <int MS, int NW>
 struct TileCfg {
   static constexpr int BM = MS * 16;
+  static constexpr int BROWS = 64 * NW;                 // weight rows per workgroup
   static constexpr int A_BYTES = BM * kARow;
-  static constexpr int B_BYTES = kBRows * kBRow;
-  static constexpr int S_BYTES = kBRows * (kChunk / 16);
+  static constexpr int B_BYTES = BROWS * kBRow;
+  static constexpr int S_BYTES = BROWS * (kChunk / 16);
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int A_LOADS = A_BYTES / 1024 / 4;   // 1 KB direct loads per wave
-  static constexpr int LOADS = A_LOADS + 2 + 1;        // per lane and chunk (A, codes, scales)
-  static_assert(A_BYTES % 4096 == 0, "activation stage splits over four waves");
+  static constexpr int A_LOADS = A_BYTES / 1024 / NW;   // 1 KB direct loads per wave
+  static constexpr int LOADS = A_LOADS + 2 + 1;         // per lane and chunk (A, codes, scales)
+  static_assert(A_BYTES % (1024 * NW) == 0, "activation stage splits over the waves");
 };
 
 template <Epi EPI>
@@ -59,22 +66,29 @@ constexpr int cols_per_wave() { return EPI == Epi::SWIGLU ? 32 : 64; }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-template <int MS, Epi EPI>
-__global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p) {
-  using C = TileCfg<MS>;
+__device__ __forceinline__ int arow_of(const GemmArgs &p, int pos) {
+  return p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
+}
+
+template <int MS, int NW, Epi EPI>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(const GemmArgs p) {
+  using C = TileCfg<MS, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
   constexpr int kCols = cols_per_wave<EPI>();
-  const int n_tiles = (N + 4 * kCols - 1) / (4 * kCols);
+  const int n_tiles = (N + NW * kCols - 1) / (NW * kCols);
+  const int ksplit = p.ksplit > 1 ? p.ksplit : 1;
   const int n_mb = p.n_mblocks_dev ? *p.n_mblocks_dev : p.n_mblocks;
-  const int n_items = n_mb * n_tiles;
+  const int n_items = n_mb * n_tiles * ksplit;
   const int per = (n_items + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
   const int item = (blockIdx.x % kXcds) * per + slot;
   if (slot >= per || item >= n_items) return;
-  const int mb = item / n_tiles, nt = item - mb * n_tiles;
+  const int kz = item % ksplit;
+  const int mn = item / ksplit;
+  const int mb = mn / n_tiles, nt = mn - mb * n_tiles;
 
   int e = 0, pos0, nrows;
   if (p.mblocks) {
@@ -86,7 +100,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
     pos0 = mb * C::BM;
     nrows = (int)(p.dense_rows - pos0 < C::BM ? p.dense_rows - pos0 : C::BM);
   }
-  const int col0 = (nt * 4 + wave) * kCols;
+  const int col0 = (nt * NW + wave) * kCols;
 
   // ---- loader state.  Workgroup-local weight row R = 64 w + 16 f + r is row
   // r of fragment f of wave w (SWIGLU: fragments 2, 3 are the up rows of the
@@ -95,15 +109,14 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
     const int w = R >> 6, f = (R >> 4) & 3, r = R & 15;
     mat = (EPI == Epi::SWIGLU && f >= 2) ? 1 : 0;
     const int fr = EPI == Epi::SWIGLU ? (f & 1) : f;
-    const int row = (nt * 4 + w) * kCols + fr * 16 + r;
+    const int row = (nt * NW + w) * kCols + fr * 16 + r;
     return row < N ? row : N - 1;
   };
   // Codes: LDS row R holds 32 bytes as two 16-byte halves, half h at
   // position h ^ ((R >> 3) & 1).  Direct load j of wave w is instruction
-  // q = 2 w + j (0..7); it fills 1 KB = rows 32 q .. 32 q + 31, lane l
-  // writing position l % 2 of row 32 q + l / 2.
+  // q = 2 w + j; it fills 1 KB = rows 32 q .. 32 q + 31, lane l writing
+  // position l % 2 of row 32 q + l / 2.
   const uint8_t *csrc[2];
-  int cdst[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int q = 2 * wave + j, R = 32 * q + (lane >> 1);
@@ -111,7 +124,6 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
     const int row = weight_row(R, mat);
     const int h = (lane & 1) ^ ((R >> 3) & 1);
     csrc[j] = p.b_codes[mat] + (int64_t)e * p.b_codes_estride + (int64_t)row * (K / 2) + h * 16;
-    cdst[j] = q * 1024;
   }
   // Scales: 4 bytes (one chunk) per row, wave w loads rows 64 w .. 64 w + 63.
   const uint8_t *ssrc;
@@ -121,17 +133,21 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
     ssrc = p.b_scales[mat] + (int64_t)e * p.b_scales_estride + (int64_t)row * (K / 16);
   }
   // Activations: LDS row r holds 128 bytes as eight 16-byte granules, granule
-  // c at position c ^ ((r >> 1) & 7); instruction q = wave + 4 j fills rows
-  // 8 q .. 8 q + 7, lane l writing position l % 8 of row 8 q + l / 8.  Rows
-  // past the block reread row 0 (finite data, results discarded).
-  int arow[C::A_LOADS];
-  // (row >> 1) & 7 = (4 q + l / 16) & 7 = (4 w + l / 16) & 7 for every j
-  const int agran = (lane & 7) ^ ((4 * wave + (lane >> 4)) & 7);
+  // c at position c ^ ((r >> 1) & 7); instruction q = wave + NW j fills rows
+  // 8 q .. 8 q + 7, lane l writing position l % 8 of row 8 q + l / 8, so it
+  // fetches granule (l % 8) ^ ((4 q + l / 16) & 7).  Rows past the block
+  // reread row 0 (finite data, results discarded).
+  // (a fixed-size array: with a size that depends on the template arguments
+  // the host pass of this compiler drops the kernel's launch stub)
+  static_assert(C::A_LOADS <= 16, "activation loads per wave");
+  int64_t aoff[16];   // element offsets of this lane's activation pieces
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
-    const int r = 8 * (wave + 4 * j) + (lane >> 3);
+    const int q = wave + NW * j;
+    const int r = 8 * q + (lane >> 3);
     const int rr = r < nrows ? r : 0;
-    arow[j] = p.a_rowmap ? p.a_rowmap[pos0 + rr] / p.a_rowdiv : pos0 + rr;
+    const int gran = (lane & 7) ^ ((4 * q + (lane >> 4)) & 7);
+    aoff[j] = (int64_t)arow_of(p, pos0 + rr) * p.lda + gran * 8;
   }
 
   f32x4 acc[MS][4];
@@ -140,8 +156,12 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[ms][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nchunks = K / kChunk;
-  const int last = nchunks - 1;
+  // this part's chunk range (the host makes every part non-empty)
+  const int nch = K / kChunk;
+  const int cps = (nch + ksplit - 1) / ksplit;
+  const int c_begin = kz * cps;
+  const int c_end = c_begin + cps < nch ? c_begin + cps : nch;
+  const int last = c_end - 1;
 
   // Issue the loads of chunk c (K is a multiple of 64) into ring slot c % 3.
   auto load_chunk = [&](int c) {
@@ -149,12 +169,13 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
     const int k0 = c * kChunk;
 #pragma unroll
     for (int j = 0; j < C::A_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds(p.A + (int64_t)arow[j] * p.lda + k0 + agran * 8,
-                                       (lds_ptr_t)(st + (wave + 4 * j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(p.A + aoff[j] + k0, (lds_ptr_t)(st + (wave + NW * j) * 1024),
+                                       16, 0, 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_global_load_lds(csrc[j] + k0 / 2, (lds_ptr_t)(st + C::A_BYTES + cdst[j]),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(csrc[j] + k0 / 2,
+                                       (lds_ptr_t)(st + C::A_BYTES + (2 * wave + j) * 1024), 16, 0,
+                                       0);
     __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
                                      (lds_ptr_t)(st + C::A_BYTES + C::B_BYTES + wave * 256), 4,
                                      0, 0);
@@ -194,9 +215,9 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
   // outstanding; the barrier then also guarantees every wave is done with
   // the slot the next loads overwrite.  Past the end the last chunk is
   // requested again (a cache hit into a slot nobody reads).
-  load_chunk(0);
-  load_chunk(last < 1 ? last : 1);
-  for (int c = 0; c <= last; ++c) {
+  load_chunk(c_begin);
+  load_chunk(c_begin + 1 <= last ? c_begin + 1 : last);
+  for (int c = c_begin; c <= last; ++c) {
     // (a plain barrier: __syncthreads would also wait for the newest loads)
     asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::LOADS) : "memory");
     load_chunk(c + 2 <= last ? c + 2 : last);
@@ -206,6 +227,27 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
 
   // ---- epilogue: lane holds rows 4*lg + j (j = 0..3) of each subtile and
   //      column lr of each fragment.
+  if (ksplit > 1) {   // raw sums of this K part -> partial[kz][pos][col]
+    const int ncols = EPI == Epi::SWIGLU ? 2 * N : N;
+    float *part = p.partial + (int64_t)kz * p.partial_rows * ncols;
+#pragma unroll
+    for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = ms * 16 + 4 * lg + j;
+        if (r >= nrows) continue;
+        float *prow = part + (int64_t)(pos0 + r) * ncols;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+          const int fr = EPI == Epi::SWIGLU ? (f & 1) : f;
+          const int col = col0 + fr * 16 + lr;
+          if (col >= N) continue;
+          prow[(EPI == Epi::SWIGLU && f >= 2 ? N : 0) + col] = acc[ms][f][j];
+        }
+      }
+    }
+    return;
+  }
   const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
   if constexpr (EPI == Epi::SWIGLU) {
     float amax = 0.0f;
@@ -217,8 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
         const int r = ms * 16 + 4 * lg + j;
         if (r >= nrows) continue;
         const int pos = pos0 + r;
-        const int arow = p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
-        const int sh = p.a_shift ? p.a_shift[arow] : 0;
+        const int sh = p.a_shift ? p.a_shift[arow_of(p, pos)] : 0;
         uint16_t *hrow = static_cast<uint16_t *>(p.out) + (int64_t)pos * p.ldo;
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
@@ -246,8 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
         const int r = ms * 16 + 4 * lg + j;
         if (r >= nrows) continue;
         const int pos = pos0 + r;
-        const int arow = p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
-        const int sh = p.a_shift ? p.a_shift[arow] : 0;
+        const int sh = p.a_shift ? p.a_shift[arow_of(p, pos)] : 0;
         int64_t orow = pos;
         float w = 1.0f;
         if constexpr (EPI == Epi::DOWN) {
@@ -271,41 +311,139 @@ __global__ __launch_bounds__(kThreads, 2) void tile_gemm_kernel(const GemmArgs p
   }
 }
 
-template <int MS>
-hipError_t launch_ms(Epi epi, const GemmArgs &a, hipStream_t s) {
-  const int cols = epi == Epi::SWIGLU ? 4 * cols_per_wave<Epi::SWIGLU>()
-                                      : 4 * cols_per_wave<Epi::LINEAR>();
+// Split-K reduce: element (pos, col) of the output adds the parts' raw sums
+// in part order, then applies the same epilogue as the tile kernel.  Row pos
+// belongs to expert ids[sorted_pairs[pos]] (expert 0 when ids is null).
+template <Epi EPI>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const GemmArgs p, int rows,
+                                                           const int32_t *ids) {
+  const int N = p.N;
+  const int ncols = EPI == Epi::SWIGLU ? 2 * N : N;
+  const int64_t total = (int64_t)rows * N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float amax = 0.0f;
+  if (idx < total) {
+    const int pos = (int)(idx / N), col = (int)(idx - (int64_t)pos * N);
+    const int e = ids ? ids[p.sorted_pairs[pos]] : 0;
+    const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
+    const int sh = p.a_shift ? p.a_shift[arow_of(p, pos)] : 0;
+    const int64_t stride = (int64_t)p.partial_rows * ncols;
+    const float *src = p.partial + (int64_t)pos * ncols + col;
+    float g = src[0], u = 0.0f;
+    if constexpr (EPI == Epi::SWIGLU) u = src[N];
+    for (int kz = 1; kz < p.ksplit; ++kz) {
+      g += src[kz * stride];
+      if constexpr (EPI == Epi::SWIGLU) u += src[kz * stride + N];
+    }
+    if constexpr (EPI == Epi::SWIGLU) {
+      const float G = __builtin_ldexpf(g, sh) * (p.b_global[0][e] * extra);
+      const float U = __builtin_ldexpf(u, sh) * (p.b_global[1][e] * extra);
+      const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
+      static_cast<uint16_t *>(p.out)[(int64_t)pos * p.ldo + col] = (uint16_t)hb;
+      amax = __builtin_fabsf(bf16_bits_to_f32(hb));
+    } else {
+      float v = __builtin_ldexpf(g, sh) * (p.b_global[0][e] * extra);
+      int64_t orow = pos;
+      if constexpr (EPI == Epi::DOWN) {
+        orow = p.sorted_pairs[pos];
+        v *= p.pair_weights[orow];
+      }
+      if (p.out_type == OutType::F32)
+        static_cast<float *>(p.out)[orow * p.ldo + col] = v;
+      else
+        static_cast<uint16_t *>(p.out)[orow * p.ldo + col] = (uint16_t)f32_to_bf16_bits(v);
+    }
+  }
+  if constexpr (EPI == Epi::SWIGLU) {
+    if (p.amax_slot) {
+      amax = wave_max(amax);
+      if ((threadIdx.x & 63) == 0 && amax > 0.0f) atomicMax(p.amax_slot, __float_as_uint(amax));
+    }
+  }
+}
+
+template <int MS, int NW>
+hipError_t launch_ms(Epi epi, const GemmArgs &a, int ksplit, hipStream_t s) {
+  const int cols = NW * (epi == Epi::SWIGLU ? cols_per_wave<Epi::SWIGLU>()
+                                            : cols_per_wave<Epi::LINEAR>());
   const int64_t n_tiles = (a.N + cols - 1) / cols;
-  int64_t items = n_tiles * (int64_t)a.n_mblocks;
+  int64_t items = n_tiles * (int64_t)a.n_mblocks * ksplit;
   items = (items + kXcds - 1) / kXcds * kXcds;
   if (items < kXcds) items = kXcds;
-  const dim3 grid((unsigned)items), block(kThreads);
+  GemmArgs g = a;
+  g.ksplit = ksplit;
+  const dim3 grid((unsigned)items), block(64 * NW);
   switch (epi) {
     case Epi::LINEAR:
-      launch_kernel((tile_gemm_kernel<MS, Epi::LINEAR>), grid, block, 0, s, a);
+      launch_kernel((tile_gemm_kernel<MS, NW, Epi::LINEAR>), grid, block, 0, s, g);
       break;
     case Epi::SWIGLU:
-      launch_kernel((tile_gemm_kernel<MS, Epi::SWIGLU>), grid, block, 0, s, a);
+      launch_kernel((tile_gemm_kernel<MS, NW, Epi::SWIGLU>), grid, block, 0, s, g);
       break;
     case Epi::DOWN:
-      launch_kernel((tile_gemm_kernel<MS, Epi::DOWN>), grid, block, 0, s, a);
+      launch_kernel((tile_gemm_kernel<MS, NW, Epi::DOWN>), grid, block, 0, s, g);
       break;
   }
   return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_nw(Epi epi, const GemmArgs &a, int bm, int ksplit, hipStream_t s) {
+  switch (bm) {
+    case 16:
+    case 32: return launch_ms<2, NW>(epi, a, ksplit, s);
+    case 64: return launch_ms<4, NW>(epi, a, ksplit, s);
+    default: return launch_ms<8, NW>(epi, a, ksplit, s);
+  }
 }
 
 }  // namespace
 
 bool tile_gemm_supported(int K) { return K % kChunk == 0; }
 
-hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s) {
+TilePlan tile_gemm_plan(Epi epi, int64_t N, int64_t K, int64_t n_mblocks_bound, int64_t rows) {
+  TilePlan t;
+  const int64_t cols = epi == Epi::SWIGLU ? cols_per_wave<Epi::SWIGLU>()
+                                          : cols_per_wave<Epi::LINEAR>();
+  const int64_t items4 = n_mblocks_bound * ((N + 4 * cols - 1) / (4 * cols));
+  if (items4 >= kFillGroups) return t;                      // four-wave tiles fill the GPU
+  // one-wave tiles: a wave keeps only two chunks of its 64 rows in flight, so
+  // streaming needs several per SIMD (kSkinnyGroups), by splitting K if needed
+  t.waves = 1;
+  const int64_t items1 = n_mblocks_bound * ((N + cols - 1) / cols);
+  if (items1 >= kSkinnyGroups) return t;
+  const int64_t nch = K / kChunk;
+  int64_t ks = (kSkinnyGroups + items1 - 1) / items1;
+  if (ks > nch / 2) ks = nch / 2;                           // parts of at least two chunks
+  if (ks < 2) return t;
+  const int64_t cps = (nch + ks - 1) / ks;
+  t.ksplit = (int)((nch + cps - 1) / cps);                  // every part non-empty
+  t.partial_floats = (size_t)t.ksplit * rows * (epi == Epi::SWIGLU ? 2 * N : N);
+  return t;
+}
+
+hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, const TilePlan &plan,
+                            const int32_t *ids, int rows, hipStream_t s) {
   if (!tile_gemm_supported(a.K)) return hipErrorInvalidValue;
-  switch (bm) {
-    case 16:
-    case 32: return launch_ms<2>(epi, a, s);
-    case 64: return launch_ms<4>(epi, a, s);
-    default: return launch_ms<8>(epi, a, s);
+  if (plan.ksplit > 1 && (!a.partial || a.partial_rows < rows)) return hipErrorInvalidValue;
+  hipError_t err = plan.waves == 4 ? launch_nw<4>(epi, a, bm, plan.ksplit, s)
+                                   : launch_nw<1>(epi, a, bm, plan.ksplit, s);
+  if (err != hipSuccess || plan.ksplit <= 1) return err;
+  GemmArgs g = a;
+  g.ksplit = plan.ksplit;
+  const dim3 grid((unsigned)(((int64_t)rows * a.N + 255) / 256)), block(256);
+  switch (epi) {
+    case Epi::LINEAR:
+      launch_kernel(split_reduce_kernel<Epi::LINEAR>, grid, block, 0, s, g, rows, ids);
+      break;
+    case Epi::SWIGLU:
+      launch_kernel(split_reduce_kernel<Epi::SWIGLU>, grid, block, 0, s, g, rows, ids);
+      break;
+    case Epi::DOWN:
+      launch_kernel(split_reduce_kernel<Epi::DOWN>, grid, block, 0, s, g, rows, ids);
+      break;
   }
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4
