@@ -256,8 +256,128 @@ struct PermuteLds {
 
 // ids: the [T, k] expert ids (global or LDS).  One workgroup of any
 // multiple of 64 threads up to kPermThreads.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+  // inclusive prefix sum over the 64 lanes (row shifts, then row broadcasts)
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  (void)lane;
+  return x;
+}
+
+// One-chunk case (T <= 32 W tokens): no separate counting pass.  The pairs
+// set their token bits; then one wave per expert turns the expert's W words
+// into running popcounts with a wave scan (the expert's total comes with
+// it), a scan over the experts gives the offsets, and each pair's position
+// is its expert's offset + the tokens before its word + the set bits below
+// it in the word.  Four barriers, no counter contention.
+__device__ void permute_block_one_chunk(const int32_t *ids, int64_t T, int E, int k, int W,
+                                        int32_t *offsets, int32_t *sorted_pairs, PermuteLds &L) {
+  uint32_t *bitmap = L.bitmap;
+  uint16_t *prefix = L.prefix;
+  int32_t *cnt = L.cnt, *off = L.off, *wave_tot = L.wave_tot;
+  const int tid = threadIdx.x, nthr = blockDim.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = nthr >> 6;
+  const int64_t P = T * k;
+  for (int i = tid; i < E * W; i += nthr) bitmap[i] = 0u;
+  __syncthreads();
+  // pairs in batches of 8 per thread, so eight id loads are in flight at once
+  constexpr int kBatchIds = 8;
+  for (int64_t p0 = tid; p0 < P; p0 += (int64_t)nthr * kBatchIds) {
+    int e8[kBatchIds];
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      e8[u] = p < P ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      if (p < P) {
+        const int64_t t = p / k;
+        atomicOr(&bitmap[e8[u] * W + (int)(t >> 5)], 1u << (t & 31));
+      }
+    }
+  }
+  __syncthreads();
+  // per expert: exclusive running popcount over its words (a thread per
+  // expert for short rows of words, a wave scan per expert for long ones)
+  if (W <= 32) {
+    for (int e = tid; e < E; e += nthr) {
+      int run = 0;
+      for (int w = 0; w < W; ++w) {
+        prefix[e * W + w] = (uint16_t)run;
+        run += __popc(bitmap[e * W + w]);
+      }
+      cnt[e] = run;
+    }
+  } else {
+    for (int e = wave; e < E; e += nwaves) {
+      int run = 0;
+      for (int w0 = 0; w0 < W; w0 += 64) {
+        const int w = w0 + lane;
+        const int c = w < W ? __popc(bitmap[e * W + w]) : 0;
+        const int incl = wave_incl_scan(c, lane);
+        if (w < W) prefix[e * W + w] = (uint16_t)(run + incl - c);
+        run += __builtin_amdgcn_readlane(incl, 63);
+      }
+      if (lane == 0) cnt[e] = run;
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the expert totals (thread tid owns ept experts)
+  {
+    const int ept = (E + nthr - 1) / nthr;
+    const int e0 = tid * ept;
+    int c = 0;
+    for (int i = 0; i < ept; ++i)
+      if (e0 + i < E) c += cnt[e0 + i];
+    const int incl = wave_incl_scan(c, lane);
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int run = incl - c;
+    for (int w = 0; w < wave; ++w) run += wave_tot[w];
+    for (int i = 0; i < ept; ++i) {
+      const int e = e0 + i;
+      if (e < E) {
+        off[e] = run;
+        offsets[e] = run;
+        run += cnt[e];
+      }
+    }
+    if (tid == 0) offsets[E] = (int32_t)P;
+  }
+  __syncthreads();
+  for (int64_t p0 = tid; p0 < P; p0 += (int64_t)nthr * kBatchIds) {
+    int e8[kBatchIds];
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      e8[u] = p < P ? ids[p] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      if (p < P) {
+        const int e = e8[u];
+        const int64_t t = p / k;
+        const int w = (int)(t >> 5);
+        const uint32_t below = bitmap[e * W + w] & ((1u << (t & 31)) - 1u);
+        sorted_pairs[off[e] + prefix[e * W + w] + __popc(below)] = (int32_t)p;
+      }
+    }
+  }
+}
+
 __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W,
                               int32_t *offsets, int32_t *sorted_pairs, PermuteLds &L) {
+  if (T <= (int64_t)W * 32) {
+    permute_block_one_chunk(ids, T, E, k, W, offsets, sorted_pairs, L);
+    return;
+  }
   uint32_t *bitmap = L.bitmap;
   uint16_t *prefix = L.prefix;
   int32_t *cnt = L.cnt, *off = L.off, *base = L.base, *chunk_cnt = L.chunk_cnt;
@@ -278,13 +398,8 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
     int c = 0;
     for (int i = 0; i < ept; ++i)
       if (e0 + i < E) c += cnt[e0 + i];
-    int incl = c;
     const int lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(c, lane);
     if (lane == 63) wave_tot[wave] = incl;
     __syncthreads();
     int run = incl - c;
@@ -370,12 +485,7 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
     int local = 0;
     for (int i = 0; i < per; ++i)
       if (e0 + i < E) local += cnt[e0 + i];
-    int incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, kWave);
-      if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(local, lane);
     int run = incl - local;
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
@@ -405,17 +515,6 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
 // permutation alone: expert counts by LDS atomics, a DPP scan into the
 // offsets, and for pair p (expert e) the position offsets[e] + (earlier
 // pairs with expert e), counted 16 ids per step from LDS.
-__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-  // inclusive prefix sum over the 64 lanes (row shifts, then row broadcasts)
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
-  (void)lane;
-  return x;
-}
 
 __global__ __launch_bounds__(64) void route_decode_kernel(const float *logits, int64_t T, int E,
                                                           int k, int renormalize, int32_t *ids,

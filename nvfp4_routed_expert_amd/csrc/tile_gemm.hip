@@ -34,6 +34,8 @@
 // into KS parts; the parts write raw fp32 sums to a workspace and a reduce
 // kernel adds them in part order and applies the epilogue, so results stay
 // deterministic.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -100,6 +102,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
     pos0 = mb * C::BM;
     nrows = (int)(p.dense_rows - pos0 < C::BM ? p.dense_rows - pos0 : C::BM);
   }
+  // the block is the same for the whole workgroup: keep it in scalar
+  // registers so the subtile tests below are scalar branches
+  e = __builtin_amdgcn_readfirstlane(e);
+  pos0 = __builtin_amdgcn_readfirstlane(pos0);
+  nrows = __builtin_amdgcn_readfirstlane(nrows);
   const int col0 = (nt * NW + wave) * kCols;
 
   // ---- loader state.  Workgroup-local weight row R = 64 w + 16 f + r is row
@@ -181,7 +188,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
                                      0, 0);
   };
 
-  auto compute = [&](int c) {
+  // FULL: every subtile holds rows, so the fragment reads and the MFMAs
+  // form one straight-line block the compiler can schedule ahead
+  auto compute = [&](int c, auto full) {
+    constexpr bool FULL = decltype(full)::value;
     const uint8_t *st = lds + (c % kStages) * C::STAGE;
     f16x8 bf[2][4];
 #pragma unroll
@@ -201,7 +211,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
       const int gran = ((2 * lg + i) ^ ((lr >> 1) & 7)) * 16;
 #pragma unroll
       for (int ms = 0; ms < MS; ++ms) {
-        if (ms * 16 >= nrows) break;   // wave-uniform: skip empty subtiles
+        if (!FULL && ms * 16 >= nrows) break;   // uniform: skip empty subtiles
         const f16x8 a = *reinterpret_cast<const f16x8 *>(abase + ms * 16 * kARow + gran);
 #pragma unroll
         for (int f = 0; f < 4; ++f)
@@ -215,14 +225,20 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
   // outstanding; the barrier then also guarantees every wave is done with
   // the slot the next loads overwrite.  Past the end the last chunk is
   // requested again (a cache hit into a slot nobody reads).
-  load_chunk(c_begin);
-  load_chunk(c_begin + 1 <= last ? c_begin + 1 : last);
-  for (int c = c_begin; c <= last; ++c) {
-    // (a plain barrier: __syncthreads would also wait for the newest loads)
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::LOADS) : "memory");
-    load_chunk(c + 2 <= last ? c + 2 : last);
-    compute(c);
-  }
+  auto run = [&](auto full) {
+    load_chunk(c_begin);
+    load_chunk(c_begin + 1 <= last ? c_begin + 1 : last);
+    for (int c = c_begin; c <= last; ++c) {
+      // (a plain barrier: __syncthreads would also wait for the newest loads)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::LOADS) : "memory");
+      load_chunk(c + 2 <= last ? c + 2 : last);
+      compute(c, full);
+    }
+  };
+  if (nrows >= C::BM)
+    run(std::true_type{});
+  else
+    run(std::false_type{});
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds rows 4*lg + j (j = 0..3) of each subtile and
