@@ -8,7 +8,9 @@ before timing starts.  Steps are captured in a HIP graph and cycle over
 several copies of the expert weights, so every step streams its active
 experts from HBM instead of the 256 MB Infinity Cache (MALL).
 
-Prints one JSON line (see README of the metric in the design doc).
+Prints one JSON line: the metric, the step throughput, the roofline figures
+of the gate/up kernel and the CPU oracle's throughput on a sample of the
+same step.
 """
 from __future__ import annotations
 
@@ -133,8 +135,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the routed-expert "
-                                   "FFN is measured on one GPU's share (see DESIGN.md for how "
-                                   "it would shard)", "n_gpus": args.gpus}))
+                                   "FFN is measured on one GPU's share (it would shard by "
+                                   "expert, one exchange of y per step)", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import numpy as np
@@ -240,6 +242,39 @@ def main():
     wall_ms = (time.perf_counter() - wall0) * 1e3
     ms_per_step = start.elapsed_time(end) / args.steps
 
+    # ---- per-step spread (events around each replay) and the FFN alone ----------
+    n_spread = min(args.steps, 100)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_spread + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(n_spread):
+        run(i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    step_us = np.array([1e3 * evs[i].elapsed_time(evs[i + 1]) for i in range(n_spread)])
+    ffn_ms = None
+    if use_graph:   # routing precomputed: graphs of the FFN call alone
+        def ffn_only(c):
+            native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
+                                         act_globals=None, out_dtype=torch.bfloat16,
+                                         workspace=ws, out=y)
+        fgraphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                ffn_only(c)
+            fgraphs.append(g)
+        for i in range(args.warmup):
+            fgraphs[i % copies].replay()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record()
+        for i in range(args.steps):
+            fgraphs[i % copies].replay()
+        f1.record()
+        torch.cuda.synchronize()
+        ffn_ms = f0.elapsed_time(f1) / args.steps
+
     # ---- stage timing: the library's stage events around each kernel ------------
     # Eager steps (events are not recorded inside graphs).  A GPU sleep kernel
     # first keeps the stream busy while the host enqueues every step, so the
@@ -314,6 +349,12 @@ def main():
                                              else HBM_PEAK_GBS)), 2),
         "stage_us": {n: round(v, 3) for n, v in stage_avg_us.items()},
         "wall_ms_timed_region": round(wall_ms, 3),
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
+        "ffn_only": None if ffn_ms is None else {
+            "ms_per_step": round(ffn_ms, 5),
+            "value": round((alg_flops / (ffn_ms * 1e-3) / 1e12) if prefill_mfma else
+                           ((alg_bytes - (T * E * 4 if route else 0)) / (ffn_ms * 1e-3) / 1e9), 2),
+            "unit": unit, "note": "routing precomputed (same routing as the steps)"},
         "setup_s": round(setup_s, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -83,7 +83,8 @@ class Workload:
     description: str = ""
 
 
-# The five workloads of the benchmark (shapes from the task's configurations).
+# The benchmark workloads: a dense MLP decode, routed MoE decode, a 512-token
+# prefill chunk with a skewed router and a W4A4 prefill.
 LINEAR_SMALL = dict(M=4, K=256, N=512)
 MLP_DECODE = [Workload(f"mlp_decode_m{m}", m, 5120, 17408, 1, 1,
                        description="dense NVFP4 MLP decode, x bf16 [M,5120], "

@@ -24,8 +24,8 @@ What it computes, in plain numpy (fp64 unless a step is defined in fp32):
   "Qwen3.8 Flash Next": all 512 MoE experts; "Performance": prefill batches
   up to 512 prompt tokens so routed expert weights are reused).
 
-Readings where the pages are silent (each one is listed with its reason in
-the design doc): element 2i sits in the low nibble; scales are row-major
+Readings where the pages are silent (each is a plain reading that the rest
+of the pages supports): element 2i sits in the low nibble; scales are row-major
 [N, K/16]; the fp32 tensor scale is the *decode* multiplier
 g = amax / (6 * 448); block scales round to nearest-even E4M3 and saturate at
 448; elements round to nearest-even E2M1 and saturate at +-6; the sign of a
