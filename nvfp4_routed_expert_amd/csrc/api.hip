@@ -162,7 +162,9 @@ bool ffn_small(int64_t T, int64_t E, int64_t k) {
 }
 int ffn_bm(int64_t T, int64_t E, int64_t k) {
   if (ffn_small(T, E, k)) return 16;
-  return E == 1 ? gemm_block_rows(T * k) : 128;
+  if (E == 1) return gemm_block_rows(T * k);
+  // experts that average under 64 rows waste most of a 128-row block
+  return T * k >= 64 * E ? 128 : 64;
 }
 // m-blocks of up to bm rows over P pairs: each expert rounds up once (a
 // single expert, the dense MLP, has exactly ceil(P / bm))
