@@ -463,6 +463,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
 // number of earlier pairs with expert e, counted directly from the ids in
 // LDS: the stable counting-sort result in three barriers.
 constexpr int kSmallPairs = 256;
+constexpr int kMaxRouteExperts = 512;   // decode routing: experts per token row
 __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, int64_t T, int E,
                                                             int k, int32_t *offsets,
                                                             int32_t *sorted_pairs) {
@@ -512,17 +513,37 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
 // then takes a ticket from a counter in the caller's workspace
 // (acquire-release at device scope), and the wave holding the last ticket,
 // which therefore sees every token's ids, resets the counter and builds the
-// permutation alone: expert counts by LDS atomics, a DPP scan into the
-// offsets, and for pair p (expert e) the position offsets[e] + (earlier
-// pairs with expert e), counted 16 ids per step from LDS.
+// permutation alone.
+//
+// Permutation by bit-sliced matching: pair p = lane + 64 s sits in slot s of
+// its lane (pairs past P carry expert E, above every real one).  Ten ballots
+// per slot hold the bits of every pair's expert; walking them from the top
+// bit, a lane derives the masks of pairs whose expert equals its own and of
+// those whose expert is smaller.  Pair p then goes to
+//   (pairs with a smaller expert) + (pairs with the same expert before p),
+// which is the stable counting-sort position, and the first pair of each
+// expert knows that expert's offset; the offsets of experts without pairs
+// are the next larger expert's (a suffix minimum over the experts).
+constexpr int kRouteBits = 10;   // expert ids and the sentinel E <= 512
+
+__device__ __forceinline__ int wave_incl_min(int x) {
+  constexpr int kMax = 0x7fffffff;
+  x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x111, 0xF, 0xF, false));   // row_shr:1
+  x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x112, 0xF, 0xF, false));   // row_shr:2
+  x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x114, 0xF, 0xF, false));   // row_shr:4
+  x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x118, 0xF, 0xF, false));   // row_shr:8
+  x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x142, 0xA, 0xF, false));   // row_bcast:15
+  x = min(x, __builtin_amdgcn_update_dpp(kMax, x, 0x143, 0xC, 0xF, false));   // row_bcast:31
+  return x;
+}
 
 __global__ __launch_bounds__(64) void route_decode_kernel(const float *logits, int64_t T, int E,
                                                           int k, int renormalize, int32_t *ids,
                                                           float *weights, int32_t *offsets,
                                                           int32_t *sorted_pairs,
                                                           uint32_t *ticket) {
-  __shared__ __attribute__((aligned(16))) int32_t ids_lds[kSmallPairs];
-  __shared__ __attribute__((aligned(16))) int32_t cnt[512];
+  constexpr int kSlots = kSmallPairs / 64;
+  __shared__ int32_t first[kMaxRouteExperts];
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
   wave_topk_merge(logits + (int64_t)t * E, E, k, renormalize, ids + (int64_t)t * k,
@@ -535,48 +556,67 @@ __global__ __launch_bounds__(64) void route_decode_kernel(const float *logits, i
   if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   const int P = (int)T * k;
-  for (int e = lane; e < E; e += 64) cnt[e] = 0;
-  for (int p = lane; p < P; p += 64) ids_lds[p] = ids[p];
-  __syncthreads();
-  for (int p = lane; p < P; p += 64) atomicAdd(&cnt[ids_lds[p]], 1);
-  __syncthreads();
-  // lane l owns experts 8 l .. 8 l + 7
-  int c8[8], local = 0;
+  const int nslot = (P + 63) / 64;   // uniform, <= kSlots
+  int ev[kSlots];
+  uint64_t bits[kSlots][kRouteBits];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = 8 * lane + i;
-    c8[i] = e < E ? cnt[e] : 0;
-    local += c8[i];
+  for (int s = 0; s < kSlots; ++s) {
+    const int p = lane + 64 * s;
+    ev[s] = p < P ? ids[p] : E;
+#pragma unroll
+    for (int b = 0; b < kRouteBits; ++b) bits[s][b] = __builtin_amdgcn_ballot_w64((ev[s] >> b) & 1);
   }
-  int run = wave_incl_scan(local, lane) - local;
+#pragma unroll
+  for (int i = 0; i < kMaxRouteExperts / 64; ++i) first[lane + 64 * i] = P;
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < kSlots; ++s) {
+    if (s >= nslot) break;   // uniform
+    const int e = ev[s];
+    int less = 0, before = 0;
+#pragma unroll
+    for (int s2 = 0; s2 < kSlots; ++s2) {
+      if (s2 >= nslot) break;   // uniform
+      uint64_t eq = ~0ull, lt = 0ull;
+#pragma unroll
+      for (int b = kRouteBits - 1; b >= 0; --b) {
+        const uint64_t m = bits[s2][b];
+        const bool one = (e >> b) & 1;
+        lt = one ? (lt | (eq & ~m)) : lt;
+        eq = one ? (eq & m) : (eq & ~m);
+      }
+      less += __builtin_popcountll(lt);
+      if (s2 < s)
+        before += __builtin_popcountll(eq);
+      else if (s2 == s)
+        before += __builtin_amdgcn_mbcnt_hi((uint32_t)(eq >> 32),
+                                            __builtin_amdgcn_mbcnt_lo((uint32_t)eq, 0u));
+    }
+    const int p = lane + 64 * s;
+    if (p < P) {
+      sorted_pairs[less + before] = p;
+      if (before == 0) first[e] = less;   // one writer per expert
+    }
+  }
+  __syncthreads();
+  // lane l holds experts 8 (63 - l) .. + 7, so an inclusive min scan over the
+  // lanes is a suffix minimum over the experts
+  int v[8], lmin = P;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int e = 8 * lane + i;
-    if (e < E) {
-      cnt[e] = run;
-      offsets[e] = run;
-    }
-    run += c8[i];
+    v[i] = first[8 * (63 - lane) + i];
+    lmin = min(lmin, v[i]);
+  }
+  const int incl = wave_incl_min(lmin);
+  int run = __shfl_up(incl, 1);   // minimum over the larger experts
+  if (lane == 0) run = P;
+#pragma unroll
+  for (int i = 7; i >= 0; --i) {
+    run = min(run, v[i]);
+    const int e = 8 * (63 - lane) + i;
+    if (e < E) offsets[e] = run;
   }
   if (lane == 0) offsets[E] = P;
-  __syncthreads();
-  for (int p = lane; p < P; p += 64) {
-    const int e = ids_lds[p];
-    int before = 0;
-    for (int q0 = 0; q0 < p; q0 += 16) {
-      const int4 *v = reinterpret_cast<const int4 *>(ids_lds + q0);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int4 w = v[u];
-        const int q = q0 + 4 * u;
-        before += (w.x == e) & (q < p);
-        before += (w.y == e) & (q + 1 < p);
-        before += (w.z == e) & (q + 2 < p);
-        before += (w.w == e) & (q + 3 < p);
-      }
-    }
-    sorted_pairs[cnt[e] + before] = p;
-  }
 }
 
 int permute_words(int64_t T, int E) {
