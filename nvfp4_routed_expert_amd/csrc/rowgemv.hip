@@ -463,7 +463,7 @@ hipError_t launch_cfg(Epi epi, const GemmArgs &a, const Routing &info, int n_pos
   const int64_t groups = (a.N + rows - 1) / rows;
   const int64_t items = groups * (int64_t)n_pos;
   // persistent units: enough to fill every SIMD a few times, never more than items
-  int64_t units = 4096 / ks;
+  int64_t units = 2048 / ks;
   if (units > items) units = items;
   const int64_t blocks = (units + units_per_wg - 1) / units_per_wg;
   const dim3 grid((unsigned)(blocks < 1 ? 1 : blocks)), block(64 * ks * units_per_wg);
