@@ -457,6 +457,111 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(
   permute_block(ids, T, E, k, W, offsets, sorted_pairs, L);
 }
 
+// Permutation of a larger batch spread over workgroups by expert: workgroup
+// g owns experts [g epw, (g + 1) epw).  It reads every pair's id twice (L2
+// hits).  The first pass counts the pairs whose expert lies below its range
+// (the offset of its first expert) and marks its own pairs' tokens in a
+// bitmap per own expert; running popcounts over each bitmap then give every
+// own expert its count and, with the count below, its offset; the second
+// pass sends own pair p (expert e, token t) to offsets[e] + (tokens of e
+// before t), the stable counting-sort position.  Each offset is written by
+// exactly one workgroup; the last also writes offsets[E].
+constexpr int kSplitThreads = 1024;
+constexpr int kSplitWords = 8192;     // own experts x words per expert
+constexpr int kSplitMaxEpw = 64;
+constexpr int kSplitGroups = 128;     // target workgroup count
+
+__global__ __launch_bounds__(kSplitThreads) void permute_split_kernel(
+    const int32_t *ids, int64_t T, int E, int k, int epw, int W, int32_t *offsets,
+    int32_t *sorted_pairs) {
+  __shared__ uint32_t bitmap[kSplitWords];
+  __shared__ uint32_t prefix[kSplitWords];
+  __shared__ int32_t own_cnt[kSplitMaxEpw];
+  __shared__ int32_t own_off[kSplitMaxEpw];
+  __shared__ int32_t wave_below[kSplitThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthr = blockDim.x, nwaves = nthr >> 6;
+  const int e_lo = blockIdx.x * epw;
+  const int e_hi = e_lo + epw < E ? e_lo + epw : E;
+  const int nown = e_hi - e_lo;
+  const int64_t P = T * k;
+  for (int i = tid; i < nown * W; i += nthr) bitmap[i] = 0u;
+  __syncthreads();
+
+  // pass 1: pairs below the range, own tokens into the bitmaps
+  constexpr int kBatchIds = 8;
+  int below = 0;
+  for (int64_t p0 = tid; p0 < P; p0 += (int64_t)nthr * kBatchIds) {
+    int e8[kBatchIds];
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      e8[u] = p < P ? ids[p] : E;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      const int e = e8[u];
+      below += e < e_lo;
+      if (e >= e_lo && e < e_hi) {
+        const int64_t t = p / k;
+        atomicOr(&bitmap[(e - e_lo) * W + (int)(t >> 5)], 1u << (t & 31));
+      }
+    }
+  }
+  {
+    const int incl = wave_incl_scan(below, lane);
+    if (lane == 63) wave_below[wave] = incl;
+  }
+  __syncthreads();
+  // running popcounts of each own expert's words (one wave per expert)
+  for (int ee = wave; ee < nown; ee += nwaves) {
+    int run = 0;
+    for (int w0 = 0; w0 < W; w0 += 64) {
+      const int w = w0 + lane;
+      const int c = w < W ? __popc(bitmap[ee * W + w]) : 0;
+      const int incl = wave_incl_scan(c, lane);
+      if (w < W) prefix[ee * W + w] = (uint32_t)(run + incl - c);
+      run += __builtin_amdgcn_readlane(incl, 63);
+    }
+    if (lane == 0) own_cnt[ee] = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) run += wave_below[w];
+    for (int ee = 0; ee < nown; ++ee) {
+      own_off[ee] = run;
+      offsets[e_lo + ee] = run;
+      run += own_cnt[ee];
+    }
+    if (e_hi == E) offsets[E] = (int32_t)P;
+  }
+  __syncthreads();
+
+  // pass 2: own pairs to their positions
+  for (int64_t p0 = tid; p0 < P; p0 += (int64_t)nthr * kBatchIds) {
+    int e8[kBatchIds];
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      e8[u] = p < P ? ids[p] : E;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatchIds; ++u) {
+      const int64_t p = p0 + (int64_t)u * nthr;
+      const int e = e8[u];
+      if (e >= e_lo && e < e_hi) {
+        const int ee = e - e_lo;
+        const int64_t t = p / k;
+        const int w = (int)(t >> 5);
+        const uint32_t lower = bitmap[ee * W + w] & ((1u << (t & 31)) - 1u);
+        sorted_pairs[own_off[ee] + (int)prefix[ee * W + w] + __popc(lower)] = (int32_t)p;
+      }
+    }
+  }
+}
+
 // Permutation of a decode-sized batch (T k <= 256 pairs, E <= 1024), one
 // workgroup of 256 threads: expert counts by LDS atomics, one wave scans
 // them into the offsets, and pair p (expert e) goes to offsets[e] plus the
@@ -656,11 +761,23 @@ hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renorm
                   renormalize, ids, weights);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // permutation: one workgroup
+  // permutation: one workgroup for a decode-sized batch, else spread over
+  // workgroups by expert while each one's bitmaps fit in LDS
   if (T * k <= kSmallPairs) {
     launch_kernel(permute_small_kernel, dim3(1), dim3(256), 0, s, ids, T, E, k, offsets,
                   sorted_pairs);
     return hipGetLastError();
+  }
+  {
+    const int64_t words = (T + 31) / 32;
+    int64_t epw = (E + kSplitGroups - 1) / kSplitGroups;
+    if (epw > kSplitMaxEpw) epw = kSplitMaxEpw;
+    if (words * epw <= kSplitWords) {
+      const int groups = (int)((E + epw - 1) / epw);
+      launch_kernel(permute_split_kernel, dim3((unsigned)groups), dim3(kSplitThreads), 0, s, ids,
+                    T, E, k, (int)epw, (int)words, offsets, sorted_pairs);
+      return hipGetLastError();
+    }
   }
   launch_kernel(permute_kernel, dim3(1), dim3(kPermThreads), 0, s, ids, T, E, k, W, offsets,
                 sorted_pairs);

@@ -113,6 +113,8 @@ ROUTE_CASES = [
     ("long_9000x64_k2", 9000, 64, 2, None, True),
     ("decode_ties_32x256_k8", 32, 256, 8, None, True),
     ("one_token_1x512_k8", 1, 512, 8, None, True),
+    ("split_ragged_700x301_k5", 700, 301, 5, None, True),     # last expert group short
+    ("past_split_lds_300000x2_k1", 300000, 2, 1, None, True),  # bitmaps beyond one workgroup's LDS
 ]
 
 
