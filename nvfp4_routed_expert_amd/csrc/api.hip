@@ -145,6 +145,8 @@ struct FfnWs {
   float *ypair;
   int4 *mblocks;
   int32_t *n_mblocks;
+  int4 *mblocks_down;   // the down projection's blocks when their size differs
+  int32_t *n_mblocks_down;
   uint32_t *slots;      // [0] running max |h| (float bits), [1] g_x, [2] g_h, [3] -
   float *partials;
   float *split;         // partial sums of a K-split GEMM
@@ -166,6 +168,14 @@ int ffn_bm(int64_t T, int64_t E, int64_t k) {
   // experts that average under 64 rows waste most of a 128-row block
   return T * k >= 64 * E ? 128 : 64;
 }
+// The down projection of light experts (64-row blocks above) runs faster on
+// 32-row blocks: its K is the short intermediate size, so a block's weight
+// stream is short and the smaller activation stage lets more workgroups share
+// a CU.
+int ffn_bm_down(int64_t T, int64_t E, int64_t k) {
+  const int bm = ffn_bm(T, E, k);
+  return E > 1 && bm == 64 ? 32 : bm;
+}
 // m-blocks of up to bm rows over P pairs: each expert rounds up once (a
 // single expert, the dense MLP, has exactly ceil(P / bm))
 int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) {
@@ -178,9 +188,10 @@ FfnPlans ffn_plans(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   FfnPlans f;
   const int64_t P = T * k;
   const int64_t mb = ffn_max_mblocks(P, E, ffn_bm(T, E, k));
+  const int64_t mb_down = ffn_max_mblocks(P, E, ffn_bm_down(T, E, k));
   if (!ffn_small(T, E, k)) {
     if (tile_gemm_supported((int)H)) f.gate_up = tile_gemm_plan(Epi::SWIGLU, I, H, mb, P);
-    if (tile_gemm_supported((int)I)) f.down = tile_gemm_plan(Epi::DOWN, H, I, mb, P);
+    if (tile_gemm_supported((int)I)) f.down = tile_gemm_plan(Epi::DOWN, H, I, mb_down, P);
   }
   return f;
 }
@@ -195,6 +206,8 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.ypair = c.take<float>((size_t)(P * H));
   w.mblocks = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
   w.n_mblocks = c.take<int32_t>(4);
+  w.mblocks_down = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
+  w.n_mblocks_down = c.take<int32_t>(4);
   w.slots = c.take<uint32_t>(4);
   w.partials = c.take<float>(kMaxPartials);
   const FfnPlans pl = ffn_plans(T, H, I, E, k);
@@ -503,6 +516,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   const FfnWs ws = carve_ffn(c, T, H, I, E, k);
   const int64_t P = T * k;
   const int bm = ffn_bm(T, E, k);
+  const int bm_down = ffn_bm_down(T, E, k);
+  const bool split_down = bm_down != bm;   // the down projection has blocks of its own
   const FfnPlans plans = ffn_plans(T, H, I, E, k);
   const bool a4 = act == NVFP4_W4A4;
   const bool given = a4 && act_global_mode == NVFP4_GLOBAL_GIVEN;
@@ -531,12 +546,14 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
     LAUNCH(launch_moe_prep(xb, T, H, ws.x16, ws.xshift, expert_offsets, E, bm, ws.mblocks,
-                           ws.n_mblocks, ws.slots, zero_words, stream),
+                           ws.n_mblocks, bm_down, split_down ? ws.mblocks_down : nullptr,
+                           ws.n_mblocks_down, ws.slots, zero_words, stream),
            "plan + x prep");
     mark(NVFP4_STAGE_X_PREP, true, stream);
   } else {
     mark(NVFP4_STAGE_PLAN, false, stream);
-    LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, ws.slots,
+    LAUNCH(launch_moe_plan(expert_offsets, E, bm, ws.mblocks, ws.n_mblocks, bm_down,
+                           split_down ? ws.mblocks_down : nullptr, ws.n_mblocks_down, ws.slots,
                            (int)zero_words, stream),
            "plan");
     mark(NVFP4_STAGE_PLAN, true, stream);
@@ -629,9 +646,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.b_scales_estride = H * (I / 16);
   d.N = (int)H;
   d.K = (int)I;
-  d.mblocks = ws.mblocks;
-  d.n_mblocks_dev = ws.n_mblocks;
-  d.n_mblocks = (int)ffn_max_mblocks(P, E, bm);
+  d.mblocks = split_down ? ws.mblocks_down : ws.mblocks;
+  d.n_mblocks_dev = split_down ? ws.n_mblocks_down : ws.n_mblocks;
+  d.n_mblocks = (int)ffn_max_mblocks(P, E, bm_down);
   d.extra_scale = a4 ? slot_gh : nullptr;
   d.out = ws.ypair;
   d.ldo = H;
@@ -656,8 +673,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else
     LAUNCH(tile_gemm_supported((int)I)
-               ? launch_tile_gemm(Epi::DOWN, d, bm, plans.down, topk_ids, (int)P, stream)
-               : launch_gemm(Epi::DOWN, d, bm, stream),
+               ? launch_tile_gemm(Epi::DOWN, d, bm_down, plans.down, topk_ids, (int)P, stream)
+               : launch_gemm(Epi::DOWN, d, bm_down, stream),
            "down");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order

@@ -248,11 +248,16 @@ __device__ void build_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
   if (tid == 0) *n_mblocks = run;
 }
 
+// A second list of bm2-row blocks (a different block size for the down
+// projection) when mblocks2 is set.
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, int E, int bm,
                                                         int4 *mblocks, int32_t *n_mblocks,
-                                                        uint32_t *zero, int zero_words) {
+                                                        int bm2, int4 *mblocks2,
+                                                        int32_t *n_mblocks2, uint32_t *zero,
+                                                        int zero_words) {
   for (int i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
   build_plan(offsets, E, bm, mblocks, n_mblocks);
+  if (mblocks2) build_plan(offsets, E, bm2, mblocks2, n_mblocks2);
 }
 
 // Blocks before the last: x rows -> fp16 with their power-of-two shift (as
@@ -262,12 +267,14 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, 
 __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_t T, int64_t H,
                                                        _Float16 *x16, int32_t *xshift,
                                                        const int32_t *offsets, int E, int bm,
-                                                       int4 *mblocks, int32_t *n_mblocks,
+                                                       int4 *mblocks, int32_t *n_mblocks, int bm2,
+                                                       int4 *mblocks2, int32_t *n_mblocks2,
                                                        uint32_t *zero, int64_t zero_words,
                                                        int wide) {
   if (blockIdx.x == gridDim.x - 1) {
     for (int64_t i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
     build_plan(offsets, E, bm, mblocks, n_mblocks);
+    if (mblocks2) build_plan(offsets, E, bm2, mblocks2, n_mblocks2);
     return;
   }
   __shared__ float wmax[4];
@@ -346,21 +353,23 @@ hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s) {
 }
 
 hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
-                           int32_t *n_mblocks, uint32_t *zero, int zero_words,
-                           hipStream_t s) {
+                           int32_t *n_mblocks, int bm2, int4 *mblocks2, int32_t *n_mblocks2,
+                           uint32_t *zero, int zero_words, hipStream_t s) {
   launch_kernel(moe_plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, bm, mblocks,
-                     n_mblocks, zero, zero_words);
+                     n_mblocks, bm2, mblocks2, n_mblocks2, zero, zero_words);
   return hipGetLastError();
 }
 
 hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x16,
                            int32_t *xshift, const int32_t *offsets, int E, int bm,
-                           int4 *mblocks, int32_t *n_mblocks, uint32_t *zero,
-                           int64_t zero_words, hipStream_t s) {
+                           int4 *mblocks, int32_t *n_mblocks, int bm2, int4 *mblocks2,
+                           int32_t *n_mblocks2, uint32_t *zero, int64_t zero_words,
+                           hipStream_t s) {
   const int wide = T <= 1024;
   const int64_t blocks = (wide ? T : (T + 3) / 4) + 1;
   launch_kernel(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16, xshift,
-                offsets, E, bm, mblocks, n_mblocks, zero, zero_words, wide);
+                offsets, E, bm, mblocks, n_mblocks, bm2, mblocks2, n_mblocks2, zero, zero_words,
+                wide);
   return hipGetLastError();
 }
 

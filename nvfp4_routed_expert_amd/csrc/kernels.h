@@ -165,16 +165,18 @@ hipError_t launch_row_down_sum(const GemmArgs &a, const int32_t *ids, int k, int
 
 // FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
 // workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.
+// (mblocks2 set: also a list of bm2-row blocks, for the down projection)
 hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x16,
                            int32_t *xshift, const int32_t *offsets, int E, int bm,
-                           int4 *mblocks, int32_t *n_mblocks, uint32_t *zero,
-                           int64_t zero_words, hipStream_t s);
+                           int4 *mblocks, int32_t *n_mblocks, int bm2, int4 *mblocks2,
+                           int32_t *n_mblocks2, uint32_t *zero, int64_t zero_words,
+                           hipStream_t s);
 int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
 
 // FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.
 hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
-                           int32_t *n_mblocks, uint32_t *zero, int zero_words,
-                           hipStream_t s);
+                           int32_t *n_mblocks, int bm2, int4 *mblocks2, int32_t *n_mblocks2,
+                           uint32_t *zero, int zero_words, hipStream_t s);
 
 // y[t] = sum_j Y[t*k + j], j ascending, fp32 -> out type.
 hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k,
