@@ -57,6 +57,7 @@ def parse():
 # only while these files are byte-identical to the ones it was taken on.
 KERNEL_SOURCES = {
     "row_gemv_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
+    "tile_gemm_kernel": ["tile_gemm.hip", "common.h", "kernels.h"],
     "grouped_gemm_kernel": ["gemm.hip", "common.h", "kernels.h"],
     "grouped_gemv_kernel": ["gemv.hip", "common.h", "kernels.h"],
 }
@@ -92,12 +93,17 @@ def stored_traffic(kernel, workload):
 
 
 def gate_up_kernel(T, H, I, E, k, act):
-    """Which kernel runs the gate/up projection (mirrors the library's dispatch)."""
-    small = 2 * T * k <= 32 * E
+    """Which kernel runs the gate/up projection (mirrors the library's dispatch:
+    decode-sized batches stream rows or run the small GEMV, anything larger
+    the LDS-tiled grouped GEMM, or the generic one when H % 64 != 0)."""
+    P = T * k
+    small = P <= 2 if E == 1 else (P <= 256 and 2 * P <= 32 * E)
     row_ok = lambda K: K in (256, 512, 1024) or (K % 32 == 0 and 2048 <= K <= 32768)
-    if small and act == "w4a16" and row_ok(H) and row_ok(I):
-        return "row_gemv_kernel"
-    return "grouped_gemv_kernel" if small else "grouped_gemm_kernel"
+    if small:
+        if act == "w4a16" and row_ok(H) and row_ok(I):
+            return "row_gemv_kernel"
+        return "grouped_gemv_kernel"
+    return "tile_gemm_kernel" if H % 64 == 0 else "grouped_gemm_kernel"
 
 
 class HipEvents:

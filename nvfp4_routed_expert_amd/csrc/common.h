@@ -32,18 +32,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   return (b & 0x80u) ? -mag : mag;
 }
 
-// E2M1 magnitude code (0..7) -> fp32, exact: {0, .5, 1, 1.5, 2, 3, 4, 6}.
-__device__ __forceinline__ float e2m1_mag_to_f32(uint32_t c) {
-  // exponent field e = c >> 1 (bias 1), mantissa bit m = c & 1
-  const uint32_t e = c >> 1, m = c & 1u;
-  return e ? __uint_as_float(((e + 126u) << 23) | (m << 22)) : 0.5f * (float)m;
-}
-
-__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  const float mag = e2m1_mag_to_f32(c & 7u);
-  return (c & 8u) ? -mag : mag;
-}
-
 // Two E2M1 codes in byte `sel` (0..3) of `word` -> fp16 pair {low nibble,
 // high nibble}, exact (gfx950 v_cvt_scalef32_pk_f16_fp4 with unit scale).
 template <int SEL>
@@ -88,17 +76,6 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat(float v) {
   const uint32_t bits = __float_as_uint(v);
   const uint32_t r = bits + 0x7FFFFu + ((bits >> 20) & 1u);  // RNE to 3 mantissa bits
   return (r >> 20) - (120u << 3);
-}
-
-// Nearest E2M1 code of a finite fp32 value, ties to even, |v| > 6 -> 6,
-// sign bit copied (a negative value rounding to zero gives 0x8).
-__device__ __forceinline__ uint32_t e2m1_rne_sat(float v) {
-  const float a = __builtin_fabsf(v);
-  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) +
-               (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
-               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-               (uint32_t)(a > 5.0f);
-  return c | ((__float_as_uint(v) >> 28) & 8u);
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
@@ -164,10 +141,23 @@ __device__ __forceinline__ Block16 quantize_block16(const float (&x)[16], float 
   b.hi = 0u;
   if (denom > 0.0f) {
     const float inv = 1.0f / denom;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b.lo |= e2m1_rne_sat(x[i] * inv) << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) b.hi |= e2m1_rne_sat(x[8 + i] * inv) << (4 * i);
+    // gfx950's packed fp32 -> E2M1 converter with unit scale: the nearest
+    // E2M1 value, ties to even, |v| > 6 -> 6, the sign bit kept (a negative
+    // value rounding to zero gives code 0x8); operand 0 goes to the low
+    // nibble of byte SEL.  (Checked on the device against these rules for
+    // every multiple of 1/128 in [-9.4, 9.4], the tie points, zeros,
+    // denormals and huge values.)
+#define NVFP4_ENC(W, SEL, A, B) \
+  W = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(W, (A) * inv, (B) * inv, 1.0f, SEL)
+    NVFP4_ENC(b.lo, 0, x[0], x[1]);
+    NVFP4_ENC(b.lo, 1, x[2], x[3]);
+    NVFP4_ENC(b.lo, 2, x[4], x[5]);
+    NVFP4_ENC(b.lo, 3, x[6], x[7]);
+    NVFP4_ENC(b.hi, 0, x[8], x[9]);
+    NVFP4_ENC(b.hi, 1, x[10], x[11]);
+    NVFP4_ENC(b.hi, 2, x[12], x[13]);
+    NVFP4_ENC(b.hi, 3, x[14], x[15]);
+#undef NVFP4_ENC
   }
   return b;
 }

@@ -52,18 +52,29 @@ __device__ float resolve_global(const float *amax_src, int n, const float *g_giv
   return global_from_amax(block_max(m, lds4));
 }
 
+// Groups of 8 elements, kAmaxBatch of them per thread and step with every
+// load issued before the first is used.
+constexpr int kAmaxBatch = 8;
 __global__ __launch_bounds__(kThreads) void amax_partials_kernel(
     const void *x, InType t, int64_t rows, int64_t cols, int64_t ld, float *partials) {
   __shared__ float lds[4];
   const int64_t gpr = cols / 8, groups = rows * gpr;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
   float m = 0.0f;
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups;
-       g += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = g / gpr, c = (g - r * gpr) * 8;
-    float v[8];
-    load8(x, t, r * ld + c, v);
+  for (int64_t g0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; g0 < groups;
+       g0 += stride * kAmaxBatch) {
+    float v[kAmaxBatch][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[i]));
+    for (int u = 0; u < kAmaxBatch; ++u) {
+      const int64_t g = g0 + u * stride;
+      const int64_t gg = g < groups ? g : g0;   // past the end: a valid group again
+      const int64_t r = gg / gpr, c = (gg - r * gpr) * 8;
+      load8(x, t, r * ld + c, v[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kAmaxBatch; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, __builtin_fabsf(v[u][i]));
   }
   m = block_max(m, lds);
   if (threadIdx.x == 0) partials[blockIdx.x] = m;
@@ -193,21 +204,39 @@ __global__ __launch_bounds__(kThreads) void row_prep_kernel(
   }
   if (r >= rows) return;
   const uint16_t *row = x + r * cols;
-  for (int64_t c = lane * 16; c < cols; c += 1024) {
-    float v[16];
-    float (&v0)[8] = *reinterpret_cast<float (*)[8]>(&v[0]);
-    float (&v1)[8] = *reinterpret_cast<float (*)[8]>(&v[8]);
-    load8(row, InType::BF16, c, v0);
-    load8(row, InType::BF16, c + 8, v1);
-    const Block16 q = quantize_block16(v, g);
-    f16x8 h0, h1;
+  // up to kPrepSteps blocks of 16 per lane: all loads first, then the blocks
+  constexpr int kPrepSteps = 4;
+  for (int64_t c0 = lane * 16; c0 < cols; c0 += 1024 * kPrepSteps) {
+    u32x4 raw[kPrepSteps][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      h0[i] = (_Float16)(e2m1_to_f32((q.lo >> (4 * i)) & 15u) * q.sdec);
-      h1[i] = (_Float16)(e2m1_to_f32((q.hi >> (4 * i)) & 15u) * q.sdec);
+    for (int st = 0; st < kPrepSteps; ++st) {
+      const int64_t c = c0 + st * 1024;
+      if (c < cols) {
+        raw[st][0] = *reinterpret_cast<const u32x4 *>(row + c);
+        raw[st][1] = *reinterpret_cast<const u32x4 *>(row + c + 8);
+      }
     }
-    *reinterpret_cast<f16x8 *>(out + r * cols + c) = h0;
-    *reinterpret_cast<f16x8 *>(out + r * cols + c + 8) = h1;
+#pragma unroll
+    for (int st = 0; st < kPrepSteps; ++st) {
+      const int64_t c = c0 + st * 1024;
+      if (c >= cols) break;
+      float v[16];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[8 * h + 2 * i] = __uint_as_float(raw[st][h][i] << 16);
+          v[8 * h + 2 * i + 1] = __uint_as_float(raw[st][h][i] & 0xFFFF0000u);
+        }
+      const Block16 q = quantize_block16(v, g);
+      // the exact fp16 products e2m1 * e4m3, as the GEMM operands expect
+      f16x2 s0, s1;
+      e4m3x2_to_f16_pairs(q.scale, s0, s1);
+      const f16x8 h0 = dequant8_f16(q.lo, s0);
+      const f16x8 h1 = dequant8_f16(q.hi, s0);
+      *reinterpret_cast<f16x8 *>(out + r * cols + c) = h0;
+      *reinterpret_cast<f16x8 *>(out + r * cols + c + 8) = h1;
+    }
   }
 }
 
