@@ -330,6 +330,7 @@ def main():
     roofline["alg_per_launch"] = int(gateup_flops if prefill_mfma else gateup_bytes)
     roofline["alg_units_per_launch"] = (f"{active} experts x 2 NVFP4 [{I},{H}] + x"
                                         if not prefill_mfma else f"{P} pairs x 4*H*I flop")
+    roofline["alg_bytes_per_launch"] = int(gateup_bytes)   # weights + x, for the traffic ratio
 
     if args.copy_calibration:
         copy_calibration()
