@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="moe_decode",
-                    help="moe_decode | moe_prefill | moe_prefill_w4a4 | mlp_decode_m{1,8,32}")
+                    help="moe_decode | moe_prefill | moe_prefill_w4a4 | mlp_decode_m{1,8,32} | "
+                         "mlp_prefill_m{512,2048}")
     ap.add_argument("--copies", type=int, default=0,
                     help="weight copies cycled per step (0 = enough for >= 2 GiB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -207,7 +208,8 @@ def main():
     alg_flops = 6 * P * H * I
     gateup_bytes = 2 * active * (nv_bytes(H * I) + 4) + T * H * 2
     gateup_flops = 4 * P * H * I
-    prefill_mfma = wl.name == "moe_prefill_w4a4"
+    # MFMA-bound when the step's arithmetic intensity exceeds the ridge point
+    prefill_mfma = alg_flops / alg_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
     # ---- timed region: K steps (graph replays), HIP events on the stream -----------
     use_graph = not args.eager
@@ -338,7 +340,7 @@ def main():
     # ---- CPU oracle on a bounded sample (rank 0, N = 1) --------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts)
+        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts, prefill_mfma)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -382,7 +384,7 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts):
+def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound):
     """Time the oracle (as it stands) on a bounded sample of the same step and
     use it as the correctness gate for the GPU output rows it covers."""
     import numpy as np
@@ -418,7 +420,7 @@ def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts):
            "sample": f"{len(tokens)} of {T} tokens ({len(need)} experts), "
                      f"fp64 numpy oracle, {dt:.2f} s",
            "seconds": round(dt, 3)}
-    if wl.name == "moe_prefill_w4a4":
+    if mfma_bound:
         res.update(value=round(sample_flops / dt / 1e12, 6), unit="TFLOP/s")
     else:
         res.update(value=round(sample_bytes / dt / 1e9, 4), unit="GB/s")

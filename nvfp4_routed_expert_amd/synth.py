@@ -99,4 +99,9 @@ MOE_PREFILL = Workload("moe_prefill", 512, 2048, 512, 512, 8, zipf_s=1.1,
 MOE_PREFILL_W4A4 = Workload("moe_prefill_w4a4", 2048, 4096, 1536, 128, 8, act="w4a4",
                             description="W4A4 MoE prefill: 2048 tokens, hidden 4096, 128 "
                                         "experts, intermediate 1536, top-8 uniform routing")
-WORKLOADS = {w.name: w for w in [*MLP_DECODE, MOE_DECODE, MOE_PREFILL, MOE_PREFILL_W4A4]}
+MLP_PREFILL = [Workload(f"mlp_prefill_m{m}", m, 5120, 17408, 1, 1,
+                        description="dense NVFP4 MLP prefill, x bf16 [M,5120], "
+                                    "gate/up [17408,5120], down [5120,17408]")
+               for m in (512, 2048)]
+WORKLOADS = {w.name: w for w in [*MLP_DECODE, *MLP_PREFILL, MOE_DECODE, MOE_PREFILL,
+                                 MOE_PREFILL_W4A4]}

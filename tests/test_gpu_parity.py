@@ -345,6 +345,16 @@ def test_moe_w4a4_full_size_sampled_given_globals():
     assert_close_f32(to_np(y)[tokens], ref, "moe w4a4 full")
 
 
+@pytest.mark.parametrize("M", [512, 2048])
+def test_dense_mlp_prefill_full_size_sampled(M):
+    wl = synth.WORKLOADS[f"mlp_prefill_m{M}"]
+    say("dense mlp prefill full size", M)
+    x, rids, rw, y, _, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, 1, 1)
+    rows = [0, 1, M // 2 + 3, M - 1]   # first and last m-blocks, a middle one
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=rows)
+    assert_close_f32(to_np(y)[rows], ref, "dense mlp prefill")
+
+
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_dense_mlp_decode_full_size(M):
     wl = synth.WORKLOADS[f"mlp_decode_m{M}"]
