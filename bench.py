@@ -48,6 +48,12 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0 = workload default)")
     ap.add_argument("--eager", action="store_true", help="no graph capture")
+    ap.add_argument("--given-globals", action="store_true",
+                    help="W4A4: static activation scales given by the caller (g_x from the "
+                         "input's amax, g_h a fixed calibration value) instead of online ones")
+    ap.add_argument("--separate-h-quant", action="store_true",
+                    help="with --given-globals: quantise h in its own pass instead of the "
+                         "gate/up epilogue (same results)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy kernel (for scaling "
                          "hardware byte counters)")
@@ -183,7 +189,11 @@ def main():
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(native.ffn_workspace_bytes(T, H, I, E, k, act), dtype=torch.uint8,
                      device=dev)
-    ag = torch.empty(2, dtype=torch.float32, device=dev) if act == native.W4A4 else None
+    ag = None
+    if act == native.W4A4 and args.given_globals:   # static calibration scales
+        ag = torch.tensor([float(x_cpu.float().abs().max()) / 2688.0, 0.05 / 2688.0],
+                          dtype=torch.float32, device=dev)
+    native.set_ffn_separate_h_quant(args.separate_h_quant)
     rws = native.route_workspace(T, E, k, dev)
     route = E > 1
 
@@ -191,7 +201,7 @@ def main():
         if route:
             native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
         native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
-                                     act_globals=None, out_dtype=torch.bfloat16,
+                                     act_globals=ag, out_dtype=torch.bfloat16,
                                      workspace=ws, out=y)
 
     if not route:   # one expert: the routing is fixed (all rows to expert 0)
@@ -264,7 +274,7 @@ def main():
     if use_graph:   # routing precomputed: graphs of the FFN call alone
         def ffn_only(c):
             native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
-                                         act_globals=None, out_dtype=torch.bfloat16,
+                                         act_globals=ag, out_dtype=torch.bfloat16,
                                          workspace=ws, out=y)
         fgraphs = []
         for c in range(copies):
@@ -349,6 +359,10 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "act": wl.act,
+                   "act_globals": ("given (static)" if ag is not None else
+                                   "online" if act == native.W4A4 else None),
+                   "h_quant": ("separate pass" if args.separate_h_quant else "fused")
+                              if ag is not None else None,
                    "zipf_s": wl.zipf_s, "active_experts": active,
                    "max_tokens_per_expert": int(counts.max()),
                    "weight_copies_cycled": copies, "graph": use_graph,

@@ -212,6 +212,19 @@ enum {
 };
 void nvfp4_set_ffn_stage_events(hipEvent_t *events);
 
+/*
+ * Execution choice (not part of the computation).  With act W4A4 and GIVEN
+ * globals, moe_grouped_nvfp4_ffn quantises h inside the gate/up GEMM's
+ * epilogue wherever the tiled kernel computes a whole h row block without a
+ * K split: the 16-element block maxima are reduced across lanes and h never
+ * goes to memory in bf16.  nvfp4_set_ffn_separate_h_quant(1) makes later
+ * calls on the calling thread write bf16 h and quantise it in a pass of its
+ * own instead (0 restores the default).  Both orders compute the same h and
+ * the same codes with the same fp32 operations, so their outputs are
+ * bit-identical; the choice only changes the kernels that run.
+ */
+void nvfp4_set_ffn_separate_h_quant(int separate);
+
 /* Text of a status code; never NULL. */
 const char *nvfp4_status_string(nvfp4_status s);
 /* Detail of the last failure on the calling thread ("" if none). */

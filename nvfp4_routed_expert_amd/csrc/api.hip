@@ -17,6 +17,7 @@ namespace {
 
 thread_local char g_last_error[512] = "";
 thread_local hipEvent_t *g_stage_events = nullptr;
+thread_local bool g_separate_h_quant = false;
 
 // Records the profiling event of stage s (before: 2s, after: 2s+1), if set.
 // Nothing is recorded while the stream is being captured into a graph.
@@ -236,6 +237,8 @@ const char *nvfp4_status_string(nvfp4_status s) {
 const char *nvfp4_last_error(void) { return g_last_error; }
 
 void nvfp4_set_ffn_stage_events(hipEvent_t *events) { g_stage_events = events; }
+
+void nvfp4_set_ffn_separate_h_quant(int separate) { g_separate_h_quant = separate != 0; }
 
 // ---- nvfp4_quantize ----------------------------------------------------------------
 
@@ -596,6 +599,15 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.ldo = I;
   g.out_type = OutType::BF16;
   g.amax_slot = a4 ? ws.slots : nullptr;
+  // W4A4 with a given h global on the tiled path: the gate/up epilogue
+  // quantises h itself and writes the down GEMM's fp16 operand directly
+  const bool h_fused = given && !small && !g_separate_h_quant && tile_gemm_supported((int)H) &&
+                       plans.gate_up.ksplit == 1;
+  if (h_fused) {
+    g.h_quant_g = act_globals + 1;
+    g.out = ws.h16;
+    g.amax_slot = nullptr;
+  }
   g.sorted_pairs = sorted_pairs;   // (split-K reduce: expert of each tile row)
   g.partial = ws.split;
   g.partial_rows = P;
@@ -623,6 +635,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
       LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::SHIFT, ws.h16, ws.hshift, nullptr, 0, nullptr,
                              nullptr, nullptr, stream),
              "h prep");
+  } else if (h_fused) {
+    // quantised in the gate/up epilogue (the down GEMM reads g_h from the caller)
   } else if (given) {
     LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::QUANT, ws.h16, nullptr, nullptr, 0,
                            act_globals + 1, slot_gh, nullptr, stream),
@@ -649,7 +663,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.mblocks = split_down ? ws.mblocks_down : ws.mblocks;
   d.n_mblocks_dev = split_down ? ws.n_mblocks_down : ws.n_mblocks;
   d.n_mblocks = (int)ffn_max_mblocks(P, E, bm_down);
-  d.extra_scale = a4 ? slot_gh : nullptr;
+  d.extra_scale = h_fused ? act_globals + 1 : a4 ? slot_gh : nullptr;
   d.out = ws.ypair;
   d.ldo = H;
   d.out_type = OutType::F32;

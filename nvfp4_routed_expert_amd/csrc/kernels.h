@@ -106,6 +106,10 @@ struct GemmArgs {
   int64_t ldo;
   OutType out_type;
   uint32_t *amax_slot;            // SWIGLU: running max of |h| (float bits) or null
+  // SWIGLU, tile GEMM without a K split: when set, h is quantised to NVFP4
+  // with this (given) global in the epilogue and out receives the exact fp16
+  // products e2m1 * e4m3 (what the down GEMM consumes) instead of bf16 h
+  const float *h_quant_g;
   const float *pair_weights;      // DOWN: routing weight of pair p
   const int32_t *sorted_pairs;    // DOWN: pair of each tile row
   // split K (tile GEMM): raw fp32 sums of part kz at partial[kz][pos][col]

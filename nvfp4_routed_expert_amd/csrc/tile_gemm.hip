@@ -72,6 +72,63 @@ __device__ __forceinline__ int arow_of(const GemmArgs &p, int pos) {
   return p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
 }
 
+// Max over the 16 lanes of each DPP row (rotations by 8, 4, 2, 1).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x122, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x121, 0xF, 0xF, false)));
+  return v;
+}
+
+// Gate/up epilogue with the h quantisation folded in (a given global g_h):
+// h = bf16(silu(G) * U) as in the plain epilogue, then NVFP4 blocks of 16
+// consecutive columns.  Column lr of a fragment sits in lane lr of the
+// 16-lane DPP row that holds the row, so each block's absolute maximum is a
+// row reduction; the block scale, the per-element code and the stored fp16
+// product follow the same fp32 steps as the quantisation kernel (one
+// correctly rounded operation each).  Blocks never straddle N (N % 16 == 0)
+// and the 16 lanes of a block share its row, so the reduction runs
+// unconditionally and only the stores are predicated.
+template <int MS>
+__device__ __forceinline__ void store_h_quantised(const GemmArgs &p, const f32x4 (&acc)[MS][4],
+                                                  int nrows, int pos0, int col0, float gg,
+                                                  float gu, int lane) {
+#pragma clang fp contract(off)
+  const int lr = lane & 15, lg = lane >> 4;
+  const int N = p.N;
+  const float g = *p.h_quant_g;
+  const float six_g = 6.0f * g;
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = ms * 16 + 4 * lg + j;
+      const int pos = pos0 + r;
+      const int sh = (p.a_shift && r < nrows) ? p.a_shift[arow_of(p, pos)] : 0;
+      _Float16 *hrow = static_cast<_Float16 *>(p.out) + (int64_t)pos * p.ldo;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        const int col = col0 + f * 16 + lr;
+        const float G = __builtin_ldexpf(acc[ms][f][j], sh) * gg;
+        const float U = __builtin_ldexpf(acc[ms][f + 2][j], sh) * gu;
+        const float x = bf16_bits_to_f32(f32_to_bf16_bits(G / (1.0f + expf(-G)) * U));
+        const float amax = row16_max(__builtin_fabsf(x));
+        const uint32_t sc = e4m3_rne_sat(amax / six_g);
+        const float sdec = e4m3_to_f32(sc);
+        const float denom = sdec * g;
+        uint32_t code = 0u;
+        if (denom > 0.0f)
+          code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x * (1.0f / denom), 0.0f, 1.0f, 0) & 15u;
+        f16x2 s0, s1;
+        e4m3x2_to_f16_pairs(sc, s0, s1);
+        const f16x2 v = e2m1x2_to_f16<0>(code) * s0;
+        if (r < nrows && col < N) hrow[col] = v[0];
+      }
+    }
+  }
+}
+
 template <int MS, int NW, Epi EPI>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(const GemmArgs p) {
   using C = TileCfg<MS, NW>;
@@ -266,8 +323,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
   }
   const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
   if constexpr (EPI == Epi::SWIGLU) {
-    float amax = 0.0f;
     const float gg = p.b_global[0][e] * extra, gu = p.b_global[1][e] * extra;
+    if (p.h_quant_g) {   // uniform
+      store_h_quantised<MS>(p, acc, nrows, pos0, col0, gg, gu, lane);
+      return;
+    }
+    float amax = 0.0f;
 #pragma unroll
     for (int ms = 0; ms < MS; ++ms) {
 #pragma unroll

@@ -71,6 +71,7 @@ def lib():
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
             "moe_grouped_nvfp4_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
             "nvfp4_set_ffn_stage_events": (None, [_vp]),
+            "nvfp4_set_ffn_separate_h_quant": (None, [ctypes.c_int]),
             "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
             "nvfp4_last_error": (ctypes.c_char_p, []),
         }
@@ -90,6 +91,7 @@ def exported_symbols():
             "nvfp4_linear", "nvfp4_linear_workspace_size", "moe_route_topk",
             "moe_route_topk_workspace_size", "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "nvfp4_set_ffn_stage_events",
+            "nvfp4_set_ffn_separate_h_quant",
             "nvfp4_status_string", "nvfp4_last_error"]
 
 
@@ -272,3 +274,10 @@ def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_ids, topk_weights, exp
                                    act, mode, _ptr(ag), _ptr(y), _dt(y.dtype), _ptr(ws),
                                    ws.numel(), _stream()))
     return y, ag
+
+
+def set_ffn_separate_h_quant(separate):
+    """W4A4 with given globals: quantise h in a pass of its own (True) rather
+    than in the gate/up epilogue (False, the default).  Per calling thread;
+    the outputs are bit-identical either way."""
+    lib().nvfp4_set_ffn_separate_h_quant(1 if separate else 0)

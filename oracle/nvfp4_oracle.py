@@ -31,7 +31,10 @@ g = amax / (6 * 448); block scales round to nearest-even E4M3 and saturate at
 448; elements round to nearest-even E2M1 and saturate at +-6; the sign of a
 zero code is kept; quantisation uses the fp32 operation order written in
 ``quantize``; ties in top-k go to the lower expert index; h is rounded to
-bf16 before the down projection.
+bf16 before the down projection.  The pages fix no precision for forming h;
+besides the fp64 h, ``expert_h_fp32`` forms it with fp32 operations (the
+FFN's fp32 accumulation) for comparisons where h's bf16 rounding and NVFP4
+codes must be decided in the same precision on both sides.
 """
 
 from __future__ import annotations
@@ -364,6 +367,34 @@ def expert_h(x_rows, w, e):
     return bf16_rne(silu(gate) * up)
 
 
+def expert_h_fp32(xv_rows, g_x, w, e):
+    """h for expert e with the gate and up values formed in fp32, for where an
+    h value decides an integer (its bf16 rounding and, in W4A4, its NVFP4
+    code) and both sides must take that decision in the same precision.
+
+    Reading: the FFN accumulates in fp32, so each value is an fp32 operation
+    rounded to nearest-even, in the order the definition is written:
+      S = fl32(exact x_v . D^T)  (x_v: the unscaled operand, e2m1*e4m3 blocks
+          of the quantised x, or the bf16 x itself; every product is exact),
+      G = fl32(S * fl32(g_gate * g_x)), U likewise with g_up (g_x = 1 for a
+          bf16 x),
+      h = bf16_rne( fl32( fl32(G / fl32(1 + fl32(exp(-G)))) * U ) ),
+    exp itself correctly rounded from fp64.
+    """
+    f32 = np.float32
+    gx = f32(1.0) if g_x is None else f32(g_x)
+    dg = block_values(w.gate_codes[e], w.gate_scales[e])
+    du = block_values(w.up_codes[e], w.up_scales[e])
+    with np.errstate(over="ignore"):
+        s_g = (xv_rows @ dg.T).astype(f32)
+        s_u = (xv_rows @ du.T).astype(f32)
+        gate = s_g * (f32(w.gate_global[e]) * gx)
+        up = s_u * (f32(w.up_global[e]) * gx)
+        ex = np.exp(-gate.astype(np.float64)).astype(f32)
+        h32 = (gate / (f32(1.0) + ex)) * up
+    return bf16_rne(h32.astype(np.float64))
+
+
 def expert_down(h_rows, w, e):
     """g_down * h D_down^T for expert e (fp64)."""
     dd = block_values(w.down_codes[e], w.down_scales[e])
@@ -371,7 +402,7 @@ def expert_down(h_rows, w, e):
 
 
 def moe_ffn(x, ids, weights, w, act_quant=False, act_globals=None,
-            tokens=None):
+            tokens=None, h_fp32=False):
     """Routed-expert FFN, fp64.
 
     y_t = sum_j weights[t, j] * down_e( h ),  e = ids[t, j], where
@@ -384,7 +415,10 @@ def moe_ffn(x, ids, weights, w, act_quant=False, act_globals=None,
     act_globals = (g_x, g_h) fixes those scales instead of computing them.
     tokens: compute only these output rows (W4A16, or W4A4 with both
     act_globals given, where the rows are independent).
-    Returns (y fp64 [T or len(tokens), H], info dict).
+    h_fp32: form h with expert_h_fp32 (fp32 gate/up values) instead of fp64;
+    everything after h stays as above.
+    Returns (y fp64 [T or len(tokens), H], info dict; info["h_bf16"] is h
+    before its W4A4 quantisation, info["h"] the h the down projection used).
     """
     x32 = np.asarray(x, dtype=np.float32)
     ids = np.asarray(ids)
@@ -404,15 +438,19 @@ def moe_ffn(x, ids, weights, w, act_quant=False, act_globals=None,
         xc, xs, g_x = quantize(x32, g_x)
         x64 = dequantize(xc, xs, g_x)
         info["g_x"] = g_x
+        xv, xv_g = block_values(xc, xs), g_x
     else:
         x64 = x32.astype(np.float64)
+        xv, xv_g = x64, None
 
     # h for every requested (token, slot), expert by expert
     sel_ids = ids[tokens]                                    # [n, k]
     h = np.zeros((len(tokens), k, w.gate_codes.shape[1]), dtype=np.float64)
     for e in np.unique(sel_ids):
         rows, slots = np.nonzero(sel_ids == e)
-        h[rows, slots] = expert_h(x64[tokens[rows]], w, e)
+        h[rows, slots] = (expert_h_fp32(xv[tokens[rows]], xv_g, w, e) if h_fp32
+                          else expert_h(x64[tokens[rows]], w, e))
+    info["h_bf16"] = h.copy()
 
     if act_quant:
         g_h = None if act_globals is None else act_globals[1]

@@ -331,6 +331,61 @@ def test_moe_prefill_full_size_sampled():
     assert_close_f32(to_np(y)[tokens], ref, "moe prefill")
 
 
+def _fused_vs_separate(T, H, I, E, k, gh, seed):
+    """Runs W4A4 with given globals twice, h quantised in the gate/up
+    epilogue and in its own pass; returns both outputs and the oracle's."""
+    x = synth.activations(T, H, seed=seed)
+    gx = O.tensor_global(x.float().numpy())
+    _, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4, seed=seed,
+                                            given_globals=[gx, np.float32(gh)])
+    ids, wts, off, pairs, w_gpu = st
+    ag = torch.tensor([gx, np.float32(gh)], dtype=torch.float32, device=DEV)
+    native.set_ffn_separate_h_quant(True)
+    try:
+        ys, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                             act=native.W4A4, act_globals=ag,
+                                             out_dtype=torch.float32)
+    finally:
+        native.set_ffn_separate_h_quant(False)
+    # h decides integers (its bf16 rounding, then its NVFP4 codes and block
+    # scales), so the oracle forms it in fp32 as the kernels do; everything
+    # after h is fp64.  (Against an fp64 h, an h value within fp32 rounding
+    # of a bf16 tie can move one code, and with it the outputs of one token
+    # by up to about 1e-1 of the RMS: at T = 300, H = 128 with g_h = 0.5/2688
+    # one such value gives rel_frob 2.1e-3, the same in an fp32 emulation on
+    # the CPU as on the device.)
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True,
+                       act_globals=(gx, np.float32(gh)), h_fp32=True)
+    return y, ys, ref
+
+
+# g_h: 0.05/2688 saturates nearly every block scale at 448; 1.1484375/2688 is
+# this input's own h maximum over 2688 (a static scale calibrated on it);
+# 2/2688 leaves every block scale small
+@pytest.mark.parametrize("gh", [0.05 / 2688, 1.1484375 / 2688, 2.0 / 2688])
+def test_moe_ffn_w4a4_h_quantised_in_gate_up_epilogue_matches_separate_pass(gh):
+    """Given globals on the four-wave tiled path without a K split: the
+    gate/up epilogue quantises h (16-column blocks reduced across lanes).
+    Its output is bit-identical to quantising the same bf16 h in a pass of
+    its own, and matches the oracle element by element."""
+    T, H, I, E, k = 1024, 256, 2048, 16, 2
+    say("moe w4a4 fused h quant", T, H, I, E, k, gh)
+    y, ys, ref = _fused_vs_separate(T, H, I, E, k, gh, seed=3)
+    assert torch.equal(y, ys), "fused and separate h quantisation differ"
+    assert_close_f32(to_np(y), ref, "moe w4a4 fused h quant")
+
+
+# H = 128 is two 64-wide K chunks, which the tiled GEMM never splits, so these
+# run the one-wave tiles with the fused epilogue (ragged m-blocks included)
+@pytest.mark.parametrize("T,H,I,E,k", [(96, 128, 512, 4, 2), (300, 128, 256, 16, 2)])
+@pytest.mark.parametrize("gh", [0.5 / 2688, 2.0 / 2688])
+def test_moe_ffn_w4a4_fused_h_quant_one_wave_tiles(T, H, I, E, k, gh):
+    say("moe w4a4 fused h quant one-wave", T, H, I, E, k, gh)
+    y, ys, ref = _fused_vs_separate(T, H, I, E, k, gh, seed=5)
+    assert torch.equal(y, ys), "fused and separate h quantisation differ"
+    assert_close_f32(to_np(y), ref, "moe w4a4 fused h quant")
+
+
 def test_moe_w4a4_full_size_sampled_given_globals():
     wl = synth.MOE_PREFILL_W4A4
     say("moe w4a4 full size", wl)

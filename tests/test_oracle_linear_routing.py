@@ -199,3 +199,66 @@ def test_moe_w4a4_single_expert_composes_quantised_linears():
     y3, _ = O.moe_ffn(x, np.zeros((t, 1), np.int32), np.ones((t, 1)), w,
                       act_quant=True, act_globals=(gx, gh), tokens=[1, 4])
     assert np.array_equal(y3, y[[1, 4]])
+
+
+def _bf16_boundary_distance(v):
+    """Relative distance of each fp64 v from the nearest bf16 rounding
+    boundary (midpoint between neighbouring bf16 values)."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(np.where(v > 0, v, 1.0))
+    q = np.exp2(np.maximum(e, -125) - 8.0)          # bf16 spacing at v
+    frac = v / q - np.floor(v / q)                  # position between neighbours
+    return np.abs(frac - 0.5) * q / np.where(v > 0, v, 1.0)
+
+
+@pytest.mark.parametrize("act_quant", [False, True])
+def test_moe_fp32_h_differs_from_fp64_h_only_next_to_bf16_ties(act_quant):
+    """The fp32 h agrees with the fp64 h, which the tests above pin, except
+    where the fp64 value before its bf16 rounding lies within fp32 rounding
+    error of a rounding boundary; there the two are neighbouring bf16
+    values.  A swapped gate/up, a dropped global or a wrong operand would
+    change most elements."""
+    rng = np.random.default_rng(21)
+    t, h, i = 2000, 64, 256          # 512000 h values: a few sit next to a tie
+    w = _rand_experts(rng, 1, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    ids, wts = np.zeros((t, 1), np.int32), np.ones((t, 1))
+    _, i64 = O.moe_ffn(x, ids, wts, w, act_quant=act_quant)
+    _, i32 = O.moe_ffn(x, ids, wts, w, act_quant=act_quant, h_fp32=True)
+    h64, h32 = i64["h_bf16"][:, 0], i32["h_bf16"][:, 0]
+    # the fp64 value before rounding, from the pinned linear maps
+    gate, _ = O.linear(x, w.gate_codes[0], w.gate_scales[0], w.gate_global[0], act_quant=act_quant)
+    up, _ = O.linear(x, w.up_codes[0], w.up_scales[0], w.up_global[0], act_quant=act_quant)
+    pre = gate / (1 + np.exp(-gate)) * up
+    assert np.array_equal(O.bf16_rne(pre), h64)
+    diff = h32 != h64
+    assert 0 < diff.sum() <= 20
+    assert np.all(_bf16_boundary_distance(pre[diff]) < 2.0 ** -18)
+    ulp = np.exp2(np.frexp(np.maximum(np.abs(h32[diff]), np.abs(h64[diff])))[1] - 8.0)
+    assert np.all(np.abs(h32[diff] - h64[diff]) <= ulp)
+
+
+def test_moe_fp32_h_closed_forms():
+    """Single expert, one nonzero column: gate = 40 makes exp(-gate) vanish
+    next to 1 in fp32, so h = gate * up exactly; gate = -200 overflows exp
+    and gives h = 0; a zero gate gives h = 0."""
+    h, i = 16, 16
+    codes = np.zeros((i, h), np.uint8)
+    codes[:, 0] = 2                                  # e2m1 code 2 = 1.0
+    scales = np.full((i, 1), 0x38, np.uint8)         # e4m3 0x38 = 1.0
+    pk = O.pack_nibbles(codes)
+
+    def experts(g_gate, g_up):
+        return O.ExpertWeights(pk[None], scales[None], np.array([g_gate], np.float32),
+                               pk[None], scales[None], np.array([g_up], np.float32),
+                               pk[None].reshape(1, h, i // 2), scales[None].reshape(1, h, 1),
+                               np.array([1.0], np.float32))
+
+    x = np.zeros((3, h), np.float32)
+    x[:, 0] = [2.0, -10.0, 0.0]
+    ids, wts = np.zeros((3, 1), np.int32), np.ones((3, 1))
+    _, info = O.moe_ffn(x, ids, wts, experts(20.0, 1.5), h_fp32=True)
+    hb = info["h_bf16"][:, 0]
+    assert np.all(hb[0] == 2.0 * 20.0 * 2.0 * 1.5)   # gate 40, up 6 -> 240
+    assert np.all(hb[1] == 0.0)                        # gate -200, up -30
+    assert np.all(hb[2] == 0.0)
