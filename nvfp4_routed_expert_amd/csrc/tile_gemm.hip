@@ -81,15 +81,26 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// Lane n of each 16-lane DPP row, broadcast to the whole row.
+template <int N>
+__device__ __forceinline__ uint32_t row16_bcast(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + N, 0xF, 0xF, false);
+}
+
 // Gate/up epilogue with the h quantisation folded in (a given global g_h):
 // h = bf16(silu(G) * U) as in the plain epilogue, then NVFP4 blocks of 16
 // consecutive columns.  Column lr of a fragment sits in lane lr of the
 // 16-lane DPP row that holds the row, so each block's absolute maximum is a
-// row reduction; the block scale, the per-element code and the stored fp16
-// product follow the same fp32 steps as the quantisation kernel (one
-// correctly rounded operation each).  Blocks never straddle N (N % 16 == 0)
-// and the 16 lanes of a block share its row, so the reduction runs
-// unconditionally and only the stores are predicated.
+// row reduction.  A lane holds 8 elements (j, f) per 16-row subtile; in a
+// group of two subtiles (16 elements e), lane lr keeps the maximum of element
+// lr's block, works out that block's scale and reciprocal (one pair of
+// divisions per 16 elements), and each element takes them back by a row
+// broadcast.  The scale, the codes
+// and the stored fp16 products follow the quantisation kernel's fp32 steps
+// (one correctly rounded operation each), so the output is the same.
+// Blocks never straddle N (N % 16 == 0) and a block's 16 lanes share its
+// row, so everything runs unconditionally and only the stores are
+// predicated.
 template <int MS>
 __device__ __forceinline__ void store_h_quantised(const GemmArgs &p, const f32x4 (&acc)[MS][4],
                                                   int nrows, int pos0, int col0, float gg,
@@ -99,31 +110,60 @@ __device__ __forceinline__ void store_h_quantised(const GemmArgs &p, const f32x4
   const int N = p.N;
   const float g = *p.h_quant_g;
   const float six_g = 6.0f * g;
+  // groups of 16 elements: subtiles 2q and 2q + 1 (one pass each, so only 16
+  // h values are live at a time)
 #pragma unroll
-  for (int ms = 0; ms < MS; ++ms) {
+  for (int q = 0; q < (MS + 1) / 2; ++q) {
+    float x[16];
+    float bmax = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int e = 0; e < 16; ++e) {
+      const int ms = 2 * q + (e >> 3), j = (e >> 1) & 3, f = e & 1;
+      if (ms >= MS) break;
       const int r = ms * 16 + 4 * lg + j;
-      const int pos = pos0 + r;
-      const int sh = (p.a_shift && r < nrows) ? p.a_shift[arow_of(p, pos)] : 0;
-      _Float16 *hrow = static_cast<_Float16 *>(p.out) + (int64_t)pos * p.ldo;
+      const int sh = (p.a_shift && r < nrows) ? p.a_shift[arow_of(p, pos0 + r)] : 0;
+      const float G = __builtin_ldexpf(acc[ms][f][j], sh) * gg;
+      const float U = __builtin_ldexpf(acc[ms][f + 2][j], sh) * gu;
+      x[e] = bf16_bits_to_f32(f32_to_bf16_bits(G / (1.0f + expf(-G)) * U));
+      const float amax = row16_max(__builtin_fabsf(x[e]));
+      if (lr == e) bmax = amax;
+    }
+    // this lane's block: element lr of the group
+    const uint32_t sc = e4m3_rne_sat(bmax / six_g);
+    const float denom = e4m3_to_f32(sc) * g;
+    const uint32_t inv_bits = __float_as_uint(denom > 0.0f ? 1.0f / denom : 0.0f);
+    // row_shl:1 -> lane lr reads lane lr + 1: even lanes pair the scales of
+    // elements f = 0 and f = 1 of one row
+    const uint32_t next = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)sc, 0x101, 0xF, 0xF, false);
+    const uint32_t sc_pair = sc | (next << 8);
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        const int col = col0 + f * 16 + lr;
-        const float G = __builtin_ldexpf(acc[ms][f][j], sh) * gg;
-        const float U = __builtin_ldexpf(acc[ms][f + 2][j], sh) * gu;
-        const float x = bf16_bits_to_f32(f32_to_bf16_bits(G / (1.0f + expf(-G)) * U));
-        const float amax = row16_max(__builtin_fabsf(x));
-        const uint32_t sc = e4m3_rne_sat(amax / six_g);
-        const float sdec = e4m3_to_f32(sc);
-        const float denom = sdec * g;
-        uint32_t code = 0u;
-        if (denom > 0.0f)
-          code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x * (1.0f / denom), 0.0f, 1.0f, 0) & 15u;
-        f16x2 s0, s1;
-        e4m3x2_to_f16_pairs(sc, s0, s1);
-        const f16x2 v = e2m1x2_to_f16<0>(code) * s0;
-        if (r < nrows && col < N) hrow[col] = v[0];
+    for (int e = 0; e < 16; e += 2) {
+      const int ms = 2 * q + (e >> 3), j = (e >> 1) & 3;
+      if (ms >= MS) break;
+      const int r = ms * 16 + 4 * lg + j;
+      float inv0, inv1;
+      uint32_t scs;
+      // (constant lane indices: the loop is unrolled)
+      switch (e) {
+#define NVFP4_BC(L)                                             \
+  case L:                                                       \
+    inv0 = __uint_as_float(row16_bcast<L>(inv_bits));           \
+    inv1 = __uint_as_float(row16_bcast<L + 1>(inv_bits));       \
+    scs = row16_bcast<L>(sc_pair);                              \
+    break;
+        NVFP4_BC(0) NVFP4_BC(2) NVFP4_BC(4) NVFP4_BC(6)
+        NVFP4_BC(8) NVFP4_BC(10) NVFP4_BC(12) default: NVFP4_BC(14)
+#undef NVFP4_BC
+      }
+      uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[e] * inv0, x[e + 1] * inv1,
+                                                               1.0f, 0);
+      code &= (inv0 > 0.0f ? 0x0Fu : 0u) | (inv1 > 0.0f ? 0xF0u : 0u);   // zero scale: +0
+      const f16x2 v = e2m1x2_to_f16<0>(code) *
+                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scs, 1.0f, false);
+      if (r < nrows && col0 < N) {
+        _Float16 *hrow = static_cast<_Float16 *>(p.out) + (int64_t)(pos0 + r) * p.ldo;
+        hrow[col0 + lr] = v[0];
+        hrow[col0 + 16 + lr] = v[1];
       }
     }
   }
