@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--given-globals", action="store_true",
                     help="W4A4: static activation scales given by the caller (g_x from the "
                          "input's amax, g_h a fixed calibration value) instead of online ones")
+    ap.add_argument("--with-router", action="store_true",
+                    help="the step starts from x and the bf16 router matrix (router GEMM + "
+                         "top-k, moe_router_topk) instead of from given logits")
     ap.add_argument("--separate-h-quant", action="store_true",
                     help="with --given-globals: quantise h in its own pass instead of the "
                          "gate/up epilogue (same results)")
@@ -196,9 +199,18 @@ def main():
     native.set_ffn_separate_h_quant(args.separate_h_quant)
     rws = native.route_workspace(T, E, k, dev)
     route = E > 1
+    with_router = args.with_router and route
+    if with_router:
+        router_w = synth.router_matrix(E, H).to(dev)
+        router_b = (None if wl.zipf_s is None else
+                    torch.from_numpy(synth.zipf_bias(E, wl.zipf_s)).to(dev))
+        rtws = native.router_workspace(T, H, E, k, dev)
 
     def step(c):
-        if route:
+        if with_router:
+            native.moe_router_topk(x, router_w, k, True, bias=router_b,
+                                   out=(ids, wts, off, pairs), workspace=rtws)
+        elif route:
             native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
         native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
                                      act_globals=ag, out_dtype=torch.bfloat16,
@@ -214,8 +226,11 @@ def main():
     active = int((counts > 0).sum())
     w_bytes_active = 3 * active * (nv_bytes(H * I) + 4)
     io_bytes = T * H * 2 * 2 + (T * E * 4 if route else 0)
+    if with_router:   # the router matrix and a second read of x replace the logits
+        io_bytes += E * H * 2 + T * H * 2 - T * E * 4
+    alg_router_flops = 2 * T * H * E if with_router else 0
     alg_bytes = w_bytes_active + io_bytes
-    alg_flops = 6 * P * H * I
+    alg_flops = 6 * P * H * I + alg_router_flops
     gateup_bytes = 2 * active * (nv_bytes(H * I) + 4) + T * H * 2
     gateup_flops = 4 * P * H * I
     # MFMA-bound when the step's arithmetic intensity exceeds the ridge point
@@ -350,7 +365,11 @@ def main():
     # ---- CPU oracle on a bounded sample (rank 0, N = 1) --------------------------
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts, prefill_mfma)
+        router = None
+        if with_router:
+            router = (router_w.float().cpu().numpy(),
+                      None if router_b is None else router_b.cpu().numpy())
+        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts, prefill_mfma, router)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -359,6 +378,8 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "act": wl.act,
+                   "router": ("bf16 router GEMM + top-k" if with_router else
+                              "top-k of given logits" if route else None),
                    "act_globals": ("given (static)" if ag is not None else
                                    "online" if act == native.W4A4 else None),
                    "h_quant": ("separate pass" if args.separate_h_quant else "fused")
@@ -398,9 +419,11 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound):
+def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound, router=None):
     """Time the oracle (as it stands) on a bounded sample of the same step and
-    use it as the correctness gate for the GPU output rows it covers."""
+    use it as the correctness gate for the GPU output rows it covers.
+    router = (R, bias): the step starts from the router, whose logits the
+    oracle computes too (for the sampled tokens, inside the timed region)."""
     import numpy as np
     import threadpoolctl
 
@@ -412,10 +435,12 @@ def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound):
     n_tok = args.cpu_tokens or {"moe_decode": 16, "moe_prefill": 8,
                                 "moe_prefill_w4a4": 1}.get(wl.name, 1)
     tokens = list(range(0, T, max(1, T // n_tok)))[:n_tok]
+    xf = x_cpu.float().numpy()
+    if router is not None:
+        logits_np = O.router_logits(xf, *router)
     rids, rw = O.route_topk(logits_np, k)
     need = np.unique(rids[tokens])
     w_ref = LazyOracleExperts(E, H, I, need, 0)        # weight quantisation is offline
-    xf = x_cpu.float().numpy()
     a4 = wl.act == "w4a4"
     act_globals = None
     if a4:
@@ -425,11 +450,17 @@ def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound):
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
+    if router is not None:
+        sl = O.router_logits(xf[tokens], *router)
+        rids[tokens], rw[tokens] = O.route_topk(sl, k)
     ref, _ = O.moe_ffn(xf, rids, rw, w_ref, act_quant=a4, act_globals=act_globals,
                        tokens=tokens)
     dt = time.perf_counter() - t0
     sample_bytes = 3 * len(need) * (nv_bytes(H * I) + 4) + len(tokens) * H * 4
     sample_flops = 6 * len(tokens) * k * H * I
+    if router is not None:
+        sample_bytes += E * H * 2
+        sample_flops += 2 * len(tokens) * H * E
     res = {"kind": "oracle", "cores": int(threads),
            "sample": f"{len(tokens)} of {T} tokens ({len(need)} experts), "
                      f"fp64 numpy oracle, {dt:.2f} s",

@@ -164,6 +164,32 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E,
 size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k);
 
 /*
+ * moe_router_topk: the router in front of moe_route_topk.  Logits
+ *   l[t][e] = sum_h x[t][h] * R[e][h]  (+ router_bias[e])
+ * with x [T, H] bf16 and the router matrix R [E, H] bf16 (one row per
+ * expert, row-major).  The router stays BF16 next to the NVFP4 routed
+ * experts (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card, "What this model
+ * is") and is replicated on every device that holds experts (DwarfStar
+ * page, GPU pairs).  Every product is exact in fp32 and the sums are fp32,
+ * in an order fixed by the shapes (deterministic run to run, not bitwise
+ * equal to a sequential sum).  router_bias: f32 [E] or NULL.  On those fp32
+ * logits the call then computes exactly what moe_route_topk computes
+ * (top-k ids / weights, expert_offsets, sorted_pairs).  logits: f32 [T, E]
+ * receives the logits when non-NULL (NULL skips the write).
+ * Requires H % 32 == 0 and moe_route_topk's limits on T, E and k.
+ * workspace (moe_router_topk_workspace_size bytes, device, 16-byte aligned):
+ * holds the K-split partial sums; its first 32-bit word must be zero when
+ * the call runs and is left zero, as for moe_route_topk.
+ */
+nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *router_w,
+                             const float *router_bias, int32_t E, int32_t k,
+                             int renormalize, float *logits, int32_t *topk_ids,
+                             float *topk_weights, int32_t *expert_offsets,
+                             int32_t *sorted_pairs, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+size_t moe_router_topk_workspace_size(int64_t T, int64_t H, int32_t E, int32_t k);
+
+/*
  * moe_grouped_nvfp4_ffn: routed-expert gated FFN.  For each pair p = t*k + j
  * routed to expert e = topk_ids[p] (moe_route_topk's ids / weights / offsets /
  * sorted_pairs, which must be consistent with each other):

@@ -443,8 +443,66 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
   TRY(check_workspace(workspace, workspace_bytes, moe_route_topk_workspace_size(T, E, k)));
-  LAUNCH(launch_route(logits, T, E, k, renormalize, topk_ids, topk_weights, expert_offsets,
-                      sorted_pairs, static_cast<uint32_t *>(workspace), stream),
+  LAUNCH(launch_route(LogitSrc{logits, 0, 1, nullptr, nullptr}, T, E, k, renormalize, topk_ids,
+                      topk_weights, expert_offsets, sorted_pairs,
+                      static_cast<uint32_t *>(workspace), stream),
+         "route");
+  return NVFP4_OK;
+}
+
+// ---- moe_router_topk ------------------------------------------------------------------
+
+size_t moe_router_topk_workspace_size(int64_t T, int64_t H, int32_t E, int32_t k) {
+  (void)k;
+  if (T < 1 || H < 1 || E < 1) return 0;
+  Carver c(nullptr);
+  c.take<uint32_t>(64);   // word 0: the routing ticket
+  c.take<float>(router_plan(T, H, E).partial_floats);
+  return c.used;
+}
+
+nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *router_w,
+                             const float *router_bias, int32_t E, int32_t k, int renormalize,
+                             float *logits, int32_t *topk_ids, float *topk_weights,
+                             int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(x);
+  CHECK_NULL(router_w);
+  CHECK_NULL(topk_ids);
+  CHECK_NULL(topk_weights);
+  CHECK_NULL(expert_offsets);
+  CHECK_NULL(sorted_pairs);
+  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  TRY(check_k(H, "H"));
+  if (E < 1 || E > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
+  if (k < 1 || k > E || k > 32)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k = %d outside 1..min(E, 32)", (int)k);
+  if (T * (int64_t)k > ((int64_t)1 << 24))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*k = %lld exceeds 2^24", (long long)(T * k));
+  if (T * H > ((int64_t)1 << 40) || T * (int64_t)E > ((int64_t)1 << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*H or T*E too large");
+  CHECK_ALIGN(x);
+  CHECK_ALIGN(router_w);
+  if (router_bias) CHECK_ALIGN(router_bias);
+  if (logits) CHECK_ALIGN(logits);
+  CHECK_ALIGN(topk_ids);
+  CHECK_ALIGN(topk_weights);
+  CHECK_ALIGN(expert_offsets);
+  CHECK_ALIGN(sorted_pairs);
+  TRY(check_workspace(workspace, workspace_bytes, moe_router_topk_workspace_size(T, H, E, k)));
+  Carver c(workspace);
+  uint32_t *ticket = c.take<uint32_t>(64);
+  const RouterPlan plan = router_plan(T, H, E);
+  float *partial = c.take<float>(plan.partial_floats);
+  LAUNCH(launch_router_logits(static_cast<const uint16_t *>(x),
+                              static_cast<const uint16_t *>(router_w), T, H, E, plan, partial,
+                              stream),
+         "router logits");
+  LAUNCH(launch_route(LogitSrc{partial, T * (int64_t)E, plan.parts, router_bias, logits}, T, E,
+                      k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_pairs,
+                      ticket, stream),
          "route");
   return NVFP4_OK;
 }

@@ -65,16 +65,43 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols,
                            const float *amax_src, int n_amax, const float *g_given,
                            float *g_out, float *g_out2, hipStream_t s);
 
-// ---- routing (route.hip) -------------------------------------------------------
+// ---- routing (route.hip, router.hip) ---------------------------------------------
 
-// Top-k ids/weights and the expert-sorted permutation (one workgroup for
-// T <= 32 tokens, else a top-k grid followed by a one-workgroup permutation).
-// ticket: a zero uint32 in the caller's workspace (left zero on return); with
-// it, decode-sized batches (route_decode_supported) route in one launch.
+// The fp32 logits [T, E] the top-k reads: logit (t, e) is the sum over parts
+// s = 0 .. parts-1 (parts <= kMaxLogitParts), in that order, of
+// part[s * part_stride + t * E + e], plus bias[e] when bias is set; out (when
+// set) receives the logits.
+constexpr int kMaxLogitParts = 4;
+struct LogitSrc {
+  const float *part;
+  int64_t part_stride;
+  int parts;
+  const float *bias;
+  float *out;
+};
+
+// Top-k ids/weights and the expert-sorted permutation (a top-k grid, then the
+// permutation by one workgroup or by a grid split over experts).  ticket: a
+// zero uint32 in the caller's workspace (left zero on return); with it,
+// decode-sized batches (route_decode_supported) route in one launch.
 bool route_decode_supported(int64_t T, int E, int k);
-hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
+hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         uint32_t *ticket, hipStream_t s);
+
+// Router logits x [T, H] bf16 . R [E, H]^T bf16 as fp32 partial sums over
+// `parts` K ranges of kpart columns: partial[s][t][e] (partial_floats floats).
+// Tiles of 16 ms tokens x 16 nb experts per wavefront (ms = nb = 1 or 2).
+// Needs H % 32 == 0.
+struct RouterPlan {
+  int ms = 1, nb = 1;
+  int kpart = 64;
+  int parts = 1;
+  size_t partial_floats = 0;
+};
+RouterPlan router_plan(int64_t T, int64_t H, int64_t E);
+hipError_t launch_router_logits(const uint16_t *x, const uint16_t *R, int64_t T, int64_t H,
+                                int64_t E, const RouterPlan &p, float *partial, hipStream_t s);
 
 // ---- grouped GEMM and FFN glue (gemm.hip) ---------------------------------------
 

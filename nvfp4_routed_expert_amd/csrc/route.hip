@@ -17,6 +17,40 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxPerLane = kMaxExperts / kWave;  // 16 logits per lane
 constexpr int kTopkThreads = 256;
 
+// Token t's logits at experts lane + 64 i (i < N; 0 past E): the part sums
+// added in part order (at most kMaxLogitParts parts), then the bias; written
+// to src.out when that is set.  Every load is issued before the first add
+// and the stores come last, so a row costs one round trip.
+template <int N>
+__device__ __forceinline__ void load_logits(const LogitSrc &src, int64_t t, int E, int lane,
+                                            float (&v)[N]) {
+  const float *row = src.part + t * E;
+  float p[N][kMaxLogitParts], b[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int e = lane + 64 * i;
+    const bool ok = e < E;
+#pragma unroll
+    for (int s = 0; s < kMaxLogitParts; ++s)
+      p[i][s] = (ok && s < src.parts) ? row[s * src.part_stride + e] : 0.0f;
+    b[i] = (ok && src.bias) ? src.bias[e] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float x = p[i][0];
+#pragma unroll
+    for (int s = 1; s < kMaxLogitParts; ++s)
+      if (s < src.parts) x += p[i][s];
+    if (src.bias) x += b[i];
+    v[i] = x;
+  }
+  if (src.out) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (lane + 64 * i < E) src.out[t * E + lane + 64 * i] = v[i];
+  }
+}
+
 // a beats b: larger logit, or equal logit and lower index (branch-free)
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
   return (av > bv) | ((av == bv) & (ai < bi));
@@ -51,16 +85,12 @@ __device__ __forceinline__ void wave_best(float &v, int &i) {
 // Top-k of one token's logits by one wavefront.  Lane l holds logits
 // l, l+64, ...; k rounds of a wave-wide argmax pick the experts in
 // descending order.  Lane j < k writes the j-th id and weight.
-__device__ void wave_topk(const float *row, int E, int k, int renormalize, int32_t *ids,
-                          float *weights, int32_t *ids_copy) {
+__device__ void wave_topk(const LogitSrc &src, int64_t t, int E, int k, int renormalize,
+                          int32_t *ids, float *weights, int32_t *ids_copy) {
   const int lane = threadIdx.x & 63;
   float v[kMaxPerLane];
   const int per_lane = (E + 63) / 64;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + 64 * i;
-    v[i] = (i < per_lane && e < E) ? row[e] : 0.0f;
-  }
+  load_logits(src, t, E, lane, v);
   uint32_t taken = 0;
   float my_val = 0.0f;   // lane j < k keeps the j-th selected logit
   int my_idx = 0;
@@ -171,15 +201,15 @@ __device__ __forceinline__ void merge_level(uint64_t (&c)[8], int lane) {
       if ((i & d) == 0) cas(c[i], c[i + d]);
 }
 
-__device__ void wave_topk_merge(const float *row, int E, int k, int renormalize, int32_t *ids,
-                                float *weights, int32_t *ids_copy) {
+__device__ void wave_topk_merge(const LogitSrc &src, int64_t t, int E, int k, int renormalize,
+                                int32_t *ids, float *weights, int32_t *ids_copy) {
   const int lane = threadIdx.x & 63;
   float v[8];
   uint64_t c[8];
+  load_logits(src, t, E, lane, v);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? row[e] : 0.0f;
     c[i] = e < E ? topk_key(v[i], e) : 0ull;
   }
   constexpr int kNet[19][2] = {{0, 2}, {1, 3}, {4, 6}, {5, 7}, {0, 4}, {1, 5}, {2, 6},
@@ -221,20 +251,20 @@ __device__ void wave_topk_merge(const float *row, int E, int k, int renormalize,
 
 // One wavefront per token.
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
-    const float *logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
+    const LogitSrc logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
     float *weights) {
   const int64_t t = (int64_t)blockIdx.x * (kTopkThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
-  wave_topk_merge(logits + t * E, E, k, renormalize, ids + t * k, weights + t * k, nullptr);
+  wave_topk_merge(logits, t, E, k, renormalize, ids + t * k, weights + t * k, nullptr);
 }
 
 // One wavefront per token.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
-    const float *logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
+    const LogitSrc logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
     float *weights) {
   const int64_t t = (int64_t)blockIdx.x * (kTopkThreads / 64) + (threadIdx.x >> 6);
   if (t >= T) return;
-  wave_topk(logits + t * E, E, k, renormalize, ids + t * k, weights + t * k, nullptr);
+  wave_topk(logits, t, E, k, renormalize, ids + t * k, weights + t * k, nullptr);
 }
 
 // Single workgroup.  Pass 1 counts pairs per expert and writes the offsets.
@@ -642,7 +672,7 @@ __device__ __forceinline__ int wave_incl_min(int x) {
   return x;
 }
 
-__global__ __launch_bounds__(64) void route_decode_kernel(const float *logits, int64_t T, int E,
+__global__ __launch_bounds__(64) void route_decode_kernel(const LogitSrc logits, int64_t T, int E,
                                                           int k, int renormalize, int32_t *ids,
                                                           float *weights, int32_t *offsets,
                                                           int32_t *sorted_pairs,
@@ -651,8 +681,8 @@ __global__ __launch_bounds__(64) void route_decode_kernel(const float *logits, i
   __shared__ int32_t first[kMaxRouteExperts];
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
-  wave_topk_merge(logits + (int64_t)t * E, E, k, renormalize, ids + (int64_t)t * k,
-                  weights + (int64_t)t * k, nullptr);
+  wave_topk_merge(logits, t, E, k, renormalize, ids + (int64_t)t * k, weights + (int64_t)t * k,
+                  nullptr);
   uint32_t mine = 0;
   if (lane == 0)
     mine = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -741,7 +771,7 @@ bool route_decode_supported(int64_t T, int E, int k) {
   return T * k <= kSmallPairs && E <= 512 && k <= 8;
 }
 
-hipError_t launch_route(const float *logits, int64_t T, int E, int k, int renormalize,
+hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         uint32_t *ticket, hipStream_t s) {
   if (ticket && route_decode_supported(T, E, k)) {

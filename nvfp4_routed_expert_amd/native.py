@@ -66,6 +66,9 @@ def lib():
             "moe_route_topk": (_i32, [_vp, _i64, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
             "moe_route_topk_workspace_size": (_sz, [_i64, _i32, _i32]),
+            "moe_router_topk": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, ctypes.c_int, _vp,
+                                       _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+            "moe_router_topk_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
             "moe_grouped_nvfp4_ffn": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                                              _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
@@ -89,7 +92,8 @@ FFN_STAGES = ("plan", "x_prep", "gate_up", "h_prep", "down", "combine")
 def exported_symbols():
     return ["nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_dequantize",
             "nvfp4_linear", "nvfp4_linear_workspace_size", "moe_route_topk",
-            "moe_route_topk_workspace_size", "moe_grouped_nvfp4_ffn",
+            "moe_route_topk_workspace_size", "moe_router_topk", "moe_router_topk_workspace_size",
+            "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "nvfp4_set_ffn_stage_events",
             "nvfp4_set_ffn_separate_h_quant",
             "nvfp4_status_string", "nvfp4_last_error"]
@@ -216,6 +220,39 @@ def moe_route_topk(logits, k, renormalize=True, out=None, workspace=None):
     _check(L.moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
                             _ptr(off), _ptr(pairs), _ptr(ws), nbytes, _stream()))
     return ids, w, off, pairs
+
+
+def router_workspace(T, H, E, k, device):
+    """A zeroed workspace for moe_router_topk (left with its first word zero
+    by every call, as for the routing workspace)."""
+    return torch.zeros(max(lib().moe_router_topk_workspace_size(T, H, E, k), 1),
+                       dtype=torch.uint8, device=device)
+
+
+def moe_router_topk(x, router_w, k, renormalize=True, bias=None, want_logits=False, out=None,
+                    workspace=None):
+    """Router logits x [T,H] bf16 . router_w [E,H]^T bf16 (+ bias [E] f32), then
+    the same top-k and permutation as moe_route_topk.  Returns (topk_ids,
+    topk_weights, expert_offsets, sorted_pairs, logits or None)."""
+    T, H = x.shape
+    E = router_w.shape[0]
+    dev = x.device
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+    else:
+        ids, w, off, pairs = out
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
+    L = lib()
+    nbytes = L.moe_router_topk_workspace_size(T, H, E, k)
+    ws = _workspace(nbytes, dev, workspace) if workspace is not None else \
+        router_workspace(T, H, E, k, dev)
+    _check(L.moe_router_topk(_ptr(x), T, H, _ptr(router_w), _ptr(bias), E, k,
+                             int(bool(renormalize)), _ptr(logits), _ptr(ids), _ptr(w), _ptr(off),
+                             _ptr(pairs), _ptr(ws), nbytes, _stream()))
+    return ids, w, off, pairs, logits
 
 
 class ExpertWeights:

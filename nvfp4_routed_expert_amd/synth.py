@@ -5,13 +5,16 @@ arithmetic (no quantisation, routing or matmul), so the oracle and the HIP
 path can both be fed from it.  Every tensor comes from numpy's PCG64 seeded
 by SeedSequence([seed, tensor_id, expert]):
 
-    tensor_id 0 = activations x, 1 = router logits, 2 = gate, 3 = up, 4 = down.
+    tensor_id 0 = activations x, 1 = router logits, 2 = gate, 3 = up, 4 = down,
+    5 = router matrix.
 
 Activations are N(0, 1) rounded to bf16 (torch's round-to-nearest-even
 cast), weights N(0, 0.02^2) in fp32 (the caller quantises them), router
 logits N(0, 1) in fp32, optionally plus a Zipf-shaped per-expert bias
 b_e = -s ln(e + 1) (the log of an unnormalised Zipf(s) weight of rank e + 1),
-which leaves many experts without tokens.
+which leaves many experts without tokens.  The bf16 router matrix R [E, H]
+is N(0, 1/H) rounded to bf16, so that x . R^T is again about N(0, 1); the
+same Zipf bias can be passed to the router as its per-expert bias.
 """
 from __future__ import annotations
 
@@ -21,7 +24,7 @@ import dataclasses
 import numpy as np
 import torch
 
-X, LOGITS, GATE, UP, DOWN = 0, 1, 2, 3, 4
+X, LOGITS, GATE, UP, DOWN, ROUTER = 0, 1, 2, 3, 4, 5
 WEIGHT_STD = 0.02
 
 
@@ -45,9 +48,20 @@ def router_logits(T: int, E: int, seed: int = 0, zipf_s: float | None = None,
     else:
         noise = g.standard_normal((T, E), dtype=np.float32)
     if zipf_s is not None:
-        bias = (-zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
-        noise = (noise + bias[None, :]).astype(np.float32)
+        noise = (noise + zipf_bias(E, zipf_s)[None, :]).astype(np.float32)
     return noise
+
+
+def router_matrix(E: int, H: int, seed: int = 0) -> torch.Tensor:
+    """bf16 [E, H] ~ N(0, 1/H) on the CPU."""
+    r = rng(seed, ROUTER).standard_normal((E, H), dtype=np.float32)
+    r *= np.float32(1.0 / np.sqrt(H))
+    return torch.from_numpy(r).to(torch.bfloat16)
+
+
+def zipf_bias(E: int, zipf_s: float) -> np.ndarray:
+    """fp32 [E]: b_e = -s ln(e + 1)."""
+    return (-zipf_s * np.log(np.arange(1, E + 1, dtype=np.float64))).astype(np.float32)
 
 
 def weight(n: int, k: int, tensor_id: int, expert: int = 0, seed: int = 0) -> np.ndarray:

@@ -19,7 +19,8 @@ What it computes, in plain numpy (fp64 unless a step is defined in fp32):
   experts of the Flash-Next NVFP4 checkpoint are W4A4 (same model card,
   "What this model is"), the DFlash2 drafter is weight-only
   (Qwen3.8-27B-nvfp4full-dflash2-NInfer model card, "Limits").
-* Top-k routing over the experts, the expert-sorted pair permutation and the
+* The BF16 router's logits (a plain product), top-k routing over the
+  experts, the expert-sorted pair permutation and the
   gated (SiLU) expert FFN with a routing-weighted combine (Eider page,
   "Qwen3.8 Flash Next": all 512 MoE experts; "Performance": prefill batches
   up to 512 prompt tokens so routed expert weights are reused).
@@ -284,6 +285,19 @@ def silu(z):
 # ---------------------------------------------------------------------------
 # Routing
 # ---------------------------------------------------------------------------
+
+def router_logits(x, r, bias=None):
+    """Router logits l[t][e] = sum_h x[t][h] r[e][h] (+ bias[e]) in fp64.
+
+    x [T, H] and r [E, H] hold bf16 values (the router stays BF16 beside the
+    NVFP4 routed experts: Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card,
+    "What this model is"); bias is fp32 [E] or None.
+    """
+    lg = np.asarray(x, dtype=np.float64) @ np.asarray(r, dtype=np.float64).T
+    if bias is not None:
+        lg = lg + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    return lg
+
 
 def route_topk(logits, k, renormalize=True):
     """Top-k experts per token from fp32 logits [T, E].

@@ -155,6 +155,57 @@ def test_route_workspace_reused_across_calls():
 
 
 # ---------------------------------------------------------------------------
+# BF16 router + top-k
+# ---------------------------------------------------------------------------
+
+# tiles: T < 64 one 16x16 subtile per wavefront with K split into up to 32
+# parts; T < 256 32x32; larger 64x64 (K split into up to 8 parts)
+@pytest.mark.parametrize("T,H,E,k,zipf,renorm", [
+    (16, 2048, 512, 8, None, True),      # the decode workload's router
+    (37, 96, 20, 3, None, True),         # ragged tiles, H % 64 == 32
+    (1, 32, 1, 1, None, True),           # one token, one expert
+    (300, 256, 64, 6, 1.1, False),       # 32 x 32 tiles, bias, full softmax
+    (1024, 512, 128, 8, None, True),     # 64 x 64 tiles
+    (512, 2048, 512, 8, 1.1, True),      # the 512-token chunk's router (Zipf bias)
+    (40, 160, 1024, 32, None, True),     # the largest E and k
+])
+def test_router_topk_parity(T, H, E, k, zipf, renorm):
+    say("router", T, H, E, k, zipf, renorm)
+    x = synth.activations(T, H, seed=2)
+    R = synth.router_matrix(E, H, seed=2)
+    b = None if zipf is None else synth.zipf_bias(E, zipf)
+    bd = None if b is None else torch.from_numpy(b).to(DEV)
+    ids, w, off, pairs, lg = native.moe_router_topk(x.to(DEV), R.to(DEV), k, renorm, bias=bd,
+                                                    want_logits=True)
+    lg = to_np(lg)
+    xf, rf = x.float().numpy().astype(np.float64), R.float().numpy().astype(np.float64)
+    ref = O.router_logits(xf, rf, b)
+    # fp32 sums of exact products: |err| <= H u sum_h |x_h r_h| (u = 2^-24),
+    # plus one rounding of the bias add
+    bound = H * 2.0 ** -24 * (np.abs(xf) @ np.abs(rf).T) + 2.0 ** -24 * np.abs(ref)
+    assert np.all(np.abs(lg - ref) <= bound), float(np.max(np.abs(lg - ref) - bound))
+    # the routing decision, taken on the same fp32 logits: exact
+    rids, rw = O.route_topk(lg, k, renorm)
+    roff, rpairs = O.permute(rids, E)
+    assert np.array_equal(to_np(ids), rids)
+    assert np.array_equal(to_np(off), roff)
+    assert np.array_equal(to_np(pairs), rpairs)
+    np.testing.assert_allclose(to_np(w), rw, rtol=5e-6, atol=1e-7)
+    # and the fp64 oracle's own choice for every token whose top k + 1 fp64
+    # logits lie further apart than twice the token's largest logit error
+    # (then both orders agree)
+    ids64, _ = O.route_topk(ref, k, renorm)
+    srt = -np.sort(-ref, axis=1)[:, :min(k + 1, E)]
+    err = np.abs(lg - ref).max(axis=1, keepdims=True)
+    clear = np.all(np.diff(-srt, axis=1) > 2 * err, axis=1)
+    assert clear.mean() > 0.9
+    assert np.array_equal(to_np(ids)[clear], ids64[clear])
+    # no logits requested: same routing; a second call is bit-identical
+    ids2, w2, off2, pairs2, _ = native.moe_router_topk(x.to(DEV), R.to(DEV), k, renorm, bias=bd)
+    assert torch.equal(ids, ids2) and torch.equal(w, w2) and torch.equal(pairs, pairs2)
+
+
+# ---------------------------------------------------------------------------
 # dense NVFP4 linear
 # ---------------------------------------------------------------------------
 

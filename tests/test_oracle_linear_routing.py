@@ -262,3 +262,26 @@ def test_moe_fp32_h_closed_forms():
     assert np.all(hb[0] == 2.0 * 20.0 * 2.0 * 1.5)   # gate 40, up 6 -> 240
     assert np.all(hb[1] == 0.0)                        # gate -200, up -30
     assert np.all(hb[2] == 0.0)
+
+
+def test_router_logits_exact_on_small_rationals():
+    """Brute force with exact rationals: every product and the bias."""
+    from fractions import Fraction
+    x = np.array([[1.0, -2.0, 0.5, 0.25], [3.0, 0.0, -1.0, 2.0]], np.float32)
+    r = np.array([[0.5, 0.5, 1.0, -4.0], [2.0, -1.0, 0.0, 1.0], [0.0, 0.0, 0.0, 0.0]],
+                 np.float32)
+    bias = np.array([0.0, -1.5, 0.125], np.float32)
+    lg = O.router_logits(x, r, bias)
+    for t in range(2):
+        for e in range(3):
+            want = sum(Fraction(float(x[t, h])) * Fraction(float(r[e, h])) for h in range(4))
+            assert Fraction(lg[t, e]) == want + Fraction(float(bias[e]))
+    assert lg[1, 0] == 1.5 - 1.0 - 8.0
+    assert np.array_equal(O.router_logits(x, r), lg - bias[None, :])
+
+
+def test_router_logits_one_hot_rows_pick_router_columns():
+    rng = np.random.default_rng(9)
+    r = rng.standard_normal((5, 8)).astype(np.float32)
+    x = np.eye(8, dtype=np.float32)[[3, 0, 7]]
+    assert np.array_equal(O.router_logits(x, r), r.T[[3, 0, 7]].astype(np.float64))
