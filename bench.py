@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--with-router", action="store_true",
                     help="the step starts from x and the bf16 router matrix (router GEMM + "
                          "top-k, moe_router_topk) instead of from given logits")
+    ap.add_argument("--with-shared", action="store_true",
+                    help="add the BF16 shared expert (intermediate size = the routed one) "
+                         "to every token's output (moe_shared_expert_ffn, accumulating)")
     ap.add_argument("--separate-h-quant", action="store_true",
                     help="with --given-globals: quantise h in its own pass instead of the "
                          "gate/up epilogue (same results)")
@@ -206,6 +209,12 @@ def main():
                     torch.from_numpy(synth.zipf_bias(E, wl.zipf_s)).to(dev))
         rtws = native.router_workspace(T, H, E, k, dev)
 
+    with_shared = args.with_shared and route
+    if with_shared:
+        sh_w = [t.to(dev) for t in synth.shared_expert_weights(H, I)]
+        sh_ws = torch.empty(max(native.lib().moe_shared_expert_ffn_workspace_size(T, H, I), 1),
+                            dtype=torch.uint8, device=dev)
+
     def step(c):
         if with_router:
             native.moe_router_topk(x, router_w, k, True, bias=router_b,
@@ -215,6 +224,8 @@ def main():
         native.moe_grouped_nvfp4_ffn(x, wcopies[c], ids, wts, off, pairs, k, act=act,
                                      act_globals=ag, out_dtype=torch.bfloat16,
                                      workspace=ws, out=y)
+        if with_shared:
+            native.moe_shared_expert_ffn(x, *sh_w, y=y, accumulate=True, workspace=sh_ws)
 
     if not route:   # one expert: the routing is fixed (all rows to expert 0)
         native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
@@ -228,9 +239,12 @@ def main():
     io_bytes = T * H * 2 * 2 + (T * E * 4 if route else 0)
     if with_router:   # the router matrix and a second read of x replace the logits
         io_bytes += E * H * 2 + T * H * 2 - T * E * 4
-    alg_router_flops = 2 * T * H * E if with_router else 0
+    alg_extra_flops = 2 * T * H * E if with_router else 0
+    if with_shared:   # three bf16 [I, H] matrices, a read of x and a read-modify-write of y
+        io_bytes += 3 * H * I * 2 + T * H * 2 * 2
+        alg_extra_flops += 6 * T * H * I
     alg_bytes = w_bytes_active + io_bytes
-    alg_flops = 6 * P * H * I + alg_router_flops
+    alg_flops = 6 * P * H * I + alg_extra_flops
     gateup_bytes = 2 * active * (nv_bytes(H * I) + 4) + T * H * 2
     gateup_flops = 4 * P * H * I
     # MFMA-bound when the step's arithmetic intensity exceeds the ridge point
@@ -369,7 +383,10 @@ def main():
         if with_router:
             router = (router_w.float().cpu().numpy(),
                       None if router_b is None else router_b.cpu().numpy())
-        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts, prefill_mfma, router)
+        shared = None
+        if with_shared:
+            shared = [t.float().cpu().numpy() for t in sh_w]
+        cpu = cpu_baseline(args, wl, x_cpu, logits_np, y, counts, prefill_mfma, router, shared)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -378,6 +395,7 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "act": wl.act,
+                   "shared_expert": (f"bf16, intermediate {I}" if with_shared else None),
                    "router": ("bf16 router GEMM + top-k" if with_router else
                               "top-k of given logits" if route else None),
                    "act_globals": ("given (static)" if ag is not None else
@@ -419,11 +437,13 @@ def copy_calibration():
     torch.cuda.synchronize()
 
 
-def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound, router=None):
+def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound, router=None,
+                 shared=None):
     """Time the oracle (as it stands) on a bounded sample of the same step and
     use it as the correctness gate for the GPU output rows it covers.
     router = (R, bias): the step starts from the router, whose logits the
-    oracle computes too (for the sampled tokens, inside the timed region)."""
+    oracle computes too (for the sampled tokens, inside the timed region);
+    shared = (Wg, Wu, Wd): the BF16 shared expert is added as well."""
     import numpy as np
     import threadpoolctl
 
@@ -455,12 +475,17 @@ def cpu_baseline(args, wl, x_cpu, logits_np, y_gpu, counts, mfma_bound, router=N
         rids[tokens], rw[tokens] = O.route_topk(sl, k)
     ref, _ = O.moe_ffn(xf, rids, rw, w_ref, act_quant=a4, act_globals=act_globals,
                        tokens=tokens)
+    if shared is not None:
+        ref = O.shared_expert(xf[tokens], *shared, y_in=ref)
     dt = time.perf_counter() - t0
     sample_bytes = 3 * len(need) * (nv_bytes(H * I) + 4) + len(tokens) * H * 4
     sample_flops = 6 * len(tokens) * k * H * I
     if router is not None:
         sample_bytes += E * H * 2
         sample_flops += 2 * len(tokens) * H * E
+    if shared is not None:
+        sample_bytes += 3 * H * I * 2
+        sample_flops += 6 * len(tokens) * H * I
     res = {"kind": "oracle", "cores": int(threads),
            "sample": f"{len(tokens)} of {T} tokens ({len(need)} experts), "
                      f"fp64 numpy oracle, {dt:.2f} s",

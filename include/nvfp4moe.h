@@ -190,6 +190,28 @@ nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *ro
 size_t moe_router_topk_workspace_size(int64_t T, int64_t H, int32_t E, int32_t k);
 
 /*
+ * moe_shared_expert_ffn: the shared expert that runs beside the routed ones
+ * on every token; it stays BF16 (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model
+ * card, "What this model is") and is replicated on every device (DwarfStar
+ * page, GPU pairs).  For x [T, H] bf16 and bf16 weights w_gate, w_up
+ * [I, H] and w_down [H, I] (row-major):
+ *   h_t = bf16_rne( silu(x_t Wg^T) * (x_t Wu^T) )
+ *   y_t = h_t Wd^T                       (accumulate = 0)
+ *   y_t = y_t + h_t Wd^T                 (accumulate != 0: y is read first,
+ *                                         e.g. the routed output)
+ * Products are exact in fp32 and the sums fp32; the result is rounded once
+ * to y's type (bf16 round-to-nearest-even or f32).
+ * Requires H % 32 == 0, I % 32 == 0, T >= 1.  workspace:
+ * moe_shared_expert_ffn_workspace_size bytes (device, 16-byte aligned).
+ */
+nvfp4_status moe_shared_expert_ffn(const void *x, int64_t T, int64_t H, int64_t I,
+                                   const void *w_gate, const void *w_up,
+                                   const void *w_down, int accumulate, void *y,
+                                   nvfp4_dtype y_dtype, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I);
+
+/*
  * moe_grouped_nvfp4_ffn: routed-expert gated FFN.  For each pair p = t*k + j
  * routed to expert e = topk_ids[p] (moe_route_topk's ids / weights / offsets /
  * sorted_pairs, which must be consistent with each other):

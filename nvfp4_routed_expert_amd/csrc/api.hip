@@ -218,6 +218,22 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   return w;
 }
 
+struct SharedWs {
+  Bf16Plan up_plan, down_plan;
+  float *gu_part;
+  uint16_t *h;
+  float *y_part;
+};
+SharedWs carve_shared(Carver &c, int64_t T, int64_t H, int64_t I) {
+  SharedWs w;
+  w.up_plan = bf16_plan(T, H, 2 * I);
+  w.down_plan = bf16_plan(T, I, H);
+  w.gu_part = c.take<float>(w.up_plan.partial_floats);
+  w.h = c.take<uint16_t>((size_t)(T * I));
+  w.y_part = c.take<float>(w.down_plan.partial_floats);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -457,7 +473,7 @@ size_t moe_router_topk_workspace_size(int64_t T, int64_t H, int32_t E, int32_t k
   if (T < 1 || H < 1 || E < 1) return 0;
   Carver c(nullptr);
   c.take<uint32_t>(64);   // word 0: the routing ticket
-  c.take<float>(router_plan(T, H, E).partial_floats);
+  c.take<float>(bf16_plan(T, H, E).partial_floats);
   return c.used;
 }
 
@@ -494,16 +510,66 @@ nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *ro
   TRY(check_workspace(workspace, workspace_bytes, moe_router_topk_workspace_size(T, H, E, k)));
   Carver c(workspace);
   uint32_t *ticket = c.take<uint32_t>(64);
-  const RouterPlan plan = router_plan(T, H, E);
+  const Bf16Plan plan = bf16_plan(T, H, E);
   float *partial = c.take<float>(plan.partial_floats);
-  LAUNCH(launch_router_logits(static_cast<const uint16_t *>(x),
-                              static_cast<const uint16_t *>(router_w), T, H, E, plan, partial,
-                              stream),
+  LAUNCH(launch_bf16_partials(static_cast<const uint16_t *>(x),
+                              static_cast<const uint16_t *>(router_w), nullptr, E, T, H, E, plan,
+                              partial, stream),
          "router logits");
   LAUNCH(launch_route(LogitSrc{partial, T * (int64_t)E, plan.parts, router_bias, logits}, T, E,
                       k, renormalize, topk_ids, topk_weights, expert_offsets, sorted_pairs,
                       ticket, stream),
          "route");
+  return NVFP4_OK;
+}
+
+// ---- moe_shared_expert_ffn -------------------------------------------------------------
+
+size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I) {
+  if (T < 1 || H < 1 || I < 1) return 0;
+  Carver c(nullptr);
+  carve_shared(c, T, H, I);
+  return c.used;
+}
+
+nvfp4_status moe_shared_expert_ffn(const void *x, int64_t T, int64_t H, int64_t I,
+                                   const void *w_gate, const void *w_up, const void *w_down,
+                                   int accumulate, void *y, nvfp4_dtype y_dtype, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(x);
+  CHECK_NULL(w_gate);
+  CHECK_NULL(w_up);
+  CHECK_NULL(w_down);
+  CHECK_NULL(y);
+  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  TRY(check_k(H, "H"));
+  TRY(check_k(I, "I"));
+  if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "y_dtype must be bf16 or f32");
+  if (T * H > ((int64_t)1 << 40) || T * 2 * I > ((int64_t)1 << 40) ||
+      T > INT32_MAX / 2 || 2 * I > INT32_MAX / 2 || H > INT32_MAX / 2)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "shape too large");
+  CHECK_ALIGN(x);
+  CHECK_ALIGN(w_gate);
+  CHECK_ALIGN(w_up);
+  CHECK_ALIGN(w_down);
+  CHECK_ALIGN(y);
+  TRY(check_workspace(workspace, workspace_bytes, moe_shared_expert_ffn_workspace_size(T, H, I)));
+  Carver c(workspace);
+  const SharedWs ws = carve_shared(c, T, H, I);
+  const uint16_t *xb = static_cast<const uint16_t *>(x);
+  LAUNCH(launch_bf16_partials(xb, static_cast<const uint16_t *>(w_gate),
+                              static_cast<const uint16_t *>(w_up), I, T, H, 2 * I, ws.up_plan,
+                              ws.gu_part, stream),
+         "shared gate/up");
+  LAUNCH(launch_shared_h(ws.gu_part, ws.up_plan.parts, T, I, ws.h, stream), "shared h");
+  LAUNCH(launch_bf16_partials(ws.h, static_cast<const uint16_t *>(w_down), nullptr, H, T, I, H,
+                              ws.down_plan, ws.y_part, stream),
+         "shared down");
+  LAUNCH(launch_shared_out(ws.y_part, ws.down_plan.parts, T, H, accumulate != 0, y,
+                           y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16, stream),
+         "shared out");
   return NVFP4_OK;
 }
 

@@ -89,19 +89,30 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         uint32_t *ticket, hipStream_t s);
 
-// Router logits x [T, H] bf16 . R [E, H]^T bf16 as fp32 partial sums over
-// `parts` K ranges of kpart columns: partial[s][t][e] (partial_floats floats).
-// Tiles of 16 ms tokens x 16 nb experts per wavefront (ms = nb = 1 or 2).
+// x [T, H] bf16 . W^T as fp32 partial sums over `parts` K ranges of kpart
+// columns: partial[s][t][n] (partial_floats floats), W [N, H] bf16 row-major,
+// or (W1 set) rows n < N0 from W0 and rows n >= N0 from W1 (row n - N0).
+// Tiles of 16 ms tokens x 16 nb rows of W per wavefront (ms = nb = 1 or 2).
 // Needs H % 32 == 0.
-struct RouterPlan {
+struct Bf16Plan {
   int ms = 1, nb = 1;
   int kpart = 64;
   int parts = 1;
   size_t partial_floats = 0;
 };
-RouterPlan router_plan(int64_t T, int64_t H, int64_t E);
-hipError_t launch_router_logits(const uint16_t *x, const uint16_t *R, int64_t T, int64_t H,
-                                int64_t E, const RouterPlan &p, float *partial, hipStream_t s);
+Bf16Plan bf16_plan(int64_t T, int64_t H, int64_t N);
+hipError_t launch_bf16_partials(const uint16_t *x, const uint16_t *W0, const uint16_t *W1,
+                                int64_t N0, int64_t T, int64_t H, int64_t N, const Bf16Plan &p,
+                                float *partial, hipStream_t s);
+
+// Shared expert (shared.hip).  h[t][i] = bf16(silu(G) * U) with G and U the
+// part sums (in part order) of gp[s][t][i] and gp[s][t][I + i]; then
+// y[t][n] = (accumulate ? y[t][n] : 0) + (part sums of yp[s][t][n]), rounded
+// once to y's type.
+hipError_t launch_shared_h(const float *gp, int parts, int64_t T, int64_t I, uint16_t *h,
+                           hipStream_t s);
+hipError_t launch_shared_out(const float *yp, int parts, int64_t T, int64_t H, bool accumulate,
+                             void *y, OutType t, hipStream_t s);
 
 // ---- grouped GEMM and FFN glue (gemm.hip) ---------------------------------------
 

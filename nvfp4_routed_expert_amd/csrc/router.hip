@@ -1,8 +1,10 @@
-// Router logits: l[t][e] = x_t . R_e for bf16 x [T, H] and the bf16 router
-// matrix R [E, H] (one row per expert; the routers stay BF16 beside the
-// NVFP4 routed experts: Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card, "What
-// this model is"), as K-split fp32 partial sums that the top-k kernels add in
-// part order while they load the logits (route.hip, LogitSrc).
+// BF16 products x . W^T as K-split fp32 partial sums, for the parts of the
+// model that stay BF16 beside the NVFP4 routed experts (Qwen3.8-Flash-Next-
+// NVFP4-SSD-Stream model card, "What this model is"): the router (logits
+// l[t][e] = x_t . R_e, R [E, H]; the top-k kernels add the parts in part
+// order while they load the logits, route.hip LogitSrc) and the shared
+// expert (shared.hip).  W is one row-major [N, K] matrix, or two stacked
+// ones (rows n < N0 from the first, the rest from the second: gate over up).
 //
 // A wavefront computes a tile of 16 MS tokens x 16 NB experts over one K
 // part with v_mfma_f32_16x16x32_bf16 (MS = NB = 1 below 64 tokens, else 2),
@@ -37,9 +39,9 @@ __device__ __forceinline__ bf16x8 load8(const uint16_t *p, bool ok) {
 }
 
 template <int MS, int NB>
-__global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(
-    const uint16_t *x, const uint16_t *R, int T, int H, int E, int kpart, int n_tb, int n_eb,
-    int n_items, float *partial) {
+__global__ __launch_bounds__(64 * kRouterWaves) void bf16_partials_kernel(
+    const uint16_t *x, const uint16_t *W0, const uint16_t *W1, int N0, int T, int H, int E,
+    int kpart, int n_tb, int n_eb, int n_items, float *partial) {
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * kRouterWaves + (threadIdx.x >> 6);
   if (item >= n_items) return;
@@ -64,7 +66,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(
   for (int nb = 0; nb < NB; ++nb) {
     const int e = eb * 16 * NB + nb * 16 + lr;
     rok[nb] = e < E;
-    rb[nb] = R + (int64_t)(rok[nb] ? e : 0) * H + 8 * lg;
+    const int ec = rok[nb] ? e : 0;
+    rb[nb] = ec < N0 ? W0 + (int64_t)ec * H + 8 * lg : W1 + (int64_t)(ec - N0) * H + 8 * lg;
   }
   f32x4 acc[MS][NB];
 #pragma unroll
@@ -136,8 +139,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(
 
 }  // namespace
 
-RouterPlan router_plan(int64_t T, int64_t H, int64_t E) {
-  RouterPlan p;
+Bf16Plan bf16_plan(int64_t T, int64_t H, int64_t E) {
+  Bf16Plan p;
   p.ms = T >= 64 ? 2 : 1;
   p.nb = p.ms;
   const int64_t n_tb = (T + 16 * p.ms - 1) / (16 * p.ms);
@@ -154,9 +157,10 @@ RouterPlan router_plan(int64_t T, int64_t H, int64_t E) {
   return p;
 }
 
-hipError_t launch_router_logits(const uint16_t *x, const uint16_t *R, int64_t T, int64_t H,
-                                int64_t E, const RouterPlan &p, float *partial,
-                                hipStream_t s) {
+hipError_t launch_bf16_partials(const uint16_t *x, const uint16_t *W0, const uint16_t *W1,
+                                int64_t N0, int64_t T, int64_t H, int64_t E, const Bf16Plan &p,
+                                float *partial, hipStream_t s) {
+  if (!W1) N0 = E;
   if (H % 32 != 0 || p.kpart % 64 != 0) return hipErrorInvalidValue;
   const int n_tb = (int)((T + 16 * p.ms - 1) / (16 * p.ms));
   const int n_eb = (int)((E + 16 * p.nb - 1) / (16 * p.nb));
@@ -166,12 +170,12 @@ hipError_t launch_router_logits(const uint16_t *x, const uint16_t *R, int64_t T,
   const int a[] = {(int)T, (int)H, (int)E, p.kpart, n_tb, n_eb, (int)n_items};
   switch (p.ms) {
     case 1:
-      launch_kernel(router_logits_kernel<1, 1>, grid, block, 0, s, x, R, a[0], a[1], a[2], a[3],
-                    a[4], a[5], a[6], partial);
+      launch_kernel(bf16_partials_kernel<1, 1>, grid, block, 0, s, x, W0, W1, (int)N0, a[0], a[1],
+                    a[2], a[3], a[4], a[5], a[6], partial);
       break;
     default:
-      launch_kernel(router_logits_kernel<2, 2>, grid, block, 0, s, x, R, a[0], a[1], a[2], a[3],
-                    a[4], a[5], a[6], partial);
+      launch_kernel(bf16_partials_kernel<2, 2>, grid, block, 0, s, x, W0, W1, (int)N0, a[0], a[1],
+                    a[2], a[3], a[4], a[5], a[6], partial);
       break;
   }
   return hipGetLastError();

@@ -69,6 +69,9 @@ def lib():
             "moe_router_topk": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, ctypes.c_int, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_router_topk_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
+            "moe_shared_expert_ffn": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_int,
+                                             _vp, _i32, _vp, _sz, _vp]),
+            "moe_shared_expert_ffn_workspace_size": (_sz, [_i64, _i64, _i64]),
             "moe_grouped_nvfp4_ffn": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                                              _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
@@ -93,6 +96,7 @@ def exported_symbols():
     return ["nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_dequantize",
             "nvfp4_linear", "nvfp4_linear_workspace_size", "moe_route_topk",
             "moe_route_topk_workspace_size", "moe_router_topk", "moe_router_topk_workspace_size",
+            "moe_shared_expert_ffn", "moe_shared_expert_ffn_workspace_size",
             "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "nvfp4_set_ffn_stage_events",
             "nvfp4_set_ffn_separate_h_quant",
@@ -253,6 +257,26 @@ def moe_router_topk(x, router_w, k, renormalize=True, bias=None, want_logits=Fal
                              int(bool(renormalize)), _ptr(logits), _ptr(ids), _ptr(w), _ptr(off),
                              _ptr(pairs), _ptr(ws), nbytes, _stream()))
     return ids, w, off, pairs, logits
+
+
+def moe_shared_expert_ffn(x, w_gate, w_up, w_down, y=None, accumulate=False,
+                          out_dtype=torch.bfloat16, workspace=None):
+    """BF16 shared expert: y (+)= down(silu(x Wg^T) * (x Wu^T)).  x [T,H] bf16,
+    w_gate / w_up [I,H] bf16, w_down [H,I] bf16.  y: the output (read first
+    when accumulate), else a new tensor of out_dtype.  Returns y."""
+    T, H = x.shape
+    I = w_gate.shape[0]
+    dev = x.device
+    if y is None:
+        if accumulate:
+            raise ValueError("accumulate needs y")
+        y = torch.empty((T, H), dtype=out_dtype, device=dev)
+    L = lib()
+    ws = _workspace(L.moe_shared_expert_ffn_workspace_size(T, H, I), dev, workspace)
+    _check(L.moe_shared_expert_ffn(_ptr(x), T, H, I, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                   int(bool(accumulate)), _ptr(y), _dt(y.dtype), _ptr(ws),
+                                   ws.numel(), _stream()))
+    return y
 
 
 class ExpertWeights:

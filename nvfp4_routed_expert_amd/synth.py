@@ -6,7 +6,7 @@ path can both be fed from it.  Every tensor comes from numpy's PCG64 seeded
 by SeedSequence([seed, tensor_id, expert]):
 
     tensor_id 0 = activations x, 1 = router logits, 2 = gate, 3 = up, 4 = down,
-    5 = router matrix.
+    5 = router matrix, 6/7/8 = shared expert gate/up/down.
 
 Activations are N(0, 1) rounded to bf16 (torch's round-to-nearest-even
 cast), weights N(0, 0.02^2) in fp32 (the caller quantises them), router
@@ -14,7 +14,8 @@ logits N(0, 1) in fp32, optionally plus a Zipf-shaped per-expert bias
 b_e = -s ln(e + 1) (the log of an unnormalised Zipf(s) weight of rank e + 1),
 which leaves many experts without tokens.  The bf16 router matrix R [E, H]
 is N(0, 1/H) rounded to bf16, so that x . R^T is again about N(0, 1); the
-same Zipf bias can be passed to the router as its per-expert bias.
+same Zipf bias can be passed to the router as its per-expert bias.  The
+shared expert's bf16 weights are N(0, 0.02^2) like the routed ones.
 """
 from __future__ import annotations
 
@@ -25,6 +26,7 @@ import numpy as np
 import torch
 
 X, LOGITS, GATE, UP, DOWN, ROUTER = 0, 1, 2, 3, 4, 5
+SHARED_GATE, SHARED_UP, SHARED_DOWN = 6, 7, 8
 WEIGHT_STD = 0.02
 
 
@@ -57,6 +59,12 @@ def router_matrix(E: int, H: int, seed: int = 0) -> torch.Tensor:
     r = rng(seed, ROUTER).standard_normal((E, H), dtype=np.float32)
     r *= np.float32(1.0 / np.sqrt(H))
     return torch.from_numpy(r).to(torch.bfloat16)
+
+
+def shared_expert_weights(H: int, I: int, seed: int = 0):
+    """bf16 (gate [I, H], up [I, H], down [H, I]) ~ N(0, 0.02^2) on the CPU."""
+    return tuple(torch.from_numpy(weight(n, k, tid, 0, seed)).to(torch.bfloat16)
+                 for n, k, tid in ((I, H, SHARED_GATE), (I, H, SHARED_UP), (H, I, SHARED_DOWN)))
 
 
 def zipf_bias(E: int, zipf_s: float) -> np.ndarray:

@@ -20,8 +20,8 @@ What it computes, in plain numpy (fp64 unless a step is defined in fp32):
   "What this model is"), the DFlash2 drafter is weight-only
   (Qwen3.8-27B-nvfp4full-dflash2-NInfer model card, "Limits").
 * The BF16 router's logits (a plain product), top-k routing over the
-  experts, the expert-sorted pair permutation and the
-  gated (SiLU) expert FFN with a routing-weighted combine (Eider page,
+  experts, the expert-sorted pair permutation, the gated (SiLU) expert FFN
+  with a routing-weighted combine and the BF16 shared expert (Eider page,
   "Qwen3.8 Flash Next": all 512 MoE experts; "Performance": prefill batches
   up to 512 prompt tokens so routed expert weights are reused).
 
@@ -480,6 +480,20 @@ def moe_ffn(x, ids, weights, w, act_quant=False, act_globals=None,
         np.add.at(y, rows, contrib * weights[tokens[rows], slots][:, None])
     info["h"] = h
     return y, info
+
+
+def shared_expert(x, w_gate, w_up, w_down, y_in=None):
+    """The BF16 shared expert (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card,
+    "What this model is": shared experts stay BF16), fp64:
+    h = bf16_rne(silu(x Wg^T) * (x Wu^T)), y = h Wd^T, plus y_in when given.
+    x [T, H], w_gate / w_up [I, H], w_down [H, I] hold bf16 values.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    gate = x64 @ np.asarray(w_gate, dtype=np.float64).T
+    up = x64 @ np.asarray(w_up, dtype=np.float64).T
+    h = bf16_rne(silu(gate) * up)
+    y = h @ np.asarray(w_down, dtype=np.float64).T
+    return y if y_in is None else np.asarray(y_in, dtype=np.float64) + y
 
 
 def dense_mlp(x, gate, up, down):

@@ -206,6 +206,44 @@ def test_router_topk_parity(T, H, E, k, zipf, renorm):
 
 
 # ---------------------------------------------------------------------------
+# BF16 shared expert
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,I", [
+    (16, 2048, 512),      # beside the decode workload (one-subtile tiles, K split)
+    (37, 96, 160),        # ragged tiles, H and I % 64 == 32
+    (1, 32, 32),          # one token, one K step
+    (300, 256, 512),      # 32 x 32 tiles
+    (512, 2048, 512),     # beside the 512-token chunk
+])
+def test_shared_expert_parity(T, H, I):
+    say("shared expert", T, H, I)
+    x = synth.activations(T, H, seed=4)
+    wg, wu, wd = synth.shared_expert_weights(H, I, seed=4)
+    dx, dg, du, dd = (t.to(DEV) for t in (x, wg, wu, wd))
+    y32 = native.moe_shared_expert_ffn(dx, dg, du, dd, out_dtype=torch.float32)
+    ref = O.shared_expert(x.float().numpy(), wg.float().numpy(), wu.float().numpy(),
+                          wd.float().numpy())
+    assert_close_f32(to_np(y32), ref, "shared expert")
+    # bf16 output: the same sums, rounded once
+    yb = native.moe_shared_expert_ffn(dx, dg, du, dd, out_dtype=torch.bfloat16)
+    assert_bf16_output(bf16_np(yb), to_np(y32), ref, "shared expert bf16")
+    # accumulate into a given output (the routed result): fl32(y_in + s), then
+    # one rounding to y's type
+    y_in = torch.from_numpy(np.random.default_rng(T).standard_normal((T, H)).astype(np.float32))
+    ya = y_in.to(DEV).clone()
+    native.moe_shared_expert_ffn(dx, dg, du, dd, y=ya, accumulate=True)
+    assert np.array_equal(to_np(ya), (y_in.numpy() + to_np(y32)).astype(np.float32))
+    yab = y_in.to(torch.bfloat16).to(DEV)
+    want = O.bf16_rne((bf16_np(yab).astype(np.float32) + to_np(y32).astype(np.float32))
+                      .astype(np.float32))
+    native.moe_shared_expert_ffn(dx, dg, du, dd, y=yab, accumulate=True)
+    assert np.array_equal(bf16_np(yab), want)
+    # deterministic
+    assert torch.equal(native.moe_shared_expert_ffn(dx, dg, du, dd, out_dtype=torch.float32), y32)
+
+
+# ---------------------------------------------------------------------------
 # dense NVFP4 linear
 # ---------------------------------------------------------------------------
 

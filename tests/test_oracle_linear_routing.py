@@ -285,3 +285,36 @@ def test_router_logits_one_hot_rows_pick_router_columns():
     r = rng.standard_normal((5, 8)).astype(np.float32)
     x = np.eye(8, dtype=np.float32)[[3, 0, 7]]
     assert np.array_equal(O.router_logits(x, r), r.T[[3, 0, 7]].astype(np.float64))
+
+
+def test_shared_expert_is_the_one_expert_ffn_on_exact_weights():
+    """With bf16 weights that are exact NVFP4 values (the dequantised
+    matrices of a one-expert FFN), the shared expert equals the routed FFN
+    with that single expert and weight 1, which the tests above pin."""
+    rng = np.random.default_rng(12)
+    t, h, i = 7, 64, 96
+    w = _rand_experts(rng, 1, h, i)
+    x = O.bf16_rne(rng.standard_normal((t, h))).astype(np.float32)
+    wg = O.dequantize(w.gate_codes[0], w.gate_scales[0], w.gate_global[0])
+    wu = O.dequantize(w.up_codes[0], w.up_scales[0], w.up_global[0])
+    wd = O.dequantize(w.down_codes[0], w.down_scales[0], w.down_global[0])
+    y_moe, _ = O.moe_ffn(x, np.zeros((t, 1), np.int32), np.ones((t, 1)), w)
+    y = O.shared_expert(x, wg, wu, wd)
+    assert np.allclose(y, y_moe, rtol=1e-12, atol=1e-15)
+    # accumulate adds the given output
+    y_in = rng.standard_normal((t, h))
+    assert np.array_equal(O.shared_expert(x, wg, wu, wd, y_in), y_in + y)
+
+
+def test_shared_expert_closed_form():
+    """Gate row = 10 e_0 (silu is then 10 up to 5e-4), up row = e_1, down = I:
+    h = bf16(silu(10 x_0) x_1), y = h."""
+    x = np.array([[1.0, 3.0, 0.0, 0.0], [-1.0, 2.0, 0.0, 0.0]], np.float32)
+    wg = np.zeros((4, 4)); wg[:, 0] = 10.0
+    wu = np.zeros((4, 4)); wu[:, 1] = 1.0
+    wd = np.eye(4)
+    y = O.shared_expert(x, wg, wu, wd)
+    s0 = 10.0 / (1 + np.exp(-10.0))
+    s1 = -10.0 / (1 + np.exp(10.0))
+    assert np.all(y[0] == O.bf16_rne(s0 * 3.0))
+    assert np.all(y[1] == O.bf16_rne(s1 * 2.0))
