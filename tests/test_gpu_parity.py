@@ -365,6 +365,65 @@ def test_moe_ffn_w4a16_tiles(T, H, I, E, k, zipf):
     assert torch.equal(y, y2)
 
 
+# W4A16 grouped-GEMM batches with skewed and flat routing: experts with a few
+# rows beside experts with several m-blocks, every expert with a few rows,
+# every expert with many
+@pytest.mark.parametrize("T,H,I,E,k,zipf", [(400, 256, 256, 64, 4, 1.1),
+                                            (512, 512, 512, 128, 8, 1.1),   # the chunk's shape, smaller
+                                            (300, 256, 512, 256, 1, None),
+                                            (700, 1024, 256, 8, 2, None)])
+def test_moe_ffn_w4a16_skewed_batches(T, H, I, E, k, zipf):
+    say("moe w4a16 skewed", T, H, I, E, k, zipf)
+    x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k, zipf=zipf)
+    counts = np.bincount(rids.ravel(), minlength=E)
+    say("experts with 1..8 rows", int(((counts > 0) & (counts <= 8)).sum()),
+        "with more", int((counts > 8).sum()))
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref)
+    assert_close_f32(to_np(y), ref, "moe skewed")
+    ids, wts, off, pairs, w_gpu = st
+    y2, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                         out_dtype=torch.float32)
+    assert torch.equal(y, y2)
+
+
+def test_moe_ffn_in_a_graph():
+    """The grouped-GEMM FFN captured into a graph: every replay (with eager
+    calls between them) equals the eager result bit for bit."""
+    T, H, I, E, k = 400, 256, 256, 64, 4
+    say("moe ffn graph", T, H, I, E, k)
+    x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k, zipf=1.1)
+    ids, wts, off, pairs, w_gpu = st
+    xd = x.to(DEV)
+    ws = torch.empty(native.ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, H), dtype=torch.float32, device=DEV)
+
+    def call():
+        native.moe_grouped_nvfp4_ffn(xd, w_gpu, ids, wts, off, pairs, k, out_dtype=torch.float32,
+                                     workspace=ws, out=out)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert torch.equal(eager, y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        y2, _ = native.moe_grouped_nvfp4_ffn(xd, w_gpu, ids, wts, off, pairs, k,
+                                             out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, eager)
+
+
 @pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (64, 512, 256, 16, 4),
                                        (96, 256, 128, 8, 4)])
 def test_moe_ffn_w4a4_small(T, H, I, E, k):
