@@ -25,7 +25,8 @@ def declared_functions():
 
 def test_header_declares_the_four_calls():
     names = declared_functions()
-    for call in ("nvfp4_quantize", "nvfp4_linear", "moe_route_topk", "moe_grouped_nvfp4_ffn"):
+    for call in ("nvfp4_quantize", "nvfp4_linear", "moe_route_topk", "moe_grouped_nvfp4_ffn",
+                 "moe_router_topk", "moe_shared_expert_ffn"):
         assert call in names
 
 
@@ -127,6 +128,51 @@ def test_ffn_validation():
     # a W4A4 call with given globals needs them
     assert L.moe_grouped_nvfp4_ffn(FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, FAKE, ctypes.byref(w), 1,
                                    1, None, FAKE, 0, FAKE, ws, None) == 1
+
+
+def test_router_validation():
+    L = native.lib()
+    T, H, E, k = 16, 256, 64, 8
+    ws = L.moe_router_topk_workspace_size(T, H, E, k)
+    assert ws > 0
+    r = lambda T=T, H=H, E=E, k=k, x=FAKE, rw=FAKE, bias=None, lg=None, ids=FAKE, wsb=ws: \
+        L.moe_router_topk(x, T, H, rw, bias, E, k, 1, lg, ids, FAKE, FAKE, FAKE, FAKE, wsb, None)
+    assert r(H=100) == 2 and "H" in _last()
+    assert r(E=0) == 2
+    assert r(E=2048) == 2
+    assert r(k=0) == 2
+    assert r(k=65) == 2
+    assert r(T=0) == 1
+    assert r(x=None) == 1 and "x" in _last()
+    assert r(rw=None) == 1 and "router_w" in _last()
+    assert r(ids=None) == 1
+    assert r(x=FAKE_MIS) == 3
+    assert r(rw=FAKE_MIS) == 3
+    assert r(bias=FAKE_MIS) == 3 and "router_bias" in _last()
+    assert r(lg=FAKE_MIS) == 3 and "logits" in _last()
+    assert r(wsb=ws - 1) == 4
+    # the workspace grows with the partial sums of the K split
+    assert L.moe_router_topk_workspace_size(16, 2048, 512, 8) > ws
+
+
+def test_shared_expert_validation():
+    L = native.lib()
+    T, H, I = 16, 256, 128
+    ws = L.moe_shared_expert_ffn_workspace_size(T, H, I)
+    assert ws > 0
+    f = lambda T=T, H=H, I=I, x=FAKE, wg=FAKE, wu=FAKE, wd=FAKE, y=FAKE, dt=0, wsb=ws: \
+        L.moe_shared_expert_ffn(x, T, H, I, wg, wu, wd, 0, y, dt, FAKE, wsb, None)
+    assert f(H=100) == 2
+    assert f(I=48) == 2
+    assert f(T=0) == 1
+    assert f(wg=None) == 1 and "w_gate" in _last()
+    assert f(wd=None) == 1 and "w_down" in _last()
+    assert f(y=None) == 1
+    assert f(dt=7) == 1 and "y_dtype" in _last()
+    assert f(wu=FAKE_MIS) == 3
+    assert f(y=FAKE_MIS) == 3
+    assert f(wsb=ws - 1) == 4
+    assert L.moe_shared_expert_ffn_workspace_size(0, H, I) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
