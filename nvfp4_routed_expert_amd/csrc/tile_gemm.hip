@@ -48,7 +48,6 @@ constexpr int kARow = kChunk * 2;      // bytes of one fp16 activation row per c
 constexpr int kBRow = kChunk / 2;      // code bytes of one weight row per chunk
 constexpr int kXcds = 8;
 constexpr int kFillGroups = 512;       // four-wave workgroups that keep every CU busy (2 per CU)
-constexpr int kSkinnyGroups = 2048;    // one-wave workgroups for the same (2 per SIMD)
 
 template <int MS, int NW>
 struct TileCfg {
@@ -524,18 +523,23 @@ TilePlan tile_gemm_plan(Epi epi, int64_t N, int64_t K, int64_t n_mblocks_bound, 
                                           : cols_per_wave<Epi::LINEAR>();
   const int64_t items4 = n_mblocks_bound * ((N + 4 * cols - 1) / (4 * cols));
   if (items4 >= kFillGroups) return t;                      // four-wave tiles fill the GPU
-  // one-wave tiles: a wave keeps only two chunks of its 64 rows in flight, so
-  // streaming needs several per SIMD (kSkinnyGroups), by splitting K if needed
-  t.waves = 1;
-  const int64_t items1 = n_mblocks_bound * ((N + cols - 1) / cols);
-  if (items1 >= kSkinnyGroups) return t;
   const int64_t nch = K / kChunk;
-  int64_t ks = (kSkinnyGroups + items1 - 1) / items1;
-  if (ks > nch / 2) ks = nch / 2;                           // parts of at least two chunks
-  if (ks < 2) return t;
-  const int64_t cps = (nch + ks - 1) / ks;
-  t.ksplit = (int)((nch + cps - 1) / cps);                  // every part non-empty
-  t.partial_floats = (size_t)t.ksplit * rows * (epi == Epi::SWIGLU ? 2 * N : N);
+  {
+    // too few tiles to fill the GPU: four-wave tiles (each activation stage
+    // shared by 256 weight rows) with K split until they fill it; measured
+    // faster than one-wave tiles at every dense MLP size (M = 8 to 2048)
+    int64_t ks = (kFillGroups + items4 - 1) / items4;
+    if (ks > nch / 2) ks = nch / 2;
+    if (ks >= 2) {
+      const int64_t cps = (nch + ks - 1) / ks;
+      t.ksplit = (int)((nch + cps - 1) / cps);
+      t.partial_floats = (size_t)t.ksplit * rows * (epi == Epi::SWIGLU ? 2 * N : N);
+      return t;
+    }
+  }
+  // K too short to split (under four chunks): one-wave tiles, four times as
+  // many items
+  t.waves = 1;
   return t;
 }
 
