@@ -8,8 +8,8 @@
 // activations.
 //
 // A work item is (m-block of up to BM = 16*MS expert-sorted rows, tile of
-// 64 NW weight rows, K range).  The NW waves (4, or 1 for skinny problems
-// that would otherwise leave CUs idle) of a workgroup split the weight rows
+// 64 NW weight rows, K range).  The NW waves (4, or 1 when the tiles are too
+// few to fill the GPU and K too short to split) of a workgroup split the weight rows
 // (64 each; for the gate/up pair 32 gate and the same 32 up rows) and share
 // the activation rows.  Both operands pass through a three-stage LDS ring of
 // 64-wide K chunks, filled by direct global-to-LDS loads (no registers), so
@@ -29,10 +29,10 @@
 // (round robin over 8), so the item space is cut into 8 contiguous ranges
 // and XCD x walks range x; the weight tiles of one m-block then run next to
 // each other on one XCD and share its L2 copy of the activation rows.
-// Split K: when even one-wave tiles are too few to fill the GPU (a dense
-// decode-sized down projection has 80 of them), each tile's K range is cut
-// into KS parts; the parts write raw fp32 sums to a workspace and a reduce
-// kernel adds them in part order and applies the epilogue, so results stay
+// Split K: when the four-wave tiles are too few to fill the GPU (a dense
+// MLP's down projection has 20 per m-block), each tile's K range is cut into
+// KS parts; the parts write raw fp32 sums to a workspace and a reduce kernel
+// adds them in part order and applies the epilogue, so results stay
 // deterministic.
 #include <type_traits>
 
