@@ -190,6 +190,82 @@ nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *ro
 size_t moe_router_topk_workspace_size(int64_t T, int64_t H, int32_t E, int32_t k);
 
 /*
+ * Expert paging.  The pages keep selected experts resident and page the
+ * others in from slower memory when the GPU cannot hold them all (Eider page,
+ * "Why Eider exists": bounded page pools, selected experts resident, the rest
+ * paged from disk; Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card, 24-32 GB
+ * GPUs: expert blocks prefetched while the GPU computes).  Here every
+ * expert's NVFP4 weights live in host memory allocated pinned
+ * (hipHostMalloc), laid out as nvfp4_expert_weights with E experts, and a
+ * device pool of S slots (the same layout with S experts) holds the resident
+ * ones.  Per step:
+ *   moe_expert_cache_plan   ids of the step -> slot ids, and the experts to
+ *                           fetch with their slots (on the device, no host
+ *                           round trip);
+ *   moe_expert_cache_fetch  copies those experts from host memory into their
+ *                           slots (a kernel reading the pinned pages);
+ *   moe_permute_pairs       the expert-sorted pair order of the slot ids;
+ *   moe_grouped_nvfp4_ffn   on the pool (E = S) with the slot ids.
+ * The FFN's result is bit-identical to the one over all E experts in device
+ * memory.  State (caller-owned device arrays, set by moe_expert_cache_init):
+ * slot_of [E] int32 (slot of each expert, -1 = not resident), expert_of [S]
+ * int32 (-1 = empty), last_use [S] uint32 (step stamp), hand [1] int32.
+ */
+nvfp4_status moe_expert_cache_init(int32_t *slot_of, int32_t E, int32_t *expert_of,
+                                   uint32_t *last_use, int32_t *hand, int32_t S,
+                                   hipStream_t stream);
+
+/*
+ * moe_expert_cache_plan: for topk_ids [T, k] (experts of the step),
+ * step = the step's stamp (>= 1, increasing): every needed resident expert is
+ * kept and stamped; every needed missing expert gets a slot that holds no
+ * expert needed now and whose stamp is below protect_from (a step whose FFN
+ * may still be running keeps its experts: pass its stamp; else pass step),
+ * taken in slot order from the clock hand on (empty slots count as free).
+ * Writes slot_ids [T, k] (slot of each pair's expert), fetch [2 S] int32
+ * (pairs {expert, slot} of the experts to copy), in ascending expert order, and
+ * *n_fetch (device int32) = their number.  S must exceed the distinct experts
+ * of a step (twice over while a previous step's FFN may still run); when the
+ * free slots do not suffice, nothing moves, *n_fetch = -1, and the missing
+ * experts' pairs (like ids outside 0..E-1) get slot 0, so a following FFN
+ * reads valid memory but its result is wrong: check *n_fetch.  Requires
+ * 1 <= E, S <= 1024, T, k >= 1, 1 <= step, protect_from <= step.  One
+ * workgroup; integer-exact.
+ */
+nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k,
+                                   int32_t E, int32_t S, int32_t *slot_of,
+                                   int32_t *expert_of, uint32_t *last_use,
+                                   int32_t *hand, uint32_t step, uint32_t protect_from,
+                                   int32_t *slot_ids, int32_t *fetch, int32_t *n_fetch,
+                                   hipStream_t stream);
+
+/*
+ * moe_expert_cache_fetch: copies the first *n_fetch experts of fetch (from
+ * moe_expert_cache_plan; at most max_fetch) from host_w (E experts, pinned
+ * host memory) into their slots of pool (S experts, device memory, written
+ * by this call): codes, scales and globals of gate, up and down.  H, I as
+ * in moe_grouped_nvfp4_ffn.  Every host_w array must be pinned host memory
+ * mapped for the current device (hipHostMalloc); any other pointer is
+ * rejected with NVFP4_ERR_INVALID_ARGUMENT before a launch.  The copy runs
+ * on stream like a kernel (no host synchronisation); host_w must not change
+ * until it has run.
+ */
+nvfp4_status moe_expert_cache_fetch(const nvfp4_expert_weights *host_w,
+                                    const nvfp4_expert_weights *pool, int64_t H,
+                                    int64_t I, const int32_t *fetch,
+                                    const int32_t *n_fetch, int32_t max_fetch,
+                                    hipStream_t stream);
+
+/*
+ * moe_permute_pairs: moe_route_topk's expert offsets [E+1] and sorted pairs
+ * [T*k] for given ids [T, k] (stable: pairs of one expert in ascending
+ * order).  Same limits as moe_route_topk.
+ */
+nvfp4_status moe_permute_pairs(const int32_t *topk_ids, int64_t T, int32_t E, int32_t k,
+                               int32_t *expert_offsets, int32_t *sorted_pairs,
+                               hipStream_t stream);
+
+/*
  * moe_shared_expert_ffn: the shared expert that runs beside the routed ones
  * on every token; it stays BF16 (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model
  * card, "What this model is") and is replicated on every device (DwarfStar

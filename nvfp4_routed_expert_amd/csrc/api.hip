@@ -523,6 +523,117 @@ nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *ro
   return NVFP4_OK;
 }
 
+// ---- expert paging ---------------------------------------------------------------------
+
+nvfp4_status moe_expert_cache_init(int32_t *slot_of, int32_t E, int32_t *expert_of,
+                                   uint32_t *last_use, int32_t *hand, int32_t S,
+                                   hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(slot_of);
+  CHECK_NULL(expert_of);
+  CHECK_NULL(last_use);
+  CHECK_NULL(hand);
+  if (E < 1 || E > 1024 || S < 1 || S > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d, S = %d outside 1..1024", (int)E, (int)S);
+  LAUNCH(launch_cache_init(slot_of, E, expert_of, last_use, hand, S, stream), "cache init");
+  return NVFP4_OK;
+}
+
+nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                                   int32_t S, int32_t *slot_of, int32_t *expert_of,
+                                   uint32_t *last_use, int32_t *hand, uint32_t step,
+                                   uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
+                                   int32_t *n_fetch, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(topk_ids);
+  CHECK_NULL(slot_of);
+  CHECK_NULL(expert_of);
+  CHECK_NULL(last_use);
+  CHECK_NULL(hand);
+  CHECK_NULL(slot_ids);
+  CHECK_NULL(fetch);
+  CHECK_NULL(n_fetch);
+  if (E < 1 || E > 1024 || S < 1 || S > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d, S = %d outside 1..1024", (int)E, (int)S);
+  if (T < 1 || k < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T and k must be >= 1");
+  if (step < 1 || protect_from > step)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "need 1 <= step and protect_from <= step");
+  const int64_t P = T * (int64_t)k;
+  if (P > (int64_t)1 << 24) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*k too large");
+  LAUNCH(launch_cache_plan(topk_ids, (int)P, E, S, slot_of, expert_of, last_use, hand, step,
+                           protect_from, slot_ids, fetch, n_fetch, stream),
+         "cache plan");
+  return NVFP4_OK;
+}
+
+namespace {
+nvfp4_status expert_ptrs(const nvfp4_expert_weights *w, ExpertPtrs &p, const char *what) {
+  if (!w) return fail(NVFP4_ERR_INVALID_ARGUMENT, "%s is NULL", what);
+  const void *q[9] = {w->gate_codes,  w->up_codes,  w->down_codes,  w->gate_scales, w->up_scales,
+                      w->down_scales, w->gate_global, w->up_global, w->down_global};
+  for (int j = 0; j < 9; ++j) {
+    if (!q[j]) return fail(NVFP4_ERR_INVALID_ARGUMENT, "%s has a NULL array", what);
+    if (j < 6 && !aligned16(q[j]))
+      return fail(NVFP4_ERR_MISALIGNED, "%s: codes and scales must be 16-byte aligned", what);
+    if (j >= 6 && (reinterpret_cast<uintptr_t>(q[j]) & 3u))
+      return fail(NVFP4_ERR_MISALIGNED, "%s: globals must be 4-byte aligned", what);
+    p.p[j] = static_cast<const uint8_t *>(q[j]);
+  }
+  return NVFP4_OK;
+}
+}  // namespace
+
+nvfp4_status moe_expert_cache_fetch(const nvfp4_expert_weights *host_w,
+                                    const nvfp4_expert_weights *pool, int64_t H, int64_t I,
+                                    const int32_t *fetch, const int32_t *n_fetch,
+                                    int32_t max_fetch, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(fetch);
+  CHECK_NULL(n_fetch);
+  TRY(check_k(H, "H"));
+  TRY(check_k(I, "I"));
+  if (max_fetch < 0 || max_fetch > 1024)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "max_fetch = %d outside 0..1024", (int)max_fetch);
+  ExpertPtrs hp, pp;
+  TRY(expert_ptrs(host_w, hp, "host_w"));
+  TRY(expert_ptrs(pool, pp, "pool"));
+  // the kernel reads the host pages through their device mapping: each array
+  // must be pinned host memory that the current device can address
+  for (int j = 0; j < 9; ++j) {
+    hipPointerAttribute_t at;
+    const hipError_t e = hipPointerGetAttributes(&at, hp.p[j]);
+    if (e != hipSuccess || at.type != hipMemoryTypeHost || !at.devicePointer) {
+      (void)hipGetLastError();
+      return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                  "host_w array %d is not pinned host memory mapped for the device", j);
+    }
+    hp.p[j] = static_cast<const uint8_t *>(at.devicePointer);
+  }
+  LAUNCH(launch_cache_fetch(hp, pp, H, I, fetch, n_fetch, max_fetch, stream), "cache fetch");
+  return NVFP4_OK;
+}
+
+nvfp4_status moe_permute_pairs(const int32_t *topk_ids, int64_t T, int32_t E, int32_t k,
+                               int32_t *expert_offsets, int32_t *sorted_pairs,
+                               hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(topk_ids);
+  CHECK_NULL(expert_offsets);
+  CHECK_NULL(sorted_pairs);
+  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (E < 1 || E > 1024)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
+  if (k < 1 || k > 32)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k = %d outside 1..32", (int)k);
+  if (T * (int64_t)k > ((int64_t)1 << 24))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*k = %lld exceeds 2^24", (long long)(T * k));
+  CHECK_ALIGN(topk_ids);
+  CHECK_ALIGN(expert_offsets);
+  CHECK_ALIGN(sorted_pairs);
+  LAUNCH(launch_permute(topk_ids, T, E, k, expert_offsets, sorted_pairs, stream), "permute");
+  return NVFP4_OK;
+}
+
 // ---- moe_shared_expert_ffn -------------------------------------------------------------
 
 size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I) {

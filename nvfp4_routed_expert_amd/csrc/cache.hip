@@ -1,0 +1,202 @@
+// Expert paging: a device pool of S expert slots in front of all E experts'
+// NVFP4 weights in pinned host memory (selected experts resident, the rest
+// paged in: Eider page, "Why Eider exists").  The plan runs on the device so
+// a step never waits for the host: one workgroup marks the experts the step
+// needs, keeps the resident ones, gives each missing one a free slot (in slot
+// order from a clock hand; a slot is free when it is empty, or holds an expert
+// the step does not need whose stamp is older than the step still in flight)
+// and remaps the routing ids to slots.  The fetch kernel then reads the
+// missing experts' pages straight from host memory into their slots.
+#include "common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kPlanThreads = 1024;   // one thread per expert and per slot (E, S <= 1024)
+
+// Exclusive prefix sum of one flag per thread over the workgroup (1024
+// threads); also returns the total.
+__device__ int block_exclusive_scan(int v, int &total) {
+  __shared__ int wave_sum[kPlanThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) wave_sum[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  total = 0;
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    if (w < wave) base += wave_sum[w];
+    total += wave_sum[w];
+  }
+  __syncthreads();
+  return base + incl - v;
+}
+
+__global__ __launch_bounds__(256) void cache_init_kernel(int32_t *slot_of, int E,
+                                                          int32_t *expert_of, uint32_t *last_use,
+                                                          int32_t *hand, int S) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < E) slot_of[i] = -1;
+  if (i < S) {
+    expert_of[i] = -1;
+    last_use[i] = 0u;
+  }
+  if (i == 0) *hand = 0;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
+    const int32_t *ids, int P, int E, int S, int32_t *slot_of, int32_t *expert_of,
+    uint32_t *last_use, int32_t *hand, uint32_t step, uint32_t protect_from, int32_t *slot_ids,
+    int32_t *fetch, int32_t *n_fetch) {
+  __shared__ uint8_t need[kPlanThreads];
+  __shared__ int32_t miss_list[kPlanThreads];
+  __shared__ int32_t victim_list[kPlanThreads];
+  const int tid = threadIdx.x;
+  need[tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kPlanThreads) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) need[e] = 1;   // (ids outside 0..E-1 are ignored)
+  }
+  __syncthreads();
+
+  // needed experts: the resident ones are stamped, the missing ones listed in
+  // ascending expert order (state entries out of range count as empty, so a
+  // damaged state never leads outside the arrays)
+  int is_miss = 0;
+  if (tid < E && need[tid]) {
+    const int s = slot_of[tid];
+    if ((unsigned)s < (unsigned)S)
+      last_use[s] = step;
+    else
+      is_miss = 1;
+  }
+  int n_miss;
+  const int mrank = block_exclusive_scan(is_miss, n_miss);
+  if (is_miss) miss_list[mrank] = tid;
+
+  // free slots, in slot order starting at the hand (rotated index r)
+  int h = *hand;
+  if ((unsigned)h >= (unsigned)S) h = 0;
+  int is_free = 0, slot = -1;
+  if (tid < S) {
+    slot = h + tid < S ? h + tid : h + tid - S;
+    const int e = expert_of[slot];
+    is_free = (unsigned)e >= (unsigned)E || (!need[e] && last_use[slot] < protect_from);
+  }
+  int n_free;
+  const int frank = block_exclusive_scan(is_free, n_free);
+  if (is_free) victim_list[frank] = slot;
+  __syncthreads();
+
+  // not enough free slots: nothing moves, *n_fetch = -1, and the missing
+  // experts' pairs go to slot 0 (valid memory, wrong values)
+  const bool fits = n_miss <= n_free;
+  // missing expert i takes free slot i
+  if (fits && tid < n_miss) {
+    const int e = miss_list[tid], s = victim_list[tid];
+    const int old = expert_of[s];
+    if ((unsigned)old < (unsigned)E) slot_of[old] = -1;
+    slot_of[e] = s;
+    expert_of[s] = e;
+    last_use[s] = step;
+    fetch[2 * tid] = e;
+    fetch[2 * tid + 1] = s;
+  }
+  if (tid == 0) {
+    *n_fetch = fits ? n_miss : -1;
+    if (fits && n_miss > 0) {
+      const int last = victim_list[n_miss - 1];
+      *hand = last + 1 < S ? last + 1 : 0;
+    }
+  }
+  __syncthreads();   // (the slot map writes above are visible to the workgroup)
+  for (int p = tid; p < P; p += kPlanThreads) {
+    const int e = ids[p];
+    const int s = (unsigned)e < (unsigned)E ? slot_of[e] : -1;
+    slot_ids[p] = (unsigned)s < (unsigned)S ? s : 0;   // (ids outside 0..E-1, or a failed plan: slot 0)
+  }
+}
+
+// One expert's bytes as segments: gate, up, down codes; gate, up, down
+// scales; the three globals.  Grid: x = 16-byte piece within a segment,
+// y = segment, z = fetch index.
+struct Seg {
+  const uint8_t *src;
+  uint8_t *dst;
+  int64_t estride_src, estride_dst, bytes;
+};
+struct FetchArgs {
+  Seg seg[9];
+};
+
+__global__ __launch_bounds__(256) void cache_fetch_kernel(const FetchArgs a, const int32_t *fetch,
+                                                           const int32_t *n_fetch) {
+  const int i = blockIdx.z;
+  if (i >= *n_fetch) return;
+  const int e = fetch[2 * i], s = fetch[2 * i + 1];
+  const Seg sg = a.seg[blockIdx.y];
+  const uint8_t *src = sg.src + (int64_t)e * sg.estride_src;
+  uint8_t *dst = sg.dst + (int64_t)s * sg.estride_dst;
+  if (sg.bytes < 16) {   // a 4-byte global
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+      *reinterpret_cast<float *>(dst) = *reinterpret_cast<const float *>(src);
+    return;
+  }
+  const int64_t n16 = sg.bytes / 16;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n16;
+       q += (int64_t)gridDim.x * 256)
+    reinterpret_cast<u32x4 *>(dst)[q] = reinterpret_cast<const u32x4 *>(src)[q];
+}
+
+}  // namespace
+
+hipError_t launch_cache_init(int32_t *slot_of, int E, int32_t *expert_of, uint32_t *last_use,
+                             int32_t *hand, int S, hipStream_t s) {
+  const int n = E > S ? E : S;
+  launch_kernel(cache_init_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, slot_of, E,
+                expert_of, last_use, hand, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_plan(const int32_t *ids, int P, int E, int S, int32_t *slot_of,
+                             int32_t *expert_of, uint32_t *last_use, int32_t *hand, uint32_t step,
+                             uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
+                             int32_t *n_fetch, hipStream_t s) {
+  if (E > kPlanThreads || S > kPlanThreads) return hipErrorInvalidValue;
+  launch_kernel(cache_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, ids, P, E, S, slot_of,
+                expert_of, last_use, hand, step, protect_from, slot_ids, fetch, n_fetch);
+  return hipGetLastError();
+}
+
+hipError_t launch_cache_fetch(const ExpertPtrs &host, const ExpertPtrs &pool, int64_t H,
+                              int64_t I, const int32_t *fetch, const int32_t *n_fetch,
+                              int max_fetch, hipStream_t s) {
+  if (max_fetch <= 0) return hipSuccess;
+  const int64_t gu_codes = I * (H / 2), gu_scales = I * (H / 16);
+  const int64_t d_codes = H * (I / 2), d_scales = H * (I / 16);
+  FetchArgs a;
+  const int64_t bytes[9] = {gu_codes, gu_codes, d_codes, gu_scales, gu_scales, d_scales, 4, 4, 4};
+  for (int j = 0; j < 9; ++j) {
+    a.seg[j].src = host.p[j];
+    a.seg[j].dst = const_cast<uint8_t *>(pool.p[j]);
+    a.seg[j].estride_src = a.seg[j].estride_dst = bytes[j];
+    a.seg[j].bytes = bytes[j];
+    if (bytes[j] >= 16 && bytes[j] % 16 != 0) return hipErrorInvalidValue;
+  }
+  // pieces per segment: the largest segment in 16-byte pieces, at most 64 workgroups of 256
+  int64_t gx = (gu_codes / 16 + 255) / 256;
+  if (gx > 64) gx = 64;
+  if (gx < 1) gx = 1;
+  launch_kernel(cache_fetch_kernel, dim3((unsigned)gx, 9, (unsigned)max_fetch), dim3(256), 0, s, a,
+                fetch, n_fetch);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

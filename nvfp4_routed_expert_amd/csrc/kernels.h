@@ -114,6 +114,28 @@ hipError_t launch_shared_h(const float *gp, int parts, int64_t T, int64_t I, uin
 hipError_t launch_shared_out(const float *yp, int parts, int64_t T, int64_t H, bool accumulate,
                              void *y, OutType t, hipStream_t s);
 
+// Permutation only (the second half of launch_route): expert offsets and the
+// expert-sorted pairs of given ids.
+hipError_t launch_permute(const int32_t *ids, int64_t T, int E, int k, int32_t *offsets,
+                          int32_t *sorted_pairs, hipStream_t s);
+
+// ---- expert paging (cache.hip) ----------------------------------------------------
+
+// An expert set's nine arrays in nvfp4_expert_weights order: gate, up, down
+// codes; gate, up, down scales; gate, up, down globals.
+struct ExpertPtrs {
+  const uint8_t *p[9];
+};
+hipError_t launch_cache_init(int32_t *slot_of, int E, int32_t *expert_of, uint32_t *last_use,
+                             int32_t *hand, int S, hipStream_t s);
+hipError_t launch_cache_plan(const int32_t *ids, int P, int E, int S, int32_t *slot_of,
+                             int32_t *expert_of, uint32_t *last_use, int32_t *hand, uint32_t step,
+                             uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
+                             int32_t *n_fetch, hipStream_t s);
+hipError_t launch_cache_fetch(const ExpertPtrs &host, const ExpertPtrs &pool, int64_t H,
+                              int64_t I, const int32_t *fetch, const int32_t *n_fetch,
+                              int max_fetch, hipStream_t s);
+
 // ---- grouped GEMM and FFN glue (gemm.hip) ---------------------------------------
 
 enum class Epi : int { LINEAR = 0, SWIGLU = 1, DOWN = 2 };

@@ -781,7 +781,6 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
   }
   // top-k: one wavefront per token, four per workgroup, so a decode batch
   // spreads over several CUs (one wave per SIMD) instead of sharing one
-  const int W = permute_words(T, E);
   const int64_t blocks = (T + 3) / 4;
   if (E <= 512 && k <= 8)
     launch_kernel(topk_merge_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
@@ -791,6 +790,12 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
                   renormalize, ids, weights);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_permute(ids, T, E, k, offsets, sorted_pairs, s);
+}
+
+hipError_t launch_permute(const int32_t *ids, int64_t T, int E, int k, int32_t *offsets,
+                          int32_t *sorted_pairs, hipStream_t s) {
+  const int W = permute_words(T, E);
   // permutation: one workgroup for a decode-sized batch, else spread over
   // workgroups by expert while each one's bitmaps fit in LDS
   if (T * k <= kSmallPairs) {

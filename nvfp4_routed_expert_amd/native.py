@@ -72,6 +72,14 @@ def lib():
             "moe_shared_expert_ffn": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, ctypes.c_int,
                                              _vp, _i32, _vp, _sz, _vp]),
             "moe_shared_expert_ffn_workspace_size": (_sz, [_i64, _i64, _i64]),
+            "moe_expert_cache_init": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
+            "moe_expert_cache_plan": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                             ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp,
+                                             _vp]),
+            "moe_expert_cache_fetch": (_i32, [ctypes.POINTER(ExpertWeightsC),
+                                              ctypes.POINTER(ExpertWeightsC), _i64, _i64, _vp,
+                                              _vp, _i32, _vp]),
+            "moe_permute_pairs": (_i32, [_vp, _i64, _i32, _i32, _vp, _vp, _vp]),
             "moe_grouped_nvfp4_ffn": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp, _vp,
                                              _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
@@ -97,6 +105,8 @@ def exported_symbols():
             "nvfp4_linear", "nvfp4_linear_workspace_size", "moe_route_topk",
             "moe_route_topk_workspace_size", "moe_router_topk", "moe_router_topk_workspace_size",
             "moe_shared_expert_ffn", "moe_shared_expert_ffn_workspace_size",
+            "moe_expert_cache_init", "moe_expert_cache_plan", "moe_expert_cache_fetch",
+            "moe_permute_pairs",
             "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "nvfp4_set_ffn_stage_events",
             "nvfp4_set_ffn_separate_h_quant",
@@ -305,6 +315,72 @@ class ExpertWeights:
             self.gate_codes, self.up_codes, self.down_codes, self.gate_scales,
             self.up_scales, self.down_scales, self.gate_global, self.up_global,
             self.down_global)))
+
+
+def moe_permute_pairs(topk_ids, num_experts, out=None):
+    """Expert offsets [E+1] and expert-sorted pairs [T*k] of given ids [T, k]."""
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if out is None:
+        off = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+        pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+    else:
+        off, pairs = out
+    _check(lib().moe_permute_pairs(_ptr(topk_ids), T, num_experts, k, _ptr(off), _ptr(pairs),
+                                   _stream()))
+    return off, pairs
+
+
+class ExpertCache:
+    """Expert paging: host_weights (an ExpertWeights of E experts whose tensors
+    are in pinned host memory) behind a device pool of `slots` experts.
+    plan_and_fetch(ids) maps a step's expert ids to slots and copies the
+    missing experts into the pool (on the current stream, no host round
+    trip); the FFN then runs on `pool` with the slot ids and slots experts."""
+
+    def __init__(self, host_weights, slots, device):
+        self.host = host_weights
+        self.E, self.S = host_weights.num_experts, slots
+        self.H, self.I = host_weights.hidden, host_weights.intermediate
+        ts = (host_weights.gate_codes, host_weights.gate_scales, host_weights.gate_global,
+              host_weights.up_codes, host_weights.up_scales, host_weights.up_global,
+              host_weights.down_codes, host_weights.down_scales, host_weights.down_global)
+        for t in ts:
+            if not t.is_pinned():
+                raise ValueError("host expert weights must be in pinned host memory")
+        self.pool = ExpertWeights(*[torch.empty((slots,) + tuple(t.shape[1:]), dtype=t.dtype,
+                                                device=device) for t in ts])
+        i32 = dict(dtype=torch.int32, device=device)
+        self.slot_of = torch.empty(self.E, **i32)
+        self.expert_of = torch.empty(slots, **i32)
+        self.last_use = torch.empty(slots, **i32)      # uint32 stamps
+        self.hand = torch.empty(1, **i32)
+        self.fetch = torch.empty(2 * slots, **i32)
+        self.n_fetch = torch.zeros(1, **i32)
+        self.step_no = 0
+        self._host_c, self._pool_c = host_weights.c_struct(), self.pool.c_struct()
+        _check(lib().moe_expert_cache_init(_ptr(self.slot_of), self.E, _ptr(self.expert_of),
+                                           _ptr(self.last_use), _ptr(self.hand), slots,
+                                           _stream()))
+
+    def plan_and_fetch(self, topk_ids, protect_previous=False, slot_ids=None):
+        """Slot ids [T, k] for this step's expert ids; the missing experts are
+        copied into the pool.  protect_previous: keep the previous step's
+        experts (its FFN may still be running)."""
+        T, k = topk_ids.shape
+        self.step_no += 1
+        protect = self.step_no - 1 if protect_previous and self.step_no > 1 else self.step_no
+        if slot_ids is None:
+            slot_ids = torch.empty_like(topk_ids)
+        L = lib()
+        _check(L.moe_expert_cache_plan(_ptr(topk_ids), T, k, self.E, self.S, _ptr(self.slot_of),
+                                       _ptr(self.expert_of), _ptr(self.last_use), _ptr(self.hand),
+                                       self.step_no, protect, _ptr(slot_ids), _ptr(self.fetch),
+                                       _ptr(self.n_fetch), _stream()))
+        _check(L.moe_expert_cache_fetch(ctypes.byref(self._host_c), ctypes.byref(self._pool_c),
+                                        self.H, self.I, _ptr(self.fetch), _ptr(self.n_fetch),
+                                        min(self.S, T * k), _stream()))
+        return slot_ids
 
 
 def ffn_workspace_bytes(T, H, I, E, k, act=W4A16):

@@ -1,0 +1,252 @@
+"""GPU tests of expert paging: the device-side slot plan against a plain
+Python model of the same policy (bit-exact: slot maps, stamps, clock hand,
+fetch list, slot ids), the fetched slots against the host pages (bit-exact),
+and the FFN over the slot pool against the FFN over all experts in device
+memory (bit-exact where both take the same kernel plan) and the fp64 oracle
+(the FFN's tolerance).  Every call goes through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_routed_expert_amd import native, synth, weights
+from oracle import nvfp4_oracle as O
+from tests.helpers import LazyOracleExperts, assert_close_f32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+class SlotModel:
+    """The paging policy written out: needed experts that are resident keep
+    their slot and get the step's stamp; the missing ones, in ascending
+    expert order, take the free slots met walking from the clock hand (free:
+    empty, or holding an expert not needed now whose stamp is below
+    protect_from); the hand moves past the last slot taken.  When the free
+    slots are too few nothing moves and the missing experts read slot 0."""
+
+    def __init__(self, E, S):
+        self.E, self.S = E, S
+        self.slot_of = [-1] * E
+        self.expert_of = [-1] * S
+        self.last_use = [0] * S
+        self.hand = 0
+
+    def plan(self, ids, step, protect_from):
+        E, S = self.E, self.S
+        need = sorted({int(e) for e in np.ravel(ids) if 0 <= e < E})
+        needed = set(need)
+        misses = []
+        for e in need:
+            if self.slot_of[e] >= 0:
+                self.last_use[self.slot_of[e]] = step
+            else:
+                misses.append(e)
+        free = []
+        for r in range(S):
+            s = (self.hand + r) % S
+            e = self.expert_of[s]
+            if e < 0 or (e not in needed and self.last_use[s] < protect_from):
+                free.append(s)
+        fetch = []
+        if len(misses) <= len(free):
+            for e, s in zip(misses, free):
+                old = self.expert_of[s]
+                if old >= 0:
+                    self.slot_of[old] = -1
+                self.slot_of[e], self.expert_of[s], self.last_use[s] = s, e, step
+                fetch.append((e, s))
+            if misses:
+                self.hand = (free[len(misses) - 1] + 1) % S
+            n_fetch = len(misses)
+        else:
+            n_fetch = -1
+        slot_ids = np.array([[self.slot_of[e] if 0 <= e < E and self.slot_of[e] >= 0 else 0
+                              for e in row] for row in np.asarray(ids)], np.int32)
+        return slot_ids, fetch, n_fetch
+
+
+class DeviceSlots:
+    """The slot state on the device, driven through the C ABI."""
+
+    def __init__(self, E, S):
+        self.E, self.S = E, S
+        i32 = dict(dtype=torch.int32, device=DEV)
+        self.slot_of = torch.full((E,), 7, **i32)     # (init must overwrite)
+        self.expert_of = torch.full((S,), 7, **i32)
+        self.last_use = torch.full((S,), 7, **i32)
+        self.hand = torch.full((1,), 7, **i32)
+        self.fetch = torch.full((2 * S,), -5, **i32)
+        self.n_fetch = torch.zeros(1, **i32)
+        P = native._ptr
+        native._check(native.lib().moe_expert_cache_init(P(self.slot_of), E, P(self.expert_of),
+                                                         P(self.last_use), P(self.hand), S,
+                                                         native._stream()))
+
+    def plan(self, ids_np, step, protect_from):
+        ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(DEV)
+        T, k = ids.shape
+        slot_ids = torch.full_like(ids, -9)
+        P = native._ptr
+        native._check(native.lib().moe_expert_cache_plan(
+            P(ids), T, k, self.E, self.S, P(self.slot_of), P(self.expert_of), P(self.last_use),
+            P(self.hand), step, protect_from, P(slot_ids), P(self.fetch), P(self.n_fetch),
+            native._stream()))
+        n = int(self.n_fetch.item())
+        f = self.fetch.cpu().numpy()
+        return slot_ids.cpu().numpy(), [(int(f[2 * i]), int(f[2 * i + 1])) for i in range(max(n, 0))], n
+
+    def state(self):
+        return (self.slot_of.cpu().tolist(), self.expert_of.cpu().tolist(),
+                self.last_use.cpu().tolist(), int(self.hand.item()))
+
+
+def _step_ids(rng, E, T, k, pool, zipf):
+    """Ids [T, k] (distinct per token) drawn from `pool` experts of E, with a
+    Zipf-like skew over them."""
+    subset = rng.choice(E, size=min(pool, E), replace=False)
+    p = 1.0 / np.arange(1, len(subset) + 1) ** zipf
+    p /= p.sum()
+    kk = min(k, len(subset))
+    return np.stack([rng.choice(subset, size=kk, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+
+
+@pytest.mark.parametrize("E,S,k,steps,pool,zipf", [
+    (48, 12, 2, 40, 16, 1.0),      # often too full: the failure path
+    (128, 64, 8, 30, 40, 0.6),     # decode-shaped
+    (64, 64, 4, 12, 64, 0.0),      # pool as large as the expert set
+    (1024, 1024, 8, 6, 1024, 0.3),  # the largest state
+    (1024, 200, 8, 10, 300, 1.2),
+    (1, 1, 1, 4, 1, 0.0),           # one expert, one slot
+    (5, 3, 1, 20, 5, 0.5),
+])
+def test_cache_plan_matches_policy_model(E, S, k, steps, pool, zipf):
+    say("cache plan", E, S, k, steps, pool, zipf)
+    rng = np.random.default_rng(E * 7 + S)
+    dev, ref = DeviceSlots(E, S), SlotModel(E, S)
+    assert dev.state() == (ref.slot_of, ref.expert_of, ref.last_use, ref.hand)
+    fails = 0
+    for step in range(1, steps + 1):
+        T = int(rng.integers(1, 40))
+        ids = _step_ids(rng, E, T, k, pool, zipf)
+        if step == 3:          # ids outside 0..E-1 are ignored and read slot 0
+            ids[0, 0] = -1
+            ids[-1, -1] = E
+        protect = step - 1 if (step % 2 == 0 and step > 1) else step
+        got = dev.plan(ids, step, protect)
+        want = ref.plan(ids, step, protect)
+        assert got[2] == want[2], f"step {step}: n_fetch {got[2]} != {want[2]}"
+        assert got[1] == want[1], f"step {step}: fetch list"
+        assert np.array_equal(got[0], want[0]), f"step {step}: slot ids"
+        assert dev.state() == (ref.slot_of, ref.expert_of, ref.last_use, ref.hand), f"step {step}"
+        fails += want[2] < 0
+        # the maps stay inverse to each other
+        so, eo = ref.slot_of, ref.expert_of
+        assert all(eo[s] == e for e, s in enumerate(so) if s >= 0)
+        assert all(so[e] == s for s, e in enumerate(eo) if e >= 0)
+    say("plans that did not fit:", fails)
+    if (E, S) == (48, 12):
+        assert fails > 0
+
+
+def test_permute_pairs_matches_routing():
+    """moe_permute_pairs on routed ids gives moe_route_topk's offsets and
+    pair order bit for bit."""
+    for T, E, k, zipf in [(37, 8, 2, None), (300, 64, 4, 1.2), (1, 128, 8, None), (700, 256, 8, 1.1)]:
+        say("permute", T, E, k, zipf)
+        logits = synth.router_logits(T, E, 3, zipf_s=zipf)
+        ids, wts, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k)
+        off2, pairs2 = native.moe_permute_pairs(ids, E)
+        assert torch.equal(off, off2) and torch.equal(pairs, pairs2)
+
+
+def _host_copy(w):
+    return native.ExpertWeights(*[t.cpu().pin_memory() for t in (
+        w.gate_codes, w.gate_scales, w.gate_global, w.up_codes, w.up_scales, w.up_global,
+        w.down_codes, w.down_scales, w.down_global)])
+
+
+def _weight_tensors(w):
+    return (w.gate_codes, w.gate_scales, w.gate_global, w.up_codes, w.up_scales, w.up_global,
+            w.down_codes, w.down_scales, w.down_global)
+
+
+def _check_pool(cache):
+    """Every occupied slot holds its expert's host pages byte for byte."""
+    torch.cuda.synchronize()
+    eo = cache.expert_of.cpu().tolist()
+    occupied = [(s, e) for s, e in enumerate(eo) if e >= 0]
+    assert occupied
+    ss = torch.tensor([s for s, _ in occupied])
+    ee = torch.tensor([e for _, e in occupied])
+    for pt, ht in zip(_weight_tensors(cache.pool), _weight_tensors(cache.host)):
+        assert torch.equal(pt.cpu()[ss].view(torch.uint8), ht[ee].view(torch.uint8))
+
+
+def _weights_for(k, T, rng):
+    w = rng.uniform(0.05, 1.0, size=(T, k)).astype(np.float32)
+    return w / w.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,S,pool,protect,bitexact", [
+    (4, 512, 256, 128, 8, 64, 32, True, True),     # decode rows: the plan is the same for any E
+    (1, 1024, 512, 64, 4, 16, 8, True, True),
+    (300, 256, 256, 64, 2, 64, 64, False, True),   # tiles, S = E: the same plan
+    (200, 256, 128, 64, 2, 40, 40, False, False),  # tiles, S < E: another plan, the tolerance
+])
+def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact):
+    say("paged ffn", T, H, I, E, k, S, pool, protect)
+    rng = np.random.default_rng(T + H + E)
+    w_dev = weights.synthetic_experts(E, H, I, 5, DEV)
+    cache = native.ExpertCache(_host_copy(w_dev), S, DEV)
+    for step in range(1, 6):
+        ids_np = _step_ids(rng, E, T, k, pool, 0.8)
+        wts_np = _weights_for(k, T, rng)
+        x = synth.activations(T, H, 100 + step)
+        xd = x.to(DEV)
+        ids = torch.from_numpy(ids_np).to(DEV)
+        wts = torch.from_numpy(wts_np).to(DEV)
+        off, pairs = native.moe_permute_pairs(ids, E)
+        y_res, _ = native.moe_grouped_nvfp4_ffn(xd, w_dev, ids, wts, off, pairs, k,
+                                                out_dtype=torch.float32)
+        slot_ids = cache.plan_and_fetch(ids, protect_previous=protect)
+        assert int(cache.n_fetch.item()) >= 0, f"step {step}: the step's experts did not fit"
+        off_s, pairs_s = native.moe_permute_pairs(slot_ids, S)
+        y_pag, _ = native.moe_grouped_nvfp4_ffn(xd, cache.pool, slot_ids, wts, off_s, pairs_s, k,
+                                                out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        # the slot ids name the same experts
+        eo = cache.expert_of.cpu().numpy()
+        assert np.array_equal(eo[slot_ids.cpu().numpy()], ids_np), f"step {step}"
+        if bitexact:
+            assert torch.equal(y_pag, y_res), f"step {step}"
+        else:
+            assert_close_f32(y_pag.cpu().numpy(), y_res.cpu().numpy().astype(np.float64),
+                             f"paged vs resident, step {step}")
+        if step in (1, 5):
+            w_ref = LazyOracleExperts(E, H, I, np.unique(ids_np), 5)
+            ref, _ = O.moe_ffn(x.float().numpy(), ids_np, wts_np, w_ref)
+            assert_close_f32(y_pag.cpu().numpy(), ref, f"paged vs oracle, step {step}")
+    _check_pool(cache)
+
+
+def test_fetch_rejects_pageable_host_memory():
+    E, H, I = 4, 64, 32
+    w_dev = weights.synthetic_experts(E, H, I, 1, DEV)
+    pageable = native.ExpertWeights(*[t.cpu() for t in _weight_tensors(w_dev)])
+    with pytest.raises(ValueError):
+        native.ExpertCache(pageable, 2, DEV)
+    pool = weights.empty_experts(2, H, I, DEV)
+    fetch = torch.zeros(4, dtype=torch.int32, device=DEV)
+    n = torch.zeros(1, dtype=torch.int32, device=DEV)
+    hc, pc = pageable.c_struct(), pool.c_struct()
+    rc = native.lib().moe_expert_cache_fetch(native.ctypes.byref(hc), native.ctypes.byref(pc), H,
+                                             I, native._ptr(fetch), native._ptr(n), 2,
+                                             native._stream())
+    assert rc == 1 and "pinned" in native.lib().nvfp4_last_error().decode()

@@ -175,6 +175,37 @@ def test_shared_expert_validation():
     assert L.moe_shared_expert_ffn_workspace_size(0, H, I) == 0
 
 
+def test_expert_cache_validation():
+    L = native.lib()
+    assert L.moe_expert_cache_init(FAKE, 0, FAKE, FAKE, FAKE, 8, None) == 2
+    assert L.moe_expert_cache_init(FAKE, 64, FAKE, FAKE, FAKE, 2048, None) == 2
+    assert L.moe_expert_cache_init(None, 64, FAKE, FAKE, FAKE, 8, None) == 1
+    plan = lambda T=4, k=2, E=64, S=16, step=1, prot=1, ids=FAKE: L.moe_expert_cache_plan(
+        ids, T, k, E, S, FAKE, FAKE, FAKE, FAKE, step, prot, FAKE, FAKE, FAKE, None)
+    assert plan(E=2000) == 2
+    assert plan(S=0) == 2
+    assert plan(T=0) == 1
+    assert plan(step=0, prot=0) == 1
+    assert plan(step=3, prot=4) == 1
+    assert plan(ids=None) == 1
+    w = native.ExpertWeightsC(*([FAKE.value] * 9))
+    mis = native.ExpertWeightsC(*([FAKE_MIS.value] + [FAKE.value] * 8))
+    odd_g = native.ExpertWeightsC(*([FAKE.value] * 8 + [FAKE.value + 2]))
+    nul = native.ExpertWeightsC(*([FAKE.value] * 8 + [None]))
+    f = lambda hw=w, pw=w, H=256, I=128, mx=8: L.moe_expert_cache_fetch(
+        ctypes.byref(hw), ctypes.byref(pw), H, I, FAKE, FAKE, mx, None)
+    assert f(H=100) == 2
+    assert f(mx=-1) == 1
+    assert f(hw=nul) == 1 and "host_w" in _last()
+    assert f(pw=mis) == 3 and "pool" in _last()
+    assert f(pw=odd_g) == 3
+    pp = lambda T=4, E=64, k=2, ids=FAKE: L.moe_permute_pairs(ids, T, E, k, FAKE, FAKE, None)
+    assert pp(E=0) == 2
+    assert pp(k=33) == 2
+    assert pp(T=0) == 1
+    assert pp(ids=FAKE_MIS) == 3
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(native, "_LIB", None)
     monkeypatch.setattr(native, "LIB_PATH", str(tmp_path / "missing.so"))
