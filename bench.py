@@ -63,6 +63,15 @@ def parse():
     ap.add_argument("--separate-h-quant", action="store_true",
                     help="with --given-globals: quantise h in its own pass instead of the "
                          "gate/up epilogue (same results)")
+    ap.add_argument("--paged", type=int, default=0, metavar="S",
+                    help="expert paging: all experts in pinned host memory, S device slots; "
+                         "times route + slot plan + fetch + FFN on the pool (own JSON line)")
+    ap.add_argument("--paged-overlap", action="store_true",
+                    help="with --paged: also time a two-stream pipeline (routing, slot plan "
+                         "and fetch of step i+1 beside the FFN of step i)")
+    ap.add_argument("--paged-zipf", type=float, default=None,
+                    help="with --paged: Zipf exponent of a router bias (expert popularity; "
+                         "default: the workload's own routing)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB elementwise copy kernel (for scaling "
                          "hardware byte counters)")
@@ -160,6 +169,9 @@ def main():
                                    "FFN is measured on one GPU's share (it would shard by "
                                    "expert, one exchange of y per step)", "n_gpus": args.gpus}))
         sys.exit(2)
+
+    if args.paged:
+        return paged_main(args)
 
     import numpy as np
     import torch
@@ -447,6 +459,207 @@ def main():
         "setup_s": round(setup_s, 1),
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+HOST_LINK_PEAK_GBS = 63.0   # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def paged_main(args):
+    """Expert paging on a routed-expert step: every expert's NVFP4 weights in
+    pinned host memory, a device pool of S slots.  A step routes
+    (moe_route_topk), plans the slots (moe_expert_cache_plan), copies the
+    missing experts into the pool (moe_expert_cache_fetch), orders the pairs
+    by slot (moe_permute_pairs) and runs the FFN on the pool.  The routing
+    batches cycle over 64 seeded logits tensors of the workload's routing (or
+    one with a Zipf router bias of the given exponent: skewed popularity).  Prints one JSON line: step
+    throughput, hit rate, bytes fetched per step, the stages' times and the
+    fetch kernel's rate against the host link; beside it the same steps with
+    every expert resident in HBM."""
+    import numpy as np
+    import torch
+
+    from nvfp4_routed_expert_amd import native, synth, weights
+
+    wl = synth.WORKLOADS[args.workload]
+    if wl.act != "w4a16" or wl.E < 2:
+        sys.exit("--paged runs the W4A16 routed-expert workloads")
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    T, H, I, E, k, S = wl.T, wl.H, wl.I, wl.E, wl.k, args.paged
+    P = T * k
+    expert_bytes = 3 * (nv_bytes(H * I) + 4)
+    n_batches = 64
+    x = synth.activations(T, H).to(dev)
+    zipf = wl.zipf_s if args.paged_zipf is None else args.paged_zipf
+    logits = [torch.from_numpy(synth.router_logits(T, E, seed=b, zipf_s=zipf)).to(dev)
+              for b in range(n_batches)]
+    w_dev = weights.synthetic_experts(E, H, I, 0, dev)
+    host = native.ExpertWeights(*[t.cpu().pin_memory() for t in (
+        w_dev.gate_codes, w_dev.gate_scales, w_dev.gate_global, w_dev.up_codes, w_dev.up_scales,
+        w_dev.up_global, w_dev.down_codes, w_dev.down_scales, w_dev.down_global)])
+    cache = native.ExpertCache(host, S, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids, slot_ids = torch.empty((T, k), **i32), torch.empty((T, k), **i32)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off, pairs = torch.empty(E + 1, **i32), torch.empty(P, **i32)
+    off_s, pairs_s = torch.empty(S + 1, **i32), torch.empty(P, **i32)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws_p = torch.empty(native.ffn_workspace_bytes(T, H, I, S, k), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(native.ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+    rws = native.route_workspace(T, E, k, dev)
+    stages = ["route", "plan", "fetch", "permute", "ffn"]
+
+    def paged_step(b, ev=None):
+        mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
+        mark(0)
+        native.moe_route_topk(logits[b], k, True, out=(ids, wts, off, pairs), workspace=rws)
+        mark(1)
+        cache.plan(ids, slot_ids=slot_ids)
+        mark(2)
+        cache.fetch_planned(P)
+        mark(3)
+        native.moe_permute_pairs(slot_ids, S, out=(off_s, pairs_s))
+        mark(4)
+        native.moe_grouped_nvfp4_ffn(x, cache.pool, slot_ids, wts, off_s, pairs_s, k,
+                                     out_dtype=torch.bfloat16, workspace=ws_p, out=y)
+        mark(5)
+
+    def resident_step(b):
+        native.moe_route_topk(logits[b], k, True, out=(ids, wts, off, pairs), workspace=rws)
+        native.moe_grouped_nvfp4_ffn(x, w_dev, ids, wts, off, pairs, k,
+                                     out_dtype=torch.bfloat16, workspace=ws_r, out=y)
+
+    def timed(fn, n):
+        # a GPU sleep first keeps the stream busy while the host enqueues the
+        # steps, so they run back to back (no host gaps inside the events)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(400_000_000)
+        a.record()
+        for i in range(n):
+            fn(i % n_batches)
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / n
+
+    # the pool warms up over the warmup steps, then K timed steps (eager
+    # launches; a step's fetch dominates its time)
+    for i in range(args.warmup):
+        paged_step(i % n_batches)
+    ms_paged = timed(lambda b: paged_step((b + args.warmup) % n_batches), args.steps)
+
+    ms_overlap = None
+    if args.paged_overlap:
+        # Two streams.  Side stream: routing, slot plan (the previous step's
+        # experts protected), fetch and pair order of step i; it first waits
+        # for the FFN of step i-2, the last reader of the buffers it reuses
+        # and of the experts it may evict.  Main stream: the FFN of step i
+        # after its fetch.  So the fetch of step i runs beside the FFN of
+        # step i-1.
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        buf = [dict(ids=torch.empty((T, k), **i32), slot=torch.empty((T, k), **i32),
+                    wts=torch.empty((T, k), dtype=torch.float32, device=dev),
+                    off=torch.empty(E + 1, **i32), pairs=torch.empty(P, **i32),
+                    off_s=torch.empty(S + 1, **i32), pairs_s=torch.empty(P, **i32))
+               for _ in range(2)]
+        rws2 = native.route_workspace(T, E, k, dev)
+
+        nlog_o = torch.zeros(max(args.steps, args.warmup, 1), **i32)
+
+        def pipeline(n, b0, start_ev):
+            ffn_done = [None] * n
+            side.wait_event(start_ev)
+            for i in range(n):
+                bb = buf[i % 2]
+                with torch.cuda.stream(side):
+                    if i >= 2:
+                        side.wait_event(ffn_done[i - 2])
+                    native.moe_route_topk(logits[(b0 + i) % n_batches], k, True,
+                                          out=(bb["ids"], bb["wts"], bb["off"], bb["pairs"]),
+                                          workspace=rws2)
+                    cache.plan(bb["ids"], protect_previous=True, slot_ids=bb["slot"])
+                    cache.fetch_planned(P)
+                    native.moe_permute_pairs(bb["slot"], S, out=(bb["off_s"], bb["pairs_s"]))
+                    fetched = torch.cuda.Event()
+                    fetched.record(side)
+                    nlog_o[i:i + 1].copy_(cache.n_fetch)
+                main.wait_event(fetched)
+                native.moe_grouped_nvfp4_ffn(x, cache.pool, bb["slot"], bb["wts"], bb["off_s"],
+                                             bb["pairs_s"], k, out_dtype=torch.bfloat16,
+                                             workspace=ws_p, out=y)
+                ffn_done[i] = torch.cuda.Event()
+                ffn_done[i].record(main)
+            main.wait_stream(side)
+
+        w0 = torch.cuda.Event()
+        w0.record(main)
+        pipeline(args.warmup, 0, w0)
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(400_000_000)
+        a.record(main)
+        pipeline(args.steps, args.warmup, a)
+        z.record(main)
+        torch.cuda.synchronize()
+        if int(nlog_o[:args.steps].min().item()) < 0:
+            sys.exit(f"--paged {S} --paged-overlap: two steps' experts did not fit in the pool")
+        ms_overlap = a.elapsed_time(z) / args.steps
+    for i in range(min(args.warmup, 8)):
+        resident_step(i % n_batches)
+    ms_res = timed(resident_step, args.steps)
+
+    # stage times and fetch counts: one more pass, events around each call
+    n_stat = min(args.steps, n_batches)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_stat)]
+    nlog = torch.empty(n_stat, **i32)
+    dlog = torch.empty((n_stat, T, k), **i32)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(400_000_000)
+    for i in range(n_stat):
+        paged_step((i + args.warmup + args.steps) % n_batches, evs[i])
+        nlog[i:i + 1].copy_(cache.n_fetch)
+        dlog[i].copy_(ids)
+    torch.cuda.synchronize()
+    st = {s: [evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(n_stat)]
+          for j, s in enumerate(stages)}
+    nf = nlog.cpu().numpy()
+    if (nf < 0).any():
+        sys.exit(f"--paged {S}: a step's experts did not fit in the pool")
+    distinct = np.array([len(np.unique(d)) for d in dlog.cpu().numpy()])
+    fetched = int(nf.sum())
+    fetch_us = np.array(st["fetch"])
+    busy = nf > 0
+    fetch_gbs = (float(nf[busy].sum()) * expert_bytes / (fetch_us[busy].sum() * 1e-6) / 1e9
+                 if busy.any() else None)
+    out = {
+        "metric": "NVFP4 MoE FFN with expert paging: tokens/s",
+        "value": round(T / (ms_paged * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_paged, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": wl.name + "_paged", "tokens": T, "hidden": H,
+                   "intermediate": I, "experts": E, "top_k": k, "slots": S,
+                   "router_bias_zipf_s": zipf, "routing_batches": n_batches,
+                   "host_weights_gb": round(E * expert_bytes / 1e9, 3),
+                   "pool_gb": round(S * expert_bytes / 1e9, 3), "graph": False,
+                   "parallelism": "single GPU"},
+        "hit_rate": round(1.0 - fetched / float(distinct.sum()), 4),
+        "experts_per_step": round(float(distinct.mean()), 2),
+        "fetched_per_step": round(float(nf.mean()), 2),
+        "fetched_mb_per_step": round(float(nf.mean()) * expert_bytes / 1e6, 3),
+        "stage_us": {s: round(float(np.mean(v)), 2) for s, v in st.items()},
+        "resident_ms_per_step": round(ms_res, 5),
+        "overlapped_ms_per_step": None if ms_overlap is None else round(ms_overlap, 5),
+        "roofline": {"bound": "host_link", "kernel": "cache_fetch_kernel",
+                     "achieved": None if fetch_gbs is None else round(fetch_gbs, 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": None if fetch_gbs is None else round(fetch_gbs / HOST_LINK_PEAK_GBS, 4),
+                     "traffic": None,
+                     "alg_per_unit": f"{expert_bytes} bytes per fetched expert"},
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 

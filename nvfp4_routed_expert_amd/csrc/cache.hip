@@ -6,7 +6,8 @@
 // order from a clock hand; a slot is free when it is empty, or holds an expert
 // the step does not need whose stamp is older than the step still in flight)
 // and remaps the routing ids to slots.  The fetch kernel then reads the
-// missing experts' pages straight from host memory into their slots.
+// missing experts' pages straight from host memory into their slots (the
+// host does not know how many there are; the kernel reads the count).
 #include "common.h"
 #include "kernels.h"
 
@@ -125,34 +126,47 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
 }
 
 // One expert's bytes as segments: gate, up, down codes; gate, up, down
-// scales; the three globals.  Grid: x = 16-byte piece within a segment,
-// y = segment, z = fetch index.
-struct Seg {
-  const uint8_t *src;
-  uint8_t *dst;
-  int64_t estride_src, estride_dst, bytes;
-};
+// scales (16-byte pieces); then the three 4-byte globals.
 struct FetchArgs {
-  Seg seg[9];
+  const uint8_t *src[9];
+  uint8_t *dst[9];
+  int64_t bytes[9];
 };
 
+// A fixed grid strides over the pieces of one fetched expert after another
+// (no barrier between experts: a wave moves on as soon as its pieces are
+// done), four pieces' loads in flight per thread, so that many host reads
+// are outstanding on the link at once.  With nothing to fetch every
+// workgroup leaves after one read.
 __global__ __launch_bounds__(256) void cache_fetch_kernel(const FetchArgs a, const int32_t *fetch,
-                                                           const int32_t *n_fetch) {
-  const int i = blockIdx.z;
-  if (i >= *n_fetch) return;
-  const int e = fetch[2 * i], s = fetch[2 * i + 1];
-  const Seg sg = a.seg[blockIdx.y];
-  const uint8_t *src = sg.src + (int64_t)e * sg.estride_src;
-  uint8_t *dst = sg.dst + (int64_t)s * sg.estride_dst;
-  if (sg.bytes < 16) {   // a 4-byte global
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-      *reinterpret_cast<float *>(dst) = *reinterpret_cast<const float *>(src);
-    return;
+                                                           const int32_t *n_fetch, int max_fetch) {
+  const int n = min(*n_fetch, max_fetch);
+  const int64_t gtid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gstride = (int64_t)gridDim.x * 256;
+  for (int i = 0; i < n; ++i) {
+    const int e = fetch[2 * i], s = fetch[2 * i + 1];
+#pragma unroll 1
+    for (int j = 0; j < 6; ++j) {
+      const u32x4 *src = reinterpret_cast<const u32x4 *>(a.src[j] + (int64_t)e * a.bytes[j]);
+      u32x4 *dst = reinterpret_cast<u32x4 *>(a.dst[j] + (int64_t)s * a.bytes[j]);
+      const int64_t n16 = a.bytes[j] / 16;
+      int64_t q = gtid;
+      for (; q + 3 * gstride < n16; q += 4 * gstride) {
+        const u32x4 v0 = src[q], v1 = src[q + gstride], v2 = src[q + 2 * gstride],
+                    v3 = src[q + 3 * gstride];
+        dst[q] = v0;
+        dst[q + gstride] = v1;
+        dst[q + 2 * gstride] = v2;
+        dst[q + 3 * gstride] = v3;
+      }
+      for (; q < n16; q += gstride) dst[q] = src[q];
+    }
+    if (gtid < 3) {   // the globals
+      const int j = 6 + (int)gtid;
+      *reinterpret_cast<float *>(a.dst[j] + (int64_t)s * 4) =
+          *reinterpret_cast<const float *>(a.src[j] + (int64_t)e * 4);
+    }
   }
-  const int64_t n16 = sg.bytes / 16;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < n16;
-       q += (int64_t)gridDim.x * 256)
-    reinterpret_cast<u32x4 *>(dst)[q] = reinterpret_cast<const u32x4 *>(src)[q];
 }
 
 }  // namespace
@@ -184,18 +198,17 @@ hipError_t launch_cache_fetch(const ExpertPtrs &host, const ExpertPtrs &pool, in
   FetchArgs a;
   const int64_t bytes[9] = {gu_codes, gu_codes, d_codes, gu_scales, gu_scales, d_scales, 4, 4, 4};
   for (int j = 0; j < 9; ++j) {
-    a.seg[j].src = host.p[j];
-    a.seg[j].dst = const_cast<uint8_t *>(pool.p[j]);
-    a.seg[j].estride_src = a.seg[j].estride_dst = bytes[j];
-    a.seg[j].bytes = bytes[j];
-    if (bytes[j] >= 16 && bytes[j] % 16 != 0) return hipErrorInvalidValue;
+    a.src[j] = host.p[j];
+    a.dst[j] = const_cast<uint8_t *>(pool.p[j]);
+    a.bytes[j] = bytes[j];
+    if (j < 6 && bytes[j] % 16 != 0) return hipErrorInvalidValue;
   }
-  // pieces per segment: the largest segment in 16-byte pieces, at most 64 workgroups of 256
-  int64_t gx = (gu_codes / 16 + 255) / 256;
-  if (gx > 64) gx = 64;
-  if (gx < 1) gx = 1;
-  launch_kernel(cache_fetch_kernel, dim3((unsigned)gx, 9, (unsigned)max_fetch), dim3(256), 0, s, a,
-                fetch, n_fetch);
+  // enough workgroups for one expert's codes in a few passes, at most 1024
+  int64_t wg = (gu_codes / 16 + 4 * 256 - 1) / (4 * 256);
+  if (wg > 1024) wg = 1024;
+  if (wg < 1) wg = 1;
+  launch_kernel(cache_fetch_kernel, dim3((unsigned)wg), dim3(256), 0, s, a, fetch, n_fetch,
+                max_fetch);
   return hipGetLastError();
 }
 

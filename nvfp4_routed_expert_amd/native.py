@@ -363,23 +363,33 @@ class ExpertCache:
                                            _ptr(self.last_use), _ptr(self.hand), slots,
                                            _stream()))
 
-    def plan_and_fetch(self, topk_ids, protect_previous=False, slot_ids=None):
-        """Slot ids [T, k] for this step's expert ids; the missing experts are
-        copied into the pool.  protect_previous: keep the previous step's
-        experts (its FFN may still be running)."""
+    def plan(self, topk_ids, protect_previous=False, slot_ids=None):
+        """Slot ids [T, k] for this step's expert ids (the missing experts
+        get slots; fetch() copies them).  protect_previous: keep the previous
+        step's experts (its FFN may still be running)."""
         T, k = topk_ids.shape
         self.step_no += 1
         protect = self.step_no - 1 if protect_previous and self.step_no > 1 else self.step_no
         if slot_ids is None:
             slot_ids = torch.empty_like(topk_ids)
-        L = lib()
-        _check(L.moe_expert_cache_plan(_ptr(topk_ids), T, k, self.E, self.S, _ptr(self.slot_of),
-                                       _ptr(self.expert_of), _ptr(self.last_use), _ptr(self.hand),
-                                       self.step_no, protect, _ptr(slot_ids), _ptr(self.fetch),
-                                       _ptr(self.n_fetch), _stream()))
-        _check(L.moe_expert_cache_fetch(ctypes.byref(self._host_c), ctypes.byref(self._pool_c),
-                                        self.H, self.I, _ptr(self.fetch), _ptr(self.n_fetch),
-                                        min(self.S, T * k), _stream()))
+        _check(lib().moe_expert_cache_plan(_ptr(topk_ids), T, k, self.E, self.S,
+                                           _ptr(self.slot_of), _ptr(self.expert_of),
+                                           _ptr(self.last_use), _ptr(self.hand), self.step_no,
+                                           protect, _ptr(slot_ids), _ptr(self.fetch),
+                                           _ptr(self.n_fetch), _stream()))
+        return slot_ids
+
+    def fetch_planned(self, pairs):
+        """Copy the experts the last plan() listed (pairs = T * k of that step)."""
+        _check(lib().moe_expert_cache_fetch(ctypes.byref(self._host_c),
+                                            ctypes.byref(self._pool_c), self.H, self.I,
+                                            _ptr(self.fetch), _ptr(self.n_fetch),
+                                            min(self.S, pairs), _stream()))
+
+    def plan_and_fetch(self, topk_ids, protect_previous=False, slot_ids=None):
+        """plan() then fetch_planned(): slot ids [T, k], the pool filled."""
+        slot_ids = self.plan(topk_ids, protect_previous, slot_ids)
+        self.fetch_planned(topk_ids.numel())
         return slot_ids
 
 

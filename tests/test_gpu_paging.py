@@ -236,6 +236,60 @@ def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact):
     _check_pool(cache)
 
 
+def test_paged_ffn_two_stream_pipeline():
+    """The slot plan, fetch and pair order of step i on a side stream beside
+    the FFN of step i-1 on the main stream (the previous step's experts
+    protected; the side stream waits for the FFN of step i-2 before reusing
+    its buffers): every step's output equals the resident FFN's bit for
+    bit (decode row kernels)."""
+    T, H, I, E, k, S, steps = 4, 512, 256, 128, 8, 64, 12
+    say("paged pipeline", T, H, I, E, k, S, steps)
+    rng = np.random.default_rng(11)
+    w_dev = weights.synthetic_experts(E, H, I, 6, DEV)
+    cache = native.ExpertCache(_host_copy(w_dev), S, DEV)
+    xs = [synth.activations(T, H, 200 + i).to(DEV) for i in range(steps)]
+    ids_np = [_step_ids(rng, E, T, k, 32, 0.5) for _ in range(steps)]
+    wts_np = [_weights_for(k, T, rng) for _ in range(steps)]
+    ids_d = [torch.from_numpy(a).to(DEV) for a in ids_np]
+    wts_d = [torch.from_numpy(a).to(DEV) for a in wts_np]
+    i32 = dict(dtype=torch.int32, device=DEV)
+    buf = [dict(slot=torch.empty((T, k), **i32), off=torch.empty(S + 1, **i32),
+                pairs=torch.empty(T * k, **i32)) for _ in range(2)]
+    nlog = torch.zeros(steps, **i32)
+    ws = torch.empty(native.ffn_workspace_bytes(T, H, I, S, k), dtype=torch.uint8, device=DEV)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs, done = [], []
+    side.wait_stream(main)
+    for i in range(steps):
+        b = buf[i % 2]
+        with torch.cuda.stream(side):
+            if i >= 2:
+                side.wait_event(done[i - 2])
+            cache.plan(ids_d[i], protect_previous=True, slot_ids=b["slot"])
+            cache.fetch_planned(T * k)
+            native.moe_permute_pairs(b["slot"], S, out=(b["off"], b["pairs"]))
+            ev = torch.cuda.Event()
+            ev.record(side)
+            nlog[i:i + 1].copy_(cache.n_fetch)
+        main.wait_event(ev)
+        y, _ = native.moe_grouped_nvfp4_ffn(xs[i], cache.pool, b["slot"], wts_d[i], b["off"],
+                                            b["pairs"], k, out_dtype=torch.float32, workspace=ws)
+        outs.append(y)
+        d = torch.cuda.Event()
+        d.record(main)
+        done.append(d)
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert int(nlog.min()) >= 0
+    for i in range(steps):
+        off, pairs = native.moe_permute_pairs(ids_d[i], E)
+        y_res, _ = native.moe_grouped_nvfp4_ffn(xs[i], w_dev, ids_d[i], wts_d[i], off, pairs, k,
+                                                out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[i], y_res), f"step {i}"
+
+
 def test_fetch_rejects_pageable_host_memory():
     E, H, I = 4, 64, 32
     w_dev = weights.synthetic_experts(E, H, I, 1, DEV)
