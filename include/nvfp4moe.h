@@ -44,12 +44,22 @@
  *     synchronisation, as usual in HIP.
  *   - Calls are deterministic: the same inputs give bit-identical outputs
  *     (no floating-point atomics; maxima use order-independent integer
- *     atomics).  The library has no global mutable state except the
- *     thread-local last-error message.
+ *     atomics).  The library has no global mutable state; its only state is
+ *     per thread (the last-error message and the two switches below).
  *   - K (the contraction length: cols, H or I) must be a positive multiple
  *     of 32, otherwise NVFP4_ERR_UNSUPPORTED_SHAPE.
  *   - Inputs must be finite; NaN or infinite activations, logits or weights
  *     are not checked and give unspecified results.
+ *   - An empty batch (T = 0 tokens, or M = 0 rows for nvfp4_linear) is
+ *     valid: the other arguments are checked as usual, the batch's empty
+ *     arrays may be NULL, and nothing is computed.  The routing calls
+ *     (moe_route_topk, moe_router_topk, moe_permute_pairs) then set the
+ *     E + 1 expert offsets to 0 and moe_expert_cache_plan sets *n_fetch to
+ *     0; every other output is left untouched (act_globals included).
+ *     Negative sizes are NVFP4_ERR_INVALID_ARGUMENT.
+ *   - The library ships a thread-local execution switch and a timing hook
+ *     (nvfp4_set_ffn_separate_h_quant, nvfp4_set_ffn_stage_events); they
+ *     change no result.
  */
 #ifndef NVFP4MOE_H
 #define NVFP4MOE_H
@@ -229,7 +239,7 @@ nvfp4_status moe_expert_cache_init(int32_t *slot_of, int32_t E, int32_t *expert_
  * free slots do not suffice, nothing moves, *n_fetch = -1, and the missing
  * experts' pairs (like ids outside 0..E-1) get slot 0, so a following FFN
  * reads valid memory but its result is wrong: check *n_fetch.  Requires
- * 1 <= E, S <= 1024, T, k >= 1, 1 <= step, protect_from <= step.  One
+ * 1 <= E, S <= 1024, T >= 0, k >= 1, 1 <= step, protect_from <= step.  One
  * workgroup; integer-exact.
  */
 nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k,
@@ -259,7 +269,9 @@ nvfp4_status moe_expert_cache_fetch(const nvfp4_expert_weights *host_w,
 /*
  * moe_permute_pairs: moe_route_topk's expert offsets [E+1] and sorted pairs
  * [T*k] for given ids [T, k] (stable: pairs of one expert in ascending
- * order).  Same limits as moe_route_topk.
+ * order).  Same limits as moe_route_topk.  Every id must lie in 0..E-1 (as
+ * the ids moe_route_topk and moe_expert_cache_plan write always do); other
+ * ids are not checked and may lead outside the arrays.
  */
 nvfp4_status moe_permute_pairs(const int32_t *topk_ids, int64_t T, int32_t E, int32_t k,
                                int32_t *expert_offsets, int32_t *sorted_pairs,
@@ -277,7 +289,7 @@ nvfp4_status moe_permute_pairs(const int32_t *topk_ids, int64_t T, int32_t E, in
  *                                         e.g. the routed output)
  * Products are exact in fp32 and the sums fp32; the result is rounded once
  * to y's type (bf16 round-to-nearest-even or f32).
- * Requires H % 32 == 0, I % 32 == 0, T >= 1.  workspace:
+ * Requires H % 32 == 0, I % 32 == 0, T >= 0.  workspace:
  * moe_shared_expert_ffn_workspace_size bytes (device, 16-byte aligned).
  */
 nvfp4_status moe_shared_expert_ffn(const void *x, int64_t T, int64_t H, int64_t I,
@@ -298,7 +310,7 @@ size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I);
  * all T rows) and h (one scale over all T*k pairs) to NVFP4 before the gate/up
  * and down products; act_globals[0..1] = {g_x, g_h} are written (COMPUTE) or
  * read (GIVEN).  act_globals may be NULL for W4A16.
- * Requires H % 32 == 0, I % 32 == 0, 1 <= k <= E, T >= 1.
+ * Requires H % 32 == 0, I % 32 == 0, 1 <= k <= E, T >= 0.
  */
 nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H,
                                    int64_t I, int32_t E, int32_t k,

@@ -346,10 +346,12 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
                           float *act_global, void *y, nvfp4_dtype y_dtype, void *workspace,
                           size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(x);
-  CHECK_NULL(y);
+  if (M > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(x);
+    CHECK_NULL(y);
+  }
   TRY(check_matrix(w));
-  if (M < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "M = %lld < 1", (long long)M);
+  if (M < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "M = %lld < 0", (long long)M);
   if (M > (1 << 30) || w->rows > (1 << 30))
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "M or N exceeds 2^30");
   if (act != NVFP4_W4A16 && act != NVFP4_W4A4)
@@ -365,6 +367,7 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   CHECK_ALIGN(y);
   const int64_t K = w->cols, N = w->rows;
   TRY(check_workspace(workspace, workspace_bytes, nvfp4_linear_workspace_size(M, N, K, act)));
+  if (M == 0) return NVFP4_OK;   // nothing to compute (act_global is not written)
   Carver c(workspace);
   const LinearWs ws = carve_linear(c, M, N, K);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -441,12 +444,14 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
                             int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(logits);
-  CHECK_NULL(topk_ids);
-  CHECK_NULL(topk_weights);
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(logits);
+    CHECK_NULL(topk_ids);
+    CHECK_NULL(topk_weights);
+    CHECK_NULL(sorted_pairs);
+  }
   CHECK_NULL(expert_offsets);
-  CHECK_NULL(sorted_pairs);
-  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
   if (E < 1 || E > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
   if (k < 1 || k > E || k > 32)
@@ -459,6 +464,10 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
   TRY(check_workspace(workspace, workspace_bytes, moe_route_topk_workspace_size(T, E, k)));
+  if (T == 0) {   // no pairs: every offset is 0
+    LAUNCH(launch_permute(nullptr, 0, E, k, expert_offsets, nullptr, stream), "offsets");
+    return NVFP4_OK;
+  }
   LAUNCH(launch_route(LogitSrc{logits, 0, 1, nullptr, nullptr}, T, E, k, renormalize, topk_ids,
                       topk_weights, expert_offsets, sorted_pairs,
                       static_cast<uint32_t *>(workspace), stream),
@@ -483,13 +492,15 @@ nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *ro
                              int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
                              size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(x);
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(x);
+    CHECK_NULL(topk_ids);
+    CHECK_NULL(topk_weights);
+    CHECK_NULL(sorted_pairs);
+  }
   CHECK_NULL(router_w);
-  CHECK_NULL(topk_ids);
-  CHECK_NULL(topk_weights);
   CHECK_NULL(expert_offsets);
-  CHECK_NULL(sorted_pairs);
-  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
   TRY(check_k(H, "H"));
   if (E < 1 || E > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
@@ -508,6 +519,10 @@ nvfp4_status moe_router_topk(const void *x, int64_t T, int64_t H, const void *ro
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
   TRY(check_workspace(workspace, workspace_bytes, moe_router_topk_workspace_size(T, H, E, k)));
+  if (T == 0) {   // no pairs: every offset is 0
+    LAUNCH(launch_permute(nullptr, 0, E, k, expert_offsets, nullptr, stream), "offsets");
+    return NVFP4_OK;
+  }
   Carver c(workspace);
   uint32_t *ticket = c.take<uint32_t>(64);
   const Bf16Plan plan = bf16_plan(T, H, E);
@@ -545,17 +560,19 @@ nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k
                                    uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
                                    int32_t *n_fetch, hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(topk_ids);
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(topk_ids);
+    CHECK_NULL(slot_ids);
+  }
   CHECK_NULL(slot_of);
   CHECK_NULL(expert_of);
   CHECK_NULL(last_use);
   CHECK_NULL(hand);
-  CHECK_NULL(slot_ids);
   CHECK_NULL(fetch);
   CHECK_NULL(n_fetch);
   if (E < 1 || E > 1024 || S < 1 || S > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d, S = %d outside 1..1024", (int)E, (int)S);
-  if (T < 1 || k < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T and k must be >= 1");
+  if (T < 0 || k < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "need T >= 0 and k >= 1");
   if (step < 1 || protect_from > step)
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "need 1 <= step and protect_from <= step");
   const int64_t P = T * (int64_t)k;
@@ -617,10 +634,12 @@ nvfp4_status moe_permute_pairs(const int32_t *topk_ids, int64_t T, int32_t E, in
                                int32_t *expert_offsets, int32_t *sorted_pairs,
                                hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(topk_ids);
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(topk_ids);
+    CHECK_NULL(sorted_pairs);
+  }
   CHECK_NULL(expert_offsets);
-  CHECK_NULL(sorted_pairs);
-  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
   if (E < 1 || E > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
   if (k < 1 || k > 32)
@@ -648,12 +667,14 @@ nvfp4_status moe_shared_expert_ffn(const void *x, int64_t T, int64_t H, int64_t 
                                    int accumulate, void *y, nvfp4_dtype y_dtype, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(x);
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(x);
+    CHECK_NULL(y);
+  }
   CHECK_NULL(w_gate);
   CHECK_NULL(w_up);
   CHECK_NULL(w_down);
-  CHECK_NULL(y);
-  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
   TRY(check_k(H, "H"));
   TRY(check_k(I, "I"));
   if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
@@ -667,6 +688,7 @@ nvfp4_status moe_shared_expert_ffn(const void *x, int64_t T, int64_t H, int64_t 
   CHECK_ALIGN(w_down);
   CHECK_ALIGN(y);
   TRY(check_workspace(workspace, workspace_bytes, moe_shared_expert_ffn_workspace_size(T, H, I)));
+  if (T == 0) return NVFP4_OK;   // nothing to compute
   Carver c(workspace);
   const SharedWs ws = carve_shared(c, T, H, I);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
@@ -703,13 +725,15 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
                                    void *y, nvfp4_dtype y_dtype, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
-  CHECK_NULL(x);
-  CHECK_NULL(topk_ids);
-  CHECK_NULL(topk_weights);
-  CHECK_NULL(expert_offsets);
-  CHECK_NULL(sorted_pairs);
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(x);
+    CHECK_NULL(topk_ids);
+    CHECK_NULL(topk_weights);
+    CHECK_NULL(expert_offsets);
+    CHECK_NULL(sorted_pairs);
+    CHECK_NULL(y);
+  }
   CHECK_NULL(w);
-  CHECK_NULL(y);
   CHECK_NULL(w->gate_codes);
   CHECK_NULL(w->up_codes);
   CHECK_NULL(w->down_codes);
@@ -719,7 +743,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   CHECK_NULL(w->gate_global);
   CHECK_NULL(w->up_global);
   CHECK_NULL(w->down_global);
-  if (T < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 1", (long long)T);
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
   TRY(check_k(H, "H"));
   TRY(check_k(I, "I"));
   if (E < 1 || E > (1 << 20))
@@ -750,6 +774,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   CHECK_ALIGN(w->down_scales);
   TRY(check_workspace(workspace, workspace_bytes,
                       moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act)));
+  if (T == 0) return NVFP4_OK;   // nothing to compute (act_globals is not written)
   Carver c(workspace);
   const FfnWs ws = carve_ffn(c, T, H, I, E, k);
   const int64_t P = T * k;

@@ -566,3 +566,65 @@ def test_dense_mlp_decode_full_size(M):
     rows = list(range(min(M, 4)))
     ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=rows)
     assert_close_f32(to_np(y)[rows], ref, "dense mlp decode")
+
+
+# ---------------------------------------------------------------------------
+# empty batches: every batch call accepts T = 0 (routing sets its offsets to
+# zero, the rest computes nothing) and the calls after it are unaffected
+# ---------------------------------------------------------------------------
+
+def test_empty_batch():
+    E, H, I, k = 16, 256, 128, 4
+    say("empty batch", E, H, I, k)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    w = weights.synthetic_experts(E, H, I, 0, DEV)
+    x0 = torch.empty((0, H), dtype=torch.bfloat16, device=DEV)
+    ids0, wts0 = torch.empty((0, k), **i32), torch.empty((0, k), dtype=torch.float32, device=DEV)
+    pairs0 = torch.empty(0, **i32)
+    off = torch.full((E + 1,), 7, **i32)
+    native.moe_route_topk(torch.empty((0, E), dtype=torch.float32, device=DEV), k,
+                          out=(ids0, wts0, off, pairs0))
+    torch.cuda.synchronize()
+    assert torch.equal(off, torch.zeros_like(off))
+    rw = synth.router_matrix(E, H).to(DEV)
+    off.fill_(7)
+    native.moe_router_topk(x0, rw, k, out=(ids0, wts0, off, pairs0))
+    torch.cuda.synchronize()
+    assert torch.equal(off, torch.zeros_like(off))
+    off.fill_(7)
+    native.moe_permute_pairs(ids0, E, out=(off, pairs0))
+    torch.cuda.synchronize()
+    assert torch.equal(off, torch.zeros_like(off))
+    for act in (native.W4A16, native.W4A4):
+        y, _ = native.moe_grouped_nvfp4_ffn(x0, w, ids0, wts0, off, pairs0, k, act=act)
+        assert y.shape == (0, H)
+    sh = [t.to(DEV) for t in synth.shared_expert_weights(H, I)]
+    assert native.moe_shared_expert_ffn(x0, *sh).shape == (0, H)
+    yl, _ = native.nvfp4_linear(x0, w.gate_codes[0], w.gate_scales[0], w.gate_global[:1])
+    assert yl.shape == (0, I)
+    # the slot plan of an empty step fetches nothing and moves nothing
+    host = native.ExpertWeights(*[t.cpu().pin_memory() for t in (
+        w.gate_codes, w.gate_scales, w.gate_global, w.up_codes, w.up_scales, w.up_global,
+        w.down_codes, w.down_scales, w.down_global)])
+    cache = native.ExpertCache(host, 8, DEV)
+    first = torch.tensor([[1, 2, 3, 4]], **i32)
+    cache.plan_and_fetch(first)
+    torch.cuda.synchronize()
+    state = (cache.slot_of.clone(), cache.expert_of.clone(), cache.hand.clone())
+    cache.n_fetch.fill_(5)
+    cache.plan_and_fetch(ids0)
+    torch.cuda.synchronize()
+    assert int(cache.n_fetch.item()) == 0
+    assert all(torch.equal(a, b) for a, b in zip(state, (cache.slot_of, cache.expert_of,
+                                                          cache.hand)))
+    # a normal batch afterwards
+    T = 9
+    x = synth.activations(T, H, 3)
+    logits = synth.router_logits(T, E, 3)
+    rids, rwts = O.route_topk(logits, k)
+    ids, wts, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k)
+    assert np.array_equal(to_np(ids), rids)
+    y, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w, ids, wts, off, pairs, k,
+                                        out_dtype=torch.float32)
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rwts, oracle_experts(E, H, I, np.unique(rids), 0))
+    assert_close_f32(to_np(y), ref, "after an empty batch")

@@ -76,7 +76,9 @@ def test_linear_validation():
     ws = L.nvfp4_linear_workspace_size(4, 64, 96, 0)
     lin = lambda M, mat, act=0, y=FAKE, wsb=ws: L.nvfp4_linear(
         FAKE, M, ctypes.byref(mat), act, 0, None, y, 0, FAKE, wsb, None)
-    assert lin(0, m) == 1
+    assert lin(-1, m) == 1
+    assert L.nvfp4_linear(None, 0, ctypes.byref(m), 0, 0, None, None, 0, None, 0, None) == 0
+    assert lin(0, bad := native.Matrix(FAKE.value, FAKE.value, FAKE.value, 64, 80)) == 2
     bad = native.Matrix(FAKE.value, FAKE.value, FAKE.value, 64, 80)
     assert lin(4, bad) == 2
     assert lin(4, m, act=3) == 1
@@ -97,7 +99,8 @@ def test_route_validation():
     assert r(16, 8, 9) == 2
     assert r(16, 2048, 8) == 2
     assert r(16, 64, 33) == 2
-    assert r(0, 64, 8) == 1
+    assert r(-1, 64, 8) == 1
+    assert r(0, 2048, 8) == 2          # an empty batch still checks E and k
     assert r(16, 64, 8, logits=None) == 1
     assert r(16, 64, 8, logits=FAKE_MIS) == 3
     assert r((1 << 22), 64, 8) == 2
@@ -116,7 +119,11 @@ def test_ffn_validation():
     assert f(H=250) == 2
     assert f(I=100) == 2
     assert f(k=9) == 2
-    assert f(T=0) == 1
+    assert f(T=-1) == 1
+    # an empty batch: no launch, its arrays may be NULL, weights still checked
+    assert L.moe_grouped_nvfp4_ffn(None, 0, H, I, E, k, None, None, None, None, ctypes.byref(w),
+                                   0, 0, None, None, 0, None, 0, None) == 0
+    assert f(T=0, H=250) == 2
     assert f(wsb=ws - 1) == 4
     assert f(act=5) == 1
     assert f(ids=None) == 1 and "topk_ids" in _last()
@@ -142,7 +149,7 @@ def test_router_validation():
     assert r(E=2048) == 2
     assert r(k=0) == 2
     assert r(k=65) == 2
-    assert r(T=0) == 1
+    assert r(T=-1) == 1
     assert r(x=None) == 1 and "x" in _last()
     assert r(rw=None) == 1 and "router_w" in _last()
     assert r(ids=None) == 1
@@ -164,7 +171,9 @@ def test_shared_expert_validation():
         L.moe_shared_expert_ffn(x, T, H, I, wg, wu, wd, 0, y, dt, FAKE, wsb, None)
     assert f(H=100) == 2
     assert f(I=48) == 2
-    assert f(T=0) == 1
+    assert f(T=-1) == 1
+    assert f(T=0, x=None, y=None, wsb=0) == 0        # an empty batch: no launch
+    assert f(T=0, x=None, y=None, wg=None) == 1
     assert f(wg=None) == 1 and "w_gate" in _last()
     assert f(wd=None) == 1 and "w_down" in _last()
     assert f(y=None) == 1
@@ -184,7 +193,7 @@ def test_expert_cache_validation():
         ids, T, k, E, S, FAKE, FAKE, FAKE, FAKE, step, prot, FAKE, FAKE, FAKE, None)
     assert plan(E=2000) == 2
     assert plan(S=0) == 2
-    assert plan(T=0) == 1
+    assert plan(T=-1) == 1
     assert plan(step=0, prot=0) == 1
     assert plan(step=3, prot=4) == 1
     assert plan(ids=None) == 1
@@ -202,7 +211,7 @@ def test_expert_cache_validation():
     pp = lambda T=4, E=64, k=2, ids=FAKE: L.moe_permute_pairs(ids, T, E, k, FAKE, FAKE, None)
     assert pp(E=0) == 2
     assert pp(k=33) == 2
-    assert pp(T=0) == 1
+    assert pp(T=-1) == 1
     assert pp(ids=FAKE_MIS) == 3
 
 
