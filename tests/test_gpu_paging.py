@@ -194,14 +194,16 @@ def _weights_for(k, T, rng):
     return w / w.sum(axis=1, keepdims=True)
 
 
-@pytest.mark.parametrize("T,H,I,E,k,S,pool,protect,bitexact", [
-    (4, 512, 256, 128, 8, 64, 32, True, True),     # decode rows: the plan is the same for any E
-    (1, 1024, 512, 64, 4, 16, 8, True, True),
-    (300, 256, 256, 64, 2, 64, 64, False, True),   # tiles, S = E: the same plan
-    (200, 256, 128, 64, 2, 40, 40, False, False),  # tiles, S < E: another plan, the tolerance
+@pytest.mark.parametrize("T,H,I,E,k,S,pool,protect,bitexact,act", [
+    (4, 512, 256, 128, 8, 64, 32, True, True, native.W4A16),   # decode rows: same plan for any E
+    (1, 1024, 512, 64, 4, 16, 8, True, True, native.W4A16),
+    (300, 256, 256, 64, 2, 64, 64, False, True, native.W4A16),   # tiles, S = E: the same plan
+    (200, 256, 128, 64, 2, 40, 40, False, False, native.W4A16),  # tiles, S < E: the tolerance
+    (300, 256, 256, 64, 2, 64, 64, False, True, native.W4A4),    # online activation globals
+    (200, 256, 128, 64, 2, 40, 40, False, False, native.W4A4),
 ])
-def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact):
-    say("paged ffn", T, H, I, E, k, S, pool, protect)
+def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact, act):
+    say("paged ffn", T, H, I, E, k, S, pool, protect, act)
     rng = np.random.default_rng(T + H + E)
     w_dev = weights.synthetic_experts(E, H, I, 5, DEV)
     cache = native.ExpertCache(_host_copy(w_dev), S, DEV)
@@ -213,17 +215,19 @@ def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact):
         ids = torch.from_numpy(ids_np).to(DEV)
         wts = torch.from_numpy(wts_np).to(DEV)
         off, pairs = native.moe_permute_pairs(ids, E)
-        y_res, _ = native.moe_grouped_nvfp4_ffn(xd, w_dev, ids, wts, off, pairs, k,
-                                                out_dtype=torch.float32)
+        y_res, g_res = native.moe_grouped_nvfp4_ffn(xd, w_dev, ids, wts, off, pairs, k, act=act,
+                                                    out_dtype=torch.float32)
         slot_ids = cache.plan_and_fetch(ids, protect_previous=protect)
         assert int(cache.n_fetch.item()) >= 0, f"step {step}: the step's experts did not fit"
         off_s, pairs_s = native.moe_permute_pairs(slot_ids, S)
-        y_pag, _ = native.moe_grouped_nvfp4_ffn(xd, cache.pool, slot_ids, wts, off_s, pairs_s, k,
-                                                out_dtype=torch.float32)
+        y_pag, g_pag = native.moe_grouped_nvfp4_ffn(xd, cache.pool, slot_ids, wts, off_s, pairs_s,
+                                                    k, act=act, out_dtype=torch.float32)
         torch.cuda.synchronize()
         # the slot ids name the same experts
         eo = cache.expert_of.cpu().numpy()
         assert np.array_equal(eo[slot_ids.cpu().numpy()], ids_np), f"step {step}"
+        if act == native.W4A4:   # the online globals are maxima over the same values
+            assert torch.equal(g_pag, g_res), f"step {step}"
         if bitexact:
             assert torch.equal(y_pag, y_res), f"step {step}"
         else:
@@ -231,7 +235,10 @@ def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact):
                              f"paged vs resident, step {step}")
         if step in (1, 5):
             w_ref = LazyOracleExperts(E, H, I, np.unique(ids_np), 5)
-            ref, _ = O.moe_ffn(x.float().numpy(), ids_np, wts_np, w_ref)
+            if act == native.W4A4:
+                ref, _ = O.moe_ffn(x.float().numpy(), ids_np, wts_np, w_ref, act_quant=True)
+            else:
+                ref, _ = O.moe_ffn(x.float().numpy(), ids_np, wts_np, w_ref)
             assert_close_f32(y_pag.cpu().numpy(), ref, f"paged vs oracle, step {step}")
     _check_pool(cache)
 
