@@ -24,6 +24,9 @@ What it computes, in plain numpy (fp64 unless a step is defined in fp32):
   with a routing-weighted combine and the BF16 shared expert (Eider page,
   "Qwen3.8 Flash Next": all 512 MoE experts; "Performance": prefill batches
   up to 512 prompt tokens so routed expert weights are reused).
+* The slot plan of expert paging (``expert_slot_plan``): which experts a
+  bounded device pool keeps, fetches and evicts in a step (Eider page, "Why
+  Eider exists"); the FFN on the pool is the FFN above.
 
 Readings where the pages are silent (each is a plain reading that the rest
 of the pages supports): element 2i sits in the low nibble; scales are row-major
@@ -509,3 +512,85 @@ def dense_mlp(x, gate, up, down):
     ids = np.zeros((t, 1), dtype=np.int32)
     y, _ = moe_ffn(x, ids, np.ones((t, 1)), w)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Expert paging: the slot plan of a bounded expert pool
+# ---------------------------------------------------------------------------
+
+class SlotState:
+    """A pool of S expert slots in front of E experts (Eider page, "Why Eider
+    exists": selected experts resident in bounded page pools, the rest paged
+    in).  slot_of[e] is expert e's slot or -1; expert_of[s] is slot s's
+    expert or -1; last_use[s] is the stamp of the last step that used slot s;
+    hand is the clock hand (the slot the next search starts from)."""
+
+    def __init__(self, E, S):
+        self.E, self.S = E, S
+        self.slot_of = [-1] * E
+        self.expert_of = [-1] * S
+        self.last_use = [0] * S
+        self.hand = 0
+
+    def copy(self):
+        c = SlotState(self.E, self.S)
+        c.slot_of, c.expert_of = list(self.slot_of), list(self.expert_of)
+        c.last_use, c.hand = list(self.last_use), self.hand
+        return c
+
+
+def expert_slot_plan(state, ids, step, protect_from):
+    """One step's slot plan (the pages give no policy; this is the reading
+    the library implements, a clock-order replacement):
+
+    1. The needed experts are the distinct ids of the step (ids outside
+       0..E-1 are ignored).  A needed expert that is resident keeps its slot
+       and the slot's stamp becomes `step`.
+    2. The missing needed experts, in ascending expert order, take the free
+       slots met walking from the hand: a slot is free when it is empty, or
+       when its expert is not needed now and its stamp is below
+       protect_from (a step whose FFN may still run passes its own stamp).
+       Missing expert i takes free slot i, evicting that slot's expert, and
+       the slot gets the stamp `step`; the hand moves just past the last
+       slot taken.
+    3. If the free slots are fewer than the missing experts, nothing of step
+       2 happens and n_fetch is -1.
+
+    Returns (slot_ids [T, k] int32: each pair's slot, or 0 for an ignored
+    id or an expert left without a slot; the fetch list [(expert, slot)];
+    n_fetch).  `state` is updated in place."""
+    E, S = state.E, state.S
+    ids = np.asarray(ids)
+    needed = sorted({int(e) for e in ids.ravel() if 0 <= e < E})
+    missing = []
+    for e in needed:
+        s = state.slot_of[e]
+        if s >= 0:
+            state.last_use[s] = step
+        else:
+            missing.append(e)
+    needed_set = set(needed)
+    free = []
+    for r in range(S):
+        s = (state.hand + r) % S
+        e = state.expert_of[s]
+        if e < 0 or (e not in needed_set and state.last_use[s] < protect_from):
+            free.append(s)
+    fetch = []
+    if len(missing) <= len(free):
+        for e, s in zip(missing, free):
+            old = state.expert_of[s]
+            if old >= 0:
+                state.slot_of[old] = -1
+            state.slot_of[e], state.expert_of[s], state.last_use[s] = s, e, step
+            fetch.append((e, s))
+        if missing:
+            state.hand = (free[len(missing) - 1] + 1) % S
+        n_fetch = len(missing)
+    else:
+        n_fetch = -1
+    slot_ids = np.zeros(ids.shape, np.int32)
+    for idx, e in np.ndenumerate(ids):
+        if 0 <= e < E and state.slot_of[int(e)] >= 0:
+            slot_ids[idx] = state.slot_of[int(e)]
+    return slot_ids, fetch, n_fetch
