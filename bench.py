@@ -634,6 +634,15 @@ def paged_main(args):
     busy = nf > 0
     fetch_gbs = (float(nf[busy].sum()) * expert_bytes / (fetch_us[busy].sum() * 1e-6) / 1e9
                  if busy.any() else None)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on a sample of routing batch 0: its slot plan from an
+        # empty pool and the FFN rows of the sampled tokens; the paged output
+        # of the same batch is checked against it
+        paged_step(0)
+        torch.cuda.synchronize()
+        cpu = paged_cpu_baseline(args, wl, S, zipf, y)
     out = {
         "metric": "NVFP4 MoE FFN with expert paging: tokens/s",
         "value": round(T / (ms_paged * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
@@ -659,9 +668,44 @@ def paged_main(args):
                      "frac": None if fetch_gbs is None else round(fetch_gbs / HOST_LINK_PEAK_GBS, 4),
                      "traffic": None,
                      "alg_per_unit": f"{expert_bytes} bytes per fetched expert"},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def paged_cpu_baseline(args, wl, S, zipf, y_gpu):
+    """The oracle (as it stands) on a bounded sample of a paged step: the slot
+    plan of routing batch 0 and the FFN rows of a token sample, timed on the
+    host; tokens/s.  Also the correctness gate for those rows."""
+    import numpy as np
+    import threadpoolctl
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import LazyOracleExperts
+    from oracle import nvfp4_oracle as O
+    from nvfp4_routed_expert_amd import synth
+
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    n_tok = args.cpu_tokens or min(T, 16)
+    tokens = list(range(0, T, max(1, T // n_tok)))[:n_tok]
+    xf = synth.activations(T, H).float().numpy()
+    logits = synth.router_logits(T, E, seed=0, zipf_s=zipf)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    rids, rw = O.route_topk(logits, k)
+    w_ref = LazyOracleExperts(E, H, I, np.unique(rids[tokens]), 0)   # offline quantisation
+    t0 = time.perf_counter()
+    O.expert_slot_plan(O.SlotState(E, S), rids, 1, 1)
+    ref, _ = O.moe_ffn(xf, rids, rw, w_ref, tokens=tokens)
+    dt = time.perf_counter() - t0
+    got = y_gpu.float().cpu().numpy()[tokens].astype(np.float64)
+    r = O.bf16_rne(ref)
+    return {"kind": "oracle", "cores": int(threads), "value": round(len(tokens) / dt, 3),
+            "unit": "tokens/s",
+            "sample": f"slot plan of one routing batch and the FFN of {len(tokens)} of {T} "
+                      f"tokens, fp64 numpy oracle, {dt:.2f} s",
+            "seconds": round(dt, 3),
+            "gate_rel_frob_vs_oracle": float(np.linalg.norm(got - r) / np.linalg.norm(r))}
 
 
 def copy_calibration():
