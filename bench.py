@@ -430,7 +430,9 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic",
+        # the decode row kernels multiply bf16 weights by bf16 activations
+        # (fp32 sums); the MFMA kernels multiply fp16 operands
+        "dtype": "bf16" if kname == "row_gemv_kernel" else "f16", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "act": wl.act,
                    "shared_expert": (f"bf16, intermediate {I}" if with_shared else None),
@@ -648,7 +650,8 @@ def paged_main(args):
         "value": round(T / (ms_paged * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_paged, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16", "data": "synthetic",
+        "dtype": "bf16" if gate_up_kernel(T, H, I, S, k, wl.act) == "row_gemv_kernel" else "f16",
+        "data": "synthetic",
         "config": {"workload": wl.name + "_paged", "tokens": T, "hidden": H,
                    "intermediate": I, "experts": E, "top_k": k, "slots": S,
                    "router_bias_zipf_s": zipf, "routing_batches": n_batches,
