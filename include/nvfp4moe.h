@@ -240,7 +240,11 @@ nvfp4_status moe_expert_cache_init(int32_t *slot_of, int32_t E, int32_t *expert_
  * experts' pairs (like ids outside 0..E-1) get slot 0, so a following FFN
  * reads valid memory but its result is wrong: check *n_fetch.  Requires
  * 1 <= E, S <= 1024, T >= 0, k >= 1, 1 <= step, protect_from <= step.  One
- * workgroup; integer-exact.
+ * workgroup; integer-exact.  step and protect_from are host values: a HIP
+ * graph that captures this call replays it with the stamps of the capture,
+ * so slots stamped by one replay are never free in the next (with
+ * protect_from = step); call it outside the graph, or capture one graph per
+ * step.
  */
 nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k,
                                    int32_t E, int32_t S, int32_t *slot_of,
