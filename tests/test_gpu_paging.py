@@ -190,6 +190,33 @@ def test_paged_ffn(T, H, I, E, k, S, pool, protect, bitexact, act):
     _check_pool(cache)
 
 
+@pytest.mark.parametrize("workload,S", [("moe_decode", 256), ("moe_prefill", 512)])
+def test_paged_ffn_full_size(workload, S):
+    """The full-size routed workloads (E = 512, H = 2048, I = 512) on a pool
+    of S slots over three routing batches: the paged output equals the
+    resident one bit for bit (decode rows at any S; the chunk's tiles with
+    S = E take the same plan), the pool equals the host pages."""
+    wl = synth.WORKLOADS[workload]
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    say("paged full size", workload, T, H, I, E, k, S)
+    w_dev = weights.synthetic_experts(E, H, I, 0, DEV)
+    cache = native.ExpertCache(_host_copy(w_dev), S, DEV)
+    x = synth.activations(T, H).to(DEV)
+    for b in range(3):
+        logits = torch.from_numpy(synth.router_logits(T, E, seed=b, zipf_s=wl.zipf_s)).to(DEV)
+        ids, wts, off, pairs = native.moe_route_topk(logits, k)
+        y_res, _ = native.moe_grouped_nvfp4_ffn(x, w_dev, ids, wts, off, pairs, k,
+                                                out_dtype=torch.float32)
+        slot_ids = cache.plan_and_fetch(ids)
+        off_s, pairs_s = native.moe_permute_pairs(slot_ids, S)
+        y_pag, _ = native.moe_grouped_nvfp4_ffn(x, cache.pool, slot_ids, wts, off_s, pairs_s, k,
+                                                out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert int(cache.n_fetch.item()) >= 0
+        assert torch.equal(y_pag, y_res), f"batch {b}"
+    _check_pool(cache)
+
+
 def test_paged_ffn_two_stream_pipeline():
     """The slot plan, fetch and pair order of step i on a side stream beside
     the FFN of step i-1 on the main stream (the previous step's experts
