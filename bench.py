@@ -81,6 +81,7 @@ def parse():
 # Sources each timed kernel is built from; a stored counter reading is used
 # only while these files are byte-identical to the ones it was taken on.
 KERNEL_SOURCES = {
+    "row_ffn_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
     "row_gemv_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
     "tile_gemm_kernel": ["tile_gemm.hip", "common.h", "kernels.h"],
     "grouped_gemm_kernel": ["gemm.hip", "common.h", "kernels.h"],
@@ -126,7 +127,8 @@ def gate_up_kernel(T, H, I, E, k, act):
     row_ok = lambda K: K in (256, 512, 1024) or (K % 32 == 0 and 2048 <= K <= 32768)
     if small:
         if act == "w4a16" and row_ok(H) and row_ok(I):
-            return "row_gemv_kernel"
+            # H = 2048 and I a multiple of 256: both projections in one launch
+            return "row_ffn_kernel" if H == 2048 and I % 256 == 0 else "row_gemv_kernel"
         return "grouped_gemv_kernel"
     return "tile_gemm_kernel" if H % 64 == 0 else "grouped_gemm_kernel"
 
@@ -262,6 +264,10 @@ def main():
     alg_flops = 6 * P * H * I + alg_extra_flops
     gateup_bytes = 2 * active * (nv_bytes(H * I) + 4) + T * H * 2
     gateup_flops = 4 * P * H * I
+    if gate_up_kernel(T, H, I, E, k, wl.act) == "row_ffn_kernel":
+        # the fused decode kernel streams the down matrices too
+        gateup_bytes = 3 * active * (nv_bytes(H * I) + 4) + T * H * 2
+        gateup_flops = 6 * P * H * I
     # MFMA-bound when the step's arithmetic intensity exceeds the ridge point
     prefill_mfma = alg_flops / alg_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
@@ -404,10 +410,14 @@ def main():
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     kname = gate_up_kernel(T, H, I, E, k, wl.act)
     roofline["traffic"] = stored_traffic(kname, wl.name)
-    roofline["kernel"] = kname + " (gate/up projection, SiLU*up epilogue)"
+    roofline["kernel"] = kname + (" (gate/up, SiLU*up, down: both projections)"
+                                  if kname == "row_ffn_kernel" else
+                                  " (gate/up projection, SiLU*up epilogue)")
     roofline["kernel_avg_us"] = round(stage_avg_us["gate_up"], 3)
     roofline["alg_per_launch"] = int(gateup_flops if prefill_mfma else gateup_bytes)
-    roofline["alg_units_per_launch"] = (f"{active} experts x 2 NVFP4 [{I},{H}] + x"
+    roofline["alg_units_per_launch"] = (f"{active} experts x 3 NVFP4 [{I},{H}] + x"
+                                        if kname == "row_ffn_kernel" and not prefill_mfma else
+                                        f"{active} experts x 2 NVFP4 [{I},{H}] + x"
                                         if not prefill_mfma else f"{P} pairs x 4*H*I flop")
     roofline["alg_bytes_per_launch"] = int(gateup_bytes)   # weights + x, for the traffic ratio
 
@@ -432,7 +442,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         # the decode row kernels multiply bf16 weights by bf16 activations
         # (fp32 sums); the MFMA kernels multiply fp16 operands
-        "dtype": "bf16" if kname == "row_gemv_kernel" else "f16", "data": "synthetic",
+        "dtype": "bf16" if kname.startswith("row_") else "f16", "data": "synthetic",
         "config": {"workload": wl.name, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "act": wl.act,
                    "shared_expert": (f"bf16, intermediate {I}" if with_shared else None),
@@ -650,7 +660,7 @@ def paged_main(args):
         "value": round(T / (ms_paged * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_paged, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if gate_up_kernel(T, H, I, S, k, wl.act) == "row_gemv_kernel" else "f16",
+        "dtype": "bf16" if gate_up_kernel(T, H, I, S, k, wl.act).startswith("row_") else "f16",
         "data": "synthetic",
         "config": {"workload": wl.name + "_paged", "tokens": T, "hidden": H,
                    "intermediate": I, "experts": E, "top_k": k, "slots": S,

@@ -204,7 +204,9 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.h = c.take<uint16_t>((size_t)(P * I));
   w.h16 = c.take<_Float16>((size_t)(P * I));
   w.hshift = c.take<int32_t>((size_t)P);
-  w.ypair = c.take<float>((size_t)(P * H));
+  // (the fused decode FFN keeps a partial row per pair and 256-column slice of I)
+  const int64_t ffn_parts = ffn_small(T, E, k) && row_ffn_supported((int)H, (int)I) ? I / 256 : 1;
+  w.ypair = c.take<float>((size_t)(P * H * (ffn_parts > 1 ? ffn_parts : 1)));
   w.mblocks = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
   w.n_mblocks = c.take<int32_t>(4);
   w.mblocks_down = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
@@ -874,6 +876,30 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   if (rows) {
     g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
     g.a_shift = nullptr;
+  }
+  // W4A16 decode with H = 2048: both projections in one launch
+  if (rows && row_ffn_supported((int)H, (int)I)) {
+    GemmArgs dd = {};
+    dd.b_codes[0] = w->down_codes;
+    dd.b_scales[0] = w->down_scales;
+    dd.b_global[0] = w->down_global;
+    dd.b_codes_estride = H * (I / 2);
+    dd.b_scales_estride = H * (I / 16);
+    dd.N = (int)H;
+    dd.K = (int)I;
+    dd.pair_weights = topk_weights;
+    mark_kernel(NVFP4_STAGE_GATE_UP, stream);
+    LAUNCH(launch_row_ffn(g, dd, sorted_pairs, topk_ids, k, (int)P, ws.ypair, stream),
+           "gate/up + down");
+    g_timed_launch = TimedLaunch{nullptr, nullptr};
+    mark(NVFP4_STAGE_H_PREP, false, stream);
+    mark(NVFP4_STAGE_H_PREP, true, stream);
+    mark(NVFP4_STAGE_DOWN, false, stream);
+    mark(NVFP4_STAGE_DOWN, true, stream);
+    mark_kernel(NVFP4_STAGE_COMBINE, stream);
+    LAUNCH(launch_ffn_combine(ws.ypair, (int)T, (int)H, (int)I, k, y, yt, stream), "combine");
+    g_timed_launch = TimedLaunch{nullptr, nullptr};
+    return NVFP4_OK;
   }
   mark_kernel(NVFP4_STAGE_GATE_UP, stream);
   if (rows)

@@ -219,6 +219,17 @@ hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pai
                            const int32_t *ids, int k, int n_pos, hipStream_t s,
                            bool h_by_pair = false);
 
+// Fused decode FFN (W4A16, H = 2048, I a multiple of 256): gate/up and down
+// in one launch (a workgroup per tile row and 256-column slice of I, h kept
+// in LDS), partial rows in ypart [P][I / 256][H] (fp32), then a combine
+// that adds each token's slots and slices in order into y.  g: the gate/up
+// arguments (A = bf16 x rows), d: the down arguments (pair weights set).
+bool row_ffn_supported(int H, int I);
+hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *sorted_pairs,
+                          const int32_t *ids, int k, int P, float *ypart, hipStream_t s);
+hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, void *y, OutType yt,
+                              hipStream_t s);
+
 // Token-major down projection for decode with the combine folded in: y[t] =
 // sum over slots j (in order) of w[t k + j] * g * (h[t k + j] . W_down[e]);
 // A = h rows in pair order (bf16), out = y.  Supported for K (= I) in

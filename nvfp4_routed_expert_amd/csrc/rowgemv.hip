@@ -482,6 +482,172 @@ hipError_t launch_down_sum(const GemmArgs &a, const int32_t *ids, int k, int T, 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Fused decode FFN: both projections in one launch (H = 2048)
+// ---------------------------------------------------------------------------
+//
+// One workgroup of 8 waves per (tile row pos, slice c of kFfnCols columns of
+// I): the slice's gate and up rows (32 + 32 per wave, whole 2048-wide rows
+// per load step as in row_gemv_kernel) give the slice of h, bf16-rounded
+// into LDS; the down rows' matching kFfnCols columns (8 lanes per row, 8
+// rows per load step, 256 rows per wave) are loaded before the barrier that
+// publishes h, and their dot products with the h slice give a partial output
+// row per (pair, slice), scaled by the down global and the routing weight.
+// ffn_combine_kernel adds the slices and the token's slots in a fixed order.
+// One launch streams all three matrices, so the down stream does not pay a
+// launch's ramp of its own.
+constexpr int kFfnCols = 256;
+constexpr int kFfnWaves = 8;
+constexpr int kXcds = 8;   // consecutive workgroups land on different XCDs
+
+__global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs g,
+                                                                 const GemmArgs d,
+                                                                 const Routing rt, int n_pos,
+                                                                 int n_c, float *ypart) {
+  __shared__ uint16_t h_lds[kFfnCols];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_items = n_pos * n_c;
+  const int per = (n_items + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int item = (blockIdx.x % kXcds) * per + slot;
+  if (slot >= per || item >= n_items) return;   // whole workgroup (uniform)
+  const int pos = item / n_c, c = item - pos * n_c;
+  const int pair = rt.sorted_pairs[pos];
+  const int e = rt.ids[pair];
+  const int token = pair / rt.k;
+  const int H = g.K, I = g.N;   // gate/up: [I, H]; down: [H, I]
+
+  // ---- gate / up: rows c * kFfnCols + 32 wave + 8 it + step, it = 0..3
+  const uint32_t gcode_row = (uint32_t)H / 2, gscale_row = (uint32_t)H / 16;
+  const uint8_t *gc[2], *gs[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    gc[m] = g.b_codes[m] + (int64_t)e * g.b_codes_estride + 16 * lane;
+    gs[m] = g.b_scales[m] + (int64_t)e * g.b_scales_estride + 2 * lane;
+  }
+  const int grow0 = c * kFfnCols + 32 * wave;
+  uint32_t a[16];
+  {
+    const uint16_t *src = reinterpret_cast<const uint16_t *>(g.A) + (int64_t)token * g.lda + 32 * lane;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(src + 8 * q);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[4 * q + j] = v[j];
+    }
+  }
+  u32x4 bq[2][kBatch][2];
+  uint32_t sq[2][kBatch][2];
+  auto load_gu = [&](int buf, int it) {
+#pragma unroll
+    for (int st = 0; st < kBatch; ++st) {
+      const uint32_t row = (uint32_t)(grow0 + 8 * it + st);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        bq[buf][st][m] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(gc[m] + row * gcode_row));
+        sq[buf][st][m] = *reinterpret_cast<const uint16_t *>(gs[m] + row * gscale_row);
+      }
+    }
+  };
+  const float gg = g.b_global[0][e], gu = g.b_global[1][e];
+  load_gu(0, 0);
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int cb = it & 1;
+    if (it < 3) load_gu(cb ^ 1, it + 1);
+    float part[2][kBatch];
+#pragma unroll
+    for (int st = 0; st < kBatch; ++st) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sq[cb][st][m], 1.0f, false);
+        uint32_t w[16];
+        decode32(bq[cb][st][m], w);
+        part[m][st] = dot32(w, a, sc[0], sc[1]);
+      }
+    }
+    const float G = reduce8<64>(part[0], lane) * gg;
+    const float U = reduce8<64>(part[1], lane) * gu;
+    if ((lane & 7) == 0)
+      h_lds[32 * wave + 8 * it + (lane >> 3)] =
+          (uint16_t)f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
+  }
+
+  // ---- down: rows 256 wave + 64 b + 8 st + lane / 8, columns c * kFfnCols +
+  // 32 (lane % 8) .. + 32
+  const int sub = lane >> 3, seg = lane & 7;
+  const uint32_t dcode_row = (uint32_t)I / 2, dscale_row = (uint32_t)I / 16;
+  const uint8_t *dc = d.b_codes[0] + (int64_t)e * d.b_codes_estride + c * (kFfnCols / 2) + 16 * seg;
+  const uint8_t *ds = d.b_scales[0] + (int64_t)e * d.b_scales_estride + c * (kFfnCols / 16) + 2 * seg;
+  const int drow0 = 256 * wave + sub;
+  u32x4 dq[2][kBatch];
+  uint32_t dsq[2][kBatch];
+  auto load_d = [&](int buf, int b) {
+#pragma unroll
+    for (int st = 0; st < kBatch; ++st) {
+      const uint32_t row = (uint32_t)(drow0 + 64 * b + 8 * st);
+      dq[buf][st] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(dc + row * dcode_row));
+      dsq[buf][st] = *reinterpret_cast<const uint16_t *>(ds + row * dscale_row);
+    }
+  };
+  load_d(0, 0);   // independent of h: in flight across the barrier
+  __syncthreads();
+  uint32_t ah[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    ah[j] = (uint32_t)h_lds[32 * seg + 2 * j] | ((uint32_t)h_lds[32 * seg + 2 * j + 1] << 16);
+  const float scale = d.b_global[0][e] * d.pair_weights[pair];
+  float *yrow = ypart + ((int64_t)pair * n_c + c) * H;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int cb = b & 1;
+    if (b < 3) load_d(cb ^ 1, b + 1);
+    float part[kBatch];
+#pragma unroll
+    for (int st = 0; st < kBatch; ++st) {
+      const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(dsq[cb][st], 1.0f, false);
+      uint32_t w[16];
+      decode32(dq[cb][st], w);
+      part[st] = dot32(w, ah, sc[0], sc[1]);
+    }
+    const float r = reduce8<8>(part, lane);
+    // lane holds step (lane & 7) of its 8-lane group (row sub = lane / 8)
+    yrow[256 * wave + 64 * b + 8 * (lane & 7) + sub] = r * scale;
+  }
+}
+
+// y[t] = sum over slots j (in order) of sum over slices c (in order) of
+// ypart[t k + j][c]: the token's k n_c partial rows are consecutive, so row
+// q = j n_c + c; four outputs per thread, eight rows' loads in flight.
+__global__ __launch_bounds__(256) void ffn_combine_kernel(const float *ypart, int64_t T, int64_t H,
+                                                          int k, int n_c, void *y, OutType yt) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= T * H) return;
+  const int64_t t = i / H, col = i - t * H;
+  const int n = k * n_c;
+  const float *base = ypart + t * n * H + col;
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int q0 = 0; q0 < n; q0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + u < n ? q0 + u : n - 1;   // (past the end: a valid row, not added)
+      v[u] = *reinterpret_cast<const f32x4 *>(base + (int64_t)q * H);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (q0 + u < n) acc += v[u];
+  }
+  if (yt == OutType::F32) {
+    *reinterpret_cast<f32x4 *>(static_cast<float *>(y) + i) = acc;
+  } else {
+    uint16_t *o = static_cast<uint16_t *>(y) + i;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = (uint16_t)f32_to_bf16_bits(acc[q]);
+  }
+}
+
 }  // namespace
 
 bool row_down_sum_supported(int K, int k) {
@@ -511,6 +677,29 @@ hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pai
   if (K == 256) return launch_cfg<8>(epi, a, info, n_pos, s);     // items of 64 rows
   if (K == 1024) return launch_cfg<32>(epi, a, info, n_pos, s);   // items of 16 rows
   return launch_cfg<64>(epi, a, info, n_pos, s);                  // items of 8 rows
+}
+
+bool row_ffn_supported(int H, int I) { return H == kSlice && I % kFfnCols == 0; }
+
+hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *sorted_pairs,
+                          const int32_t *ids, int k, int P, float *ypart, hipStream_t s) {
+  if (!row_ffn_supported(g.K, g.N) || d.K != g.N || d.N != g.K) return hipErrorInvalidValue;
+  const int n_c = g.N / kFfnCols;
+  const int64_t items = (int64_t)P * n_c;
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  const Routing rt{sorted_pairs, ids, k, false};
+  launch_kernel(row_ffn_kernel, dim3((unsigned)grid), dim3(64 * kFfnWaves), 0, s, g, d, rt, P, n_c,
+                ypart);
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, void *y, OutType yt,
+                              hipStream_t s) {
+  if (H % 4 != 0) return hipErrorInvalidValue;
+  const int64_t threads = ((int64_t)T * H + 3) / 4;
+  launch_kernel(ffn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                ypart, (int64_t)T, (int64_t)H, k, I / kFfnCols, y, yt);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4
