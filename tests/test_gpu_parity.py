@@ -327,7 +327,9 @@ def _moe_run(T, H, I, E, k, act=native.W4A16, zipf=None, seed=0, tokens=None,
 @pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (1, 64, 32, 4, 1), (12, 128, 96, 6, 6),
                                        (40, 512, 256, 16, 4), (24, 2048, 1024, 32, 4),
                                        (9, 5120, 512, 16, 2), (30, 4096, 256, 24, 6),
-                                       (3, 1024, 2048, 64, 8)])
+                                       (3, 1024, 2048, 64, 8),
+                                       # H = 2048 takes the fused decode kernel: 1 and 3 slices of I
+                                       (16, 2048, 256, 64, 8), (5, 2048, 768, 16, 3)])
 def test_moe_ffn_w4a16_small(T, H, I, E, k):
     say("moe w4a16 small", T, H, I, E, k)
     x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k)
