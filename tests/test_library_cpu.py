@@ -224,9 +224,12 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def test_bench_names_the_kernel_the_library_dispatches():
     """The bench's roofline line names the gate/up kernel by mirroring the
-    library's dispatch: decode-sized batches stream rows, larger ones tile."""
+    library's dispatch: decode-sized batches stream rows (both projections
+    in one kernel at H = 2048), larger ones tile."""
     import bench
-    assert bench.gate_up_kernel(16, 2048, 512, 512, 8, "w4a16") == "row_gemv_kernel"
+    assert bench.gate_up_kernel(16, 2048, 512, 512, 8, "w4a16") == "row_ffn_kernel"
+    assert bench.gate_up_kernel(16, 2048, 2080, 512, 8, "w4a16") == "row_gemv_kernel"
+    assert bench.gate_up_kernel(16, 1024, 512, 512, 8, "w4a16") == "row_gemv_kernel"
     assert bench.gate_up_kernel(512, 2048, 512, 512, 8, "w4a16") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(2048, 4096, 1536, 128, 8, "w4a4") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(1, 5120, 17408, 1, 1, "w4a16") == "row_gemv_kernel"
