@@ -461,6 +461,9 @@ def main():
         "pct_of_peak": round(100 * (value / (MFMA_F16_PEAK_TFLOPS if prefill_mfma
                                              else HBM_PEAK_GBS)), 2),
         "stage_us": {n: round(v, 3) for n, v in stage_avg_us.items()},
+        "stage_us_note": ("per-stage HIP events over an eager pass; a stage that runs no "
+                          "kernel at this shape (it is folded into another) reads the ~4.4 us "
+                          "of two back-to-back event packets, not work"),
         "wall_ms_timed_region": round(wall_ms, 3),
         "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
         "ffn_only": None if ffn_ms is None else {
