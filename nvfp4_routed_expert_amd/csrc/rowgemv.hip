@@ -497,7 +497,12 @@ hipError_t launch_down_sum(const GemmArgs &a, const int32_t *ids, int k, int T, 
 // One launch streams all three matrices, so the down stream does not pay a
 // launch's ramp of its own.
 constexpr int kFfnCols = 256;
-constexpr int kFfnWaves = 8;
+constexpr int kFfnWaves = 16;
+constexpr int kFfnGuRows = kFfnCols / kFfnWaves;        // gate (and up) rows per wave
+constexpr int kFfnGuIts = kFfnGuRows / kBatch;           // ... in batches of kBatch
+constexpr int kFfnDnRows = 2048 / kFfnWaves;             // down rows per wave (H = 2048)
+constexpr int kFfnDnBatches = kFfnDnRows / (8 * kBatch); // 8 rows per load step
+static_assert(kFfnGuIts >= 1 && kFfnDnBatches >= 1, "fused FFN split");
 constexpr int kXcds = 8;   // consecutive workgroups land on different XCDs
 
 __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs g,
@@ -525,7 +530,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
     gc[m] = g.b_codes[m] + (int64_t)e * g.b_codes_estride + 16 * lane;
     gs[m] = g.b_scales[m] + (int64_t)e * g.b_scales_estride + 2 * lane;
   }
-  const int grow0 = c * kFfnCols + 32 * wave;
+  const int grow0 = c * kFfnCols + kFfnGuRows * wave;
   uint32_t a[16];
   {
     const uint16_t *src = reinterpret_cast<const uint16_t *>(g.A) + (int64_t)token * g.lda + 32 * lane;
@@ -553,9 +558,9 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   const float gg = g.b_global[0][e], gu = g.b_global[1][e];
   load_gu(0, 0);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
+  for (int it = 0; it < kFfnGuIts; ++it) {
     const int cb = it & 1;
-    if (it < 3) load_gu(cb ^ 1, it + 1);
+    if (it < kFfnGuIts - 1) load_gu(cb ^ 1, it + 1);
     float part[2][kBatch];
 #pragma unroll
     for (int st = 0; st < kBatch; ++st) {
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
     const float G = reduce8<64>(part[0], lane) * gg;
     const float U = reduce8<64>(part[1], lane) * gu;
     if ((lane & 7) == 0)
-      h_lds[32 * wave + 8 * it + (lane >> 3)] =
+      h_lds[kFfnGuRows * wave + 8 * it + (lane >> 3)] =
           (uint16_t)f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
   }
 
@@ -580,7 +585,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   const uint32_t dcode_row = (uint32_t)I / 2, dscale_row = (uint32_t)I / 16;
   const uint8_t *dc = d.b_codes[0] + (int64_t)e * d.b_codes_estride + c * (kFfnCols / 2) + 16 * seg;
   const uint8_t *ds = d.b_scales[0] + (int64_t)e * d.b_scales_estride + c * (kFfnCols / 16) + 2 * seg;
-  const int drow0 = 256 * wave + sub;
+  const int drow0 = kFfnDnRows * wave + sub;
   u32x4 dq[2][kBatch];
   uint32_t dsq[2][kBatch];
   auto load_d = [&](int buf, int b) {
@@ -600,9 +605,9 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   const float scale = d.b_global[0][e] * d.pair_weights[pair];
   float *yrow = ypart + ((int64_t)pair * n_c + c) * H;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < kFfnDnBatches; ++b) {
     const int cb = b & 1;
-    if (b < 3) load_d(cb ^ 1, b + 1);
+    if (b < kFfnDnBatches - 1) load_d(cb ^ 1, b + 1);
     float part[kBatch];
 #pragma unroll
     for (int st = 0; st < kBatch; ++st) {
@@ -613,7 +618,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
     }
     const float r = reduce8<8>(part, lane);
     // lane holds step (lane & 7) of its 8-lane group (row sub = lane / 8)
-    yrow[256 * wave + 64 * b + 8 * (lane & 7) + sub] = r * scale;
+    yrow[kFfnDnRows * wave + 64 * b + 8 * (lane & 7) + sub] = r * scale;
   }
 }
 
