@@ -222,6 +222,15 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         native.lib()
 
 
+def test_ffn_workspace_holds_the_fused_decode_partials():
+    """The fused decode FFN keeps a partial output row per pair and
+    256-column slice of I (fp32): the workspace query covers them."""
+    L = native.lib()
+    for T, H, I, E, k in [(16, 2048, 512, 512, 8), (16, 2048, 1024, 64, 8), (4, 2048, 768, 16, 3)]:
+        need = T * k * (I // 256) * H * 4
+        assert L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, 0) >= need
+
+
 def test_bench_names_the_kernel_the_library_dispatches():
     """The bench's roofline line names the gate/up kernel by mirroring the
     library's dispatch: decode-sized batches stream rows (both projections
