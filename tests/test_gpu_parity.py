@@ -328,8 +328,10 @@ def _moe_run(T, H, I, E, k, act=native.W4A16, zipf=None, seed=0, tokens=None,
                                        (40, 512, 256, 16, 4), (24, 2048, 1024, 32, 4),
                                        (9, 5120, 512, 16, 2), (30, 4096, 256, 24, 6),
                                        (3, 1024, 2048, 64, 8),
-                                       # H = 2048 takes the fused decode kernel: 1 and 3 slices of I
-                                       (16, 2048, 256, 64, 8), (5, 2048, 768, 16, 3)])
+                                       # H = 2048 takes the fused decode kernel: 1 and 3 slices of I,
+                                       # one token with one slot, the largest decode batch (256 pairs)
+                                       (16, 2048, 256, 64, 8), (5, 2048, 768, 16, 3),
+                                       (1, 2048, 512, 512, 1), (32, 2048, 512, 512, 8)])
 def test_moe_ffn_w4a16_small(T, H, I, E, k):
     say("moe w4a16 small", T, H, I, E, k)
     x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k)
