@@ -111,7 +111,11 @@ typedef struct {
 
 /*
  * nvfp4_quantize: quantise x [rows, cols] (row stride ld_x elements, bf16 or
- * f32) to NVFP4.  codes [rows, cols/2], scales [rows, cols/16] are written.
+ * f32) to NVFP4.  codes [rows, cols/2], scales [rows, cols/16] are written,
+ * two 4-bit values per code byte (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model
+ * card, "Why Hugging Face shows 68B parameters and 8-bit precision": each
+ * packed byte holds two NVFP4 values); the same encoder serves the offline
+ * weights and the online W4A4 activations (same card, "What this model is").
  * mode COMPUTE: g = amax(|x|) / 2688 (1.0 for an all-zero x), written to
  * *global_scale.  mode GIVEN: g is read from *global_scale.
  * Per 16-block: s = E4M3_rne_saturate(amax_b / (6 g)); per element:
@@ -129,13 +133,21 @@ size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols);
 /*
  * nvfp4_dequantize: out [rows, cols] f32 = e2m1 * e4m3 * g, each element the
  * correctly rounded fp32 product (a debug and test aid; not on the hot path).
+ * The value of a packed NVFP4 element (Qwen3.8-Flash-Next-NVFP4-SSD-Stream
+ * model card, "Why Hugging Face shows 68B parameters and 8-bit precision").
+ * Errors: NULL or misaligned pointers, cols % 32 != 0.  out is caller-owned.
  */
 nvfp4_status nvfp4_dequantize(const nvfp4_matrix *w, float *out,
                               hipStream_t stream);
 
 /*
  * nvfp4_linear: y [M, N] = x [M, K] . W^T for an NVFP4 W [N, K], fp32
- * accumulation, y in bf16 (round-to-nearest-even) or f32.  x is bf16,
+ * accumulation, y in bf16 (round-to-nearest-even) or f32.  The dense NVFP4
+ * linear of the MLP weights (Eider page, "Qwen3.8 27B": NVFP4 for most MLP
+ * weights); W4A16 is the weight-only form (Qwen3.8-27B-nvfp4full-dflash2-
+ * NInfer model card, "Limits": NVFP4 parents quantised weight-only), W4A4
+ * the activation-quantised one (Qwen3.8-Flash-Next-NVFP4-SSD-Stream model
+ * card, "What this model is").  x is bf16,
  * row-major, contiguous.  act W4A4: x is first quantised to NVFP4 with one
  * tensor scale over all of x (mode COMPUTE writes it to *act_global, GIVEN
  * reads it), and the product uses the dequantised x.  act_global may be
@@ -150,7 +162,9 @@ size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K,
                                    nvfp4_act_mode act);
 
 /*
- * moe_route_topk: per token t of logits [T, E] (f32), the k experts with the
+ * moe_route_topk: the routing step in front of the routed experts (Eider
+ * page, "Qwen3.8 Flash Next": all 512 MoE experts of the model are served).
+ * Per token t of logits [T, E] (f32), the k experts with the
  * largest logits in descending order, equal logits going to the lower expert
  * index -> topk_ids [T, k] int32.  topk_weights [T, k] f32: with renormalize,
  * exp(l_j - l_max) / sum over the k chosen (top-k of softmax, renormalised);
@@ -172,6 +186,20 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E,
                             int32_t *sorted_pairs, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
 size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_route_workspace_init: makes a workspace ready for moe_route_topk and
+ * moe_router_topk by zeroing its first 32-bit word on `stream` (a one-
+ * wavefront kernel, no memset, so it may be captured into a graph).  Call it
+ * once after allocating a workspace, or whenever its contents are unknown
+ * (reused from another call, or a routing launch that did not finish);
+ * successive routing calls on one stream then keep it ready.  A workspace
+ * whose first word is not zero makes the one-launch decode routing skip its
+ * permutation (sorted_pairs and expert_offsets are left as they were).
+ * Errors: NULL or misaligned workspace, workspace_bytes < 4.
+ */
+nvfp4_status moe_route_workspace_init(void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /*
  * moe_router_topk: the router in front of moe_route_topk.  Logits
@@ -234,12 +262,18 @@ nvfp4_status moe_expert_cache_init(int32_t *slot_of, int32_t E, int32_t *expert_
  * taken in slot order from the clock hand on (empty slots count as free).
  * Writes slot_ids [T, k] (slot of each pair's expert), fetch [2 S] int32
  * (pairs {expert, slot} of the experts to copy), in ascending expert order, and
- * *n_fetch (device int32) = their number.  S must exceed the distinct experts
- * of a step (twice over while a previous step's FFN may still run); when the
- * free slots do not suffice, nothing moves, *n_fetch = -1, and the missing
- * experts' pairs (like ids outside 0..E-1) get slot 0, so a following FFN
- * reads valid memory but its result is wrong: check *n_fetch.  Requires
- * 1 <= E, S <= 1024, T >= 0, k >= 1, 1 <= step, protect_from <= step.  One
+ * *n_fetch (device int32) = their number.  max_fetch is the most experts the
+ * following moe_expert_cache_fetch will copy (pass the same value to both).
+ * S must exceed the distinct experts of a step (twice over while a previous
+ * step's FFN may still run).  A plan that does not fit (fewer free slots
+ * than missing experts, or more missing experts than max_fetch) moves
+ * nothing: *n_fetch = -1 (the device-side status of the step), the resident
+ * experts keep their slots and stamps, and the missing experts' pairs (like
+ * ids outside 0..E-1) get slot id -1.  Every later call drops such pairs
+ * (moe_permute_pairs leaves them out, moe_grouped_nvfp4_ffn gives them no
+ * contribution), so the step's output is the FFN over its placed pairs
+ * only, with no read outside the pool.  Requires 1 <= E, S <= 1024, T >= 0,
+ * k >= 1, 1 <= step, protect_from <= step, 0 <= max_fetch <= 1024.  One
  * workgroup; integer-exact.  step and protect_from are host values: a HIP
  * graph that captures this call replays it with the stamps of the capture,
  * so slots stamped by one replay are never free in the next (with
@@ -250,12 +284,13 @@ nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k
                                    int32_t E, int32_t S, int32_t *slot_of,
                                    int32_t *expert_of, uint32_t *last_use,
                                    int32_t *hand, uint32_t step, uint32_t protect_from,
-                                   int32_t *slot_ids, int32_t *fetch, int32_t *n_fetch,
-                                   hipStream_t stream);
+                                   int32_t max_fetch, int32_t *slot_ids, int32_t *fetch,
+                                   int32_t *n_fetch, hipStream_t stream);
 
 /*
  * moe_expert_cache_fetch: copies the first *n_fetch experts of fetch (from
- * moe_expert_cache_plan; at most max_fetch) from host_w (E experts, pinned
+ * moe_expert_cache_plan with the same max_fetch; nothing when *n_fetch is -1)
+ * from host_w (E experts, pinned
  * host memory) into their slots of pool (S experts, device memory, written
  * by this call): codes, scales and globals of gate, up and down.  H, I as
  * in moe_grouped_nvfp4_ffn.  Every host_w array must be pinned host memory
@@ -273,9 +308,14 @@ nvfp4_status moe_expert_cache_fetch(const nvfp4_expert_weights *host_w,
 /*
  * moe_permute_pairs: moe_route_topk's expert offsets [E+1] and sorted pairs
  * [T*k] for given ids [T, k] (stable: pairs of one expert in ascending
- * order).  Same limits as moe_route_topk.  Every id must lie in 0..E-1 (as
- * the ids moe_route_topk and moe_expert_cache_plan write always do); other
- * ids are not checked and may lead outside the arrays.
+ * order), the pair order of a step on the expert pool (Eider page, "Why
+ * Eider exists": selected experts resident in bounded page pools).  Same
+ * limits as moe_route_topk.  The kept ids of one token must be distinct (as
+ * the ids of moe_route_topk and the slot ids of moe_expert_cache_plan are);
+ * this is not checked, and repeated ids leave the pair order undefined.  An id
+ * outside 0..E-1 drops its pair: it takes
+ * no position, offsets[E] counts the kept pairs only, and the positions
+ * offsets[E] .. T*k-1 of sorted_pairs are set to -1.
  */
 nvfp4_status moe_permute_pairs(const int32_t *topk_ids, int64_t T, int32_t E, int32_t k,
                                int32_t *expert_offsets, int32_t *sorted_pairs,
@@ -304,7 +344,12 @@ nvfp4_status moe_shared_expert_ffn(const void *x, int64_t T, int64_t H, int64_t 
 size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I);
 
 /*
- * moe_grouped_nvfp4_ffn: routed-expert gated FFN.  For each pair p = t*k + j
+ * moe_grouped_nvfp4_ffn: routed-expert gated FFN, a grouped GEMV in decode
+ * and an expert-grouped GEMM over prefill chunks (Eider page, "Performance":
+ * prefill takes up to 512 prompt tokens per iteration so that the routed
+ * expert weights are reused; the routed experts are NVFP4 W4A4 in the
+ * Flash-Next checkpoint: Qwen3.8-Flash-Next-NVFP4-SSD-Stream model card,
+ * "What this model is").  For each pair p = t*k + j
  * routed to expert e = topk_ids[p] (moe_route_topk's ids / weights / offsets /
  * sorted_pairs, which must be consistent with each other):
  *   h_p = bf16_rne( silu(g_gate[e] x_t D_gate[e]^T) * (g_up[e] x_t D_up[e]^T) )
@@ -315,6 +360,15 @@ size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I);
  * and down products; act_globals[0..1] = {g_x, g_h} are written (COMPUTE) or
  * read (GIVEN).  act_globals may be NULL for W4A16.
  * Requires H % 32 == 0, I % 32 == 0, 1 <= k <= E, T >= 0.
+ * Dropped pairs: a pair whose id lies outside 0..E-1 (a slot id of -1 from a
+ * failed moe_expert_cache_plan, or a pair that another device's experts
+ * serve) contributes nothing: y_t sums only the token's kept pairs (0 when
+ * it has none), and in W4A4 g_h is taken over the kept pairs only.  The
+ * offsets and sorted pairs must then come from moe_permute_pairs on the
+ * same ids (it leaves dropped pairs out).
+ * workspace: moe_grouped_nvfp4_ffn_workspace_size bytes (device, 16-byte
+ * aligned), scratch only; its contents after the call are unspecified
+ * except as moe_grouped_nvfp4_ffn_debug_h describes.
  */
 nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H,
                                    int64_t I, int32_t E, int32_t k,
@@ -331,6 +385,24 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H,
 size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I,
                                             int32_t E, int32_t k,
                                             nvfp4_act_mode act);
+
+/*
+ * moe_grouped_nvfp4_ffn_debug_h: a test aid (not part of the computation)
+ * for checking h element by element where it decides an integer: its bf16
+ * rounding and, in W4A4, its NVFP4 codes (Qwen3.8-Flash-Next-NVFP4-SSD-
+ * Stream model card, "What this model is": W4A4 routed experts).  For a
+ * moe_grouped_nvfp4_ffn call with these arguments, made on the calling
+ * thread, *h_offset receives the byte offset in its workspace of h in bf16
+ * and *hq_offset that of h's W4A4 operand (fp16 values e2m1 * e4m3 of the
+ * quantised h, without g_h); both are [T*k, I] row-major with row pos
+ * holding pair sorted_pairs[pos] (rows past the kept pairs are
+ * unspecified).  Returns a bit mask of what the call leaves there: 1 = the
+ * bf16 h, 2 = the W4A4 operand; 0 when the call keeps h elsewhere (the
+ * decode row kernels).  Either pointer may be NULL.
+ */
+int moe_grouped_nvfp4_ffn_debug_h(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                                  nvfp4_act_mode act, nvfp4_global_mode act_global_mode,
+                                  size_t *h_offset, size_t *hq_offset);
 
 /*
  * Profiling aid (not part of the computation).  While a non-NULL array is

@@ -441,6 +441,18 @@ size_t moe_route_topk_workspace_size(int64_t T, int32_t E, int32_t k) {
   return 256;   // word 0: the ticket counter of the one-launch decode routing
 }
 
+nvfp4_status moe_route_workspace_init(void *workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(workspace);
+  CHECK_ALIGN(workspace);
+  if (workspace_bytes < sizeof(uint32_t))
+    return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs at least 4",
+                workspace_bytes);
+  LAUNCH(launch_ticket_reset(static_cast<uint32_t *>(workspace), stream), "workspace init");
+  return NVFP4_OK;
+}
+
 nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
                             int renormalize, int32_t *topk_ids, float *topk_weights,
                             int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
@@ -559,8 +571,8 @@ nvfp4_status moe_expert_cache_init(int32_t *slot_of, int32_t E, int32_t *expert_
 nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
                                    int32_t S, int32_t *slot_of, int32_t *expert_of,
                                    uint32_t *last_use, int32_t *hand, uint32_t step,
-                                   uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
-                                   int32_t *n_fetch, hipStream_t stream) {
+                                   uint32_t protect_from, int32_t max_fetch, int32_t *slot_ids,
+                                   int32_t *fetch, int32_t *n_fetch, hipStream_t stream) {
   g_last_error[0] = 0;
   if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
     CHECK_NULL(topk_ids);
@@ -577,10 +589,12 @@ nvfp4_status moe_expert_cache_plan(const int32_t *topk_ids, int64_t T, int32_t k
   if (T < 0 || k < 1) return fail(NVFP4_ERR_INVALID_ARGUMENT, "need T >= 0 and k >= 1");
   if (step < 1 || protect_from > step)
     return fail(NVFP4_ERR_INVALID_ARGUMENT, "need 1 <= step and protect_from <= step");
+  if (max_fetch < 0 || max_fetch > 1024)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "max_fetch = %d outside 0..1024", (int)max_fetch);
   const int64_t P = T * (int64_t)k;
   if (P > (int64_t)1 << 24) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "T*k too large");
   LAUNCH(launch_cache_plan(topk_ids, (int)P, E, S, slot_of, expert_of, last_use, hand, step,
-                           protect_from, slot_ids, fetch, n_fetch, stream),
+                           protect_from, max_fetch, slot_ids, fetch, n_fetch, stream),
          "cache plan");
   return NVFP4_OK;
 }
@@ -717,6 +731,31 @@ size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I, int
   Carver c(nullptr);
   carve_ffn(c, T, H, I, E, k);
   return c.used;
+}
+
+int moe_grouped_nvfp4_ffn_debug_h(int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                                  nvfp4_act_mode act, nvfp4_global_mode act_global_mode,
+                                  size_t *h_offset, size_t *hq_offset) {
+  if (h_offset) *h_offset = 0;
+  if (hq_offset) *hq_offset = 0;
+  if (T < 1 || H < 1 || I < 1 || E < 1 || k < 1 || k > E) return 0;
+  // the offsets of carve_ffn's h and h16 regions
+  Carver c(nullptr);
+  c.take<_Float16>((size_t)(T * H));
+  c.take<int32_t>((size_t)T);
+  const size_t h_at = c.used;
+  c.take<uint16_t>((size_t)(T * k * I));
+  const size_t hq_at = c.used;
+  if (h_offset) *h_offset = h_at;
+  if (hq_offset) *hq_offset = hq_at;
+  // which of them the call writes, by the dispatch of moe_grouped_nvfp4_ffn
+  const bool small = ffn_small(T, E, k);
+  if (act != NVFP4_W4A4) return small ? 0 : 1;   // (the row paths keep h elsewhere)
+  const bool given = act_global_mode == NVFP4_GLOBAL_GIVEN;
+  const FfnPlans plans = ffn_plans(T, H, I, E, k);
+  const bool h_fused = given && !small && !g_separate_h_quant && tile_gemm_supported((int)H) &&
+                       plans.gate_up.ksplit == 1;
+  return h_fused ? 2 : 3;
 }
 
 nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t I, int32_t E,
@@ -897,7 +936,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     mark(NVFP4_STAGE_DOWN, false, stream);
     mark(NVFP4_STAGE_DOWN, true, stream);
     mark_kernel(NVFP4_STAGE_COMBINE, stream);
-    LAUNCH(launch_ffn_combine(ws.ypair, (int)T, (int)H, (int)I, k, y, yt, stream), "combine");
+    LAUNCH(launch_ffn_combine(ws.ypair, (int)T, (int)H, (int)I, k, topk_ids, E, y, yt, stream),
+           "combine");
     g_timed_launch = TimedLaunch{nullptr, nullptr};
     return NVFP4_OK;
   }
@@ -955,6 +995,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.out_type = OutType::F32;
   d.pair_weights = topk_weights;
   d.sorted_pairs = sorted_pairs;
+  d.n_experts = E;
   d.partial = ws.split;
   d.partial_rows = P;
   mark_kernel(NVFP4_STAGE_DOWN, stream);
@@ -984,7 +1025,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     return NVFP4_OK;
   }
   mark_kernel(NVFP4_STAGE_COMBINE, stream);
-  LAUNCH(launch_combine(ws.ypair, T, H, k, y, yt, stream), "combine");
+  LAUNCH(launch_combine(ws.ypair, T, H, k, topk_ids, E, y, yt, stream), "combine");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   return NVFP4_OK;
 }

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void cache_init_kernel(int32_t *slot_of, int E
 
 __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
     const int32_t *ids, int P, int E, int S, int32_t *slot_of, int32_t *expert_of,
-    uint32_t *last_use, int32_t *hand, uint32_t step, uint32_t protect_from, int32_t *slot_ids,
-    int32_t *fetch, int32_t *n_fetch) {
+    uint32_t *last_use, int32_t *hand, uint32_t step, uint32_t protect_from, int max_fetch,
+    int32_t *slot_ids, int32_t *fetch, int32_t *n_fetch) {
   __shared__ uint8_t need[kPlanThreads];
   __shared__ int32_t miss_list[kPlanThreads];
   __shared__ int32_t victim_list[kPlanThreads];
@@ -96,9 +96,10 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
   if (is_free) victim_list[frank] = slot;
   __syncthreads();
 
-  // not enough free slots: nothing moves, *n_fetch = -1, and the missing
-  // experts' pairs go to slot 0 (valid memory, wrong values)
-  const bool fits = n_miss <= n_free;
+  // not enough free slots (or more misses than the fetch will copy): nothing
+  // moves, *n_fetch = -1, and the missing experts' pairs get slot -1, which
+  // every later call drops (the FFN gives them no contribution)
+  const bool fits = n_miss <= n_free && n_miss <= max_fetch;
   // missing expert i takes free slot i
   if (fits && tid < n_miss) {
     const int e = miss_list[tid], s = victim_list[tid];
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(kPlanThreads) void cache_plan_kernel(
   for (int p = tid; p < P; p += kPlanThreads) {
     const int e = ids[p];
     const int s = (unsigned)e < (unsigned)E ? slot_of[e] : -1;
-    slot_ids[p] = (unsigned)s < (unsigned)S ? s : 0;   // (ids outside 0..E-1, or a failed plan: slot 0)
+    slot_ids[p] = (unsigned)s < (unsigned)S ? s : -1;   // (ids outside 0..E-1, or a failed plan: -1)
   }
 }
 
@@ -181,11 +182,12 @@ hipError_t launch_cache_init(int32_t *slot_of, int E, int32_t *expert_of, uint32
 
 hipError_t launch_cache_plan(const int32_t *ids, int P, int E, int S, int32_t *slot_of,
                              int32_t *expert_of, uint32_t *last_use, int32_t *hand, uint32_t step,
-                             uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
-                             int32_t *n_fetch, hipStream_t s) {
+                             uint32_t protect_from, int max_fetch, int32_t *slot_ids,
+                             int32_t *fetch, int32_t *n_fetch, hipStream_t s) {
   if (E > kPlanThreads || S > kPlanThreads) return hipErrorInvalidValue;
   launch_kernel(cache_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, ids, P, E, S, slot_of,
-                expert_of, last_use, hand, step, protect_from, slot_ids, fetch, n_fetch);
+                expert_of, last_use, hand, step, protect_from, max_fetch, slot_ids, fetch,
+                n_fetch);
   return hipGetLastError();
 }
 

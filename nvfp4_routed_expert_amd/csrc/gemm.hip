@@ -312,16 +312,22 @@ __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_
   if (t0 == 0) xshift[r] = s;
 }
 
+// A dropped slot (id outside 0..E-1: its Y row was never written) is not
+// added; a token without kept slots gets 0.
 __global__ __launch_bounds__(256) void combine_kernel(const float *ypair, int64_t T, int64_t H,
-                                                      int k, void *y, OutType t) {
+                                                      int k, const int32_t *ids, int E, void *y,
+                                                      OutType t) {
   const int64_t groups = T * (H / 4);
   for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups;
        g += (int64_t)gridDim.x * 256) {
     const int64_t tok = g / (H / 4), c = (g - tok * (H / 4)) * 4;
-    f32x4 s = *reinterpret_cast<const f32x4 *>(ypair + (tok * k) * H + c);
-    for (int j = 1; j < k; ++j) {
+    f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+    bool any = false;
+    for (int j = 0; j < k; ++j) {
+      if ((unsigned)ids[tok * k + j] >= (unsigned)E) continue;
       const f32x4 v = *reinterpret_cast<const f32x4 *>(ypair + (tok * k + j) * H + c);
-      s += v;
+      s = any ? s + v : v;
+      any = true;
     }
     if (t == OutType::F32) {
       *reinterpret_cast<f32x4 *>(static_cast<float *>(y) + tok * H + c) = s;
@@ -373,13 +379,13 @@ hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x1
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k, void *y,
-                          OutType t, hipStream_t s) {
+hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k, const int32_t *ids,
+                          int E, void *y, OutType t, hipStream_t s) {
   int64_t blocks = (T * (H / 4) + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (blocks < 1) blocks = 1;
-  launch_kernel(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ypair, T, H, k,
-                     y, t);
+  launch_kernel(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, ypair, T, H, k, ids, E,
+                y, t);
   return hipGetLastError();
 }
 

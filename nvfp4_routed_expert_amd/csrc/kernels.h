@@ -85,6 +85,7 @@ struct LogitSrc {
 // zero uint32 in the caller's workspace (left zero on return); with it,
 // decode-sized batches (route_decode_supported) route in one launch.
 bool route_decode_supported(int64_t T, int E, int k);
+hipError_t launch_ticket_reset(uint32_t *ticket, hipStream_t s);
 hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         uint32_t *ticket, hipStream_t s);
@@ -130,8 +131,8 @@ hipError_t launch_cache_init(int32_t *slot_of, int E, int32_t *expert_of, uint32
                              int32_t *hand, int S, hipStream_t s);
 hipError_t launch_cache_plan(const int32_t *ids, int P, int E, int S, int32_t *slot_of,
                              int32_t *expert_of, uint32_t *last_use, int32_t *hand, uint32_t step,
-                             uint32_t protect_from, int32_t *slot_ids, int32_t *fetch,
-                             int32_t *n_fetch, hipStream_t s);
+                             uint32_t protect_from, int max_fetch, int32_t *slot_ids,
+                             int32_t *fetch, int32_t *n_fetch, hipStream_t s);
 hipError_t launch_cache_fetch(const ExpertPtrs &host, const ExpertPtrs &pool, int64_t H,
                               int64_t I, const int32_t *fetch, const int32_t *n_fetch,
                               int max_fetch, hipStream_t s);
@@ -172,6 +173,7 @@ struct GemmArgs {
   const float *h_quant_g;
   const float *pair_weights;      // DOWN: routing weight of pair p
   const int32_t *sorted_pairs;    // DOWN: pair of each tile row
+  int n_experts;                  // E: ids outside 0..E-1 mark dropped pairs
   // split K (tile GEMM): raw fp32 sums of part kz at partial[kz][pos][col]
   // (SWIGLU: gate columns 0..N-1, up columns N..2N-1); partial_rows = rows
   // per part
@@ -227,8 +229,8 @@ hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pai
 bool row_ffn_supported(int H, int I);
 hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *sorted_pairs,
                           const int32_t *ids, int k, int P, float *ypart, hipStream_t s);
-hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, void *y, OutType yt,
-                              hipStream_t s);
+hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, const int32_t *ids,
+                              int E, void *y, OutType yt, hipStream_t s);
 
 // Token-major down projection for decode with the combine folded in: y[t] =
 // sum over slots j (in order) of w[t k + j] * g * (h[t k + j] . W_down[e]);
@@ -253,8 +255,9 @@ hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
                            int32_t *n_mblocks, int bm2, int4 *mblocks2, int32_t *n_mblocks2,
                            uint32_t *zero, int zero_words, hipStream_t s);
 
-// y[t] = sum_j Y[t*k + j], j ascending, fp32 -> out type.
-hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k,
-                          void *y, OutType t, hipStream_t s);
+// y[t] = sum_j Y[t*k + j] over the kept slots (ids[t*k + j] in 0..E-1),
+// j ascending, fp32 -> out type.
+hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k, const int32_t *ids,
+                          int E, void *y, OutType t, hipStream_t s);
 
 }  // namespace nvfp4

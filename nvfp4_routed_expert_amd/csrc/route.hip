@@ -298,6 +298,22 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
   return x;
 }
 
+// Pairs whose id lies outside 0..E-1 are dropped: they take no position, the
+// expert offsets count only the kept pairs (offsets[E] = kept), and the
+// positions kept .. P-1 of sorted_pairs hold -1.
+
+// Sum of the per-wave totals of a workgroup scan (read after its barrier).
+__device__ __forceinline__ int64_t block_total(const int32_t *wave_tot, int nwaves) {
+  int64_t total = 0;
+  for (int w = 0; w < nwaves; ++w) total += wave_tot[w];
+  return total;
+}
+
+// -1 into positions kept .. P-1 of sorted_pairs (the workgroup's threads).
+__device__ __forceinline__ void fill_dropped(int32_t *sorted_pairs, int64_t kept, int64_t P) {
+  for (int64_t q = kept + threadIdx.x; q < P; q += blockDim.x) sorted_pairs[q] = -1;
+}
+
 // One-chunk case (T <= 32 W tokens): no separate counting pass.  The pairs
 // set their token bits; then one wave per expert turns the expert's W words
 // into running popcounts with a wave scan (the expert's total comes with
@@ -321,12 +337,12 @@ __device__ void permute_block_one_chunk(const int32_t *ids, int64_t T, int E, in
 #pragma unroll
     for (int u = 0; u < kBatchIds; ++u) {
       const int64_t p = p0 + (int64_t)u * nthr;
-      e8[u] = p < P ? ids[p] : 0;
+      e8[u] = p < P ? ids[p] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatchIds; ++u) {
       const int64_t p = p0 + (int64_t)u * nthr;
-      if (p < P) {
+      if (p < P && (unsigned)e8[u] < (unsigned)E) {   // (other ids: dropped pairs)
         const int64_t t = p / k;
         atomicOr(&bitmap[e8[u] * W + (int)(t >> 5)], 1u << (t & 31));
       }
@@ -378,20 +394,22 @@ __device__ void permute_block_one_chunk(const int32_t *ids, int64_t T, int E, in
         run += cnt[e];
       }
     }
-    if (tid == 0) offsets[E] = (int32_t)P;
   }
+  const int64_t kept = block_total(L.wave_tot, nwaves);
+  if (tid == 0) offsets[E] = (int32_t)kept;
+  fill_dropped(sorted_pairs, kept, P);
   __syncthreads();
   for (int64_t p0 = tid; p0 < P; p0 += (int64_t)nthr * kBatchIds) {
     int e8[kBatchIds];
 #pragma unroll
     for (int u = 0; u < kBatchIds; ++u) {
       const int64_t p = p0 + (int64_t)u * nthr;
-      e8[u] = p < P ? ids[p] : 0;
+      e8[u] = p < P ? ids[p] : -1;
     }
 #pragma unroll
     for (int u = 0; u < kBatchIds; ++u) {
       const int64_t p = p0 + (int64_t)u * nthr;
-      if (p < P) {
+      if (p < P && (unsigned)e8[u] < (unsigned)E) {
         const int e = e8[u];
         const int64_t t = p / k;
         const int w = (int)(t >> 5);
@@ -417,7 +435,10 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
 
   for (int e = tid; e < E; e += nthr) { cnt[e] = 0; base[e] = 0; }
   __syncthreads();
-  for (int64_t p = tid; p < P; p += nthr) atomicAdd(&cnt[ids[p]], 1);
+  for (int64_t p = tid; p < P; p += nthr) {
+    const int e = ids[p];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);   // (other ids: dropped pairs)
+  }
   __syncthreads();
 
   // exclusive scan of cnt over E <= 1024 experts: thread tid owns the ept
@@ -442,8 +463,10 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
         run += cnt[e];
       }
     }
-    if (tid == 0) offsets[E] = (int32_t)P;
   }
+  const int64_t kept = block_total(wave_tot, nthr >> 6);
+  if (tid == 0) offsets[E] = (int32_t)kept;
+  fill_dropped(sorted_pairs, kept, P);
   __syncthreads();
 
   const int64_t chunk_tokens = (int64_t)W * 32;
@@ -452,8 +475,10 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
     for (int i = tid; i < E * W; i += nthr) bitmap[i] = 0u;
     __syncthreads();
     for (int64_t p = t0 * k + tid; p < t1 * k; p += nthr) {
+      const int e = ids[p];
+      if ((unsigned)e >= (unsigned)E) continue;   // dropped pair
       const int64_t tl = p / k - t0;
-      atomicOr(&bitmap[ids[p] * W + (int)(tl >> 5)], 1u << (tl & 31));
+      atomicOr(&bitmap[e * W + (int)(tl >> 5)], 1u << (tl & 31));
     }
     __syncthreads();
     for (int e = tid; e < E; e += nthr) {
@@ -467,6 +492,7 @@ __device__ void permute_block(const int32_t *ids, int64_t T, int E, int k, int W
     __syncthreads();
     for (int64_t p = t0 * k + tid; p < t1 * k; p += nthr) {
       const int e = ids[p];
+      if ((unsigned)e >= (unsigned)E) continue;   // dropped pair
       const int64_t tl = p / k - t0;
       const int w = (int)(tl >> 5);
       const uint32_t below = bitmap[e * W + w] & ((1u << (tl & 31)) - 1u);
@@ -509,6 +535,7 @@ __global__ __launch_bounds__(kSplitThreads) void permute_split_kernel(
   __shared__ int32_t own_cnt[kSplitMaxEpw];
   __shared__ int32_t own_off[kSplitMaxEpw];
   __shared__ int32_t wave_below[kSplitThreads / 64];
+  __shared__ int32_t kept_lds;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthr = blockDim.x, nwaves = nthr >> 6;
   const int e_lo = blockIdx.x * epw;
@@ -526,7 +553,8 @@ __global__ __launch_bounds__(kSplitThreads) void permute_split_kernel(
 #pragma unroll
     for (int u = 0; u < kBatchIds; ++u) {
       const int64_t p = p0 + (int64_t)u * nthr;
-      e8[u] = p < P ? ids[p] : E;
+      const int v = p < P ? ids[p] : E;
+      e8[u] = (unsigned)v < (unsigned)E ? v : E;   // (dropped pairs: above every expert)
     }
 #pragma unroll
     for (int u = 0; u < kBatchIds; ++u) {
@@ -565,9 +593,13 @@ __global__ __launch_bounds__(kSplitThreads) void permute_split_kernel(
       offsets[e_lo + ee] = run;
       run += own_cnt[ee];
     }
-    if (e_hi == E) offsets[E] = (int32_t)P;
+    if (e_hi == E) {   // the last group: every kept pair lies below its end
+      offsets[E] = run;
+      kept_lds = run;
+    }
   }
   __syncthreads();
+  if (e_hi == E) fill_dropped(sorted_pairs, kept_lds, P);
 
   // pass 2: own pairs to their positions
   for (int64_t p0 = tid; p0 < P; p0 += (int64_t)nthr * kBatchIds) {
@@ -581,7 +613,7 @@ __global__ __launch_bounds__(kSplitThreads) void permute_split_kernel(
     for (int u = 0; u < kBatchIds; ++u) {
       const int64_t p = p0 + (int64_t)u * nthr;
       const int e = e8[u];
-      if (e >= e_lo && e < e_hi) {
+      if (e >= e_lo && e < e_hi) {   // (a dropped pair's id never lies in 0..E-1)
         const int ee = e - e_lo;
         const int64_t t = p / k;
         const int w = (int)(t >> 5);
@@ -607,13 +639,15 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int P = (int)T * k;
   for (int e = tid; e < E; e += 256) cnt[e] = 0;
-  int my_e = 0;
+  __shared__ int32_t kept_lds;
+  int my_e = -1;   // -1: no pair, or a dropped one (id outside 0..E-1)
   if (tid < P) {
-    my_e = ids[tid];
+    const int v = ids[tid];
+    my_e = (unsigned)v < (unsigned)E ? v : -1;
     ids_lds[tid] = my_e;
   }
   __syncthreads();
-  if (tid < P) atomicAdd(&cnt[my_e], 1);
+  if (my_e >= 0) atomicAdd(&cnt[my_e], 1);
   __syncthreads();
   if (tid < 64) {   // exclusive scan: lane l owns experts l * per .. (l + 1) * per - 1
     const int per = (E + 63) / 64;
@@ -632,10 +666,14 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
         run += c;
       }
     }
-    if (lane == 0) offsets[E] = P;
+    if (lane == 63) {   // the last lane's run ends after every kept pair
+      offsets[E] = run;
+      kept_lds = run;
+    }
   }
   __syncthreads();
-  if (tid < P) {
+  if (tid >= kept_lds && tid < P) sorted_pairs[tid] = -1;
+  if (my_e >= 0) {
     int before = 0;
     for (int q = 0; q < tid; ++q) before += ids_lds[q] == my_e;
     sorted_pairs[cnt[my_e] + before] = tid;
@@ -765,7 +803,18 @@ int permute_words(int64_t T, int E) {
   return W;
 }
 
+// Zeroes the ticket word of a routing workspace (a kernel rather than a
+// memset, so the call may sit in a captured graph).
+__global__ __launch_bounds__(64) void ticket_reset_kernel(uint32_t *ticket) {
+  if (threadIdx.x == 0) *ticket = 0u;
+}
+
 }  // namespace
+
+hipError_t launch_ticket_reset(uint32_t *ticket, hipStream_t s) {
+  launch_kernel(ticket_reset_kernel, dim3(1), dim3(64), 0, s, ticket);
+  return hipGetLastError();
+}
 
 bool route_decode_supported(int64_t T, int E, int k) {
   return T * k <= kSmallPairs && E <= 512 && k <= 8;

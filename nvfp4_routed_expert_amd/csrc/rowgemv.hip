@@ -244,7 +244,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void row_gemv_kernel(const GemmA
     }
   };
   auto load_a = [&](const Geo &gm, uint32_t (&a)[16]) {
-    const int arow = EPI == Epi::SWIGLU ? gm.pair / rt.k : gm.pos;
+    const int arow = EPI == Epi::SWIGLU ? (gm.pair >= 0 ? gm.pair / rt.k : 0) : gm.pos;
     const uint16_t *src = reinterpret_cast<const uint16_t *>(p.A) + (int64_t)arow * p.lda + kc;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -259,7 +259,9 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void row_gemv_kernel(const GemmA
     const int pos = clamp(item) / groups;
     return rt.sorted_pairs ? rt.sorted_pairs[pos] : pos;
   };
-  auto expert_of = [&](int pair) { return rt.sorted_pairs ? rt.ids[pair] : 0; };
+  // (positions past the kept pairs hold -1: they stream expert 0's rows and
+  // write nothing)
+  auto expert_of = [&](int pair) { return rt.sorted_pairs && pair >= 0 ? rt.ids[pair] : 0; };
 
   // prologue: item u loaded; routing of u + U known, pair of u + 2U known
   int item = unit;
@@ -317,7 +319,7 @@ __global__ __launch_bounds__(WIDE ? 1024 : 256) void row_gemv_kernel(const GemmA
     else if constexpr (C::G == 16) idx = (lane >> 1) & 7;
     else idx = lane & 7;
     const int row = cur.r0 + idx * C::RPL + lane / LPR;
-    if (kw == 0 && (lane % C::DUP) == 0 && row < N) {
+    if (kw == 0 && (lane % C::DUP) == 0 && row < N && cur.pair >= 0) {
       if constexpr (EPI == Epi::SWIGLU) {
         const float G = r[0] * p.b_global[0][cur.e] * extra;
         const float U = r[1] * p.b_global[NMAT - 1][cur.e] * extra;
@@ -370,9 +372,13 @@ __global__ __launch_bounds__(256) void row_down_sum_kernel(const GemmArgs p, con
   const int r0 = (blockIdx.x - t * groups) * C::ROWS;
   const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
 
-  // the token's experts and routing weights, lane j holding slot j
-  const int my_e = lane < k ? ids[t * k + lane] : 0;
+  // the token's experts and routing weights, lane j holding slot j; a
+  // dropped slot (id outside 0..E-1) reads expert 0 and contributes zero
+  const int raw_e = lane < k ? ids[t * k + lane] : 0;
+  const bool my_keep = (unsigned)raw_e < (unsigned)p.n_experts;
+  const int my_e = my_keep ? raw_e : 0;
   const float my_w = lane < k ? p.pair_weights[t * k + lane] : 0.0f;
+  const uint64_t keep_mask = __builtin_amdgcn_ballot_w64(my_keep);
 
   const uint32_t last_code = (uint32_t)(N - 1) * code_row + kc / 2;
   const uint32_t last_scale = (uint32_t)(N - 1) * scale_row + kc / 16;
@@ -421,8 +427,14 @@ __global__ __launch_bounds__(256) void row_down_sum_kernel(const GemmArgs p, con
   }
   __syncthreads();
   if (wave == 0) {
-    float acc = slot_val[lane];
-    for (int j = 1; j < k; ++j) acc += slot_val[j * 64 + lane];
+    // kept slots in order j = 0 .. k-1 (the first kept one starts the sum)
+    float acc = 0.0f;
+    bool any = false;
+    for (int j = 0; j < k; ++j) {
+      if (!((keep_mask >> j) & 1ull)) continue;   // uniform
+      acc = any ? acc + slot_val[j * 64 + lane] : slot_val[j * 64 + lane];
+      any = true;
+    }
     int idx;
     if constexpr (C::G == 64) idx = lane >> 3;
     else if constexpr (C::G == 32) idx = (lane >> 2) & 7;
@@ -518,6 +530,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   if (slot >= per || item >= n_items) return;   // whole workgroup (uniform)
   const int pos = item / n_c, c = item - pos * n_c;
   const int pair = rt.sorted_pairs[pos];
+  if (pair < 0) return;   // past the kept pairs (dropped ones have no position)
   const int e = rt.ids[pair];
   const int token = pair / rt.k;
   const int H = g.K, I = g.N;   // gate/up: [I, H]; down: [H, I]
@@ -626,13 +639,19 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
 // ypart[t k + j][c]: the token's k n_c partial rows are consecutive, so row
 // q = j n_c + c; four outputs per thread, eight rows' loads in flight.
 __global__ __launch_bounds__(256) void ffn_combine_kernel(const float *ypart, int64_t T, int64_t H,
-                                                          int k, int n_c, void *y, OutType yt) {
+                                                          int k, int n_c, const int32_t *ids,
+                                                          int E, void *y, OutType yt) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= T * H) return;
   const int64_t t = i / H, col = i - t * H;
   const int n = k * n_c;
   const float *base = ypart + t * n * H + col;
+  // kept slots (ids in 0..E-1) as a bit mask; a dropped slot's rows were
+  // never written and are not added
+  uint32_t keep = 0;
+  for (int j = 0; j < k; ++j) keep |= ((unsigned)ids[t * k + j] < (unsigned)E ? 1u : 0u) << j;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  bool any = false;
   for (int q0 = 0; q0 < n; q0 += 8) {
     f32x4 v[8];
 #pragma unroll
@@ -641,8 +660,13 @@ __global__ __launch_bounds__(256) void ffn_combine_kernel(const float *ypart, in
       v[u] = *reinterpret_cast<const f32x4 *>(base + (int64_t)q * H);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (q0 + u < n) acc += v[u];
+    for (int u = 0; u < 8; ++u) {
+      const int q = q0 + u;
+      if (q < n && ((keep >> (q / n_c)) & 1u)) {
+        acc = any ? acc + v[u] : v[u];
+        any = true;
+      }
+    }
   }
   if (yt == OutType::F32) {
     *reinterpret_cast<f32x4 *>(static_cast<float *>(y) + i) = acc;
@@ -698,12 +722,12 @@ hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *s
   return hipGetLastError();
 }
 
-hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, void *y, OutType yt,
-                              hipStream_t s) {
-  if (H % 4 != 0) return hipErrorInvalidValue;
+hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, const int32_t *ids,
+                              int E, void *y, OutType yt, hipStream_t s) {
+  if (H % 4 != 0 || k > 32) return hipErrorInvalidValue;
   const int64_t threads = ((int64_t)T * H + 3) / 4;
   launch_kernel(ffn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                ypart, (int64_t)T, (int64_t)H, k, I / kFfnCols, y, yt);
+                ypart, (int64_t)T, (int64_t)H, k, I / kFfnCols, ids, E, y, yt);
   return hipGetLastError();
 }
 

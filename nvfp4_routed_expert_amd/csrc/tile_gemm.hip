@@ -438,7 +438,8 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const GemmArgs p, int
   const int64_t total = (int64_t)rows * N;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float amax = 0.0f;
-  if (idx < total) {
+  // (positions past the kept pairs hold pair -1: nothing to write)
+  if (idx < total && (!ids || p.sorted_pairs[idx / N] >= 0)) {
     const int pos = (int)(idx / N), col = (int)(idx - (int64_t)pos * N);
     const int e = ids ? ids[p.sorted_pairs[pos]] : 0;
     const float extra = p.extra_scale ? *p.extra_scale : 1.0f;

@@ -66,6 +66,7 @@ def lib():
             "moe_route_topk": (_i32, [_vp, _i64, _i32, _i32, ctypes.c_int, _vp, _vp, _vp, _vp,
                                       _vp, _sz, _vp]),
             "moe_route_topk_workspace_size": (_sz, [_i64, _i32, _i32]),
+            "moe_route_workspace_init": (_i32, [_vp, _sz, _vp]),
             "moe_router_topk": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, ctypes.c_int, _vp,
                                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
             "moe_router_topk_workspace_size": (_sz, [_i64, _i64, _i32, _i32]),
@@ -74,8 +75,8 @@ def lib():
             "moe_shared_expert_ffn_workspace_size": (_sz, [_i64, _i64, _i64]),
             "moe_expert_cache_init": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _vp]),
             "moe_expert_cache_plan": (_i32, [_vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
-                                             ctypes.c_uint32, ctypes.c_uint32, _vp, _vp, _vp,
-                                             _vp]),
+                                             ctypes.c_uint32, ctypes.c_uint32, _i32, _vp, _vp,
+                                             _vp, _vp]),
             "moe_expert_cache_fetch": (_i32, [ctypes.POINTER(ExpertWeightsC),
                                               ctypes.POINTER(ExpertWeightsC), _i64, _i64, _vp,
                                               _vp, _i32, _vp]),
@@ -84,6 +85,9 @@ def lib():
                                              _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
             "moe_grouped_nvfp4_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+            "moe_grouped_nvfp4_ffn_debug_h": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _i32,
+                                                             _i32, ctypes.POINTER(_sz),
+                                                             ctypes.POINTER(_sz)]),
             "nvfp4_set_ffn_stage_events": (None, [_vp]),
             "nvfp4_set_ffn_separate_h_quant": (None, [ctypes.c_int]),
             "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
@@ -103,12 +107,14 @@ FFN_STAGES = ("plan", "x_prep", "gate_up", "h_prep", "down", "combine")
 def exported_symbols():
     return ["nvfp4_quantize", "nvfp4_quantize_workspace_size", "nvfp4_dequantize",
             "nvfp4_linear", "nvfp4_linear_workspace_size", "moe_route_topk",
-            "moe_route_topk_workspace_size", "moe_router_topk", "moe_router_topk_workspace_size",
+            "moe_route_topk_workspace_size", "moe_route_workspace_init", "moe_router_topk",
+            "moe_router_topk_workspace_size",
             "moe_shared_expert_ffn", "moe_shared_expert_ffn_workspace_size",
             "moe_expert_cache_init", "moe_expert_cache_plan", "moe_expert_cache_fetch",
             "moe_permute_pairs",
             "moe_grouped_nvfp4_ffn",
-            "moe_grouped_nvfp4_ffn_workspace_size", "nvfp4_set_ffn_stage_events",
+            "moe_grouped_nvfp4_ffn_workspace_size", "moe_grouped_nvfp4_ffn_debug_h",
+            "nvfp4_set_ffn_stage_events",
             "nvfp4_set_ffn_separate_h_quant",
             "nvfp4_status_string", "nvfp4_last_error"]
 
@@ -207,11 +213,18 @@ def nvfp4_linear(x, codes, scales, g, act=W4A16, act_global=None,
     return y, ag
 
 
+def _init_route_workspace(ws):
+    _check(lib().moe_route_workspace_init(_ptr(ws), ws.numel(), _stream()))
+    return ws
+
+
 def route_workspace(T, E, k, device):
-    """A zeroed routing workspace; every call leaves it zeroed again, so one
-    workspace serves successive (not overlapping) calls on a stream."""
-    return torch.zeros(max(lib().moe_route_topk_workspace_size(T, E, k), 1), dtype=torch.uint8,
-                       device=device)
+    """A routing workspace made ready by moe_route_workspace_init (its ticket
+    word zeroed on the current stream); every call leaves it ready again, so
+    one workspace serves successive (not overlapping) calls on a stream."""
+    ws = torch.empty(max(lib().moe_route_topk_workspace_size(T, E, k), 4), dtype=torch.uint8,
+                     device=device)
+    return _init_route_workspace(ws)
 
 
 def moe_route_topk(logits, k, renormalize=True, out=None, workspace=None):
@@ -239,8 +252,9 @@ def moe_route_topk(logits, k, renormalize=True, out=None, workspace=None):
 def router_workspace(T, H, E, k, device):
     """A zeroed workspace for moe_router_topk (left with its first word zero
     by every call, as for the routing workspace)."""
-    return torch.zeros(max(lib().moe_router_topk_workspace_size(T, H, E, k), 1),
-                       dtype=torch.uint8, device=device)
+    ws = torch.empty(max(lib().moe_router_topk_workspace_size(T, H, E, k), 4),
+                     dtype=torch.uint8, device=device)
+    return _init_route_workspace(ws)
 
 
 def moe_router_topk(x, router_w, k, renormalize=True, bias=None, want_logits=False, out=None,
@@ -375,16 +389,20 @@ class ExpertCache:
         _check(lib().moe_expert_cache_plan(_ptr(topk_ids), T, k, self.E, self.S,
                                            _ptr(self.slot_of), _ptr(self.expert_of),
                                            _ptr(self.last_use), _ptr(self.hand), self.step_no,
-                                           protect, _ptr(slot_ids), _ptr(self.fetch),
-                                           _ptr(self.n_fetch), _stream()))
+                                           protect, self.max_fetch(T * k), _ptr(slot_ids),
+                                           _ptr(self.fetch), _ptr(self.n_fetch), _stream()))
         return slot_ids
+
+    def max_fetch(self, pairs):
+        """The most experts one step can fetch: min(slots, pairs)."""
+        return min(self.S, pairs)
 
     def fetch_planned(self, pairs):
         """Copy the experts the last plan() listed (pairs = T * k of that step)."""
         _check(lib().moe_expert_cache_fetch(ctypes.byref(self._host_c),
                                             ctypes.byref(self._pool_c), self.H, self.I,
                                             _ptr(self.fetch), _ptr(self.n_fetch),
-                                            min(self.S, pairs), _stream()))
+                                            self.max_fetch(pairs), _stream()))
 
     def plan_and_fetch(self, topk_ids, protect_previous=False, slot_ids=None):
         """plan() then fetch_planned(): slot ids [T, k], the pool filled."""
@@ -421,6 +439,25 @@ def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_ids, topk_weights, exp
                                    act, mode, _ptr(ag), _ptr(y), _dt(y.dtype), _ptr(ws),
                                    ws.numel(), _stream()))
     return y, ag
+
+
+def ffn_debug_h(workspace, T, H, I, E, k, act=W4A16, given=False):
+    """The h rows a moe_grouped_nvfp4_ffn call (same arguments, this thread)
+    left in `workspace`: (h_bf16 [T*k, I] as float32 or None, h_operand
+    [T*k, I] float32 (W4A4 e2m1*e4m3 values) or None), rows in expert-sorted
+    position order."""
+    ho, hq = _sz(), _sz()
+    mask = lib().moe_grouped_nvfp4_ffn_debug_h(T, H, I, E, k, act,
+                                               GLOBAL_GIVEN if given else GLOBAL_COMPUTE,
+                                               ctypes.byref(ho), ctypes.byref(hq))
+    P = T * k
+    raw = workspace.view(torch.uint8)
+    hb = hqv = None
+    if mask & 1:
+        hb = raw[ho.value: ho.value + 2 * P * I].view(torch.bfloat16).view(P, I).float()
+    if mask & 2:
+        hqv = raw[hq.value: hq.value + 2 * P * I].view(torch.float16).view(P, I).float()
+    return hb, hqv
 
 
 def set_ffn_separate_h_quant(separate):

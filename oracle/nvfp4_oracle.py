@@ -38,7 +38,12 @@ zero code is kept; quantisation uses the fp32 operation order written in
 bf16 before the down projection.  The pages fix no precision for forming h;
 besides the fp64 h, ``expert_h_fp32`` forms it with fp32 operations (the
 FFN's fp32 accumulation) for comparisons where h's bf16 rounding and NVFP4
-codes must be decided in the same precision on both sides.
+codes must be decided in the same precision on both sides.  Where a device
+computes h in fp32, ``expert_h_bound`` bounds its distance from the fp64 h
+and ``check_h_choices`` tells which bf16 values of h are then valid: the
+exact rounding, or either neighbour where the bound reaches the rounding
+boundary (several results are correct there); ``moe_ffn(h_given=...)``
+computes everything after h from such valid choices.
 """
 
 from __future__ import annotations
@@ -333,7 +338,9 @@ def permute(ids, num_experts):
     """Expert-sorted list of pairs.
 
     A pair is p = t*k + j (token t, slot j).  Pairs are ordered by expert,
-    then by token (a stable counting sort).  Returns
+    then by token (a stable counting sort).  A pair whose id lies outside
+    0..E-1 is dropped: it takes no position, offsets[E] counts the kept
+    pairs, and the positions after them hold -1.  Returns
     (offsets [E+1] int32 with offsets[e]..offsets[e+1] the rows of expert
     e, sorted_pairs [T*k] int32).
     """
@@ -341,13 +348,16 @@ def permute(ids, num_experts):
     t, k = ids.shape
     counts = np.zeros(num_experts, dtype=np.int64)
     for e in ids.reshape(-1):
-        counts[e] += 1
+        if 0 <= e < num_experts:
+            counts[e] += 1
     offsets = np.zeros(num_experts + 1, dtype=np.int64)
     offsets[1:] = np.cumsum(counts)
     fill = offsets[:-1].copy()
-    sorted_pairs = np.empty(t * k, dtype=np.int64)
+    sorted_pairs = np.full(t * k, -1, dtype=np.int64)
     for p in range(t * k):                     # p ascending => t ascending
         e = ids[p // k, p % k]
+        if not 0 <= e < num_experts:
+            continue
         sorted_pairs[fill[e]] = p
         fill[e] += 1
     return offsets.astype(np.int32), sorted_pairs.astype(np.int32)
@@ -412,6 +422,82 @@ def expert_h_fp32(xv_rows, g_x, w, e):
     return bf16_rne(h32.astype(np.float64))
 
 
+# ---------------------------------------------------------------------------
+# Where h decides an integer: the fp32 error of h and the valid roundings
+# ---------------------------------------------------------------------------
+
+U32 = 2.0 ** -24   # unit roundoff of fp32
+
+
+def bf16_bracket(v):
+    """The bf16 values lo <= v <= hi around each fp64 v (lo == hi when v is a
+    bf16 value).  bf16 keeps 8 significant bits: in the binade
+    [2**(e-1), 2**e) the spacing is 2**(e-8)."""
+    v = np.asarray(v, dtype=np.float64)
+    _, e = np.frexp(v)
+    q = np.exp2(np.maximum(e, -125) - 8.0)
+    lo = np.floor(v / q) * q
+    hi = np.where(lo == v, lo, lo + q)
+    return lo, hi
+
+
+def expert_h_bound(xv_rows, g_x, w, e, lam=8.0):
+    """h of expert e before its bf16 rounding, in fp64, and a bound on how far
+    an fp32 evaluation of the same definition can land from it.
+
+    xv_rows are the unscaled activation operand (the e2m1 * e4m3 blocks of
+    the quantised x with g_x, or the bf16 x itself with g_x = None); every
+    product p_i = xv_i * D_i is exact in fp32.  Reading of "within a few
+    fp32 ulps" for a K-term fp32 sum S = sum p_i: the rounding errors of
+    the additions behave as independent and the partial sums as random
+    walks (the products have random signs), so in any summation order
+    |fl32(S) - S| <= lam * u * sqrt(K) * ||p||_2  (u = 2**-24; with errors
+    uniform in [-u, u] relative to each partial sum the standard deviation
+    is about 0.4 u sqrt(K) ||p||_2, so lam = 8 keeps twenty of them; sums
+    of these few-bit products are often exact, so real errors sit far
+    lower).  The scale products and the SiLU * up step add a few more
+    roundings:
+      dG = |g| dS_g + 2 u |G|,  dU likewise,
+      dh = |silu'(G) U| dG + |silu(G)| dU + 8 u |h|.
+    Returns (h64 [n, I], dh [n, I])."""
+    xv = np.asarray(xv_rows, dtype=np.float64)
+    gx = 1.0 if g_x is None else float(np.float32(g_x))
+    dg = block_values(w.gate_codes[e], w.gate_scales[e])
+    du = block_values(w.up_codes[e], w.up_scales[e])
+    k = dg.shape[1]
+    cg = float(np.float32(w.gate_global[e])) * gx
+    cu = float(np.float32(w.up_global[e])) * gx
+    x2 = xv * xv
+    gate = (xv @ dg.T) * cg
+    up = (xv @ du.T) * cu
+    d_sg = lam * np.sqrt(k) * U32 * np.sqrt(x2 @ (dg * dg).T)
+    d_su = lam * np.sqrt(k) * U32 * np.sqrt(x2 @ (du * du).T)
+    d_gate = abs(cg) * d_sg + 2 * U32 * np.abs(gate)
+    d_up = abs(cu) * d_su + 2 * U32 * np.abs(up)
+    sig = 1.0 / (1.0 + np.exp(-gate))
+    h64 = gate * sig * up
+    dsilu = sig * (1.0 + gate * (1.0 - sig))
+    dh = np.abs(dsilu * up) * d_gate + np.abs(gate * sig) * d_up + 8 * U32 * np.abs(h64)
+    return h64, dh
+
+
+def check_h_choices(h64, dh, h_dev):
+    """Which bf16 values of h are valid results (the several-results-correct
+    reading for where h decides an integer).  Where h64 lies further than dh
+    from the midpoint of its two bf16 neighbours, only bf16_rne(h64) is
+    valid; within dh of it, either neighbour is (an fp32 evaluation can land
+    on either side).  Returns (ok, flagged, flips): boolean arrays of the
+    shape of h64 (ok: h_dev is a valid value; flagged: both neighbours are
+    valid there; flips: h_dev differs from bf16_rne(h64))."""
+    h64 = np.asarray(h64, dtype=np.float64)
+    h_dev = np.asarray(h_dev, dtype=np.float64)
+    lo, hi = bf16_bracket(h64)
+    rne = bf16_rne(h64)
+    flagged = (lo != hi) & (np.abs(h64 - 0.5 * (lo + hi)) <= np.asarray(dh, dtype=np.float64))
+    ok = (h_dev == rne) | (flagged & ((h_dev == lo) | (h_dev == hi)))
+    return ok, flagged, h_dev != rne
+
+
 def expert_down(h_rows, w, e):
     """g_down * h D_down^T for expert e (fp64)."""
     dd = block_values(w.down_codes[e], w.down_scales[e])
@@ -419,29 +505,39 @@ def expert_down(h_rows, w, e):
 
 
 def moe_ffn(x, ids, weights, w, act_quant=False, act_globals=None,
-            tokens=None, h_fp32=False):
+            tokens=None, h_fp32=False, h_given=None, with_bound=False):
     """Routed-expert FFN, fp64.
 
     y_t = sum_j weights[t, j] * down_e( h ),  e = ids[t, j], where
     h = bf16_rne(silu(gate_e(x_t)) * up_e(x_t)).  The experts are visited
-    one at a time, so only one expert is ever dense in memory.
+    one at a time, so only one expert is ever dense in memory.  A pair whose
+    id lies outside 0..E-1 is dropped: it contributes nothing to y (a token
+    without kept pairs gets 0) and takes no part in any tensor scale.
 
     W4A4 (act_quant): x is replaced by deq(quantize(x)) with one tensor scale
-    over all T rows, and h (over all T*k pairs) by deq(quantize(h)) with one
-    tensor scale over all pairs, before the down projection.
+    over all T rows, and h (over all kept pairs) by deq(quantize(h)) with one
+    tensor scale over those pairs, before the down projection.
     act_globals = (g_x, g_h) fixes those scales instead of computing them.
     tokens: compute only these output rows (W4A16, or W4A4 with both
     act_globals given, where the rows are independent).
     h_fp32: form h with expert_h_fp32 (fp32 gate/up values) instead of fp64;
     everything after h stays as above.
+    h_given: bf16 values [len(tokens), k, I] to use as h of the kept pairs
+    (a device's valid choices where h decides an integer; everything after h
+    is computed from them as above).
+    with_bound: also return info["h64"] (h before its bf16 rounding) and
+    info["h_bound"] (expert_h_bound's dh) for the kept pairs.
     Returns (y fp64 [T or len(tokens), H], info dict; info["h_bf16"] is h
-    before its W4A4 quantisation, info["h"] the h the down projection used).
+    before its W4A4 quantisation, info["h"] the h the down projection used,
+    info["kept"] the [n, k] mask of kept pairs).
     """
     x32 = np.asarray(x, dtype=np.float32)
     ids = np.asarray(ids)
     weights = np.asarray(weights, dtype=np.float64)
     t_all, hdim = x32.shape
     k = ids.shape[1]
+    n_exp = w.gate_codes.shape[0]
+    idim = w.gate_codes.shape[1]
     info = {}
     if tokens is None:
         tokens = np.arange(t_all)
@@ -460,28 +556,43 @@ def moe_ffn(x, ids, weights, w, act_quant=False, act_globals=None,
         x64 = x32.astype(np.float64)
         xv, xv_g = x64, None
 
-    # h for every requested (token, slot), expert by expert
+    # h for every requested (token, slot) of a kept pair, expert by expert
     sel_ids = ids[tokens]                                    # [n, k]
-    h = np.zeros((len(tokens), k, w.gate_codes.shape[1]), dtype=np.float64)
-    for e in np.unique(sel_ids):
+    kept = (sel_ids >= 0) & (sel_ids < n_exp)
+    experts = np.unique(sel_ids[kept])
+    h = np.zeros((len(tokens), k, idim), dtype=np.float64)
+    if with_bound:
+        h64 = np.zeros_like(h)
+        hb = np.zeros_like(h)
+    for e in experts:
         rows, slots = np.nonzero(sel_ids == e)
+        if with_bound:
+            h64[rows, slots], hb[rows, slots] = expert_h_bound(xv[tokens[rows]], xv_g, w, e)
+        if h_given is not None:
+            continue
         h[rows, slots] = (expert_h_fp32(xv[tokens[rows]], xv_g, w, e) if h_fp32
                           else expert_h(x64[tokens[rows]], w, e))
+    if h_given is not None:
+        h = np.where(kept[:, :, None], np.asarray(h_given, dtype=np.float64), 0.0)
+    if with_bound:
+        info["h64"], info["h_bound"] = h64, hb
     info["h_bf16"] = h.copy()
 
     if act_quant:
         g_h = None if act_globals is None else act_globals[1]
-        flat = h.reshape(-1, h.shape[-1])
-        hc, hs, g_h = quantize(flat.astype(np.float32), g_h)
-        h = dequantize(hc, hs, g_h).reshape(h.shape)
-        info["g_h"] = g_h
+        flat = h[kept]                                       # [kept pairs, I]
+        if flat.shape[0]:
+            hc, hs, g_h = quantize(flat.astype(np.float32), g_h)
+            h[kept] = dequantize(hc, hs, g_h)
+        info["g_h"] = np.float32(1.0) if g_h is None else np.float32(g_h)
 
     y = np.zeros((len(tokens), hdim), dtype=np.float64)
-    for e in np.unique(sel_ids):
+    for e in experts:
         rows, slots = np.nonzero(sel_ids == e)
         contrib = expert_down(h[rows, slots], w, e)
         np.add.at(y, rows, contrib * weights[tokens[rows], slots][:, None])
     info["h"] = h
+    info["kept"] = kept
     return y, info
 
 
@@ -539,7 +650,7 @@ class SlotState:
         return c
 
 
-def expert_slot_plan(state, ids, step, protect_from):
+def expert_slot_plan(state, ids, step, protect_from, max_fetch=None):
     """One step's slot plan (the pages give no policy; this is the reading
     the library implements, a clock-order replacement):
 
@@ -553,12 +664,13 @@ def expert_slot_plan(state, ids, step, protect_from):
        Missing expert i takes free slot i, evicting that slot's expert, and
        the slot gets the stamp `step`; the hand moves just past the last
        slot taken.
-    3. If the free slots are fewer than the missing experts, nothing of step
-       2 happens and n_fetch is -1.
+    3. If the free slots are fewer than the missing experts, or the missing
+       experts are more than max_fetch (the most one step's fetch copies;
+       None: no limit), nothing of step 2 happens and n_fetch is -1.
 
-    Returns (slot_ids [T, k] int32: each pair's slot, or 0 for an ignored
-    id or an expert left without a slot; the fetch list [(expert, slot)];
-    n_fetch).  `state` is updated in place."""
+    Returns (slot_ids [T, k] int32: each pair's slot, or -1 for an ignored
+    id or an expert left without a slot, so that later steps drop the pair;
+    the fetch list [(expert, slot)]; n_fetch).  `state` is updated in place."""
     E, S = state.E, state.S
     ids = np.asarray(ids)
     needed = sorted({int(e) for e in ids.ravel() if 0 <= e < E})
@@ -577,7 +689,7 @@ def expert_slot_plan(state, ids, step, protect_from):
         if e < 0 or (e not in needed_set and state.last_use[s] < protect_from):
             free.append(s)
     fetch = []
-    if len(missing) <= len(free):
+    if len(missing) <= len(free) and (max_fetch is None or len(missing) <= max_fetch):
         for e, s in zip(missing, free):
             old = state.expert_of[s]
             if old >= 0:
@@ -589,7 +701,7 @@ def expert_slot_plan(state, ids, step, protect_from):
         n_fetch = len(missing)
     else:
         n_fetch = -1
-    slot_ids = np.zeros(ids.shape, np.int32)
+    slot_ids = np.full(ids.shape, -1, np.int32)
     for idx, e in np.ndenumerate(ids):
         if 0 <= e < E and state.slot_of[int(e)] >= 0:
             slot_ids[idx] = state.slot_of[int(e)]

@@ -40,14 +40,15 @@ class DeviceSlots:
                                                          P(self.last_use), P(self.hand), S,
                                                          native._stream()))
 
-    def plan(self, ids_np, step, protect_from):
+    def plan(self, ids_np, step, protect_from, max_fetch=None):
         ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).to(DEV)
         T, k = ids.shape
         slot_ids = torch.full_like(ids, -9)
         P = native._ptr
+        mx = self.S if max_fetch is None else max_fetch
         native._check(native.lib().moe_expert_cache_plan(
             P(ids), T, k, self.E, self.S, P(self.slot_of), P(self.expert_of), P(self.last_use),
-            P(self.hand), step, protect_from, P(slot_ids), P(self.fetch), P(self.n_fetch),
+            P(self.hand), step, protect_from, mx, P(slot_ids), P(self.fetch), P(self.n_fetch),
             native._stream()))
         n = int(self.n_fetch.item())
         f = self.fetch.cpu().numpy()
@@ -86,12 +87,13 @@ def test_cache_plan_matches_policy_model(E, S, k, steps, pool, zipf):
     for step in range(1, steps + 1):
         T = int(rng.integers(1, 40))
         ids = _step_ids(rng, E, T, k, pool, zipf)
-        if step == 3:          # ids outside 0..E-1 are ignored and read slot 0
+        if step == 3:          # ids outside 0..E-1 are ignored and get slot -1
             ids[0, 0] = -1
             ids[-1, -1] = E
         protect = step - 1 if (step % 2 == 0 and step > 1) else step
-        got = dev.plan(ids, step, protect)
-        want = O.expert_slot_plan(ref, ids, step, protect)
+        max_fetch = S if step % 3 else max(1, S // 3)   # (a fetch limit below the misses fails)
+        got = dev.plan(ids, step, protect, max_fetch)
+        want = O.expert_slot_plan(ref, ids, step, protect, max_fetch)
         assert got[2] == want[2], f"step {step}: n_fetch {got[2]} != {want[2]}"
         assert got[1] == want[1], f"step {step}: fetch list"
         assert np.array_equal(got[0], want[0]), f"step {step}: slot ids"
@@ -269,6 +271,79 @@ def test_paged_ffn_two_stream_pipeline():
                                                 out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert torch.equal(outs[i], y_res), f"step {i}"
+
+
+@pytest.mark.parametrize("T,H,I,E,k,S,act", [
+    (4, 512, 256, 64, 4, 8, native.W4A16),      # decode row kernels
+    (4, 2048, 512, 64, 4, 8, native.W4A16),     # fused decode FFN
+    (4, 512, 256, 64, 4, 8, native.W4A4),       # decode GEMV, online globals
+    (300, 256, 256, 64, 2, 8, native.W4A16),    # tiles
+    (300, 256, 256, 64, 2, 8, native.W4A4),
+])
+def test_overfull_plan_drops_unplaced_pairs(T, H, I, E, k, S, act):
+    """A step whose experts do not fit the pool: the plan reports -1, moves
+    nothing, gives the missing experts' pairs slot id -1 and keeps the hits;
+    the FFN on the pool then equals, bit for bit, the resident FFN with those
+    pairs dropped (ids -1), tokens without a placed pair are exactly 0, and
+    the result matches the oracle with the same pairs dropped."""
+    say("over-full plan", T, H, I, E, k, S, act)
+    rng = np.random.default_rng(T + E + S)
+    w_dev = weights.synthetic_experts(E, H, I, 9, DEV)
+    cache = native.ExpertCache(_host_copy(w_dev), S, DEV)
+    resident = np.arange(S // 2)                       # step 1 makes these resident
+    warm = np.stack([rng.choice(resident, size=min(k, len(resident)), replace=False)
+                     for _ in range(T)]).astype(np.int32)
+    if warm.shape[1] < k:
+        warm = np.concatenate([warm, np.full((T, k - warm.shape[1]), -1, np.int32)], axis=1)
+    cache.plan_and_fetch(torch.from_numpy(warm).to(DEV))
+    torch.cuda.synchronize()
+    assert int(cache.n_fetch.item()) >= 0
+    # step 2: hits among the resident experts and more misses than free slots
+    misses = np.arange(20, 20 + S + 4)
+    ids_np = np.stack([rng.choice(np.concatenate([resident, misses]), size=k, replace=False)
+                       for _ in range(T)]).astype(np.int32)
+    m = len(misses)   # every miss needed (more than the free slots); token 0 has no placed pair
+    for t in range((m + k - 1) // k):
+        ids_np[t] = misses[(t * k + np.arange(k)) % m]
+    wts_np = _weights_for(k, T, rng)
+    before = (cache.slot_of.clone(), cache.expert_of.clone(), cache.hand.clone())
+    ids = torch.from_numpy(ids_np).to(DEV)
+    slot_ids = cache.plan_and_fetch(ids)
+    torch.cuda.synchronize()
+    assert int(cache.n_fetch.item()) == -1
+    assert all(torch.equal(a, b) for a, b in zip(before, (cache.slot_of, cache.expert_of,
+                                                          cache.hand)))
+    placed = np.isin(ids_np, resident)
+    sid = slot_ids.cpu().numpy()
+    assert np.all(sid[~placed] == -1)
+    assert np.array_equal(cache.expert_of.cpu().numpy()[sid[placed]], ids_np[placed])
+    x = synth.activations(T, H, 42)
+    xd = x.to(DEV)
+    wts = torch.from_numpy(wts_np).to(DEV)
+    off_s, pairs_s = native.moe_permute_pairs(slot_ids, S)
+    y_pag, g_pag = native.moe_grouped_nvfp4_ffn(xd, cache.pool, slot_ids, wts, off_s, pairs_s, k,
+                                                act=act, out_dtype=torch.float32)
+    ids_drop = np.where(placed, ids_np, -1).astype(np.int32)
+    idd = torch.from_numpy(ids_drop).to(DEV)
+    off, pairs = native.moe_permute_pairs(idd, E)
+    y_res, g_res = native.moe_grouped_nvfp4_ffn(xd, w_dev, idd, wts, off, pairs, k, act=act,
+                                                out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y = y_pag.cpu().numpy()
+    assert np.all(y[0] == 0.0)
+    if T * k <= 256:   # (the tile plan depends on the expert count: S != E)
+        assert torch.equal(y_pag, y_res)
+    if act == native.W4A4:
+        assert torch.equal(g_pag, g_res)
+    assert_close_f32(y, y_res.cpu().numpy().astype(np.float64), "over-full plan vs resident")
+    w_ref = LazyOracleExperts(E, H, I, np.unique(ids_np[placed]), 9)
+    ref, info = O.moe_ffn(x.float().numpy(), ids_drop, wts_np, w_ref,
+                          act_quant=act == native.W4A4)
+    if act == native.W4A16:
+        assert_close_f32(y, ref, "over-full plan vs oracle")
+    else:   # the scales over the kept pairs (g_h: up to a flip of the largest h)
+        g = g_pag.cpu().numpy()
+        assert g[0] == info["g_x"] and abs(g[1] / info["g_h"] - 1) <= 2 ** -7
 
 
 def test_fetch_rejects_pageable_host_memory():

@@ -14,7 +14,8 @@ import torch
 
 from nvfp4_routed_expert_amd import native, synth, weights
 from oracle import nvfp4_oracle as O
-from tests.helpers import LazyOracleExperts, assert_bf16_output, assert_close_f32
+from tests.helpers import (LazyOracleExperts, assert_bf16_output, assert_close_f32,
+                           check_device_h, rows_by_pair, spread_tokens)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -152,6 +153,32 @@ def test_route_workspace_reused_across_calls():
         assert np.array_equal(to_np(off), roff)
         assert np.array_equal(to_np(pairs), rpairs)
         assert int(to_np(ws[:4].view(torch.int32))[0]) == 0
+    # a workspace of unknown contents, made ready by moe_route_workspace_init
+    ws.fill_(0xFF)
+    native._init_route_workspace(ws)
+    logits = synth.router_logits(T, E, seed=7)
+    ids, w, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k, workspace=ws)
+    rids, _ = O.route_topk(logits, k)
+    roff, rpairs = O.permute(rids, E)
+    assert np.array_equal(to_np(off), roff) and np.array_equal(to_np(pairs), rpairs)
+
+
+@pytest.mark.parametrize("T,E,k", [(16, 64, 8), (37, 20, 3), (600, 64, 4), (300000, 2, 1),
+                                   (2048, 128, 8)])
+def test_permute_drops_ids_outside_the_experts(T, E, k):
+    """moe_permute_pairs on ids with dropped pairs (-1 and E): bit-exact with
+    the oracle's permutation (kept pairs only, -1 after them), on each of the
+    permutation kernels (one workgroup, split by expert, chunked)."""
+    say("permute with dropped pairs", T, E, k)
+    rng = np.random.default_rng(T + E)
+    # distinct experts per token, as routing and slot plans give
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    drop = rng.random((T, k)) < 0.2
+    ids[drop] = np.where(rng.random(int(drop.sum())) < 0.5, -1, E)
+    off, pairs = native.moe_permute_pairs(torch.from_numpy(ids).to(DEV), E)
+    roff, rpairs = O.permute(ids, E)
+    assert np.array_equal(to_np(off), roff)
+    assert np.array_equal(to_np(pairs), rpairs)
 
 
 # ---------------------------------------------------------------------------
@@ -328,12 +355,15 @@ def _moe_run(T, H, I, E, k, act=native.W4A16, zipf=None, seed=0, tokens=None,
                                        (40, 512, 256, 16, 4), (24, 2048, 1024, 32, 4),
                                        (9, 5120, 512, 16, 2), (30, 4096, 256, 24, 6),
                                        (3, 1024, 2048, 64, 8),
-                                       # H = 2048 takes the fused decode kernel: 1 and 3 slices of I,
+                                       # H = 2048 takes the fused decode kernel: 1 and 9 slices of I,
                                        # one token with one slot, the largest decode batch (256 pairs)
-                                       (16, 2048, 256, 64, 8), (5, 2048, 768, 16, 3),
+                                       (16, 2048, 256, 64, 8), (5, 2048, 2304, 16, 3),
                                        (1, 2048, 512, 512, 1), (32, 2048, 512, 512, 8)])
 def test_moe_ffn_w4a16_small(T, H, I, E, k):
     say("moe w4a16 small", T, H, I, E, k)
+    import bench
+    if H == 2048:   # the cases labelled fused do take the fused decode kernel
+        assert bench.gate_up_kernel(T, H, I, E, k, "w4a16") == "row_ffn_kernel"
     x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k)
     ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref)
     assert_close_f32(to_np(y), ref, "moe w4a16")
@@ -428,17 +458,57 @@ def test_moe_ffn_in_a_graph():
         assert torch.equal(y2, eager)
 
 
+def _w4a4_device_h_check(x, rids, rw, w_ref, st, y, g_out, T, H, I, E, k, tokens=None,
+                         given=False, ws=None):
+    """Reads the device's bf16 h and W4A4 operand from the FFN's workspace
+    and runs the several-results-correct check (tests.helpers.check_device_h)
+    on the sampled tokens; also checks g_x, and g_h against the device's own h
+    (bit-exact).  Returns (flips, flagged, checked)."""
+    ids, wts, off, pairs, w_gpu = st
+    P = T * k
+    hb, hq = native.ffn_debug_h(ws, T, H, I, E, k, native.W4A4, given)
+    assert hb is not None, "this call keeps no bf16 h in its workspace"
+    sp = to_np(pairs)
+    h_pairs = rows_by_pair(to_np(hb), sp, P)
+    hq_pairs = None if hq is None else rows_by_pair(to_np(hq), sp, P)
+    xf = x.float().numpy()
+    g_x, g_h = to_np(g_out)[0], to_np(g_out)[1]
+    assert g_x == O.tensor_global(xf)
+    kept_rows = h_pairs[~np.isnan(h_pairs[:, 0])]
+    if not given:   # the online h scale is the device h's own
+        assert g_h == O.tensor_global(kept_rows.astype(np.float32))
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    fl = check_device_h(xf, rids, rw, w_ref, h_pairs, hq_pairs, g_x, g_h, tokens, True,
+                        to_np(y)[tokens], f"w4a4 T={T} H={H} I={I} E={E} k={k}")
+    say("h flips / flagged / checked", *fl)
+    return fl
+
+
+def _ffn_ws(T, H, I, E, k, act):
+    return torch.empty(native.ffn_workspace_bytes(T, H, I, E, k, act), dtype=torch.uint8,
+                       device=DEV)
+
+
 @pytest.mark.parametrize("T,H,I,E,k", [(37, 256, 160, 8, 2), (64, 512, 256, 16, 4),
-                                       (96, 256, 128, 8, 4)])
+                                       (96, 256, 128, 8, 4), (300, 256, 512, 16, 2)])
 def test_moe_ffn_w4a4_small(T, H, I, E, k):
+    """W4A4 with online globals (GEMV and tiled paths): g_x bit-exact, the
+    device's h a valid rounding of the fp64 h everywhere, its NVFP4 codes
+    and g_h exact for that h, and the output within tolerance of the oracle
+    run downstream from it."""
     say("moe w4a4 small", T, H, I, E, k)
-    x, rids, rw, y, g_out, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4)
+    x, rids, rw, _, _, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4)
+    ids, wts, off, pairs, w_gpu = st
+    ws = _ffn_ws(T, H, I, E, k, native.W4A4)
+    y, g_out = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                            act=native.W4A4, out_dtype=torch.float32,
+                                            workspace=ws)
+    torch.cuda.synchronize()
+    _w4a4_device_h_check(x, rids, rw, w_ref, st, y, g_out, T, H, I, E, k, ws=ws)
+    # the fp64 oracle run on its own h stays within the bound as well
     ref, info = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True)
     assert to_np(g_out)[0] == info["g_x"]
-    # g_h is the amax of the bf16 h, which can differ from the oracle's by a
-    # bf16 rounding flip of the largest element
     assert abs(to_np(g_out)[1] / info["g_h"] - 1) <= 2 ** -7
-    assert_close_f32(to_np(y), ref, "moe w4a4")
     # with the oracle's own globals given, the two runs agree as well
     ids, wts, off, pairs, w_gpu = st
     yg, _ = native.moe_grouped_nvfp4_ffn(
@@ -461,54 +531,92 @@ def test_moe_single_expert_is_dense_mlp():
 
 # ---- the full-size workloads, checked on sampled tokens ----------------------------
 
-def test_moe_decode_full_size_sampled():
+def test_moe_decode_full_size():
+    """The routed decode workload at full size, every token, fp32 and bf16
+    outputs (the benchmarked launch configuration)."""
     wl = synth.MOE_DECODE
     say("moe decode full size", wl)
-    tokens = [0, 7, 15]
-    x, rids, rw, y, _, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k, tokens=tokens)
-    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=tokens)
-    assert_close_f32(to_np(y)[tokens], ref, "moe decode")
+    x, rids, rw, y, _, w_ref, st = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k)
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref)
+    assert_close_f32(to_np(y), ref, "moe decode")
+    ids, wts, off, pairs, w_gpu = st
+    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, wl.k,
+                                         out_dtype=torch.bfloat16)
+    assert_bf16_output(bf16_np(yb), to_np(y), ref, "moe decode bf16")
+
+
+def _block_covering_tokens(rids, e, bm, extra):
+    """Tokens of expert e that land in every bm-row block of its expert-sorted
+    rows (first and last row of each block), plus `extra` other tokens."""
+    rows = np.nonzero((np.asarray(rids) == e).any(axis=1))[0]   # ascending: the sorted order
+    pick = set()
+    for b0 in range(0, len(rows), bm):
+        pick.add(int(rows[b0]))
+        pick.add(int(rows[min(b0 + bm, len(rows)) - 1]))
+    pick |= set(int(t) for t in extra)
+    return sorted(pick)
 
 
 def test_moe_prefill_full_size_sampled():
+    """The 512-token chunk (Zipf-skewed routing) at full size: tokens at the
+    first and last row of every 64-row block of the heaviest expert (gate/up
+    block size) and of every 32-row block (down), plus tokens spread over the
+    chunk: at least 32 tokens."""
     wl = synth.MOE_PREFILL
     say("moe prefill full size", wl)
-    tokens = [0, 1, 255, 511]
+    logits = synth.router_logits(wl.T, wl.E, 0, zipf_s=wl.zipf_s)
+    rids, _ = O.route_topk(logits, wl.k)
+    heavy = int(np.bincount(rids.ravel(), minlength=wl.E).argmax())
+    tokens = _block_covering_tokens(rids, heavy, 32, range(0, wl.T, 37))
+    assert len(tokens) >= 32
     x, rids, rw, y, _, w_ref, st = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k, zipf=wl.zipf_s,
                                             tokens=tokens)
     off = to_np(st[2])
     counts = np.diff(off)
-    say("active experts", int((counts > 0).sum()), "max tokens per expert", int(counts.max()))
+    say("active experts", int((counts > 0).sum()), "max tokens per expert", int(counts.max()),
+        "tokens checked", len(tokens))
     ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=tokens)
     assert_close_f32(to_np(y)[tokens], ref, "moe prefill")
 
 
-def _fused_vs_separate(T, H, I, E, k, gh, seed):
-    """Runs W4A4 with given globals twice, h quantised in the gate/up
-    epilogue and in its own pass; returns both outputs and the oracle's."""
+def _fused_vs_separate(T, H, I, E, k, gh, seed, tokens=None):
+    """W4A4 with given globals, h quantised in the gate/up epilogue and in a
+    pass of its own: the two outputs and the two h operands are bit-identical,
+    and the separate pass's bf16 h passes the several-results-correct check
+    (valid roundings of the fp64 h; codes exact for it; output to tolerance
+    downstream from it)."""
     x = synth.activations(T, H, seed=seed)
     gx = O.tensor_global(x.float().numpy())
-    _, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4, seed=seed,
-                                            given_globals=[gx, np.float32(gh)])
+    _, rids, rw, _, _, w_ref, st = _moe_run(T, H, I, E, k, act=native.W4A4, seed=seed,
+                                            given_globals=[gx, np.float32(gh)], tokens=tokens)
     ids, wts, off, pairs, w_gpu = st
     ag = torch.tensor([gx, np.float32(gh)], dtype=torch.float32, device=DEV)
+    ws_f, ws_s = _ffn_ws(T, H, I, E, k, native.W4A4), _ffn_ws(T, H, I, E, k, native.W4A4)
+    y, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                        act=native.W4A4, act_globals=ag,
+                                        out_dtype=torch.float32, workspace=ws_f)
+    torch.cuda.synchronize()
+    _, hq_f = native.ffn_debug_h(ws_f, T, H, I, E, k, native.W4A4, given=True)
     native.set_ffn_separate_h_quant(True)
     try:
         ys, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
                                              act=native.W4A4, act_globals=ag,
-                                             out_dtype=torch.float32)
+                                             out_dtype=torch.float32, workspace=ws_s)
+        torch.cuda.synchronize()
+        hb_s, hq_s = native.ffn_debug_h(ws_s, T, H, I, E, k, native.W4A4, given=True)
     finally:
         native.set_ffn_separate_h_quant(False)
-    # h decides integers (its bf16 rounding, then its NVFP4 codes and block
-    # scales), so the oracle forms it in fp32 as the kernels do; everything
-    # after h is fp64.  (Against an fp64 h, an h value within fp32 rounding
-    # of a bf16 tie can move one code, and with it the outputs of one token
-    # by up to about 1e-1 of the RMS: at T = 300, H = 128 with g_h = 0.5/2688
-    # one such value gives rel_frob 2.1e-3, the same in an fp32 emulation on
-    # the CPU as on the device.)
-    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True,
-                       act_globals=(gx, np.float32(gh)), h_fp32=True)
-    return y, ys, ref
+    assert torch.equal(y, ys), "fused and separate h quantisation differ"
+    kept = to_np(pairs) >= 0
+    assert np.array_equal(to_np(hq_f)[kept], to_np(hq_s)[kept]), "h operands differ"
+    P = T * k
+    sp = to_np(pairs)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens)
+    fl = check_device_h(x.float().numpy(), rids, rw, w_ref, rows_by_pair(to_np(hb_s), sp, P),
+                        rows_by_pair(to_np(hq_s), sp, P), gx, np.float32(gh), tok, True,
+                        to_np(y)[tok], f"w4a4 given g_h={gh}")
+    say("h flips / flagged / checked", *fl)
+    return fl
 
 
 # g_h: 0.05/2688 saturates nearly every block scale at 448; 1.1484375/2688 is
@@ -518,13 +626,11 @@ def _fused_vs_separate(T, H, I, E, k, gh, seed):
 def test_moe_ffn_w4a4_h_quantised_in_gate_up_epilogue_matches_separate_pass(gh):
     """Given globals on the four-wave tiled path without a K split: the
     gate/up epilogue quantises h (16-column blocks reduced across lanes).
-    Its output is bit-identical to quantising the same bf16 h in a pass of
-    its own, and matches the oracle element by element."""
+    Its output and operand are bit-identical to quantising the same bf16 h
+    in a pass of its own, and that h is a valid rounding of the fp64 h."""
     T, H, I, E, k = 1024, 256, 2048, 16, 2
     say("moe w4a4 fused h quant", T, H, I, E, k, gh)
-    y, ys, ref = _fused_vs_separate(T, H, I, E, k, gh, seed=3)
-    assert torch.equal(y, ys), "fused and separate h quantisation differ"
-    assert_close_f32(to_np(y), ref, "moe w4a4 fused h quant")
+    _fused_vs_separate(T, H, I, E, k, gh, seed=3)
 
 
 # H = 128 is two 64-wide K chunks, which the tiled GEMM never splits, so these
@@ -533,23 +639,52 @@ def test_moe_ffn_w4a4_h_quantised_in_gate_up_epilogue_matches_separate_pass(gh):
 @pytest.mark.parametrize("gh", [0.5 / 2688, 2.0 / 2688])
 def test_moe_ffn_w4a4_fused_h_quant_one_wave_tiles(T, H, I, E, k, gh):
     say("moe w4a4 fused h quant one-wave", T, H, I, E, k, gh)
-    y, ys, ref = _fused_vs_separate(T, H, I, E, k, gh, seed=5)
-    assert torch.equal(y, ys), "fused and separate h quantisation differ"
-    assert_close_f32(to_np(y), ref, "moe w4a4 fused h quant")
+    _fused_vs_separate(T, H, I, E, k, gh, seed=5)
 
 
-def test_moe_w4a4_full_size_sampled_given_globals():
+@pytest.mark.timeout(900)
+def test_moe_w4a4_full_size_online_globals():
+    """The W4A4 prefill workload at full size, in the mode it is benchmarked
+    (online x and h globals): g_x bit-exact; g_h exact for the device's own
+    h; on 16 tokens spread over the batch, every h value a valid rounding of
+    the fp64 h, its NVFP4 codes exact, and the outputs within tolerance of
+    the oracle downstream from it.  Then the same step with that g_h given as
+    a static scale (the run's own amax(h)/2688, the fused epilogue) gives the
+    identical output and h operand."""
     wl = synth.MOE_PREFILL_W4A4
-    say("moe w4a4 full size", wl)
-    x = synth.activations(wl.T, wl.H)
-    gx = O.tensor_global(x.float().numpy())
-    gh = np.float32(0.05 / 2688)       # a fixed static calibration scale for h
-    tokens = [5]
-    _, rids, rw, y, g_out, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, wl.E, wl.k, act=native.W4A4,
-                                               tokens=tokens, given_globals=[gx, gh])
-    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, act_quant=True, act_globals=(gx, gh),
-                       tokens=tokens)
-    assert_close_f32(to_np(y)[tokens], ref, "moe w4a4 full")
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    say("moe w4a4 full size online", wl)
+    x = synth.activations(T, H)
+    logits = synth.router_logits(T, E)
+    rids, rw = O.route_topk(logits, k)
+    tokens = spread_tokens(rids, 16)
+    need = np.unique(rids[tokens])
+    say("tokens", tokens, "experts for the oracle", len(need))
+    import concurrent.futures
+    pool = concurrent.futures.ThreadPoolExecutor(max_workers=1)
+    fut = pool.submit(LazyOracleExperts, E, H, I, need, 0, 16)   # overlaps the GPU work
+    w_gpu = weights.synthetic_experts(E, H, I, 0, DEV)
+    ids, wts, off, pairs = native.moe_route_topk(torch.from_numpy(logits).to(DEV), k)
+    assert np.array_equal(to_np(ids), rids)
+    ws = _ffn_ws(T, H, I, E, k, native.W4A4)
+    y, g_out = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                            act=native.W4A4, out_dtype=torch.float32,
+                                            workspace=ws)
+    torch.cuda.synchronize()
+    hq_online = native.ffn_debug_h(ws, T, H, I, E, k, native.W4A4)[1].clone()
+    ws2 = _ffn_ws(T, H, I, E, k, native.W4A4)
+    y2, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, k,
+                                         act=native.W4A4, act_globals=g_out.clone(),
+                                         out_dtype=torch.float32, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2), "static g_h (fused epilogue) differs from the online step"
+    hq_given = native.ffn_debug_h(ws2, T, H, I, E, k, native.W4A4, given=True)[1]
+    kept = to_np(pairs) >= 0
+    assert np.array_equal(to_np(hq_given)[kept], to_np(hq_online)[kept])
+    w_ref = fut.result()
+    pool.shutdown()
+    _w4a4_device_h_check(x, rids, rw, w_ref, (ids, wts, off, pairs, w_gpu), y, g_out, T, H, I,
+                         E, k, tokens=tokens, ws=ws)
 
 
 @pytest.mark.parametrize("M", [512, 2048])
@@ -564,12 +699,12 @@ def test_dense_mlp_prefill_full_size_sampled(M):
 
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_dense_mlp_decode_full_size(M):
+    """The dense NVFP4 MLP decode at full size, every row."""
     wl = synth.WORKLOADS[f"mlp_decode_m{M}"]
     say("dense mlp decode full size", M)
     x, rids, rw, y, _, w_ref, _ = _moe_run(wl.T, wl.H, wl.I, 1, 1)
-    rows = list(range(min(M, 4)))
-    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref, tokens=rows)
-    assert_close_f32(to_np(y)[rows], ref, "dense mlp decode")
+    ref, _ = O.moe_ffn(x.float().numpy(), rids, rw, w_ref)
+    assert_close_f32(to_np(y), ref, "dense mlp decode")
 
 
 # ---------------------------------------------------------------------------

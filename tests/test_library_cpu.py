@@ -189,14 +189,16 @@ def test_expert_cache_validation():
     assert L.moe_expert_cache_init(FAKE, 0, FAKE, FAKE, FAKE, 8, None) == 2
     assert L.moe_expert_cache_init(FAKE, 64, FAKE, FAKE, FAKE, 2048, None) == 2
     assert L.moe_expert_cache_init(None, 64, FAKE, FAKE, FAKE, 8, None) == 1
-    plan = lambda T=4, k=2, E=64, S=16, step=1, prot=1, ids=FAKE: L.moe_expert_cache_plan(
-        ids, T, k, E, S, FAKE, FAKE, FAKE, FAKE, step, prot, FAKE, FAKE, FAKE, None)
+    plan = lambda T=4, k=2, E=64, S=16, step=1, prot=1, ids=FAKE, mx=8: L.moe_expert_cache_plan(
+        ids, T, k, E, S, FAKE, FAKE, FAKE, FAKE, step, prot, mx, FAKE, FAKE, FAKE, None)
     assert plan(E=2000) == 2
     assert plan(S=0) == 2
     assert plan(T=-1) == 1
     assert plan(step=0, prot=0) == 1
     assert plan(step=3, prot=4) == 1
     assert plan(ids=None) == 1
+    assert plan(mx=-1) == 1 and "max_fetch" in _last()
+    assert plan(mx=1025) == 1
     w = native.ExpertWeightsC(*([FAKE.value] * 9))
     mis = native.ExpertWeightsC(*([FAKE_MIS.value] + [FAKE.value] * 8))
     odd_g = native.ExpertWeightsC(*([FAKE.value] * 8 + [FAKE.value + 2]))
@@ -213,6 +215,40 @@ def test_expert_cache_validation():
     assert pp(k=33) == 2
     assert pp(T=-1) == 1
     assert pp(ids=FAKE_MIS) == 3
+
+
+def test_route_workspace_init_validation():
+    """moe_route_workspace_init checks its workspace on the host before any
+    launch (NULL, misaligned, fewer than 4 bytes), and the binding's routing
+    workspaces go through it (no caller relies on a zeroed allocation)."""
+    L = native.lib()
+    assert L.moe_route_workspace_init(None, 256, None) == 1
+    assert L.moe_route_workspace_init(FAKE_MIS, 256, None) == 3
+    assert L.moe_route_workspace_init(FAKE, 3, None) == 4
+    import inspect
+    assert "_init_route_workspace" in inspect.getsource(native.route_workspace)
+    assert "_init_route_workspace" in inspect.getsource(native.router_workspace)
+
+
+def test_ffn_debug_h_layout():
+    """The debug query places h and its W4A4 operand where the FFN's
+    workspace holds them, inside the workspace, and names what each path
+    leaves there."""
+    L = native.lib()
+    ho, hq = ctypes.c_size_t(), ctypes.c_size_t()
+    for T, H, I, E, k, act, given, want in [
+            (2048, 4096, 1536, 128, 8, 1, 0, 3),    # W4A4 online: bf16 h, then its operand
+            (2048, 4096, 1536, 128, 8, 1, 1, 2),    # W4A4 given: h quantised in the epilogue
+            (512, 2048, 512, 512, 8, 0, 0, 1),      # W4A16 tiles: bf16 h
+            (16, 2048, 512, 512, 8, 0, 0, 0),       # decode rows: h stays in LDS
+            (16, 2048, 512, 512, 8, 1, 0, 3)]:      # W4A4 decode GEMV
+        m = L.moe_grouped_nvfp4_ffn_debug_h(T, H, I, E, k, act, given, ctypes.byref(ho),
+                                            ctypes.byref(hq))
+        assert m == want, (T, H, I, E, k, act, given, m)
+        ws = L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act)
+        P = T * k
+        assert ho.value >= 2 * T * H and hq.value >= ho.value + 2 * P * I
+        assert hq.value + 2 * P * I <= ws
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

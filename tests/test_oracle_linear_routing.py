@@ -318,3 +318,182 @@ def test_shared_expert_closed_form():
     s1 = -10.0 / (1 + np.exp(10.0))
     assert np.all(y[0] == O.bf16_rne(s0 * 3.0))
     assert np.all(y[1] == O.bf16_rne(s1 * 2.0))
+
+
+# ---------------------------------------------------------------------------
+# dropped pairs (ids outside 0..E-1), given h, and the valid roundings of h
+# ---------------------------------------------------------------------------
+
+def test_permute_drops_ids_outside_the_experts():
+    rng = np.random.default_rng(31)
+    t, e, k = 23, 7, 3
+    ids, _ = O.route_topk(rng.standard_normal((t, e)).astype(np.float32), k)
+    full_off, full_pairs = O.permute(ids, e)
+    drop = rng.random((t, k)) < 0.3
+    ids_d = np.where(drop, np.where(rng.random((t, k)) < 0.5, -1, e), ids)
+    off, pairs = O.permute(ids_d, e)
+    kept = int((~drop).sum())
+    assert off[-1] == kept and np.all(pairs[kept:] == -1)
+    # the kept pairs keep the relative order of the full permutation
+    keep_flat = ~drop.reshape(-1)
+    assert np.array_equal(pairs[:kept], full_pairs[keep_flat[full_pairs]])
+    assert np.array_equal(np.diff(off), np.bincount(ids_d[~drop], minlength=e))
+
+
+def test_moe_dropped_pairs_contribute_nothing():
+    """W4A16: a dropped pair gives the same output as a kept pair with routing
+    weight 0 (adding an exact zero changes no fp64 sum); a token whose pairs
+    are all dropped gets 0."""
+    rng = np.random.default_rng(32)
+    t, h, i, e, k = 9, 32, 32, 5, 3
+    w = _rand_experts(rng, e, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    ids, wts = O.route_topk(rng.standard_normal((t, e)).astype(np.float32), k)
+    drop = rng.random((t, k)) < 0.4
+    drop[4] = True
+    y_d, info = O.moe_ffn(x, np.where(drop, -1, ids), wts, w)
+    y_0, _ = O.moe_ffn(x, ids, np.where(drop, 0.0, wts), w)
+    assert np.array_equal(y_d, y_0)
+    assert np.all(y_d[4] == 0) and np.array_equal(info["kept"], ~drop)
+
+
+def test_moe_w4a4_dropped_pairs_take_no_part_in_the_h_scale():
+    """W4A4 online: dropping every pair of the second half of the tokens
+    gives, for the first half, exactly the call on those tokens alone with
+    the full x's activation scale (the h scale then spans the same pairs),
+    and zeros for the second half."""
+    rng = np.random.default_rng(33)
+    t, h, i, e, k = 10, 64, 32, 4, 2
+    w = _rand_experts(rng, e, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    ids, wts = O.route_topk(rng.standard_normal((t, e)).astype(np.float32), k)
+    ids_d = ids.copy()
+    ids_d[t // 2:] = -1
+    y_d, info_d = O.moe_ffn(x, ids_d, wts, w, act_quant=True)
+    g_x = O.tensor_global(x)
+    y_h, info_h = O.moe_ffn(x[:t // 2], ids[:t // 2], wts[:t // 2], w, act_quant=True,
+                            act_globals=(g_x, None))
+    assert info_d["g_x"] == g_x and info_d["g_h"] == info_h["g_h"]
+    assert np.array_equal(y_d[:t // 2], y_h) and np.all(y_d[t // 2:] == 0)
+
+
+@pytest.mark.parametrize("act_quant", [False, True])
+def test_moe_given_h_reproduces_the_computed_one(act_quant):
+    rng = np.random.default_rng(34)
+    t, h, i, e, k = 8, 64, 48, 5, 2
+    w = _rand_experts(rng, e, h, i)
+    x = rng.standard_normal((t, h)).astype(np.float32)
+    ids, wts = O.route_topk(rng.standard_normal((t, e)).astype(np.float32), k)
+    y, info = O.moe_ffn(x, ids, wts, w, act_quant=act_quant)
+    y2, info2 = O.moe_ffn(x, ids, wts, w, act_quant=act_quant, h_given=info["h_bf16"])
+    assert np.array_equal(y, y2) and np.array_equal(info["h"], info2["h"])
+    # a different h changes the result: the given values are what is used
+    other = info["h_bf16"].copy()
+    other[0, 0, 0] += 1.0
+    y3, _ = O.moe_ffn(x, ids, wts, w, act_quant=act_quant, h_given=other)
+    assert not np.array_equal(y3[0], y[0])
+    if not act_quant:   # (in W4A4 the larger h may also move the h scale)
+        assert np.array_equal(y3[1:], y[1:])
+
+
+def test_bf16_bracket():
+    rng = np.random.default_rng(35)
+    v = rng.standard_normal(20000) * np.exp2(rng.integers(-40, 40, 20000))
+    v[:4] = [1.0, -1.5, 2.0 ** -130, 0.0]
+    lo, hi = O.bf16_bracket(v)
+    assert np.all(lo <= v) and np.all(v <= hi)
+    assert np.array_equal(O.bf16_rne(lo), lo) and np.array_equal(O.bf16_rne(hi), hi)
+    r = O.bf16_rne(v)
+    assert np.all((r == lo) | (r == hi))
+    exact = O.bf16_rne(v) == v
+    assert np.array_equal(lo == hi, exact)
+    # neighbours: nothing representable strictly between lo and hi
+    mid = 0.5 * (lo + hi)
+    assert np.all((O.bf16_rne(mid) == lo) | (O.bf16_rne(mid) == hi))
+
+
+def test_check_h_choices_cases():
+    one = 1.0
+    mid = 1.0 + 2.0 ** -8                    # half-way between 1 and 1 + 2^-7
+    up = 1.0 + 2.0 ** -7
+    # exactly on the boundary: both neighbours valid; the rounding picks 1 (even)
+    ok, fl, fp = O.check_h_choices([mid, mid], [0.0, 0.0], [one, up])
+    assert ok.all() and fl.all() and fp.tolist() == [False, True]
+    # off the boundary by more than the bound: only the rounding is valid
+    v = mid + 2.0 ** -20
+    ok, fl, _ = O.check_h_choices([v, v], [2.0 ** -22] * 2, [up, one])
+    assert ok.tolist() == [True, False] and not fl.any()
+    # within the bound: either neighbour
+    ok, fl, _ = O.check_h_choices([v, v], [2.0 ** -19] * 2, [up, one])
+    assert ok.all() and fl.all()
+    # two ulps away is never valid; an exact bf16 value has one valid result
+    ok, _, _ = O.check_h_choices([v, 1.5, 1.5], [1.0, 1.0, 1.0], [1.0 + 2.0 ** -6, 1.5, up])
+    assert ok.tolist() == [False, True, False]
+    # negative values mirror
+    ok, fl, _ = O.check_h_choices([-mid], [0.0], [-up])
+    assert ok.all() and fl.all()
+
+
+def _fp32_h(xv, g_x, w, e, order, rng):
+    """h of expert e evaluated in fp32 with a given summation order of the
+    K products (each product is exact in fp32), then the fp32 globals,
+    SiLU and product; bf16 rounding left out."""
+    f32 = np.float32
+    dg = O.block_values(w.gate_codes[e], w.gate_scales[e]).astype(f32)
+    du = O.block_values(w.up_codes[e], w.up_scales[e]).astype(f32)
+    xv = np.asarray(xv, f32)
+    k = dg.shape[1]
+    perm = np.arange(k)
+    if order == "reversed":
+        perm = perm[::-1]
+    elif order == "random":
+        perm = rng.permutation(k)
+
+    def acc(d):
+        if order == "blocked32":   # exact 32-term blocks, then fp32 accumulation
+            s = np.zeros((xv.shape[0], d.shape[0]), f32)
+            for b in range(0, k, 32):
+                blk = (xv[:, b:b + 32].astype(np.float64) @ d[:, b:b + 32].T.astype(np.float64))
+                s = (s + blk.astype(f32)).astype(f32)
+            return s
+        s = np.zeros((xv.shape[0], d.shape[0]), f32)
+        for j in perm:
+            s = (s + xv[:, j:j + 1] * d[None, :, j]).astype(f32)
+        return s
+    gx = f32(1.0) if g_x is None else f32(g_x)
+    g = acc(dg) * (f32(w.gate_global[e]) * gx)
+    u = acc(du) * (f32(w.up_global[e]) * gx)
+    with np.errstate(over="ignore"):
+        return ((g / (f32(1.0) + np.exp(-g))) * u).astype(np.float64)
+
+
+@pytest.mark.parametrize("act_quant", [False, True])
+def test_h_bound_covers_fp32_evaluations(act_quant):
+    """The bound of expert_h_bound holds for fp32 evaluations of h in several
+    summation orders (sequential, reversed, random, exact 32-term blocks),
+    computed independently here; it stays far below the bf16 spacing for
+    most values (so the rounding is decided almost everywhere)."""
+    rng = np.random.default_rng(36)
+    t, h, i = 48, 512, 64
+    w = _rand_experts(rng, 1, h, i)
+    x = O.bf16_rne(rng.standard_normal((t, h))).astype(np.float32)
+    if act_quant:
+        xc, xs, g_x = O.quantize(x)
+        xv = O.block_values(xc, xs)
+    else:
+        xv, g_x = x.astype(np.float64), None
+    h64, dh = O.expert_h_bound(xv, g_x, w, 0)
+    # the fp64 h is the one moe_ffn rounds
+    _, info = O.moe_ffn(x, np.zeros((t, 1), np.int32), np.ones((t, 1)), w, act_quant=act_quant,
+                        with_bound=True)
+    assert np.allclose(info["h64"][:, 0], h64, rtol=1e-12, atol=0)
+    assert np.array_equal(O.bf16_rne(h64), info["h_bf16"][:, 0])
+    worst = 0.0
+    for order in ("sequential", "reversed", "random", "blocked32"):
+        h32 = _fp32_h(xv, g_x, w, 0, order, rng)
+        err = np.abs(h32 - h64)
+        assert np.all(err <= dh), order
+        worst = max(worst, float(np.max(err / np.where(dh > 0, dh, 1))))
+    assert worst > 1e-3                     # the bound is not vacuous
+    rel = dh / np.maximum(np.abs(h64), 1e-30)
+    assert np.median(rel) < 2.0 ** -12      # far below bf16's half spacing (2^-9)

@@ -25,10 +25,11 @@ def test_worked_example():
     assert sid.tolist() == [[0, 2]]
     assert st.expert_of == [1, 4, 5] and st.last_use == [2, 1, 2] and st.hand == 0
     # step 3 while step 2 may still run (protect_from = 2): only slot 1 is
-    # free for two missing experts, so nothing moves and both pairs read slot 0
+    # free for two missing experts, so nothing moves and both pairs get slot
+    # -1 (dropped by the later calls)
     before = st.copy()
     sid, fetch, n = O.expert_slot_plan(st, [[0, 2]], 3, 2)
-    assert n == -1 and fetch == [] and sid.tolist() == [[0, 0]]
+    assert n == -1 and fetch == [] and sid.tolist() == [[-1, -1]]
     assert (st.slot_of, st.expert_of, st.last_use, st.hand) == \
         (before.slot_of, before.expert_of, before.last_use, before.hand)
     # the same step once step 2 is done (protect_from = 3): experts 0 and 2
@@ -38,13 +39,26 @@ def test_worked_example():
     assert sid.tolist() == [[0, 1]]
     assert st.slot_of == [0, -1, 1, -1, -1, 2] and st.expert_of == [0, 2, 5]
     assert st.last_use == [3, 3, 2] and st.hand == 2
+    # step 4: experts 1 (a miss), 5 (a hit) and 3 (a miss) with room for
+    # two fetches but a fetch limit of one: nothing moves, the hit keeps
+    # slot 2 (stamp 4) and the misses get -1; with a limit of two, experts 1
+    # and 3 take slots 0 and 1 (neither holds a needed expert: 0 and 2 are
+    # not needed, and their stamps 3 are below protect_from 4)
+    before = st.copy()
+    sid, fetch, n = O.expert_slot_plan(st, [[1, 5], [3, 5]], 4, 4, max_fetch=1)
+    assert n == -1 and fetch == [] and sid.tolist() == [[-1, 2], [-1, 2]]
+    assert st.slot_of == before.slot_of and st.hand == before.hand
+    assert st.last_use == [3, 3, 4]
+    sid, fetch, n = O.expert_slot_plan(st, [[1, 5], [3, 5]], 4, 4, max_fetch=2)
+    assert n == 2 and fetch == [(1, 0), (3, 1)]
+    assert sid.tolist() == [[0, 2], [1, 2]] and st.expert_of == [1, 3, 5]
 
 
 def test_ids_outside_the_experts_are_ignored():
     st = O.SlotState(4, 2)
     sid, fetch, n = O.expert_slot_plan(st, [[-1, 3], [4, 3]], 1, 1)
     assert n == 1 and fetch == [(3, 0)]
-    assert sid.tolist() == [[0, 0], [0, 0]] and st.slot_of == [-1, -1, -1, 0]
+    assert sid.tolist() == [[-1, 0], [-1, 0]] and st.slot_of == [-1, -1, -1, 0]
 
 
 @pytest.mark.parametrize("E,S,k,steps,seed", [(12, 4, 2, 300, 0), (40, 16, 4, 300, 1),
@@ -58,22 +72,32 @@ def test_invariants_over_random_steps(E, S, k, steps, seed):
         T = int(rng.integers(1, 5))
         ids = np.stack([rng.choice(E, size=min(k, E), replace=False) for _ in range(T)])
         protect = int(rng.choice([step, step - 1, max(step - 3, 0)]))
+        max_fetch = int(rng.choice([S, S, max(1, S // 2)]))
         before = st.copy()
         needed = set(int(e) for e in ids.ravel())
-        sid, fetch, n = O.expert_slot_plan(st, ids, step, protect)
+        sid, fetch, n = O.expert_slot_plan(st, ids, step, protect, max_fetch)
         # the maps stay inverse to each other
         assert all(st.expert_of[s] == e for e, s in enumerate(st.slot_of) if s >= 0)
         assert all(st.slot_of[e] == s for s, e in enumerate(st.expert_of) if e >= 0)
         hits = {e for e in needed if before.slot_of[e] >= 0}
         if n < 0:
             fails += 1
-            # nothing moves; only the hits' stamps change
+            # nothing moves; only the hits' stamps change; the hits' pairs
+            # read their slots and every other pair is dropped (-1)
             assert st.slot_of == before.slot_of and st.expert_of == before.expert_of
             assert st.hand == before.hand
             for s in range(S):
                 want = step if before.expert_of[s] in hits else before.last_use[s]
                 assert st.last_use[s] == want
+            want_sid = np.array([[before.slot_of[e] if e in hits else -1 for e in row]
+                                 for row in ids])
+            assert np.array_equal(sid, want_sid)
+            assert len(needed - hits) > min(max_fetch, S)  or \
+                sum(1 for s in range(S) if before.expert_of[s] < 0 or
+                    (before.expert_of[s] not in needed and before.last_use[s] < protect)) \
+                < len(needed - hits)
             continue
+        assert n <= max_fetch
         fits += 1
         # every needed expert is resident and every pair reads its expert
         assert all(st.slot_of[e] >= 0 for e in needed)
