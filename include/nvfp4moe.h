@@ -437,6 +437,17 @@ void nvfp4_set_ffn_stage_events(hipEvent_t *events);
  */
 void nvfp4_set_ffn_separate_h_quant(int separate);
 
+/*
+ * Measurement aid (not part of the computation): a plain streaming read of
+ * `bytes` (a positive multiple of 16) of device memory at buf, 16-byte
+ * non-temporal loads, four in flight per thread, up to 8192 workgroups.
+ * Its rate is the practical HBM read ceiling the decode kernels are
+ * compared with, beside the 8 TB/s peak.  sink: >= 1024 device words,
+ * written only in the (data-dependent, practically never met) case that
+ * keeps the loads from being optimised away.
+ */
+nvfp4_status nvfp4_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream);
+
 /* Text of a status code; never NULL. */
 const char *nvfp4_status_string(nvfp4_status s);
 /* Detail of the last failure on the calling thread ("" if none). */

@@ -258,6 +258,18 @@ void nvfp4_set_ffn_stage_events(hipEvent_t *events) { g_stage_events = events; }
 
 void nvfp4_set_ffn_separate_h_quant(int separate) { g_separate_h_quant = separate != 0; }
 
+nvfp4_status nvfp4_read_probe(const void *buf, size_t bytes, uint32_t *sink, hipStream_t stream) {
+  g_last_error[0] = 0;
+  CHECK_NULL(buf);
+  CHECK_NULL(sink);
+  CHECK_ALIGN(buf);
+  if (bytes == 0 || bytes % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "bytes = %zu must be a positive multiple of 16",
+                bytes);
+  LAUNCH(launch_read_probe(buf, (int64_t)bytes, sink, stream), "read probe");
+  return NVFP4_OK;
+}
+
 // ---- nvfp4_quantize ----------------------------------------------------------------
 
 size_t nvfp4_quantize_workspace_size(int64_t rows, int64_t cols) {

@@ -260,4 +260,9 @@ hipError_t launch_moe_plan(const int32_t *offsets, int E, int bm, int4 *mblocks,
 hipError_t launch_combine(const float *ypair, int64_t T, int64_t H, int k, const int32_t *ids,
                           int E, void *y, OutType t, hipStream_t s);
 
+// ---- measurement aid (probe.hip) ---------------------------------------------------
+
+// Streaming read of `bytes` (a multiple of 16) at buf; sink: >= 1024 words.
+hipError_t launch_read_probe(const void *buf, int64_t bytes, uint32_t *sink, hipStream_t s);
+
 }  // namespace nvfp4

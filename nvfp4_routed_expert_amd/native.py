@@ -90,6 +90,7 @@ def lib():
                                                              ctypes.POINTER(_sz)]),
             "nvfp4_set_ffn_stage_events": (None, [_vp]),
             "nvfp4_set_ffn_separate_h_quant": (None, [ctypes.c_int]),
+            "nvfp4_read_probe": (_i32, [_vp, _sz, _vp, _vp]),
             "nvfp4_status_string": (ctypes.c_char_p, [_i32]),
             "nvfp4_last_error": (ctypes.c_char_p, []),
         }
@@ -115,7 +116,7 @@ def exported_symbols():
             "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "moe_grouped_nvfp4_ffn_debug_h",
             "nvfp4_set_ffn_stage_events",
-            "nvfp4_set_ffn_separate_h_quant",
+            "nvfp4_set_ffn_separate_h_quant", "nvfp4_read_probe",
             "nvfp4_status_string", "nvfp4_last_error"]
 
 
@@ -458,6 +459,12 @@ def ffn_debug_h(workspace, T, H, I, E, k, act=W4A16, given=False):
     if mask & 2:
         hqv = raw[hq.value: hq.value + 2 * P * I].view(torch.float16).view(P, I).float()
     return hb, hqv
+
+
+def read_probe(buf, sink):
+    """A plain streaming read of buf (device memory; a measurement aid)."""
+    _check(lib().nvfp4_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                  _stream()))
 
 
 def set_ffn_separate_h_quant(separate):
