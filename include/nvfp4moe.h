@@ -44,8 +44,9 @@
  *     synchronisation, as usual in HIP.
  *   - Calls are deterministic: the same inputs give bit-identical outputs
  *     (no floating-point atomics; maxima use order-independent integer
- *     atomics).  The library has no global mutable state; its only state is
- *     per thread (the last-error message and the two switches below).
+ *     atomics).  The library's state is per thread (the last-error message
+ *     and the two switches below), except for moe_grouped_nvfp4_ffn_static's
+ *     scratch array, one per device (see there).
  *   - K (the contraction length: cols, H or I) must be a positive multiple
  *     of 32, otherwise NVFP4_ERR_UNSUPPORTED_SHAPE.
  *   - Inputs must be finite; NaN or infinite activations, logits or weights
@@ -385,6 +386,35 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H,
 size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I,
                                             int32_t E, int32_t k,
                                             nvfp4_act_mode act);
+
+/*
+ * moe_grouped_nvfp4_ffn_static: moe_grouped_nvfp4_ffn without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops and harnesses that forbid hipMalloc.
+ * Its scratch is a file-scope device array inside the library, one copy per
+ * device (each device holds it, moe_grouped_nvfp4_ffn_static_max_bytes()
+ * = 64 MiB, from the library's load until the process ends); the device
+ * address of the current device's copy is looked up once per device on the
+ * first call there.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine) and computes exactly what
+ * moe_grouped_nvfp4_ffn computes with a workspace (bit-identical outputs).
+ * Shapes whose moe_grouped_nvfp4_ffn_workspace_size exceeds the maximum
+ * return NVFP4_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the
+ * routed decode and 512-token prefill shapes fit; a 2048-token W4A4 batch
+ * with H = 4096 does not).  Every call on a device shares that device's
+ * array and leaves its contents behind; the call clears what it needs
+ * cleared itself.  Calls that may overlap on one device (several streams
+ * or host threads) race on the array: serialise them.
+ */
+nvfp4_status moe_grouped_nvfp4_ffn_static(const void *x, int64_t T, int64_t H, int64_t I,
+                                          int32_t E, int32_t k, const int32_t *topk_ids,
+                                          const float *topk_weights,
+                                          const int32_t *expert_offsets,
+                                          const int32_t *sorted_pairs,
+                                          const nvfp4_expert_weights *w, nvfp4_act_mode act,
+                                          nvfp4_global_mode act_global_mode, float *act_globals,
+                                          void *y, nvfp4_dtype y_dtype, hipStream_t stream);
+size_t moe_grouped_nvfp4_ffn_static_max_bytes(void);
 
 /*
  * moe_grouped_nvfp4_ffn_debug_h: a test aid (not part of the computation)

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4moe.h"
 #include "kernels.h"
 
@@ -1040,6 +1042,72 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   LAUNCH(launch_combine(ws.ypair, T, H, k, topk_ids, E, y, yt, stream), "combine");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   return NVFP4_OK;
+}
+
+}  // extern "C"
+
+// ---- moe_grouped_nvfp4_ffn_static: the FFN with the library's own scratch --------
+
+namespace {
+// Scratch of moe_grouped_nvfp4_ffn_static: a file-scope device array, one
+// copy per device, held until the process ends.  Host code never uses the
+// array's name as an address: the device address of each device's copy comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxScratchDevices] = {};
+
+nvfp4_status static_scratch(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "device %d outside 0..%d", dev,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(NVFP4_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NVFP4_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t moe_grouped_nvfp4_ffn_static_max_bytes(void) { return kStaticScratchBytes; }
+
+nvfp4_status moe_grouped_nvfp4_ffn_static(const void *x, int64_t T, int64_t H, int64_t I,
+                                          int32_t E, int32_t k, const int32_t *topk_ids,
+                                          const float *topk_weights,
+                                          const int32_t *expert_offsets,
+                                          const int32_t *sorted_pairs,
+                                          const nvfp4_expert_weights *w, nvfp4_act_mode act,
+                                          nvfp4_global_mode act_global_mode, float *act_globals,
+                                          void *y, nvfp4_dtype y_dtype, hipStream_t stream) {
+  g_last_error[0] = 0;
+  // the scratch this call needs (a host computation: nothing is allocated)
+  const size_t need = (T >= 1 && H >= 1 && I >= 1 && E >= 1 && k >= 1 && T <= ((int64_t)1 << 24) &&
+                       H <= ((int64_t)1 << 30) && I <= ((int64_t)1 << 30))
+                          ? moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act)
+                          : 0;
+  if (need > kStaticScratchBytes)
+    return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL,
+                "moe_grouped_nvfp4_ffn_static: this call needs %zu bytes of scratch, the "
+                "library's static scratch holds %zu (use moe_grouped_nvfp4_ffn with a "
+                "workspace)",
+                need, kStaticScratchBytes);
+  void *ws = nullptr;
+  if (need > 0) TRY(static_scratch(&ws));
+  return moe_grouped_nvfp4_ffn(x, T, H, I, E, k, topk_ids, topk_weights, expert_offsets,
+                               sorted_pairs, w, act, act_global_mode, act_globals, y, y_dtype,
+                               ws, need > 0 ? kStaticScratchBytes : 0, stream);
 }
 
 }  // extern "C"

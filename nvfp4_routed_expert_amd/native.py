@@ -85,6 +85,10 @@ def lib():
                                              _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
             "moe_grouped_nvfp4_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+            "moe_grouped_nvfp4_ffn_static": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
+                                                    _vp, _vp, ctypes.POINTER(ExpertWeightsC),
+                                                    _i32, _i32, _vp, _vp, _i32, _vp]),
+            "moe_grouped_nvfp4_ffn_static_max_bytes": (_sz, []),
             "moe_grouped_nvfp4_ffn_debug_h": (ctypes.c_int, [_i64, _i64, _i64, _i32, _i32, _i32,
                                                              _i32, ctypes.POINTER(_sz),
                                                              ctypes.POINTER(_sz)]),
@@ -115,6 +119,7 @@ def exported_symbols():
             "moe_permute_pairs",
             "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "moe_grouped_nvfp4_ffn_debug_h",
+            "moe_grouped_nvfp4_ffn_static", "moe_grouped_nvfp4_ffn_static_max_bytes",
             "nvfp4_set_ffn_stage_events",
             "nvfp4_set_ffn_separate_h_quant", "nvfp4_read_probe",
             "nvfp4_status_string", "nvfp4_last_error"]
@@ -439,6 +444,28 @@ def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_ids, topk_weights, exp
                                    _ptr(expert_offsets), _ptr(sorted_pairs), ctypes.byref(cw),
                                    act, mode, _ptr(ag), _ptr(y), _dt(y.dtype), _ptr(ws),
                                    ws.numel(), _stream()))
+    return y, ag
+
+
+def moe_grouped_nvfp4_ffn_static(x, weights: ExpertWeights, topk_ids, topk_weights,
+                                 expert_offsets, sorted_pairs, k, act=W4A16, act_globals=None,
+                                 out_dtype=torch.bfloat16, out=None):
+    """moe_grouped_nvfp4_ffn on the library's static scratch (no workspace, no
+    allocation inside the call).  Returns (y [T,H], act_globals or None)."""
+    T, H = x.shape
+    E, I = weights.num_experts, weights.intermediate
+    y = out if out is not None else torch.empty((T, H), dtype=out_dtype, device=x.device)
+    mode, ag = GLOBAL_COMPUTE, None
+    if act == W4A4:
+        if act_globals is None:
+            ag = torch.empty(2, dtype=torch.float32, device=x.device)
+        else:
+            ag, mode = act_globals, GLOBAL_GIVEN
+    cw = weights.c_struct()
+    _check(lib().moe_grouped_nvfp4_ffn_static(
+        _ptr(x), T, H, I, E, k, _ptr(topk_ids), _ptr(topk_weights), _ptr(expert_offsets),
+        _ptr(sorted_pairs), ctypes.byref(cw), act, mode, _ptr(ag), _ptr(y), _dt(y.dtype),
+        _stream()))
     return y, ag
 
 
