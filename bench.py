@@ -96,6 +96,7 @@ KERNEL_SOURCES = {
     "row_ffn_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
     "row_gemv_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
     "tile_gemm_kernel": ["tile_gemm.hip", "common.h", "kernels.h"],
+    "dense_gemv_kernel": ["densegemv.hip", "common.h", "kernels.h"],
     "grouped_gemm_kernel": ["gemm.hip", "common.h", "kernels.h"],
     "grouped_gemv_kernel": ["gemv.hip", "common.h", "kernels.h"],
 }
@@ -137,6 +138,8 @@ def gate_up_kernel(T, H, I, E, k, act):
     P = T * k
     small = P <= 2 if E == 1 else (P <= 256 and 2 * P <= 32 * E)
     row_ok = lambda K: K in (256, 512, 1024) or (K % 32 == 0 and 2048 <= K <= 32768)
+    if E == 1 and not small and P <= 32 and H % 256 == 0 and I % 256 == 0:
+        return "dense_gemv_kernel"   # a dense MLP with a few rows: one shared weight stream
     if small:
         if act == "w4a16" and row_ok(H) and row_ok(I):
             # H = 2048 and I a multiple of 256: both projections in one launch

@@ -125,17 +125,24 @@ struct LinearWs {
 bool linear_rows(int64_t M, int64_t K, nvfp4_act_mode act) {
   return act == NVFP4_W4A16 && M <= 2 && row_gemv_supported((int)K);
 }
-TilePlan linear_plan(int64_t M, int64_t N, int64_t K) {
+// a few rows (up to 32) share one weight stream in the dense GEMV
+bool linear_dense(int64_t M, int64_t K, nvfp4_act_mode act) {
+  return !linear_rows(M, K, act) && dense_gemv_supported(M, K);
+}
+TilePlan linear_plan(int64_t M, int64_t N, int64_t K, nvfp4_act_mode act) {
+  if (linear_dense(M, K, act)) return dense_gemv_plan(Epi::LINEAR, N, K, M);
   const int bm = gemm_block_rows(M);
   return tile_gemm_plan(Epi::LINEAR, N, K, (M + bm - 1) / bm, M);
 }
-LinearWs carve_linear(Carver &c, int64_t M, int64_t N, int64_t K) {
+LinearWs carve_linear(Carver &c, int64_t M, int64_t N, int64_t K, nvfp4_act_mode act) {
   LinearWs w;
   w.x16 = c.take<_Float16>((size_t)(M * K));
   w.shift = c.take<int32_t>((size_t)M);
   w.partials = c.take<float>(kMaxPartials);
   w.g_x = c.take<float>(4);
-  w.split = c.take<float>(tile_gemm_supported((int)K) ? linear_plan(M, N, K).partial_floats : 0);
+  w.split = c.take<float>(tile_gemm_supported((int)K) || linear_dense(M, K, act)
+                              ? linear_plan(M, N, K, act).partial_floats
+                              : 0);
   return w;
 }
 
@@ -181,6 +188,12 @@ int ffn_bm_down(int64_t T, int64_t E, int64_t k) {
 }
 // m-blocks of up to bm rows over P pairs: each expert rounds up once (a
 // single expert, the dense MLP, has exactly ceil(P / bm))
+// A single expert (a dense MLP) with 3 to 32 rows: one weight stream shared
+// by every row in the dense GEMV (K of both projections a multiple of 256).
+bool ffn_dense(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
+  return E == 1 && !ffn_small(T, E, k) && dense_gemv_supported(T * k, H) &&
+         dense_gemv_supported(T * k, I);
+}
 int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) {
   return (P + bm - 1) / bm + (E > 1 ? (E < P ? E : P) : 0);
 }
@@ -192,7 +205,10 @@ FfnPlans ffn_plans(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   const int64_t P = T * k;
   const int64_t mb = ffn_max_mblocks(P, E, ffn_bm(T, E, k));
   const int64_t mb_down = ffn_max_mblocks(P, E, ffn_bm_down(T, E, k));
-  if (!ffn_small(T, E, k)) {
+  if (ffn_dense(T, H, I, E, k)) {
+    f.gate_up = dense_gemv_plan(Epi::SWIGLU, I, H, P);
+    f.down = dense_gemv_plan(Epi::DOWN, H, I, P);
+  } else if (!ffn_small(T, E, k)) {
     if (tile_gemm_supported((int)H)) f.gate_up = tile_gemm_plan(Epi::SWIGLU, I, H, mb, P);
     if (tile_gemm_supported((int)I)) f.down = tile_gemm_plan(Epi::DOWN, H, I, mb_down, P);
   }
@@ -350,10 +366,9 @@ nvfp4_status nvfp4_dequantize(const nvfp4_matrix *w, float *out, hipStream_t str
 // ---- nvfp4_linear -------------------------------------------------------------------
 
 size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K, nvfp4_act_mode act) {
-  (void)act;
   if (M < 1 || K < 1 || N < 1) return 0;
   Carver c(nullptr);
-  carve_linear(c, M, N, K);
+  carve_linear(c, M, N, K, act);
   return c.used;
 }
 
@@ -385,7 +400,7 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   TRY(check_workspace(workspace, workspace_bytes, nvfp4_linear_workspace_size(M, N, K, act)));
   if (M == 0) return NVFP4_OK;   // nothing to compute (act_global is not written)
   Carver c(workspace);
-  const LinearWs ws = carve_linear(c, M, N, K);
+  const LinearWs ws = carve_linear(c, M, N, K, act);
   const uint16_t *xb = static_cast<const uint16_t *>(x);
   // decode-sized W4A16: stream the weight rows against the bf16 rows as given
   if (linear_rows(M, K, act)) {
@@ -435,8 +450,13 @@ nvfp4_status nvfp4_linear(const void *x, int64_t M, const nvfp4_matrix *w,
   a.out = y;
   a.ldo = N;
   a.out_type = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
-  if (tile_gemm_supported((int)K)) {
-    const TilePlan plan = linear_plan(M, N, K);
+  if (linear_dense(M, K, act)) {
+    const TilePlan plan = linear_plan(M, N, K, act);
+    a.partial = ws.split;
+    a.partial_rows = M;
+    LAUNCH(launch_dense_gemv(Epi::LINEAR, a, (int)M, plan, nullptr, stream), "dense gemv");
+  } else if (tile_gemm_supported((int)K)) {
+    const TilePlan plan = linear_plan(M, N, K, act);
     a.partial = ws.split;
     a.partial_rows = M;
     LAUNCH(launch_tile_gemm(Epi::LINEAR, a, bm, plan, nullptr, (int)M, stream), "gemm");
@@ -767,8 +787,8 @@ int moe_grouped_nvfp4_ffn_debug_h(int64_t T, int64_t H, int64_t I, int32_t E, in
   if (act != NVFP4_W4A4) return small ? 0 : 1;   // (the row paths keep h elsewhere)
   const bool given = act_global_mode == NVFP4_GLOBAL_GIVEN;
   const FfnPlans plans = ffn_plans(T, H, I, E, k);
-  const bool h_fused = given && !small && !g_separate_h_quant && tile_gemm_supported((int)H) &&
-                       plans.gate_up.ksplit == 1;
+  const bool h_fused = given && !small && !ffn_dense(T, H, I, E, k) && !g_separate_h_quant &&
+                       tile_gemm_supported((int)H) && plans.gate_up.ksplit == 1;
   return h_fused ? 2 : 3;
 }
 
@@ -916,8 +936,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.amax_slot = a4 ? ws.slots : nullptr;
   // W4A4 with a given h global on the tiled path: the gate/up epilogue
   // quantises h itself and writes the down GEMM's fp16 operand directly
-  const bool h_fused = given && !small && !g_separate_h_quant && tile_gemm_supported((int)H) &&
-                       plans.gate_up.ksplit == 1;
+  const bool dense = ffn_dense(T, H, I, E, k);
+  const bool h_fused = given && !small && !dense && !g_separate_h_quant &&
+                       tile_gemm_supported((int)H) && plans.gate_up.ksplit == 1;
   if (h_fused) {
     g.h_quant_g = act_globals + 1;
     g.out = ws.h16;
@@ -961,6 +982,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
            "gate/up");
   else if (small)
     LAUNCH(launch_gemv(Epi::SWIGLU, g, false, stream), "gate/up");
+  else if (dense)
+    LAUNCH(launch_dense_gemv(Epi::SWIGLU, g, (int)P, plans.gate_up, nullptr, stream),
+           "gate/up");
   else
     LAUNCH(tile_gemm_supported((int)H)
                ? launch_tile_gemm(Epi::SWIGLU, g, bm, plans.gate_up, topk_ids, (int)P, stream)
@@ -1026,6 +1050,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     }
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
+  else if (dense)
+    LAUNCH(launch_dense_gemv(Epi::DOWN, d, (int)P, plans.down, nullptr, stream), "down");
   else
     LAUNCH(tile_gemm_supported((int)I)
                ? launch_tile_gemm(Epi::DOWN, d, bm_down, plans.down, topk_ids, (int)P, stream)

@@ -201,6 +201,20 @@ bool tile_gemm_supported(int K);
 TilePlan tile_gemm_plan(Epi epi, int64_t N, int64_t K, int64_t n_mblocks_bound, int64_t rows);
 hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, const TilePlan &plan,
                             const int32_t *ids, int rows, hipStream_t s);
+// The split-K reduce alone: adds the a.ksplit parts of a.partial in part
+// order for `rows` tile rows and applies the epilogue.
+hipError_t launch_split_reduce(Epi epi, const GemmArgs &a, int rows, const int32_t *ids,
+                               hipStream_t s);
+
+// Dense GEMV for M <= 32 rows (densegemv.hip): one weight stream shared by
+// all rows (dense mode: A rows pos = 0..M-1 through a_rowmap / a_shift as in
+// the tile GEMM, expert 0), weights in 128-byte row lines through an LDS
+// ring, MFMA 16x16x32 f16.  Needs K % 256 == 0.  dense_gemv_plan picks the
+// K split (partial_floats floats of workspace in GemmArgs::partial).
+bool dense_gemv_supported(int64_t M, int64_t K);
+TilePlan dense_gemv_plan(Epi epi, int64_t N, int64_t K, int64_t M);
+hipError_t launch_dense_gemv(Epi epi, const GemmArgs &a, int M, const TilePlan &plan,
+                             const int32_t *ids, hipStream_t s);
 
 // Small-M grouped GEMV (tiles of 16 rows): waves of a workgroup split K and
 // keep several 128-wide chunks of weight loads in flight.  a_bf16: A rows are

@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const GemmArgs p, int
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   float amax = 0.0f;
   // (positions past the kept pairs hold pair -1: nothing to write)
-  if (idx < total && (!ids || p.sorted_pairs[idx / N] >= 0)) {
+  if (idx < total && (!p.sorted_pairs || p.sorted_pairs[idx / N] >= 0)) {
     const int pos = (int)(idx / N), col = (int)(idx - (int64_t)pos * N);
     const int e = ids ? ids[p.sorted_pairs[pos]] : 0;
     const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
@@ -553,7 +553,12 @@ hipError_t launch_tile_gemm(Epi epi, const GemmArgs &a, int bm, const TilePlan &
   if (err != hipSuccess || plan.ksplit <= 1) return err;
   GemmArgs g = a;
   g.ksplit = plan.ksplit;
-  const dim3 grid((unsigned)(((int64_t)rows * a.N + 255) / 256)), block(256);
+  return launch_split_reduce(epi, g, rows, ids, s);
+}
+
+hipError_t launch_split_reduce(Epi epi, const GemmArgs &g, int rows, const int32_t *ids,
+                               hipStream_t s) {
+  const dim3 grid((unsigned)(((int64_t)rows * g.N + 255) / 256)), block(256);
   switch (epi) {
     case Epi::LINEAR:
       launch_kernel(split_reduce_kernel<Epi::LINEAR>, grid, block, 0, s, g, rows, ids);

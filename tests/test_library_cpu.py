@@ -278,6 +278,8 @@ def test_bench_names_the_kernel_the_library_dispatches():
     assert bench.gate_up_kernel(512, 2048, 512, 512, 8, "w4a16") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(2048, 4096, 1536, 128, 8, "w4a4") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(1, 5120, 17408, 1, 1, "w4a16") == "row_gemv_kernel"
-    assert bench.gate_up_kernel(8, 5120, 17408, 1, 1, "w4a16") == "tile_gemm_kernel"
+    assert bench.gate_up_kernel(8, 5120, 17408, 1, 1, "w4a16") == "dense_gemv_kernel"
+    assert bench.gate_up_kernel(32, 5120, 17408, 1, 1, "w4a16") == "dense_gemv_kernel"
+    assert bench.gate_up_kernel(33, 5120, 17408, 1, 1, "w4a16") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(16, 2048, 512, 512, 8, "w4a4") == "grouped_gemv_kernel"
     assert bench.gate_up_kernel(300, 96, 64, 4, 2, "w4a16") == "grouped_gemm_kernel"
