@@ -44,6 +44,7 @@ namespace {
 
 constexpr int kChunk = 64;             // K per pipeline stage
 constexpr int kStages = 3;
+constexpr int kSGroup = 4;             // chunks whose scales one load brings
 constexpr int kARow = kChunk * 2;      // bytes of one fp16 activation row per chunk
 constexpr int kBRow = kChunk / 2;      // code bytes of one weight row per chunk
 constexpr int kXcds = 8;
@@ -55,10 +56,19 @@ struct TileCfg {
   static constexpr int BROWS = 64 * NW;                 // weight rows per workgroup
   static constexpr int A_BYTES = BM * kARow;
   static constexpr int B_BYTES = BROWS * kBRow;
-  static constexpr int S_BYTES = BROWS * (kChunk / 16);
+  // 128-row blocks: scales in groups of kSGroup chunks (16 bytes per weight
+  // row, double-buffered after the ring) and the straight-line chunk.
+  // Smaller blocks, mostly a few rows of many small experts, are bound by
+  // latency and gain from more workgroups per CU, which LDS decides: their
+  // scales stay in the ring stage (4 bytes per row) and the footprint small.
+  static constexpr bool BIG = MS == 8;
+  static constexpr int S_BYTES = BIG ? 0 : BROWS * (kChunk / 16);
   static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int SG_BYTES = BIG ? BROWS * kSGroup * (kChunk / 16) : 0;
+  static constexpr int STAGES = kStages;
+  static constexpr int LDS_BYTES = STAGES * STAGE + 2 * SG_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024 / NW;   // 1 KB direct loads per wave
-  static constexpr int LOADS = A_LOADS + 2 + 1;         // per lane and chunk (A, codes, scales)
+  static constexpr int LOADS = A_LOADS + 2;             // per lane and chunk (A, codes)
   static_assert(A_BYTES % (1024 * NW) == 0, "activation stage splits over the waves");
 };
 
@@ -66,6 +76,22 @@ template <Epi EPI>
 constexpr int cols_per_wave() { return EPI == Epi::SWIGLU ? 32 : 64; }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// s_waitcnt vmcnt(min(n, N)) then s_barrier, for a run-time n (the count is
+// an instruction immediate; waiting for fewer outstanding loads is safe)
+template <int N>
+__device__ __forceinline__ void wait_vm_then_barrier(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      // (a plain barrier: __syncthreads would also wait for the newest loads)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+      return;
+    }
+    wait_vm_then_barrier<N - 1>(n);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
 
 __device__ __forceinline__ int arow_of(const GemmArgs &p, int pos) {
   return p.a_rowmap ? p.a_rowmap[pos] / p.a_rowdiv : pos;
@@ -171,7 +197,7 @@ __device__ __forceinline__ void store_h_quantised(const GemmArgs &p, const f32x4
 template <int MS, int NW, Epi EPI>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(const GemmArgs p) {
   using C = TileCfg<MS, NW>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kStages * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
@@ -228,7 +254,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
     const int h = (lane & 1) ^ ((R >> 3) & 1);
     csrc[j] = p.b_codes[mat] + (int64_t)e * p.b_codes_estride + (int64_t)row * (K / 2) + h * 16;
   }
-  // Scales: 4 bytes (one chunk) per row, wave w loads rows 64 w .. 64 w + 63.
+  // Scales: wave w loads rows 64 w .. 64 w + 63, lane l row 64 w + l.  One
+  // 16-byte load per row brings the scales of kSGroup chunks (a group; LDS
+  // row stride 16); the chunks of a part's last, incomplete group load their
+  // 4 bytes each (LDS row stride 4, one BROWS * 4 area per chunk).  Scale
+  // traffic is one row-sized request per weight row per group instead of one
+  // per chunk, which the load path, not the byte count, makes worth having.
   const uint8_t *ssrc;
   {
     int mat;
@@ -259,16 +290,35 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[ms][f] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this part's chunk range (the host makes every part non-empty)
+  // this part's chunk range: parts of whole scale groups where groups apply
+  // (the host makes every part non-empty; an empty one would write zeros)
   const int nch = K / kChunk;
-  const int cps = (nch + ksplit - 1) / ksplit;
+  int cps = (nch + ksplit - 1) / ksplit;
+  if (K % (kSGroup * kChunk) == 0) cps = (cps + kSGroup - 1) / kSGroup * kSGroup;
   const int c_begin = kz * cps;
   const int c_end = c_begin + cps < nch ? c_begin + cps : nch;
   const int last = c_end - 1;
+  // chunks from c_tail on form the incomplete last group.  Group loads need
+  // 16-byte aligned scale rows (K % 256 == 0, aligned matrices) and a part
+  // that starts on a group boundary of the row; otherwise every chunk loads
+  // its own 4 bytes.
+  const int64_t s_off = (int64_t)e * p.b_scales_estride;
+  const bool grouped =
+      C::BIG && K % (kSGroup * kChunk) == 0 && c_begin % kSGroup == 0 &&
+      ((reinterpret_cast<uintptr_t>(p.b_scales[0] + s_off) |
+        (EPI == Epi::SWIGLU ? reinterpret_cast<uintptr_t>(p.b_scales[1] + s_off) : 0)) & 15) == 0;
+  const int c_tail = grouped ? c_begin + (c_end - c_begin) / kSGroup * kSGroup : c_begin;
+  uint8_t *const sgroups = lds + C::STAGES * C::STAGE;
+  // scale loads issued with chunk c: 1 at a group's first chunk and at each
+  // chunk of the incomplete group, else 0
+  auto scale_loads = [&](int c) {
+    return (c >= c_tail || ((c - c_begin) & (kSGroup - 1)) == 0) ? 1 : 0;
+  };
 
-  // Issue the loads of chunk c (K is a multiple of 64) into ring slot c % 3.
+  // Issue the loads of chunk c (K is a multiple of 64) into ring slot c % 3,
+  // and its scale load if it has one.
   auto load_chunk = [&](int c) {
-    uint8_t *st = lds + (c % kStages) * C::STAGE;
+    uint8_t *st = lds + (c % C::STAGES) * C::STAGE;
     const int k0 = c * kChunk;
 #pragma unroll
     for (int j = 0; j < C::A_LOADS; ++j)
@@ -279,25 +329,99 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
       __builtin_amdgcn_global_load_lds(csrc[j] + k0 / 2,
                                        (lds_ptr_t)(st + C::A_BYTES + (2 * wave + j) * 1024), 16, 0,
                                        0);
-    __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
-                                     (lds_ptr_t)(st + C::A_BYTES + C::B_BYTES + wave * 256), 4,
-                                     0, 0);
+    const int rel = c - c_begin;
+    uint8_t *sg = sgroups + ((rel / kSGroup) & 1) * C::SG_BYTES;
+    if constexpr (!C::BIG)
+      __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
+                                       (lds_ptr_t)(st + C::A_BYTES + C::B_BYTES + wave * 256), 4,
+                                       0, 0);
+    else if (c >= c_tail)
+      __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
+                                       (lds_ptr_t)(sg + (rel & (kSGroup - 1)) * C::BROWS * 4 +
+                                                   wave * 256),
+                                       4, 0, 0);
+    else if ((rel & (kSGroup - 1)) == 0)
+      __builtin_amdgcn_global_load_lds(ssrc + k0 / 16, (lds_ptr_t)(sg + wave * 1024), 16, 0, 0);
   };
 
-  // FULL: every subtile holds rows, so the fragment reads and the MFMAs
-  // form one straight-line block the compiler can schedule ahead
-  auto compute = [&](int c, auto full) {
+  // One chunk with NSUB (a compile-time count) subtiles holding rows, so the
+  // whole chunk is straight-line code.  Order: the weight codes, the scales
+  // and step 0's activation fragments are requested together; step 0's
+  // weight fragments are dequantised while those reads land; then each
+  // subtile's four step-0 MFMAs are followed by the request of its step-1
+  // fragment into the same registers, with step 1's dequantisation spread
+  // between them, so LDS latency and VALU work overlap the matrix pipe.
+  auto compute = [&](int c, auto nsub_c) {
+    constexpr int NSUB = decltype(nsub_c)::value;
+    const uint8_t *st = lds + (c % C::STAGES) * C::STAGE;
+    const int rel = c - c_begin;
+    const uint8_t *sg = sgroups + ((rel / kSGroup) & 1) * C::SG_BYTES;
+    const bool tail = c >= c_tail;   // uniform
+    const int s_row = tail ? 4 : 16;
+    const uint8_t *sc = sg + (tail ? (rel & (kSGroup - 1)) * C::BROWS * 4
+                                   : (rel & (kSGroup - 1)) * 4) + lg;
+    u32x2 w[4];
+    uint32_t sb[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const int R = 64 * wave + 16 * f + lr;
+      const int pos = (((lg >> 1) ^ ((R >> 3) & 1)) << 4) + ((lg & 1) << 3);
+      w[f] = *reinterpret_cast<const u32x2 *>(st + C::A_BYTES + R * kBRow + pos);
+      sb[f] = sc[R * s_row];
+    }
+    const uint8_t *abase = st + lr * kARow;
+    const int gran0 = ((2 * lg) ^ ((lr >> 1) & 7)) * 16;
+    const int gran1 = ((2 * lg + 1) ^ ((lr >> 1) & 7)) * 16;
+    f16x8 a[NSUB];
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms)
+      a[ms] = *reinterpret_cast<const f16x8 *>(abase + ms * 16 * kARow + gran0);
+    // (scheduling fences keep this order: the compiler otherwise sinks each
+    // fragment read next to its MFMAs and waits on it there)
+    if constexpr (NSUB >= 4) __builtin_amdgcn_sched_barrier(0);
+    f16x2 s2[4];
+    f16x8 b0[4], b1[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      f16x2 unused;
+      e4m3x2_to_f16_pairs(sb[f], s2[f], unused);
+      b0[f] = dequant8_f16(w[f][0], s2[f]);
+    }
+    if constexpr (NSUB >= 4) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        acc[ms][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], b0[f], acc[ms][f], 0, 0, 0);
+      a[ms] = *reinterpret_cast<const f16x8 *>(abase + ms * 16 * kARow + gran1);
+      if (ms < 4) b1[ms] = dequant8_f16(w[ms][1], s2[ms]);
+      if constexpr (NSUB >= 4) __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int f = NSUB; f < 4; ++f) b1[f] = dequant8_f16(w[f][1], s2[f]);
+    if constexpr (NSUB >= 4) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ms = 0; ms < NSUB; ++ms) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        acc[ms][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[ms], b1[f], acc[ms][f], 0, 0, 0);
+    }
+  };
+
+  // The compact chunk for smaller blocks: subtiles past the block's rows are
+  // skipped by uniform branches (FULL: all hold rows).
+  auto compute_small = [&](int c, auto full) {
     constexpr bool FULL = decltype(full)::value;
-    const uint8_t *st = lds + (c % kStages) * C::STAGE;
+    const uint8_t *st = lds + (c % C::STAGES) * C::STAGE;
+    const uint8_t *sc = st + C::A_BYTES + C::B_BYTES + lg;
     f16x8 bf[2][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int R = 64 * wave + 16 * f + lr;
       const int pos = (((lg >> 1) ^ ((R >> 3) & 1)) << 4) + ((lg & 1) << 3);
       const u32x2 w = *reinterpret_cast<const u32x2 *>(st + C::A_BYTES + R * kBRow + pos);
-      const uint32_t sb = st[C::A_BYTES + C::B_BYTES + R * 4 + lg];
       f16x2 s0, s1;
-      e4m3x2_to_f16_pairs(sb, s0, s1);
+      e4m3x2_to_f16_pairs(sc[R * 4], s0, s1);
       bf[0][f] = dequant8_f16(w[0], s0);
       bf[1][f] = dequant8_f16(w[1], s0);
     }
@@ -316,25 +440,47 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
     }
   };
 
-  // Ring: chunks c + 1 and c + 2 are in flight while chunk c is multiplied.
-  // The wait before each barrier leaves only the newest chunk's loads
-  // outstanding; the barrier then also guarantees every wave is done with
-  // the slot the next loads overwrite.  Past the end the last chunk is
-  // requested again (a cache hit into a slot nobody reads).
-  auto run = [&](auto full) {
-    load_chunk(c_begin);
-    load_chunk(c_begin + 1 <= last ? c_begin + 1 : last);
+  // Ring of S stages: chunks c + 1 .. c + S - 1 are in flight while chunk c
+  // is multiplied.  The wait before each barrier leaves only the loads of
+  // chunks c + 1 .. c + S - 2 outstanding (their count depends on which bring
+  // scales, and shrinks past the end); the barrier then also guarantees every
+  // wave is done with the ring slot and the scale buffer the next loads
+  // overwrite (a scale buffer is reused two groups later: S <= 5).
+  auto run = [&](auto step) {
+    constexpr int S = C::STAGES;
+#pragma unroll
+    for (int d = 0; d < S - 1; ++d)
+      if (c_begin + d <= last) load_chunk(c_begin + d);
     for (int c = c_begin; c <= last; ++c) {
-      // (a plain barrier: __syncthreads would also wait for the newest loads)
-      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(C::LOADS) : "memory");
-      load_chunk(c + 2 <= last ? c + 2 : last);
-      compute(c, full);
+      // loads still allowed in flight: those of chunks c + 1 .. c + S - 2
+      int n = 0;
+#pragma unroll
+      for (int d = 1; d <= S - 2; ++d)
+        if (c + d <= last) n += C::LOADS + scale_loads(c + d);
+      wait_vm_then_barrier<(S - 2) * (C::LOADS + 1)>(n);
+      if (c + S - 1 <= last) load_chunk(c + S - 1);
+      step(c);
     }
   };
-  if (nrows >= C::BM)
-    run(std::true_type{});
-  else
-    run(std::false_type{});
+  if (c_begin > last) {
+  } else if constexpr (C::BIG) {
+    // subtiles holding rows (uniform): one straight-line loop per count
+    const int nsub = nrows >= C::BM ? MS : (nrows + 15) / 16;
+    auto pick = [&](auto self, auto n) {
+      constexpr int NS = decltype(n)::value;
+      if constexpr (NS >= 1) {
+        if (nsub == NS)
+          run([&](int c) { compute(c, std::integral_constant<int, NS>{}); });
+        else
+          self(self, std::integral_constant<int, NS - 1>{});
+      }
+    };
+    pick(pick, std::integral_constant<int, MS>{});
+  } else if (nrows >= C::BM) {
+    run([&](int c) { compute_small(c, std::true_type{}); });
+  } else {
+    run([&](int c) { compute_small(c, std::false_type{}); });
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds rows 4*lg + j (j = 0..3) of each subtile and
@@ -532,7 +678,9 @@ TilePlan tile_gemm_plan(Epi epi, int64_t N, int64_t K, int64_t n_mblocks_bound, 
     int64_t ks = (kFillGroups + items4 - 1) / items4;
     if (ks > nch / 2) ks = nch / 2;
     if (ks >= 2) {
-      const int64_t cps = (nch + ks - 1) / ks;
+      // (the kernel rounds a part up to whole scale groups when K % 256 == 0)
+      int64_t cps = (nch + ks - 1) / ks;
+      if (K % (kSGroup * kChunk) == 0) cps = (cps + kSGroup - 1) / kSGroup * kSGroup;
       t.ksplit = (int)((nch + cps - 1) / cps);
       t.partial_floats = (size_t)t.ksplit * rows * (epi == Epi::SWIGLU ? 2 * N : N);
       return t;
