@@ -637,11 +637,18 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
 
 // y[t] = sum over slots j (in order) of sum over slices c (in order) of
 // ypart[t k + j][c]: the token's k n_c partial rows are consecutive, so row
-// q = j n_c + c; four outputs per thread, eight rows' loads in flight.
-__global__ __launch_bounds__(256) void ffn_combine_kernel(const float *ypart, int64_t T, int64_t H,
-                                                          int k, int n_c, const int32_t *ids,
-                                                          int E, void *y, OutType yt) {
-  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+// q = j n_c + c; four outputs per thread, sixteen rows' loads in flight (a
+// decode step's rows in one round trip), one wave per workgroup so the small
+// grid spreads over many CUs.  (Folding this sum into the fused kernel, the
+// last workgroup of each token adding the rows, measured slower: the
+// store-publish-reload chain it puts at the kernel's end costs more than
+// this launch.)
+constexpr int kCombineThreads = 64;
+constexpr int kCombineBatch = 16;
+__global__ __launch_bounds__(kCombineThreads) void ffn_combine_kernel(
+    const float *ypart, int64_t T, int64_t H, int k, int n_c, const int32_t *ids, int E, void *y,
+    OutType yt) {
+  const int64_t i = ((int64_t)blockIdx.x * kCombineThreads + threadIdx.x) * 4;
   if (i >= T * H) return;
   const int64_t t = i / H, col = i - t * H;
   const int n = k * n_c;
@@ -652,15 +659,15 @@ __global__ __launch_bounds__(256) void ffn_combine_kernel(const float *ypart, in
   for (int j = 0; j < k; ++j) keep |= ((unsigned)ids[t * k + j] < (unsigned)E ? 1u : 0u) << j;
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
   bool any = false;
-  for (int q0 = 0; q0 < n; q0 += 8) {
-    f32x4 v[8];
+  for (int q0 = 0; q0 < n; q0 += kCombineBatch) {
+    f32x4 v[kCombineBatch];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kCombineBatch; ++u) {
       const int q = q0 + u < n ? q0 + u : n - 1;   // (past the end: a valid row, not added)
       v[u] = *reinterpret_cast<const f32x4 *>(base + (int64_t)q * H);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kCombineBatch; ++u) {
       const int q = q0 + u;
       if (q < n && ((keep >> (q / n_c)) & 1u)) {
         acc = any ? acc + v[u] : v[u];
@@ -726,7 +733,9 @@ hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, co
                               int E, void *y, OutType yt, hipStream_t s) {
   if (H % 4 != 0 || k > 32) return hipErrorInvalidValue;
   const int64_t threads = ((int64_t)T * H + 3) / 4;
-  launch_kernel(ffn_combine_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+  launch_kernel(ffn_combine_kernel,
+                dim3((unsigned)((threads + kCombineThreads - 1) / kCombineThreads)),
+                dim3(kCombineThreads), 0, s,
                 ypart, (int64_t)T, (int64_t)H, k, I / kFfnCols, ids, E, y, yt);
   return hipGetLastError();
 }

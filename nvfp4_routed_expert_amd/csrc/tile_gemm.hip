@@ -198,13 +198,17 @@ template <int MS, int NW, Epi EPI>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(const GemmArgs p) {
   using C = TileCfg<MS, NW>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index is uniform: in a scalar register, LDS offsets and loop
+  // conditions derived from it stay scalar)
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
   const int K = p.K, N = p.N;
   constexpr int kCols = cols_per_wave<EPI>();
   const int n_tiles = (N + NW * kCols - 1) / (NW * kCols);
   const int ksplit = p.ksplit > 1 ? p.ksplit : 1;
-  const int n_mb = p.n_mblocks_dev ? *p.n_mblocks_dev : p.n_mblocks;
+  const int n_mb =
+      __builtin_amdgcn_readfirstlane(p.n_mblocks_dev ? *p.n_mblocks_dev : p.n_mblocks);
   const int n_items = n_mb * n_tiles * ksplit;
   const int per = (n_items + kXcds - 1) / kXcds;
   const int slot = blockIdx.x / kXcds;
@@ -307,7 +311,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
       C::BIG && K % (kSGroup * kChunk) == 0 && c_begin % kSGroup == 0 &&
       ((reinterpret_cast<uintptr_t>(p.b_scales[0] + s_off) |
         (EPI == Epi::SWIGLU ? reinterpret_cast<uintptr_t>(p.b_scales[1] + s_off) : 0)) & 15) == 0;
-  const int c_tail = grouped ? c_begin + (c_end - c_begin) / kSGroup * kSGroup : c_begin;
+  const int c_tail = __builtin_amdgcn_readfirstlane(
+      grouped ? c_begin + (c_end - c_begin) / kSGroup * kSGroup : c_begin);
   uint8_t *const sgroups = lds + C::STAGES * C::STAGE;
   // scale loads issued with chunk c: 1 at a group's first chunk and at each
   // chunk of the incomplete group, else 0
