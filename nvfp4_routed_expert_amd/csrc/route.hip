@@ -202,7 +202,8 @@ __device__ __forceinline__ void merge_level(uint64_t (&c)[8], int lane) {
 }
 
 __device__ void wave_topk_merge(const LogitSrc &src, int64_t t, int E, int k, int renormalize,
-                                int32_t *ids, float *weights, int32_t *ids_copy) {
+                                int32_t *ids, float *weights, int32_t *ids_copy,
+                                bool device_scope_ids = false) {
   const int lane = threadIdx.x & 63;
   float v[8];
   uint64_t c[8];
@@ -243,7 +244,10 @@ __device__ void wave_topk_merge(const LogitSrc &src, int64_t t, int E, int k, in
     denom = wave_sum(s);
   }
   if (lane < k) {
-    ids[lane] = my_idx;
+    if (device_scope_ids)
+      __hip_atomic_store(ids + lane, my_idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      ids[lane] = my_idx;
     weights[lane] = ex / denom;
     if (ids_copy) ids_copy[lane] = my_idx;
   }
@@ -683,10 +687,14 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
 // Decode-sized routing in one launch (T k <= 256 pairs, E <= 512, k <= 8):
 // one wavefront per token (own workgroup, so tokens spread over CUs) takes
 // the top-k with the merge network and publishes ids and weights; each wave
-// then takes a ticket from a counter in the caller's workspace
-// (acquire-release at device scope), and the wave holding the last ticket,
-// which therefore sees every token's ids, resets the counter and builds the
-// permutation alone.
+// then takes a ticket from a counter in the caller's workspace, and the wave
+// holding the last ticket, which therefore sees every token's ids, resets
+// the counter and builds the permutation alone.  The ids are written and
+// read as device-scope (relaxed agent) atomics, performed at the device's
+// coherence point past the per-XCD L2s, and each wave waits for its stores
+// to complete before taking its ticket: this orders them before the last
+// wave's reads without the whole-L2 write-back and invalidate that release
+// and acquire fences cost.
 //
 // Permutation by bit-sliced matching: pair p = lane + 64 s sits in slot s of
 // its lane (pairs past P carry expert E, above every real one).  Ten ballots
@@ -720,10 +728,11 @@ __global__ __launch_bounds__(64) void route_decode_kernel(const LogitSrc logits,
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
   wave_topk_merge(logits, t, E, k, renormalize, ids + (int64_t)t * k, weights + (int64_t)t * k,
-                  nullptr);
+                  nullptr, true);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's ids stores complete
   uint32_t mine = 0;
   if (lane == 0)
-    mine = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    mine = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   mine = __builtin_amdgcn_readfirstlane(mine);
   if (mine != (uint32_t)T - 1) return;
   if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -735,7 +744,7 @@ __global__ __launch_bounds__(64) void route_decode_kernel(const LogitSrc logits,
 #pragma unroll
   for (int s = 0; s < kSlots; ++s) {
     const int p = lane + 64 * s;
-    ev[s] = p < P ? ids[p] : E;
+    ev[s] = p < P ? __hip_atomic_load(ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : E;
 #pragma unroll
     for (int b = 0; b < kRouteBits; ++b) bits[s][b] = __builtin_amdgcn_ballot_w64((ev[s] >> b) & 1);
   }
