@@ -626,6 +626,269 @@ def read_ceiling(step_bytes):
     return res
 
 
+HOST_LINK_PEAK_GBS = 63.0   # PCIe 5.0 x16, one direction (32 GT/s x 16 lanes, 128b/130b)
+
+
+def paged_main(args):
+    """Expert paging on a routed-expert step: every expert's NVFP4 weights in
+    pinned host memory, a device pool of S slots.  A step routes
+    (moe_route_topk), plans the slots (moe_expert_cache_plan), copies the
+    missing experts into the pool (moe_expert_cache_fetch), orders the pairs
+    by slot (moe_permute_pairs) and runs the FFN on the pool.  The routing
+    batches cycle over 64 seeded logits tensors of the workload's routing (or
+    one with a Zipf router bias of the given exponent: skewed popularity).  Prints one JSON line: step
+    throughput, hit rate, bytes fetched per step, the stages' times and the
+    fetch kernel's rate against the host link; beside it the same steps with
+    every expert resident in HBM."""
+    import numpy as np
+    import torch
+
+    from nvfp4_routed_expert_amd import native, synth, weights
+
+    wl = synth.WORKLOADS[args.workload or "moe_decode"]
+    if wl.act != "w4a16" or wl.E < 2:
+        sys.exit("--paged runs the W4A16 routed-expert workloads")
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    T, H, I, E, k, S = wl.T, wl.H, wl.I, wl.E, wl.k, args.paged
+    P = T * k
+    expert_bytes = 3 * (nv_bytes(H * I) + 4)
+    n_batches = 64
+    x = synth.activations(T, H).to(dev)
+    zipf = wl.zipf_s if args.paged_zipf is None else args.paged_zipf
+    logits = [torch.from_numpy(synth.router_logits(T, E, seed=b, zipf_s=zipf)).to(dev)
+              for b in range(n_batches)]
+    w_dev = weights.synthetic_experts(E, H, I, 0, dev)
+    host = native.ExpertWeights(*[t.cpu().pin_memory() for t in (
+        w_dev.gate_codes, w_dev.gate_scales, w_dev.gate_global, w_dev.up_codes, w_dev.up_scales,
+        w_dev.up_global, w_dev.down_codes, w_dev.down_scales, w_dev.down_global)])
+    cache = native.ExpertCache(host, S, dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    ids, slot_ids = torch.empty((T, k), **i32), torch.empty((T, k), **i32)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off, pairs = torch.empty(E + 1, **i32), torch.empty(P, **i32)
+    off_s, pairs_s = torch.empty(S + 1, **i32), torch.empty(P, **i32)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws_p = torch.empty(native.ffn_workspace_bytes(T, H, I, S, k), dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(native.ffn_workspace_bytes(T, H, I, E, k), dtype=torch.uint8, device=dev)
+    rws = native.route_workspace(T, E, k, dev)
+    stages = ["route", "plan", "fetch", "permute", "ffn"]
+
+    def paged_step(b, ev=None):
+        mark = (lambda j: ev[j].record()) if ev else (lambda j: None)
+        mark(0)
+        native.moe_route_topk(logits[b], k, True, out=(ids, wts, off, pairs), workspace=rws)
+        mark(1)
+        cache.plan(ids, slot_ids=slot_ids)
+        mark(2)
+        cache.fetch_planned(P)
+        mark(3)
+        native.moe_permute_pairs(slot_ids, S, out=(off_s, pairs_s))
+        mark(4)
+        native.moe_grouped_nvfp4_ffn(x, cache.pool, slot_ids, wts, off_s, pairs_s, k,
+                                     out_dtype=torch.bfloat16, workspace=ws_p, out=y)
+        mark(5)
+
+    def resident_step(b):
+        native.moe_route_topk(logits[b], k, True, out=(ids, wts, off, pairs), workspace=rws)
+        native.moe_grouped_nvfp4_ffn(x, w_dev, ids, wts, off, pairs, k,
+                                     out_dtype=torch.bfloat16, workspace=ws_r, out=y)
+
+    def timed(fn, n):
+        # a GPU sleep first keeps the stream busy while the host enqueues the
+        # steps, so they run back to back (no host gaps inside the events)
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(400_000_000)
+        a.record()
+        for i in range(n):
+            fn(i % n_batches)
+        z.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(z) / n
+
+    # the pool warms up over the warmup steps, then K timed steps (eager
+    # launches; a step's fetch dominates its time)
+    for i in range(args.warmup):
+        paged_step(i % n_batches)
+    ms_paged = timed(lambda b: paged_step((b + args.warmup) % n_batches), args.steps)
+
+    ms_overlap = None
+    if args.paged_overlap:
+        # Two streams.  Side stream: routing, slot plan (the previous step's
+        # experts protected), fetch and pair order of step i; it first waits
+        # for the FFN of step i-2, the last reader of the buffers it reuses
+        # and of the experts it may evict.  Main stream: the FFN of step i
+        # after its fetch.  So the fetch of step i runs beside the FFN of
+        # step i-1.
+        main = torch.cuda.current_stream()
+        side = torch.cuda.Stream()
+        buf = [dict(ids=torch.empty((T, k), **i32), slot=torch.empty((T, k), **i32),
+                    wts=torch.empty((T, k), dtype=torch.float32, device=dev),
+                    off=torch.empty(E + 1, **i32), pairs=torch.empty(P, **i32),
+                    off_s=torch.empty(S + 1, **i32), pairs_s=torch.empty(P, **i32))
+               for _ in range(2)]
+        rws2 = native.route_workspace(T, E, k, dev)
+
+        nlog_o = torch.zeros(max(args.steps, args.warmup, 1), **i32)
+
+        def pipeline(n, b0, start_ev):
+            ffn_done = [None] * n
+            side.wait_event(start_ev)
+            for i in range(n):
+                bb = buf[i % 2]
+                with torch.cuda.stream(side):
+                    if i >= 2:
+                        side.wait_event(ffn_done[i - 2])
+                    native.moe_route_topk(logits[(b0 + i) % n_batches], k, True,
+                                          out=(bb["ids"], bb["wts"], bb["off"], bb["pairs"]),
+                                          workspace=rws2)
+                    cache.plan(bb["ids"], protect_previous=True, slot_ids=bb["slot"])
+                    cache.fetch_planned(P)
+                    native.moe_permute_pairs(bb["slot"], S, out=(bb["off_s"], bb["pairs_s"]))
+                    fetched = torch.cuda.Event()
+                    fetched.record(side)
+                    nlog_o[i:i + 1].copy_(cache.n_fetch)
+                main.wait_event(fetched)
+                native.moe_grouped_nvfp4_ffn(x, cache.pool, bb["slot"], bb["wts"], bb["off_s"],
+                                             bb["pairs_s"], k, out_dtype=torch.bfloat16,
+                                             workspace=ws_p, out=y)
+                ffn_done[i] = torch.cuda.Event()
+                ffn_done[i].record(main)
+            main.wait_stream(side)
+
+        w0 = torch.cuda.Event()
+        w0.record(main)
+        pipeline(args.warmup, 0, w0)
+        torch.cuda.synchronize()
+        a, z = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(400_000_000)
+        a.record(main)
+        pipeline(args.steps, args.warmup, a)
+        z.record(main)
+        torch.cuda.synchronize()
+        if int(nlog_o[:args.steps].min().item()) < 0:
+            sys.exit(f"--paged {S} --paged-overlap: two steps' experts did not fit in the pool")
+        ms_overlap = a.elapsed_time(z) / args.steps
+    for i in range(min(args.warmup, 8)):
+        resident_step(i % n_batches)
+    ms_res = timed(resident_step, args.steps)
+
+    # stage times and fetch counts: one more pass, events around each call
+    n_stat = min(args.steps, n_batches)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_stat)]
+    nlog = torch.empty(n_stat, **i32)
+    dlog = torch.empty((n_stat, T, k), **i32)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(400_000_000)
+    for i in range(n_stat):
+        paged_step((i + args.warmup + args.steps) % n_batches, evs[i])
+        nlog[i:i + 1].copy_(cache.n_fetch)
+        dlog[i].copy_(ids)
+    torch.cuda.synchronize()
+    st = {s: [evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3 for i in range(n_stat)]
+          for j, s in enumerate(stages)}
+    nf = nlog.cpu().numpy()
+    if (nf < 0).any():
+        sys.exit(f"--paged {S}: a step's experts did not fit in the pool")
+    distinct = np.array([len(np.unique(d)) for d in dlog.cpu().numpy()])
+    fetched = int(nf.sum())
+    fetch_us = np.array(st["fetch"])
+    busy = nf > 0
+    fetch_gbs = (float(nf[busy].sum()) * expert_bytes / (fetch_us[busy].sum() * 1e-6) / 1e9
+                 if busy.any() else None)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle on a sample of routing batch 0: its slot plan from an
+        # empty pool and the FFN rows of the sampled tokens; the paged output
+        # of the same batch is checked against it
+        paged_step(0)
+        torch.cuda.synchronize()
+        cpu = paged_cpu_baseline(args, wl, S, zipf, y)
+        if not cpu["gate_rel_frob_vs_oracle"] <= 1e-3:
+            print(json.dumps({"error": "correctness gate failed", "cpu_baseline": cpu}),
+                  flush=True)
+            sys.exit(3)
+    out = {
+        "metric": "NVFP4 MoE FFN with expert paging: tokens/s",
+        "value": round(T / (ms_paged * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_paged, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if gate_up_kernel(T, H, I, S, k, wl.act).startswith("row_") else "f16",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "_paged", "tokens": T, "hidden": H,
+                   "intermediate": I, "experts": E, "top_k": k, "slots": S,
+                   "router_bias_zipf_s": zipf, "routing_batches": n_batches,
+                   "host_weights_gb": round(E * expert_bytes / 1e9, 3),
+                   "pool_gb": round(S * expert_bytes / 1e9, 3), "graph": False,
+                   "parallelism": "single GPU"},
+        "hit_rate": round(1.0 - fetched / float(distinct.sum()), 4),
+        "experts_per_step": round(float(distinct.mean()), 2),
+        "fetched_per_step": round(float(nf.mean()), 2),
+        "fetched_mb_per_step": round(float(nf.mean()) * expert_bytes / 1e6, 3),
+        "stage_us": {s: round(float(np.mean(v)), 2) for s, v in st.items()},
+        "resident_ms_per_step": round(ms_res, 5),
+        "overlapped_ms_per_step": None if ms_overlap is None else round(ms_overlap, 5),
+        "roofline": {"bound": "host_link", "kernel": "cache_fetch_kernel",
+                     "achieved": None if fetch_gbs is None else round(fetch_gbs, 2),
+                     "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                     "frac": None if fetch_gbs is None else round(fetch_gbs / HOST_LINK_PEAK_GBS, 4),
+                     "traffic": None,
+                     "alg_per_unit": f"{expert_bytes} bytes per fetched expert"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def paged_cpu_baseline(args, wl, S, zipf, y_gpu):
+    """The oracle (as it stands) on a bounded sample of a paged step: the slot
+    plan of routing batch 0 and the FFN rows of a token sample, timed on the
+    host; tokens/s.  Also the correctness gate for those rows."""
+    import numpy as np
+    import threadpoolctl
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from helpers import LazyOracleExperts
+    from oracle import nvfp4_oracle as O
+    from nvfp4_routed_expert_amd import synth
+
+    T, H, I, E, k = wl.T, wl.H, wl.I, wl.E, wl.k
+    n_tok = args.cpu_tokens or min(T, 16)
+    tokens = list(range(0, T, max(1, T // n_tok)))[:n_tok]
+    xf = synth.activations(T, H).float().numpy()
+    logits = synth.router_logits(T, E, seed=0, zipf_s=zipf)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    rids, rw = O.route_topk(logits, k)
+    w_ref = LazyOracleExperts(E, H, I, np.unique(rids[tokens]), 0)   # offline quantisation
+    t0 = time.perf_counter()
+    O.expert_slot_plan(O.SlotState(E, S), rids, 1, 1)
+    ref, _ = O.moe_ffn(xf, rids, rw, w_ref, tokens=tokens)
+    dt = time.perf_counter() - t0
+    got = y_gpu.float().cpu().numpy()[tokens].astype(np.float64)
+    r = O.bf16_rne(ref)
+    return {"kind": "oracle", "cores": int(threads), "value": round(len(tokens) / dt, 3),
+            "unit": "tokens/s",
+            "sample": f"slot plan of one routing batch and the FFN of {len(tokens)} of {T} "
+                      f"tokens, fp64 numpy oracle, {dt:.2f} s",
+            "seconds": round(dt, 3),
+            "gate_rel_frob_vs_oracle": float(np.linalg.norm(got - r) / np.linalg.norm(r))}
+
+
+def copy_calibration():
+    """A plain elementwise copy of 1 GiB (reads 1 GiB, writes 1 GiB), run a few
+    times; under rocprofv3 --pmc its FETCH_SIZE / WRITE_SIZE give the scale
+    from counter units to bytes."""
+    import torch
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
 def oracle_leg(args, wl, gumbel, x, x_cpu, logits_np, ids, wts, off, pairs, w0, act, ag,
                counts, mfma_bound, with_router, with_shared, router_w, router_b, sh_w):
     """The correctness gate and the CPU baseline of one workload, before any

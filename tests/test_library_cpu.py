@@ -283,3 +283,29 @@ def test_bench_names_the_kernel_the_library_dispatches():
     assert bench.gate_up_kernel(33, 5120, 17408, 1, 1, "w4a16") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(16, 2048, 512, 512, 8, "w4a4") == "grouped_gemv_kernel"
     assert bench.gate_up_kernel(300, 96, 64, 4, 2, "w4a16") == "grouped_gemm_kernel"
+
+
+def test_bench_and_entry_reference_only_defined_names():
+    """Every name bench.py and __graft_entry__.py load at module or function
+    level is bound somewhere in the file, imported, or a builtin: a helper
+    dropped in an edit (a flag whose handler no longer exists) fails here
+    rather than on the GPU machine."""
+    import ast
+    import builtins
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for fname in ("bench.py", "__graft_entry__.py"):
+        tree = ast.parse(open(os.path.join(root, fname)).read())
+        bound = set(dir(builtins)) | {"__file__"}
+        for node in ast.walk(tree):
+            if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+                bound.add(node.name)
+            elif isinstance(node, (ast.Import, ast.ImportFrom)):
+                bound |= {(a.asname or a.name).split(".")[0] for a in node.names}
+            elif isinstance(node, ast.arg):
+                bound.add(node.arg)
+            elif isinstance(node, ast.ExceptHandler) and node.name:
+                bound.add(node.name)
+            elif isinstance(node, ast.Name) and isinstance(node.ctx, ast.Store):
+                bound.add(node.id)
+        used = {n.id for n in ast.walk(tree) if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load)}
+        assert not (used - bound), (fname, sorted(used - bound))
