@@ -498,13 +498,14 @@ hipError_t launch_down_sum(const GemmArgs &a, const int32_t *ids, int k, int T, 
 // Fused decode FFN: both projections in one launch (H = 2048)
 // ---------------------------------------------------------------------------
 //
-// One workgroup of 8 waves per (tile row pos, slice c of kFfnCols columns of
-// I): the slice's gate and up rows (32 + 32 per wave, whole 2048-wide rows
-// per load step as in row_gemv_kernel) give the slice of h, bf16-rounded
-// into LDS; the down rows' matching kFfnCols columns (8 lanes per row, 8
-// rows per load step, 256 rows per wave) are loaded before the barrier that
-// publishes h, and their dot products with the h slice give a partial output
-// row per (pair, slice), scaled by the down global and the routing weight.
+// One workgroup of kFfnWaves = 16 waves per (tile row pos, slice c of
+// kFfnCols = 256 columns of I): the slice's gate and up rows (16 + 16 per
+// wave, whole 2048-wide rows per load step as in row_gemv_kernel) give the
+// slice of h, bf16-rounded into LDS; the down rows' matching kFfnCols
+// columns (8 lanes per row, 8 rows per load step, 128 rows per wave) are
+// loaded before the barrier that publishes h, and their dot products with
+// the h slice give a partial output row per (pair, slice), scaled by the
+// down global and the routing weight.
 // ffn_combine_kernel adds the slices and the token's slots in a fixed order.
 // One launch streams all three matrices, so the down stream does not pay a
 // launch's ramp of its own.
@@ -535,7 +536,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   const int token = pair / rt.k;
   const int H = g.K, I = g.N;   // gate/up: [I, H]; down: [H, I]
 
-  // ---- gate / up: rows c * kFfnCols + 32 wave + 8 it + step, it = 0..3
+  // ---- gate / up: rows c * kFfnCols + 16 wave + 8 it + step, it = 0..1
   const uint32_t gcode_row = (uint32_t)H / 2, gscale_row = (uint32_t)H / 16;
   const uint8_t *gc[2], *gs[2];
 #pragma unroll
@@ -592,7 +593,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
           (uint16_t)f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
   }
 
-  // ---- down: rows 256 wave + 64 b + 8 st + lane / 8, columns c * kFfnCols +
+  // ---- down: rows 128 wave + 64 b + 8 st + lane / 8, columns c * kFfnCols +
   // 32 (lane % 8) .. + 32
   const int sub = lane >> 3, seg = lane & 7;
   const uint32_t dcode_row = (uint32_t)I / 2, dscale_row = (uint32_t)I / 16;

@@ -19,7 +19,10 @@
 // scale in packed fp16: exact) and issues 4 * MS v_mfma_f32_16x16x32_f16 per
 // 32-wide step.  Subtiles of 16 rows beyond the block's row count are
 // skipped, so a block of an expert with few tokens costs its weight stream
-// and little else.
+// and little else.  128-row blocks load the scales of four chunks at once
+// (one 16-byte load per weight row) and run one straight-line loop per
+// count of filled subtiles; smaller blocks, whose occupancy LDS decides,
+// keep per-chunk scales in the ring stage and a compact loop.
 //
 // K permutation: in a 64-wide chunk lane group g = lane / 16 supplies
 // k = 16 g + 8 i .. +8 at step i (0, 1) for both operands, so a lane needs
