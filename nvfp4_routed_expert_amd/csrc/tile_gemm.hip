@@ -282,6 +282,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
   // the host pass of this compiler drops the kernel's launch stub)
   static_assert(C::A_LOADS <= 16, "activation loads per wave");
   int64_t aoff[16];   // element offsets of this lane's activation pieces
+  // Only the 16-row subtiles that hold rows are staged: instruction j of
+  // this wave (rows 8 (wave + NW j) ..) is issued when those rows lie below
+  // rows16, so a block of a few rows does not fetch 64 or 128 rows of
+  // padding; a_loads counts this wave's activation loads per chunk.
+  const int rows16 = nrows >= C::BM ? C::BM : (nrows + 15) / 16 * 16;
+  int a_loads = 0;
+#pragma unroll
+  for (int j = 0; j < C::A_LOADS; ++j) a_loads += 8 * (wave + NW * j) < rows16 ? 1 : 0;
 #pragma unroll
   for (int j = 0; j < C::A_LOADS; ++j) {
     const int q = wave + NW * j;
@@ -330,8 +338,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
     const int k0 = c * kChunk;
 #pragma unroll
     for (int j = 0; j < C::A_LOADS; ++j)
-      __builtin_amdgcn_global_load_lds(p.A + aoff[j] + k0, (lds_ptr_t)(st + (wave + NW * j) * 1024),
-                                       16, 0, 0);
+      if (8 * (wave + NW * j) < rows16)   // uniform per wave
+        __builtin_amdgcn_global_load_lds(p.A + aoff[j] + k0,
+                                         (lds_ptr_t)(st + (wave + NW * j) * 1024), 16, 0, 0);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_global_load_lds(csrc[j] + k0 / 2,
@@ -464,7 +473,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
       int n = 0;
 #pragma unroll
       for (int d = 1; d <= S - 2; ++d)
-        if (c + d <= last) n += C::LOADS + scale_loads(c + d);
+        if (c + d <= last) n += a_loads + 2 + scale_loads(c + d);
       wait_vm_then_barrier<(S - 2) * (C::LOADS + 1)>(n);
       if (c + S - 1 <= last) load_chunk(c + S - 1);
       step(c);
