@@ -180,6 +180,12 @@ size_t nvfp4_linear_workspace_size(int64_t M, int64_t N, int64_t K,
  * stream; calls that may run at the same time need separate workspaces.
  * (Decode-sized batches route in one launch whose last finishing wavefront
  * builds the permutation; the word counts finished wavefronts.)
+ * Top-k only: with expert_offsets and sorted_pairs both NULL the call writes
+ * the ids and weights and nothing else; workspace may then be NULL (it is
+ * not touched).  The permutation can follow later from moe_permute_pairs on
+ * the ids, e.g. on another stream beside the fused decode FFN, which takes
+ * the pairs in pair order (moe_grouped_nvfp4_ffn).  Exactly one of the two
+ * NULL is NVFP4_ERR_INVALID_ARGUMENT.
  */
 nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E,
                             int32_t k, int renormalize, int32_t *topk_ids,
@@ -367,6 +373,13 @@ size_t moe_shared_expert_ffn_workspace_size(int64_t T, int64_t H, int64_t I);
  * it has none), and in W4A4 g_h is taken over the kept pairs only.  The
  * offsets and sorted pairs must then come from moe_permute_pairs on the
  * same ids (it leaves dropped pairs out).
+ * Pair order: expert_offsets and sorted_pairs may both be NULL where the
+ * decode batch runs on the fused per-row kernels (W4A16, H = 2048,
+ * I % 256 == 0, T*k <= 256, 2*T*k <= 32*E); each pair p then takes its expert
+ * from topk_ids[p] directly, dropped ids included, and y is bit-identical to
+ * the call with the permutation (the combine sums a token's pairs in j order
+ * either way).  Elsewhere, or with one of the two NULL,
+ * NVFP4_ERR_INVALID_ARGUMENT.
  * workspace: moe_grouped_nvfp4_ffn_workspace_size bytes (device, 16-byte
  * aligned), scratch only; its contents after the call are unspecified
  * except as moe_grouped_nvfp4_ffn_debug_h describes.

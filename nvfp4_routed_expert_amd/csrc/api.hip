@@ -186,14 +186,20 @@ int ffn_bm_down(int64_t T, int64_t E, int64_t k) {
   const int bm = ffn_bm(T, E, k);
   return E > 1 && bm == 64 ? 32 : bm;
 }
-// m-blocks of up to bm rows over P pairs: each expert rounds up once (a
-// single expert, the dense MLP, has exactly ceil(P / bm))
+// The fused decode path (W4A16 decode batch, H = 2048, I a multiple of 256)
+// reads the routing in pair order when it is given no permutation.
+bool ffn_pair_order_ok(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, nvfp4_act_mode act) {
+  return act == NVFP4_W4A16 && ffn_small(T, E, k) && row_gemv_supported((int)H) &&
+         row_gemv_supported((int)I) && row_ffn_supported((int)H, (int)I);
+}
 // A single expert (a dense MLP) with 3 to 32 rows: one weight stream shared
 // by every row in the dense GEMV (K of both projections a multiple of 256).
 bool ffn_dense(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
   return E == 1 && !ffn_small(T, E, k) && dense_gemv_supported(T * k, H) &&
          dense_gemv_supported(T * k, I);
 }
+// m-blocks of up to bm rows over P pairs: each expert rounds up once (a
+// single expert, the dense MLP, has exactly ceil(P / bm))
 int64_t ffn_max_mblocks(int64_t P, int64_t E, int bm) {
   return (P + bm - 1) / bm + (E > 1 ? (E < P ? E : P) : 0);
 }
@@ -492,13 +498,16 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
                             int32_t *expert_offsets, int32_t *sorted_pairs, void *workspace,
                             size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
+  // both permutation outputs NULL: the top-k alone (moe_permute_pairs can
+  // make the permutation later, e.g. on a second stream)
+  const bool topk_only = !expert_offsets && !sorted_pairs;
   if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
     CHECK_NULL(logits);
     CHECK_NULL(topk_ids);
     CHECK_NULL(topk_weights);
-    CHECK_NULL(sorted_pairs);
+    if (!topk_only) CHECK_NULL(sorted_pairs);
   }
-  CHECK_NULL(expert_offsets);
+  if (!topk_only) CHECK_NULL(expert_offsets);
   if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
   if (E < 1 || E > 1024)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "E = %d outside 1..1024", (int)E);
@@ -511,6 +520,13 @@ nvfp4_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k
   CHECK_ALIGN(topk_weights);
   CHECK_ALIGN(expert_offsets);
   CHECK_ALIGN(sorted_pairs);
+  if (topk_only) {   // (no ticket: the workspace is not used)
+    if (T > 0)
+      LAUNCH(launch_topk(LogitSrc{logits, 0, 1, nullptr, nullptr}, T, E, k, renormalize, topk_ids,
+                         topk_weights, stream),
+             "top-k");
+    return NVFP4_OK;
+  }
   TRY(check_workspace(workspace, workspace_bytes, moe_route_topk_workspace_size(T, E, k)));
   if (T == 0) {   // no pairs: every offset is 0
     LAUNCH(launch_permute(nullptr, 0, E, k, expert_offsets, nullptr, stream), "offsets");
@@ -800,12 +816,17 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
                                    void *y, nvfp4_dtype y_dtype, void *workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
   g_last_error[0] = 0;
+  // no permutation (both NULL): only on the fused decode path, which then
+  // takes the pairs in pair order
+  const bool pair_order = !expert_offsets && !sorted_pairs;
   if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
     CHECK_NULL(x);
     CHECK_NULL(topk_ids);
     CHECK_NULL(topk_weights);
-    CHECK_NULL(expert_offsets);
-    CHECK_NULL(sorted_pairs);
+    if (!pair_order) {
+      CHECK_NULL(expert_offsets);
+      CHECK_NULL(sorted_pairs);
+    }
     CHECK_NULL(y);
   }
   CHECK_NULL(w);
@@ -835,6 +856,10 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
       return fail(NVFP4_ERR_INVALID_ARGUMENT, "act_global_mode %d invalid", (int)act_global_mode);
     if (act_global_mode == NVFP4_GLOBAL_GIVEN) CHECK_NULL(act_globals);
   }
+  if (T > 0 && pair_order && !ffn_pair_order_ok(T, H, I, E, k, act))
+    return fail(NVFP4_ERR_INVALID_ARGUMENT,
+                "expert_offsets and sorted_pairs may be NULL only on the fused decode path "
+                "(W4A16, H = 2048, I %% 256 == 0, T*k <= 256, 2*T*k <= 32*E)");
   CHECK_ALIGN(x);
   CHECK_ALIGN(y);
   CHECK_ALIGN(topk_ids);
@@ -929,6 +954,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.mblocks = ws.mblocks;
   g.n_mblocks_dev = ws.n_mblocks;
   g.n_mblocks = (int)ffn_max_mblocks(P, E, bm);
+  g.n_experts = E;
   g.extra_scale = a4 ? slot_gx : nullptr;
   g.out = ws.h;
   g.ldo = I;

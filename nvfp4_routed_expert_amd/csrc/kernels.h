@@ -86,6 +86,9 @@ struct LogitSrc {
 // decode-sized batches (route_decode_supported) route in one launch.
 bool route_decode_supported(int64_t T, int E, int k);
 hipError_t launch_ticket_reset(uint32_t *ticket, hipStream_t s);
+// The top-k alone (ids and weights, no permutation).
+hipError_t launch_topk(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
+                       int32_t *ids, float *weights, hipStream_t s);
 hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         uint32_t *ticket, hipStream_t s);
@@ -236,6 +239,7 @@ hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pai
                            bool h_by_pair = false);
 
 // Fused decode FFN (W4A16, H = 2048, I a multiple of 256): gate/up and down
+// (sorted_pairs null: pairs in pair order, ids outside 0..g.n_experts-1 skipped)
 // in one launch (a workgroup per tile row and 256-column slice of I, h kept
 // in LDS), partial rows in ypart [P][I / 256][H] (fp32), then a combine
 // that adds each token's slots and slices in order into y.  g: the gate/up

@@ -837,8 +837,15 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
                   renormalize, ids, weights, offsets, sorted_pairs, ticket);
     return hipGetLastError();
   }
-  // top-k: one wavefront per token, four per workgroup, so a decode batch
-  // spreads over several CUs (one wave per SIMD) instead of sharing one
+  hipError_t e = launch_topk(logits, T, E, k, renormalize, ids, weights, s);
+  if (e != hipSuccess) return e;
+  return launch_permute(ids, T, E, k, offsets, sorted_pairs, s);
+}
+
+hipError_t launch_topk(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
+                       int32_t *ids, float *weights, hipStream_t s) {
+  // one wavefront per token, four per workgroup, so a decode batch spreads
+  // over several CUs (one wave per SIMD) instead of sharing one
   const int64_t blocks = (T + 3) / 4;
   if (E <= 512 && k <= 8)
     launch_kernel(topk_merge_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
@@ -846,9 +853,7 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
   else
     launch_kernel(topk_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T, E, k,
                   renormalize, ids, weights);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_permute(ids, T, E, k, offsets, sorted_pairs, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_permute(const int32_t *ids, int64_t T, int E, int k, int32_t *offsets,

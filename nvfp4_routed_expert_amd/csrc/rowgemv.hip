@@ -530,9 +530,13 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   const int item = (blockIdx.x % kXcds) * per + slot;
   if (slot >= per || item >= n_items) return;   // whole workgroup (uniform)
   const int pos = item / n_c, c = item - pos * n_c;
-  const int pair = rt.sorted_pairs[pos];
-  if (pair < 0) return;   // past the kept pairs (dropped ones have no position)
+  // expert order (pair = sorted_pairs[pos]; positions past the kept pairs
+  // hold -1), or pair order without a permutation (dropped pairs skipped
+  // here by their id)
+  const int pair = rt.sorted_pairs ? rt.sorted_pairs[pos] : pos;
+  if (pair < 0) return;
   const int e = rt.ids[pair];
+  if (!rt.sorted_pairs && (unsigned)e >= (unsigned)g.n_experts) return;
   const int token = pair / rt.k;
   const int H = g.K, I = g.N;   // gate/up: [I, H]; down: [H, I]
 

@@ -233,23 +233,29 @@ def route_workspace(T, E, k, device):
     return _init_route_workspace(ws)
 
 
-def moe_route_topk(logits, k, renormalize=True, out=None, workspace=None):
+def moe_route_topk(logits, k, renormalize=True, out=None, workspace=None, permute=True):
     """Returns (topk_ids [T,k] i32, topk_weights [T,k] f32, expert_offsets [E+1] i32,
     sorted_pairs [T*k] i32).  workspace: from route_workspace (a fresh zeroed
-    one is made when omitted)."""
+    one is made when omitted).  permute=False: the top-k alone (offsets and
+    pairs returned as None; moe_permute_pairs makes them)."""
     T, E = logits.shape
     dev = logits.device
     if out is None:
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
         w = torch.empty((T, k), dtype=torch.float32, device=dev)
-        off = torch.empty(E + 1, dtype=torch.int32, device=dev)
-        pairs = torch.empty(T * k, dtype=torch.int32, device=dev)
+        off = torch.empty(E + 1, dtype=torch.int32, device=dev) if permute else None
+        pairs = torch.empty(T * k, dtype=torch.int32, device=dev) if permute else None
     else:
         ids, w, off, pairs = out
+        if not permute:
+            off = pairs = None
     L = lib()
     nbytes = L.moe_route_topk_workspace_size(T, E, k)
-    ws = _workspace(nbytes, dev, workspace) if workspace is not None else \
-        route_workspace(T, E, k, dev)
+    if not permute:
+        ws, nbytes = None, 0
+    else:
+        ws = _workspace(nbytes, dev, workspace) if workspace is not None else \
+            route_workspace(T, E, k, dev)
     _check(L.moe_route_topk(_ptr(logits), T, E, k, int(bool(renormalize)), _ptr(ids), _ptr(w),
                             _ptr(off), _ptr(pairs), _ptr(ws), nbytes, _stream()))
     return ids, w, off, pairs
@@ -424,8 +430,9 @@ def ffn_workspace_bytes(T, H, I, E, k, act=W4A16):
 def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_ids, topk_weights, expert_offsets,
                           sorted_pairs, k, act=W4A16, act_globals=None,
                           out_dtype=torch.bfloat16, workspace=None, out=None):
-    """Routed-expert gated FFN over moe_route_topk's outputs.
-    Returns (y [T,H], act_globals or None)."""
+    """Routed-expert gated FFN over moe_route_topk's outputs.  expert_offsets
+    and sorted_pairs may both be None on the fused decode path (the pairs are
+    then read in pair order).  Returns (y [T,H], act_globals or None)."""
     T, H = x.shape
     E, I = weights.num_experts, weights.intermediate
     dev = x.device

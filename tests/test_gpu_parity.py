@@ -420,6 +420,40 @@ def test_moe_ffn_w4a16_skewed_batches(T, H, I, E, k, zipf):
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("T,I,E,k", [(16, 512, 512, 8), (5, 2304, 16, 3), (32, 512, 512, 8)])
+def test_fused_decode_in_pair_order(T, I, E, k):
+    """The fused decode path given no permutation (expert_offsets and
+    sorted_pairs NULL) reads the pairs in pair order: bit-identical to the
+    call with the permutation, also with dropped slots (ids -1 and E); the
+    top-k alone (moe_route_topk without its permutation outputs) gives the
+    same ids and weights; NULL permutation outputs are refused off that
+    path."""
+    import bench
+    H = 2048
+    assert bench.gate_up_kernel(T, H, I, E, k, "w4a16") == "row_ffn_kernel"
+    say("fused decode pair order", T, H, I, E, k)
+    x = synth.activations(T, H, 4).to(DEV)
+    logits = torch.from_numpy(synth.router_logits(T, E, 4)).to(DEV)
+    ids, wts, off, pairs = native.moe_route_topk(logits, k)
+    ids2, wts2, off2, pairs2 = native.moe_route_topk(logits, k, permute=False)
+    assert off2 is None and pairs2 is None
+    assert torch.equal(ids, ids2) and torch.equal(wts, wts2)
+    w = weights.synthetic_experts(E, H, I, 4, DEV, experts=np.unique(to_np(ids)))
+    for ids_c in (ids, ids.clone().index_fill_(1, torch.tensor([0], device=DEV), -1)):
+        if ids_c is not ids:
+            ids_c[1, :] = -1
+            ids_c[2, k - 1] = E
+        off_c, pairs_c = native.moe_permute_pairs(ids_c, E)
+        for dt in (torch.float32, torch.bfloat16):
+            y_ref, _ = native.moe_grouped_nvfp4_ffn(x, w, ids_c, wts, off_c, pairs_c, k,
+                                                    out_dtype=dt)
+            y_po, _ = native.moe_grouped_nvfp4_ffn(x, w, ids_c, wts, None, None, k, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert torch.equal(y_po, y_ref), (dt, ids_c is ids)
+    with pytest.raises(native.NVFP4Error):   # not the fused decode path
+        native.moe_grouped_nvfp4_ffn(x, w, ids, wts, None, None, k, act=native.W4A4)
+
+
 def test_moe_ffn_in_a_graph():
     """The grouped-GEMM FFN captured into a graph: every replay (with eager
     calls between them) equals the eager result bit for bit."""

@@ -105,6 +105,11 @@ def test_route_validation():
     assert r(16, 64, 8, logits=FAKE_MIS) == 3
     assert r((1 << 22), 64, 8) == 2
     assert r(16, 64, 8) == 4 and "workspace" in _last()
+    # the top-k alone: both permutation outputs NULL (no workspace needed);
+    # one of them NULL is a missing argument
+    assert L.moe_route_topk(FAKE, 16, 64, 8, 1, FAKE, FAKE, None, FAKE, FAKE, 256, None) == 1
+    assert L.moe_route_topk(FAKE, 16, 64, 8, 1, FAKE, FAKE, FAKE, None, FAKE, 256, None) == 1
+    assert L.moe_route_topk(FAKE_MIS, 16, 64, 8, 1, FAKE, FAKE, None, None, None, 0, None) == 3
 
 
 def test_ffn_validation():
@@ -135,6 +140,15 @@ def test_ffn_validation():
     # a W4A4 call with given globals needs them
     assert L.moe_grouped_nvfp4_ffn(FAKE, T, H, I, E, k, FAKE, FAKE, FAKE, FAKE, ctypes.byref(w), 1,
                                    1, None, FAKE, 0, FAKE, ws, None) == 1
+    # no permutation (both NULL) only on the fused decode path; one NULL alone
+    # is a missing argument everywhere
+    g = lambda off, pairs, H=H, I=I, E=E, k=k, act=0: L.moe_grouped_nvfp4_ffn(
+        FAKE, T, H, I, E, k, FAKE, FAKE, off, pairs, ctypes.byref(w), act, 0, None, FAKE, 0, FAKE,
+        L.moe_grouped_nvfp4_ffn_workspace_size(T, H, I, E, k, act), None)
+    assert g(None, None) == 1 and "fused decode path" in _last()      # H = 256
+    assert g(None, None, H=2048, I=512, E=512, k=8, act=1) == 1      # W4A4
+    assert g(None, FAKE, H=2048, I=512, E=512, k=8) == 1
+    assert g(FAKE, None, H=2048, I=512, E=512, k=8) == 1
 
 
 def test_router_validation():
