@@ -19,10 +19,12 @@
 // scale in packed fp16: exact) and issues 4 * MS v_mfma_f32_16x16x32_f16 per
 // 32-wide step.  Subtiles of 16 rows beyond the block's row count are
 // skipped, so a block of an expert with few tokens costs its weight stream
-// and little else.  128-row blocks load the scales of four chunks at once
-// (one 16-byte load per weight row) and run one straight-line loop per
-// count of filled subtiles; smaller blocks, whose occupancy LDS decides,
-// keep per-chunk scales in the ring stage and a compact loop.
+// and little else.  Scales of four chunks arrive at once (one 16-byte load
+// per weight row instead of four 4-byte ones: the loads, not their bytes,
+// limit this path, and a 4-byte load costs the L2 a whole line).  128-row
+// blocks run one straight-line loop per count of filled subtiles; smaller
+// blocks, whose occupancy LDS decides, keep a single scale buffer and a
+// compact loop.
 //
 // K permutation: in a 64-wide chunk lane group g = lane / 16 supplies
 // k = 16 g + 8 i .. +8 at step i (0, 1) for both operands, so a lane needs
@@ -59,17 +61,18 @@ struct TileCfg {
   static constexpr int BROWS = 64 * NW;                 // weight rows per workgroup
   static constexpr int A_BYTES = BM * kARow;
   static constexpr int B_BYTES = BROWS * kBRow;
-  // 128-row blocks: scales in groups of kSGroup chunks (16 bytes per weight
-  // row, double-buffered after the ring) and the straight-line chunk.
-  // Smaller blocks, mostly a few rows of many small experts, are bound by
-  // latency and gain from more workgroups per CU, which LDS decides: their
-  // scales stay in the ring stage (4 bytes per row) and the footprint small.
+  // Scales arrive in groups of kSGroup chunks (16 bytes per weight row) in a
+  // buffer after the ring.  128-row blocks (the straight-line chunk)
+  // double-buffer it.  Smaller blocks, mostly a few rows of many small
+  // experts, are bound by latency and gain from more workgroups per CU,
+  // which LDS decides: they keep one buffer and copy each lane's bytes of a
+  // group into registers at the group's first chunk.
   static constexpr bool BIG = MS == 8;
-  static constexpr int S_BYTES = BIG ? 0 : BROWS * (kChunk / 16);
-  static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int SG_BYTES = BIG ? BROWS * kSGroup * (kChunk / 16) : 0;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int SG_BYTES = BROWS * kSGroup * (kChunk / 16);
+  static constexpr int SG_BUFS = BIG ? 2 : 1;
   static constexpr int STAGES = kStages;
-  static constexpr int LDS_BYTES = STAGES * STAGE + 2 * SG_BYTES;
+  static constexpr int LDS_BYTES = STAGES * STAGE + SG_BUFS * SG_BYTES;
   static constexpr int A_LOADS = A_BYTES / 1024 / NW;   // 1 KB direct loads per wave
   static constexpr int LOADS = A_LOADS + 2;             // per lane and chunk (A, codes)
   static_assert(A_BYTES % (1024 * NW) == 0, "activation stage splits over the waves");
@@ -319,7 +322,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
   // its own 4 bytes.
   const int64_t s_off = (int64_t)e * p.b_scales_estride;
   const bool grouped =
-      C::BIG && K % (kSGroup * kChunk) == 0 && c_begin % kSGroup == 0 &&
+      K % (kSGroup * kChunk) == 0 && c_begin % kSGroup == 0 &&
       ((reinterpret_cast<uintptr_t>(p.b_scales[0] + s_off) |
         (EPI == Epi::SWIGLU ? reinterpret_cast<uintptr_t>(p.b_scales[1] + s_off) : 0)) & 15) == 0;
   const int c_tail = __builtin_amdgcn_readfirstlane(
@@ -347,12 +350,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
                                        (lds_ptr_t)(st + C::A_BYTES + (2 * wave + j) * 1024), 16, 0,
                                        0);
     const int rel = c - c_begin;
-    uint8_t *sg = sgroups + ((rel / kSGroup) & 1) * C::SG_BYTES;
-    if constexpr (!C::BIG)
-      __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
-                                       (lds_ptr_t)(st + C::A_BYTES + C::B_BYTES + wave * 256), 4,
-                                       0, 0);
-    else if (c >= c_tail)
+    uint8_t *sg = sgroups + (C::SG_BUFS == 2 ? ((rel / kSGroup) & 1) * C::SG_BYTES : 0);
+    if (c >= c_tail)
       __builtin_amdgcn_global_load_lds(ssrc + k0 / 16,
                                        (lds_ptr_t)(sg + (rel & (kSGroup - 1)) * C::BROWS * 4 +
                                                    wave * 256),
@@ -372,7 +371,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
     constexpr int NSUB = decltype(nsub_c)::value;
     const uint8_t *st = lds + (c % C::STAGES) * C::STAGE;
     const int rel = c - c_begin;
-    const uint8_t *sg = sgroups + ((rel / kSGroup) & 1) * C::SG_BYTES;
+    const uint8_t *sg = sgroups + ((rel / kSGroup) & 1) * C::SG_BYTES;   // (two buffers)
     const bool tail = c >= c_tail;   // uniform
     const int s_row = tail ? 4 : 16;
     const uint8_t *sc = sg + (tail ? (rel & (kSGroup - 1)) * C::BROWS * 4
@@ -427,18 +426,40 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void tile_gemm_kernel(con
 
   // The compact chunk for smaller blocks: subtiles past the block's rows are
   // skipped by uniform branches (FULL: all hold rows).
+  // Scale bytes of the current group for the compact chunk: byte c' of
+  // gbytes[f] is this lane's scale (block lg) of fragment f's row in the
+  // group's chunk c'.  They are read from the one group buffer at the
+  // group's first chunk, before the loads of the next group (issued two
+  // chunks later, after two barriers) overwrite it.
+  uint32_t gbytes[4] = {0u, 0u, 0u, 0u};
   auto compute_small = [&](int c, auto full) {
     constexpr bool FULL = decltype(full)::value;
     const uint8_t *st = lds + (c % C::STAGES) * C::STAGE;
-    const uint8_t *sc = st + C::A_BYTES + C::B_BYTES + lg;
+    const int rel = c - c_begin, cg = rel & (kSGroup - 1);
+    const bool tail = c >= c_tail;   // uniform
+    if (!tail && cg == 0) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const int R = 64 * wave + 16 * f + lr;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(sgroups + R * 16);
+        // byte lg of each chunk's word: selector lg, lg + 4 picks from
+        // (hi, lo) = (word 1, word 0), then the two halves are joined
+        const uint32_t sel = 0x0c0c0400u + (uint32_t)lg * 0x0101u;
+        const uint32_t lo = __builtin_amdgcn_perm(v[1], v[0], sel);
+        const uint32_t hi = __builtin_amdgcn_perm(v[3], v[2], sel);
+        gbytes[f] = lo | (hi << 16);
+      }
+    }
     f16x8 bf[2][4];
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
       const int R = 64 * wave + 16 * f + lr;
       const int pos = (((lg >> 1) ^ ((R >> 3) & 1)) << 4) + ((lg & 1) << 3);
       const u32x2 w = *reinterpret_cast<const u32x2 *>(st + C::A_BYTES + R * kBRow + pos);
+      const uint32_t sbyte = tail ? sgroups[cg * C::BROWS * 4 + R * 4 + lg]
+                                  : (gbytes[f] >> (8 * cg)) & 0xffu;
       f16x2 s0, s1;
-      e4m3x2_to_f16_pairs(sc[R * 4], s0, s1);
+      e4m3x2_to_f16_pairs(sbyte, s0, s1);
       bf[0][f] = dequant8_f16(w[0], s0);
       bf[1][f] = dequant8_f16(w[1], s0);
     }
