@@ -113,6 +113,8 @@ ROUTE_CASES = [
     ("big_e_3x1024_k32", 3, 1024, 32, None, True),
     ("long_9000x64_k2", 9000, 64, 2, None, True),
     ("decode_ties_32x256_k8", 32, 256, 8, None, True),
+    ("decode_ties_16x300_k8", 16, 300, 8, None, True),
+    ("ragged_2x3_k2", 2, 3, 2, None, False),
     ("one_token_1x512_k8", 1, 512, 8, None, True),
     ("split_ragged_700x301_k5", 700, 301, 5, None, True),     # last expert group short
     ("past_split_lds_300000x2_k1", 300000, 2, 1, None, True),  # bitmaps beyond one workgroup's LDS
@@ -135,11 +137,12 @@ def test_route_topk_parity(case):
     np.testing.assert_allclose(to_np(w), rw, rtol=5e-6, atol=1e-7)
 
 
-def test_route_workspace_reused_across_calls():
+@pytest.mark.parametrize("T", [16, 32])
+def test_route_workspace_reused_across_calls(T):
     """One zeroed workspace serves successive decode-sized calls: each call's
     last wavefront resets the counter, and every call is exact."""
-    T, E, k = 16, 512, 8
-    say("route workspace reuse")
+    E, k = 512, 8
+    say("route workspace reuse", T)
     ws = native.route_workspace(T, E, k, DEV)
     for seed in (3, 4, 5, 6):
         logits = synth.router_logits(T, E, seed=seed)
