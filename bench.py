@@ -63,6 +63,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0 = workload default)")
     ap.add_argument("--eager", action="store_true", help="no graph capture")
+    ap.add_argument("--separate-routing", action="store_true",
+                    help="decode: route in its own launch (moe_route_topk) instead of inside "
+                         "the FFN launch (moe_route_ffn_decode)")
     ap.add_argument("--given-globals", action="store_true",
                     help="W4A4: static activation scales given by the caller (g_x from the "
                          "input's amax, g_h a fixed calibration value) instead of online ones")
@@ -325,13 +328,27 @@ def measure(args, name, gumbel=False, steps=200, warmup=20):
                                          act_globals=ag, out_dtype=out.dtype, workspace=ws_,
                                          out=out)
 
+    # Decode on the fused kernel: the routing runs inside the FFN launch (each
+    # workgroup takes its token's top-k) and the permutation beside the combine.
+    fused_route = (route and not with_router and act == native.W4A16 and
+                   not args.separate_routing and
+                   native.route_ffn_decode_supported(T, H, I, E, k))
+    if fused_route:
+        fws = torch.empty(native.lib().moe_route_ffn_decode_workspace_size(T, H, I, E, k),
+                          dtype=torch.uint8, device=dev)
+
     def step(wset):
         if with_router:
             native.moe_router_topk(x, router_w, k, True, bias=router_b,
                                    out=(ids, wts, off, pairs), workspace=rtws)
-        elif route:
-            native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
-        ffn(wset)
+            ffn(wset)
+        elif fused_route:
+            native.moe_route_ffn_decode(logits, x, wset, k, True, route_out=(ids, wts, off, pairs),
+                                        out=y, workspace=fws)
+        else:
+            if route:
+                native.moe_route_topk(logits, k, True, out=(ids, wts, off, pairs), workspace=rws)
+            ffn(wset)
         if with_shared:
             native.moe_shared_expert_ffn(x, *sh_w, y=y, accumulate=True, workspace=sh_ws)
 
@@ -358,6 +375,8 @@ def measure(args, name, gumbel=False, steps=200, warmup=20):
     gateup_flops = 4 * P * H * I
     if kname == "row_ffn_kernel":   # the fused decode kernel streams the down matrices too
         gateup_bytes = 3 * active * (nv_bytes(H * I) + 4) + T * H * 2
+        if fused_route:   # ... and reads the logits of the tokens it routes
+            gateup_bytes += T * E * 4
         gateup_flops = 6 * P * H * I
     # MFMA-bound when the step's arithmetic intensity exceeds the ridge point
     prefill_mfma = alg_flops / alg_bytes > MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -502,12 +521,16 @@ def measure(args, name, gumbel=False, steps=200, warmup=20):
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     wname = wl.name + ("_gumbel" if gumbel else "")
     roofline["traffic"] = stored_traffic(kname, wname)
-    roofline["kernel"] = kname + (" (gate/up, SiLU*up, down: both projections)"
+    roofline["kernel"] = kname + (" (routing top-k, gate/up, SiLU*up, down)"
+                                  if kname == "row_ffn_kernel" and fused_route else
+                                  " (gate/up, SiLU*up, down: both projections)"
                                   if kname == "row_ffn_kernel" else
                                   " (gate/up projection, SiLU*up epilogue)")
     roofline["kernel_avg_us"] = round(stage_avg_us["gate_up"], 3)
     roofline["alg_per_launch"] = int(gateup_flops if prefill_mfma else gateup_bytes)
-    roofline["alg_units_per_launch"] = (f"{active} experts x 3 NVFP4 [{I},{H}] + x"
+    roofline["alg_units_per_launch"] = (f"{active} experts x 3 NVFP4 [{I},{H}] + x + logits"
+                                        if kname == "row_ffn_kernel" and fused_route else
+                                        f"{active} experts x 3 NVFP4 [{I},{H}] + x"
                                         if kname == "row_ffn_kernel" and not prefill_mfma else
                                         f"{active} experts x 2 NVFP4 [{I},{H}] + x"
                                         if not prefill_mfma else f"{P} pairs x 4*H*I flop")
@@ -535,6 +558,9 @@ def measure(args, name, gumbel=False, steps=200, warmup=20):
                    "shared_expert": (f"bf16, intermediate {I}" if with_shared else None),
                    "router": ("bf16 router GEMM + top-k" if with_router else
                               "top-k of given logits" if route else None),
+                   "routing": ("inside the FFN launch (each workgroup takes its token's top-k; "
+                               "the permutation beside the combine)" if fused_route else
+                               "own launch" if route else None),
                    "act_globals": ("given (static)" if ag is not None else
                                    "online" if act == native.W4A4 else None),
                    "h_quant": ("separate pass" if args.separate_h_quant else "fused")

@@ -401,6 +401,35 @@ size_t moe_grouped_nvfp4_ffn_workspace_size(int64_t T, int64_t H, int64_t I,
                                             nvfp4_act_mode act);
 
 /*
+ * moe_route_ffn_decode: the routing and the routed-expert FFN of a decode
+ * batch in two launches instead of three.  Decode streams the routed
+ * experts' weights once per step, so the step's time is that stream plus
+ * whatever runs before it (Eider page, "Performance"; "Qwen3.8 Flash Next":
+ * the 512 experts).  Computes exactly what moe_route_topk(logits, T, E, k,
+ * renormalize) followed by moe_grouped_nvfp4_ffn(act W4A16) computes on the
+ * same inputs: topk_ids, topk_weights, expert_offsets, sorted_pairs and y
+ * are bit-identical to theirs.  Each workgroup of the fused FFN kernel takes
+ * the top-k of its own token (the same merge network) before it streams
+ * that pair's expert, so the stream does not wait for a routing launch; the
+ * permutation is made by one more workgroup of the combine launch.
+ * logits f32 [T, E]; x bf16 [T, H]; y [T, H] bf16 or f32; the other
+ * outputs as moe_route_topk's.
+ * Requires the fused decode shapes: H = 2048, I % 256 == 0, 1 <= k <= 8,
+ * k <= E <= 512, T*k <= 256, 2*T*k <= 32*E (NVFP4_ERR_UNSUPPORTED_SHAPE
+ * otherwise; use the two calls there).  T = 0 writes E + 1 zero offsets.
+ * workspace: moe_route_ffn_decode_workspace_size bytes (device, 16-byte
+ * aligned), scratch only (no state between calls).
+ */
+nvfp4_status moe_route_ffn_decode(const float *logits, const void *x, int64_t T, int64_t H,
+                                  int64_t I, int32_t E, int32_t k, int renormalize,
+                                  int32_t *topk_ids, float *topk_weights,
+                                  int32_t *expert_offsets, int32_t *sorted_pairs,
+                                  const nvfp4_expert_weights *w, void *y, nvfp4_dtype y_dtype,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+size_t moe_route_ffn_decode_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E,
+                                           int32_t k);
+
+/*
  * moe_grouped_nvfp4_ffn_static: moe_grouped_nvfp4_ffn without a workspace
  * argument, for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops and harnesses that forbid hipMalloc.

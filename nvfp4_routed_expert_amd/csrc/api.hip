@@ -1096,6 +1096,119 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   return NVFP4_OK;
 }
 
+size_t moe_route_ffn_decode_workspace_size(int64_t T, int64_t H, int64_t I, int32_t E,
+                                           int32_t k) {
+  (void)E;
+  if (T < 0 || H < 0 || I < 0 || k < 0) return 0;
+  const int64_t parts = I / 256 > 0 ? I / 256 : 1;
+  const size_t bytes = (size_t)(T * k * parts * H) * sizeof(float);
+  return (bytes + 255) / 256 * 256 + 256;
+}
+
+nvfp4_status moe_route_ffn_decode(const float *logits, const void *x, int64_t T, int64_t H,
+                                  int64_t I, int32_t E, int32_t k, int renormalize,
+                                  int32_t *topk_ids, float *topk_weights,
+                                  int32_t *expert_offsets, int32_t *sorted_pairs,
+                                  const nvfp4_expert_weights *w, void *y, nvfp4_dtype y_dtype,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  if (T > 0) {   // (an empty batch may pass NULL for its empty arrays)
+    CHECK_NULL(logits);
+    CHECK_NULL(x);
+    CHECK_NULL(topk_ids);
+    CHECK_NULL(topk_weights);
+    CHECK_NULL(sorted_pairs);
+    CHECK_NULL(y);
+  }
+  CHECK_NULL(expert_offsets);
+  CHECK_NULL(w);
+  CHECK_NULL(w->gate_codes);
+  CHECK_NULL(w->up_codes);
+  CHECK_NULL(w->down_codes);
+  CHECK_NULL(w->gate_scales);
+  CHECK_NULL(w->up_scales);
+  CHECK_NULL(w->down_scales);
+  CHECK_NULL(w->gate_global);
+  CHECK_NULL(w->up_global);
+  CHECK_NULL(w->down_global);
+  if (T < 0) return fail(NVFP4_ERR_INVALID_ARGUMENT, "T = %lld < 0", (long long)T);
+  if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARGUMENT, "y_dtype %d is not BF16 or F32", (int)y_dtype);
+  if (k < 1 || k > kMaxFfnRouteK || E < k || E > 512)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k = %d, E = %d: needs 1 <= k <= 8, k <= E <= 512",
+                (int)k, (int)E);
+  if (!row_ffn_supported((int)H, (int)I) || !ffn_small(T, E, k))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE,
+                "the fused decode path needs H = 2048, I %% 256 == 0 (I > 0), T*k <= 256 and "
+                "2*T*k <= 32*E (H = %lld, I = %lld, T = %lld)",
+                (long long)H, (long long)I, (long long)T);
+  CHECK_ALIGN(logits);
+  CHECK_ALIGN(x);
+  CHECK_ALIGN(y);
+  CHECK_ALIGN(topk_ids);
+  CHECK_ALIGN(topk_weights);
+  CHECK_ALIGN(expert_offsets);
+  CHECK_ALIGN(sorted_pairs);
+  CHECK_ALIGN(w->gate_codes);
+  CHECK_ALIGN(w->up_codes);
+  CHECK_ALIGN(w->down_codes);
+  CHECK_ALIGN(w->gate_scales);
+  CHECK_ALIGN(w->up_scales);
+  CHECK_ALIGN(w->down_scales);
+  TRY(check_workspace(workspace, workspace_bytes,
+                      moe_route_ffn_decode_workspace_size(T, H, I, E, k)));
+  if (T == 0) {   // no pairs: every offset is 0
+    LAUNCH(launch_permute(nullptr, 0, E, k, expert_offsets, nullptr, stream), "offsets");
+    return NVFP4_OK;
+  }
+  const int64_t P = T * k;
+  float *ypart = static_cast<float *>(workspace);
+  GemmArgs g = {};
+  g.A = static_cast<const _Float16 *>(x);   // bf16 rows, read as given
+  g.lda = H;
+  g.b_codes[0] = w->gate_codes;
+  g.b_codes[1] = w->up_codes;
+  g.b_scales[0] = w->gate_scales;
+  g.b_scales[1] = w->up_scales;
+  g.b_global[0] = w->gate_global;
+  g.b_global[1] = w->up_global;
+  g.b_codes_estride = I * (H / 2);
+  g.b_scales_estride = I * (H / 16);
+  g.N = (int)I;
+  g.K = (int)H;
+  g.n_experts = E;
+  GemmArgs dd = {};
+  dd.b_codes[0] = w->down_codes;
+  dd.b_scales[0] = w->down_scales;
+  dd.b_global[0] = w->down_global;
+  dd.b_codes_estride = H * (I / 2);
+  dd.b_scales_estride = H * (I / 16);
+  dd.N = (int)H;
+  dd.K = (int)I;
+  const FfnRoute fr{logits, (int)E, renormalize, topk_ids, topk_weights};
+  // (the stage hook sees the same stages as moe_grouped_nvfp4_ffn; the plan,
+  // preparation and separate down stages are empty here)
+  mark(NVFP4_STAGE_PLAN, false, stream);
+  mark(NVFP4_STAGE_PLAN, true, stream);
+  mark(NVFP4_STAGE_X_PREP, false, stream);
+  mark(NVFP4_STAGE_X_PREP, true, stream);
+  mark_kernel(NVFP4_STAGE_GATE_UP, stream);
+  LAUNCH(launch_row_ffn(g, dd, nullptr, topk_ids, k, (int)P, ypart, stream, &fr),
+         "routing + gate/up + down");
+  g_timed_launch = TimedLaunch{nullptr, nullptr};
+  mark(NVFP4_STAGE_H_PREP, false, stream);
+  mark(NVFP4_STAGE_H_PREP, true, stream);
+  mark(NVFP4_STAGE_DOWN, false, stream);
+  mark(NVFP4_STAGE_DOWN, true, stream);
+  mark_kernel(NVFP4_STAGE_COMBINE, stream);
+  LAUNCH(launch_ffn_combine(ypart, (int)T, (int)H, (int)I, k, topk_ids, E, y,
+                            y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16, stream,
+                            expert_offsets, sorted_pairs),
+         "combine + permutation");
+  g_timed_launch = TimedLaunch{nullptr, nullptr};
+  return NVFP4_OK;
+}
+
 }  // extern "C"
 
 // ---- moe_grouped_nvfp4_ffn_static: the FFN with the library's own scratch --------

@@ -244,11 +244,28 @@ hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pai
 // in LDS), partial rows in ypart [P][I / 256][H] (fp32), then a combine
 // that adds each token's slots and slices in order into y.  g: the gate/up
 // arguments (A = bf16 x rows), d: the down arguments (pair weights set).
+// With a route (logits set, sorted_pairs null, E <= 512, k <= 8), each
+// workgroup takes the top-k of its own token from the fp32 logits [T, E]
+// (what the routing kernels compute, bit for bit) and the workgroup of slot
+// 0, slice 0 writes the token's ids_out / weights_out; ids and the pair
+// weights of g / d are then unused.  The combine given offsets (and
+// sorted_pairs) adds one workgroup that makes the permutation of the ids
+// (T k <= 256, E <= 512) beside the sums.
+struct FfnRoute {
+  const float *logits;
+  int E;
+  int renormalize;
+  int32_t *ids_out;
+  float *weights_out;
+};
+constexpr int kMaxFfnRouteK = 8;
 bool row_ffn_supported(int H, int I);
 hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *sorted_pairs,
-                          const int32_t *ids, int k, int P, float *ypart, hipStream_t s);
+                          const int32_t *ids, int k, int P, float *ypart, hipStream_t s,
+                          const FfnRoute *route = nullptr);
 hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, const int32_t *ids,
-                              int E, void *y, OutType yt, hipStream_t s);
+                              int E, void *y, OutType yt, hipStream_t s,
+                              int32_t *offsets = nullptr, int32_t *sorted_pairs = nullptr);
 
 // Token-major down projection for decode with the combine folded in: y[t] =
 // sum over slots j (in order) of w[t k + j] * g * (h[t k + j] . W_down[e]);

@@ -29,6 +29,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -520,9 +521,14 @@ constexpr int kXcds = 8;   // consecutive workgroups land on different XCDs
 
 __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs g,
                                                                  const GemmArgs d,
-                                                                 const Routing rt, int n_pos,
+                                                                 const Routing rt,
+                                                                 const FfnRoute fr, int n_pos,
                                                                  int n_c, float *ypart) {
   __shared__ uint16_t h_lds[kFfnCols];
+  __shared__ int32_t r_ids[kMaxFfnRouteK];
+  __shared__ float r_wts[kMaxFfnRouteK];
+  __shared__ uint64_t r_cand[kMaxRouteExperts / 8];   // each wave's 8 best keys
+  __shared__ float r_logit[kMaxRouteExperts];          // (the full softmax only)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n_items = n_pos * n_c;
   const int per = (n_items + kXcds - 1) / kXcds;
@@ -532,23 +538,14 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
   const int pos = item / n_c, c = item - pos * n_c;
   // expert order (pair = sorted_pairs[pos]; positions past the kept pairs
   // hold -1), or pair order without a permutation (dropped pairs skipped
-  // here by their id)
+  // here by their id), or pair order routed here from the logits
   const int pair = rt.sorted_pairs ? rt.sorted_pairs[pos] : pos;
   if (pair < 0) return;
-  const int e = rt.ids[pair];
-  if (!rt.sorted_pairs && (unsigned)e >= (unsigned)g.n_experts) return;
+  const int e_given = fr.logits ? 0 : rt.ids[pair];
+  if (!fr.logits && !rt.sorted_pairs && (unsigned)e_given >= (unsigned)g.n_experts) return;
   const int token = pair / rt.k;
   const int H = g.K, I = g.N;   // gate/up: [I, H]; down: [H, I]
 
-  // ---- gate / up: rows c * kFfnCols + 16 wave + 8 it + step, it = 0..1
-  const uint32_t gcode_row = (uint32_t)H / 2, gscale_row = (uint32_t)H / 16;
-  const uint8_t *gc[2], *gs[2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    gc[m] = g.b_codes[m] + (int64_t)e * g.b_codes_estride + 16 * lane;
-    gs[m] = g.b_scales[m] + (int64_t)e * g.b_scales_estride + 2 * lane;
-  }
-  const int grow0 = c * kFfnCols + kFfnGuRows * wave;
   uint32_t a[16];
   {
     const uint16_t *src = reinterpret_cast<const uint16_t *>(g.A) + (int64_t)token * g.lda + 32 * lane;
@@ -559,6 +556,65 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
       for (int j = 0; j < 4; ++j) a[4 * q + j] = v[j];
     }
   }
+  // Routed here, while the x row loads are in flight: waves 0..7 each take
+  // the 8 best of 64 logits (keys and order of the routing kernels), wave 0
+  // the 8 best of those 64 and the weights with the routing kernels'
+  // arithmetic in the same lanes, so ids and weights are theirs bit for bit;
+  // the workgroup of slot 0, slice 0 publishes them.
+  int e = e_given;
+  float route_w = 0.0f;
+  if (fr.logits) {   // uniform
+    const int j = pair - token * rt.k, k = rt.k, E = fr.E;
+    if (wave < kMaxRouteExperts / 64) {
+      const int ex = 64 * wave + lane;
+      const float v = ex < E ? fr.logits[(int64_t)token * E + ex] : 0.0f;
+      r_logit[ex] = v;
+      const uint64_t key = wave_top8_lanes(ex < E ? topk_key(v, ex) : 0ull, lane);
+      if (lane < 8) r_cand[8 * wave + lane] = key;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t mine = wave_top8_lanes(r_cand[lane], lane);   // lane j: the j-th key
+      const int my_idx = (int)~(uint32_t)mine;
+      const uint32_t m = (uint32_t)(mine >> 32);
+      const float my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+      const float lmax =
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
+      const float ex = lane < k ? expf(my_val - lmax) : 0.0f;
+      float denom;
+      if (fr.renormalize) {
+        denom = wave_sum(ex);
+      } else {   // this lane's logits lane + 64 i in i order, as the routing kernels add them
+        float sm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kMaxRouteExperts / 64; ++i)
+          if (lane + 64 * i < E) sm += expf(r_logit[lane + 64 * i] - lmax);
+        denom = wave_sum(sm);
+      }
+      if (lane < k) {
+        const float wgt = ex / denom;
+        r_ids[lane] = my_idx;
+        r_wts[lane] = wgt;
+        if (j == 0 && c == 0) {
+          fr.ids_out[(int64_t)token * k + lane] = my_idx;
+          fr.weights_out[(int64_t)token * k + lane] = wgt;
+        }
+      }
+    }
+    __syncthreads();
+    e = r_ids[j];
+    route_w = r_wts[j];
+  }
+
+  // ---- gate / up: rows c * kFfnCols + 16 wave + 8 it + step, it = 0..1
+  const uint32_t gcode_row = (uint32_t)H / 2, gscale_row = (uint32_t)H / 16;
+  const uint8_t *gc[2], *gs[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    gc[m] = g.b_codes[m] + (int64_t)e * g.b_codes_estride + 16 * lane;
+    gs[m] = g.b_scales[m] + (int64_t)e * g.b_scales_estride + 2 * lane;
+  }
+  const int grow0 = c * kFfnCols + kFfnGuRows * wave;
   u32x4 bq[2][kBatch][2];
   uint32_t sq[2][kBatch][2];
   auto load_gu = [&](int buf, int it) {
@@ -620,7 +676,7 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
 #pragma unroll
   for (int j = 0; j < 16; ++j)
     ah[j] = (uint32_t)h_lds[32 * seg + 2 * j] | ((uint32_t)h_lds[32 * seg + 2 * j + 1] << 16);
-  const float scale = d.b_global[0][e] * d.pair_weights[pair];
+  const float scale = d.b_global[0][e] * (fr.logits ? route_w : d.pair_weights[pair]);
   float *yrow = ypart + ((int64_t)pair * n_c + c) * H;
 #pragma unroll
   for (int b = 0; b < kFfnDnBatches; ++b) {
@@ -652,7 +708,13 @@ constexpr int kCombineThreads = 64;
 constexpr int kCombineBatch = 16;
 __global__ __launch_bounds__(kCombineThreads) void ffn_combine_kernel(
     const float *ypart, int64_t T, int64_t H, int k, int n_c, const int32_t *ids, int E, void *y,
-    OutType yt) {
+    OutType yt, int32_t *offsets, int32_t *sorted_pairs) {
+  if (offsets && blockIdx.x == gridDim.x - 1) {   // the extra workgroup: the permutation
+    __shared__ int32_t first[kMaxRouteExperts];
+    wave_permute_small([&](int p) { return ids[p]; }, (int)T * k, E, offsets, sorted_pairs,
+                       first);
+    return;
+  }
   const int64_t i = ((int64_t)blockIdx.x * kCombineThreads + threadIdx.x) * 4;
   if (i >= T * H) return;
   const int64_t t = i / H, col = i - t * H;
@@ -723,25 +785,33 @@ hipError_t launch_row_gemv(Epi epi, const GemmArgs &a, const int32_t *sorted_pai
 bool row_ffn_supported(int H, int I) { return H == kSlice && I % kFfnCols == 0; }
 
 hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *sorted_pairs,
-                          const int32_t *ids, int k, int P, float *ypart, hipStream_t s) {
+                          const int32_t *ids, int k, int P, float *ypart, hipStream_t s,
+                          const FfnRoute *route) {
   if (!row_ffn_supported(g.K, g.N) || d.K != g.N || d.N != g.K) return hipErrorInvalidValue;
+  FfnRoute fr{};
+  if (route) {
+    if (sorted_pairs || route->E > kMaxRouteExperts || k > kMaxFfnRouteK) return hipErrorInvalidValue;
+    fr = *route;
+  }
   const int n_c = g.N / kFfnCols;
   const int64_t items = (int64_t)P * n_c;
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   const Routing rt{sorted_pairs, ids, k, false};
-  launch_kernel(row_ffn_kernel, dim3((unsigned)grid), dim3(64 * kFfnWaves), 0, s, g, d, rt, P, n_c,
-                ypart);
+  launch_kernel(row_ffn_kernel, dim3((unsigned)grid), dim3(64 * kFfnWaves), 0, s, g, d, rt, fr, P,
+                n_c, ypart);
   return hipGetLastError();
 }
 
 hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, const int32_t *ids,
-                              int E, void *y, OutType yt, hipStream_t s) {
+                              int E, void *y, OutType yt, hipStream_t s, int32_t *offsets,
+                              int32_t *sorted_pairs) {
   if (H % 4 != 0 || k > 32) return hipErrorInvalidValue;
+  if (offsets && (!sorted_pairs || (int64_t)T * k > kSmallPairs || E > kMaxRouteExperts))
+    return hipErrorInvalidValue;
   const int64_t threads = ((int64_t)T * H + 3) / 4;
-  launch_kernel(ffn_combine_kernel,
-                dim3((unsigned)((threads + kCombineThreads - 1) / kCombineThreads)),
-                dim3(kCombineThreads), 0, s,
-                ypart, (int64_t)T, (int64_t)H, k, I / kFfnCols, ids, E, y, yt);
+  const int64_t blocks = (threads + kCombineThreads - 1) / kCombineThreads + (offsets ? 1 : 0);
+  launch_kernel(ffn_combine_kernel, dim3((unsigned)blocks), dim3(kCombineThreads), 0, s, ypart,
+                (int64_t)T, (int64_t)H, k, I / kFfnCols, ids, E, y, yt, offsets, sorted_pairs);
   return hipGetLastError();
 }
 

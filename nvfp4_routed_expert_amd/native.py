@@ -85,6 +85,10 @@ def lib():
                                              _vp, ctypes.POINTER(ExpertWeightsC), _i32, _i32,
                                              _vp, _vp, _i32, _vp, _sz, _vp]),
             "moe_grouped_nvfp4_ffn_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32]),
+            "moe_route_ffn_decode": (_i32, [_vp, _vp, _i64, _i64, _i64, _i32, _i32, ctypes.c_int,
+                                            _vp, _vp, _vp, _vp, ctypes.POINTER(ExpertWeightsC),
+                                            _vp, _i32, _vp, _sz, _vp]),
+            "moe_route_ffn_decode_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32]),
             "moe_grouped_nvfp4_ffn_static": (_i32, [_vp, _i64, _i64, _i64, _i32, _i32, _vp, _vp,
                                                     _vp, _vp, ctypes.POINTER(ExpertWeightsC),
                                                     _i32, _i32, _vp, _vp, _i32, _vp]),
@@ -119,6 +123,7 @@ def exported_symbols():
             "moe_permute_pairs",
             "moe_grouped_nvfp4_ffn",
             "moe_grouped_nvfp4_ffn_workspace_size", "moe_grouped_nvfp4_ffn_debug_h",
+            "moe_route_ffn_decode", "moe_route_ffn_decode_workspace_size",
             "moe_grouped_nvfp4_ffn_static", "moe_grouped_nvfp4_ffn_static_max_bytes",
             "nvfp4_set_ffn_stage_events",
             "nvfp4_set_ffn_separate_h_quant", "nvfp4_read_probe",
@@ -452,6 +457,36 @@ def moe_grouped_nvfp4_ffn(x, weights: ExpertWeights, topk_ids, topk_weights, exp
                                    act, mode, _ptr(ag), _ptr(y), _dt(y.dtype), _ptr(ws),
                                    ws.numel(), _stream()))
     return y, ag
+
+
+def moe_route_ffn_decode(logits, x, weights: ExpertWeights, k, renormalize=True,
+                         out_dtype=torch.bfloat16, route_out=None, out=None, workspace=None):
+    """Routing and the routed-expert FFN of a decode batch (W4A16) in two
+    launches, bit-identical to moe_route_topk then moe_grouped_nvfp4_ffn.
+    Returns (y [T,H], (topk_ids, topk_weights, expert_offsets, sorted_pairs))."""
+    T, H = x.shape
+    E, I = weights.num_experts, weights.intermediate
+    dev = x.device
+    if route_out is None:
+        route_out = (torch.empty((T, k), dtype=torch.int32, device=dev),
+                     torch.empty((T, k), dtype=torch.float32, device=dev),
+                     torch.empty(E + 1, dtype=torch.int32, device=dev),
+                     torch.empty(T * k, dtype=torch.int32, device=dev))
+    ids, w, off, pairs = route_out
+    y = out if out is not None else torch.empty((T, H), dtype=out_dtype, device=dev)
+    L = lib()
+    ws = _workspace(L.moe_route_ffn_decode_workspace_size(T, H, I, E, k), dev, workspace)
+    cw = weights.c_struct()
+    _check(L.moe_route_ffn_decode(_ptr(logits), _ptr(x), T, H, I, E, k, int(bool(renormalize)),
+                                  _ptr(ids), _ptr(w), _ptr(off), _ptr(pairs), ctypes.byref(cw),
+                                  _ptr(y), _dt(y.dtype), _ptr(ws), ws.numel(), _stream()))
+    return y, route_out
+
+
+def route_ffn_decode_supported(T, H, I, E, k):
+    """Whether moe_route_ffn_decode takes this shape (the fused decode path)."""
+    return (H == 2048 and I > 0 and I % 256 == 0 and 1 <= k <= 8 and k <= E <= 512
+            and T * k <= 256 and 2 * T * k <= 32 * E)
 
 
 def moe_grouped_nvfp4_ffn_static(x, weights: ExpertWeights, topk_ids, topk_weights,

@@ -457,6 +457,45 @@ def test_fused_decode_in_pair_order(T, I, E, k):
         native.moe_grouped_nvfp4_ffn(x, w, ids, wts, None, None, k, act=native.W4A4)
 
 
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+@pytest.mark.parametrize("T,I,E,k,renorm,ties", [
+    (16, 512, 512, 8, True, False),    # the decode workload
+    (16, 512, 512, 8, True, True),     # planted ties in the logits
+    (5, 2304, 16, 3, False, False),    # nine slices, softmax over all experts
+    (32, 512, 512, 8, True, False),    # 256 pairs: four permutation slots
+    (1, 256, 8, 2, True, False),       # one token, one slice
+])
+def test_route_ffn_decode_bit_identical(T, I, E, k, renorm, ties):
+    """moe_route_ffn_decode (each FFN workgroup routes its own token; the
+    combine launch makes the permutation) equals moe_route_topk followed by
+    moe_grouped_nvfp4_ffn bit for bit in all five outputs, and its ids equal
+    the oracle's top-k."""
+    H = 2048
+    say("route + ffn decode", T, H, I, E, k, renorm, ties)
+    x = synth.activations(T, H, 5).to(DEV)
+    lg = synth.router_logits(T, E, 5)
+    if ties:
+        lg = np.round(lg * 2) / 2
+    logits = torch.from_numpy(lg).to(DEV)
+    ids, wts, off, pairs = native.moe_route_topk(logits, k, renorm)
+    rids, _ = O.route_topk(lg, k, renorm)
+    w = weights.synthetic_experts(E, H, I, 5, DEV, experts=np.unique(to_np(ids)))
+    for dt in (torch.bfloat16, torch.float32):
+        y_ref, _ = native.moe_grouped_nvfp4_ffn(x, w, ids, wts, off, pairs, k, out_dtype=dt)
+        y, (ids2, wts2, off2, pairs2) = native.moe_route_ffn_decode(logits, x, w, k, renorm,
+                                                                    out_dtype=dt)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_np(ids2), rids)
+        assert torch.equal(ids2, ids) and torch.equal(_bits(wts2), _bits(wts))
+        assert torch.equal(off2, off) and torch.equal(pairs2, pairs)
+        assert torch.equal(_bits(y), _bits(y_ref)), dt
+    with pytest.raises(native.NVFP4Error):   # H = 2048 only
+        native.moe_route_ffn_decode(logits, synth.activations(T, 1024, 5).to(DEV), w, k)
+
+
 def test_moe_ffn_in_a_graph():
     """The grouped-GEMM FFN captured into a graph: every replay (with eager
     calls between them) equals the eager result bit for bit."""

@@ -112,6 +112,31 @@ def test_route_validation():
     assert L.moe_route_topk(FAKE_MIS, 16, 64, 8, 1, FAKE, FAKE, None, None, None, 0, None) == 3
 
 
+def test_route_ffn_decode_validation():
+    """moe_route_ffn_decode takes only the fused decode shapes and checks its
+    arguments before anything is enqueued."""
+    L = native.lib()
+    w = native.ExpertWeightsC(*([FAKE.value] * 9))
+    T, H, I, E, k = 16, 2048, 512, 512, 8
+    ws = L.moe_route_ffn_decode_workspace_size(T, H, I, E, k)
+    assert ws >= T * k * (I // 256) * H * 4
+    f = lambda T=T, H=H, I=I, E=E, k=k, wsb=ws, lg=FAKE, off=FAKE, dt=0: L.moe_route_ffn_decode(
+        lg, FAKE, T, H, I, E, k, 1, FAKE, FAKE, off, FAKE, ctypes.byref(w), FAKE, dt, FAKE, wsb,
+        None)
+    assert f(H=4096) == 2 and "fused decode path" in _last()
+    assert f(I=384) == 2
+    assert f(k=9) == 2
+    assert f(E=600) == 2
+    assert f(T=64) == 2                  # T*k > 256
+    assert f(T=32, E=4, k=4) == 2        # 2*T*k > 32*E
+    assert f(T=-1) == 1
+    assert f(lg=None) == 1 and "logits" in _last()
+    assert f(off=None) == 1
+    assert f(dt=7) == 1
+    assert f(wsb=ws - 1) == 4
+    assert f(lg=FAKE_MIS) == 3
+
+
 def test_ffn_validation():
     L = native.lib()
     w = native.ExpertWeightsC(*([FAKE.value] * 9))
