@@ -17,6 +17,7 @@ namespace {
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxPerLane = kMaxExperts / kWave;  // 16 logits per lane
 constexpr int kTopkThreads = 256;
+constexpr int kRouteDecodeThreads = 64 * (kMaxRouteExperts / 64);   // 8 waves per token
 
 // a beats b: larger logit, or equal logit and lower index (branch-free)
 __device__ __forceinline__ bool beats(float av, int ai, float bv, int bi) {
@@ -528,38 +529,52 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *ids, 
 }
 
 // Decode-sized routing in one launch (T k <= 256 pairs, E <= 512, k <= 8):
-// one wavefront per token (own workgroup, so tokens spread over CUs) takes
-// the top-k with the merge network and publishes ids and weights; each wave
-// then takes a ticket from a counter in the caller's workspace, and the wave
-// holding the last ticket, which therefore sees every token's ids, resets
-// the counter and builds the permutation alone.  The ids are written and
-// read as device-scope (relaxed agent) atomics, performed at the device's
-// coherence point past the per-XCD L2s, and each wave waits for its stores
-// to complete before taking its ticket: this orders them before the last
-// wave's reads without the whole-L2 write-back and invalidate that release
-// and acquire fences cost.  The last wave's permutation is
-// wave_permute_small (bit-sliced matching).
-__global__ __launch_bounds__(64) void route_decode_kernel(const LogitSrc logits, int64_t T, int E,
-                                                          int k, int renormalize, int32_t *ids,
-                                                          float *weights, int32_t *offsets,
-                                                          int32_t *sorted_pairs,
-                                                          uint32_t *ticket) {
+// one workgroup of 8 waves per token (tokens spread over CUs) takes the
+// top-k (block_topk8) and its wave 0 publishes ids and weights, then takes
+// a ticket from a counter in the caller's workspace; the workgroup holding
+// the last ticket, which therefore sees every token's ids, resets the
+// counter and its wave 0 builds the permutation (wave_permute_small,
+// bit-sliced matching).  The ids are written and read as device-scope
+// (relaxed agent) atomics, performed at the device's coherence point past
+// the per-XCD L2s, and the wave waits for its stores to complete before
+// taking its ticket: this orders them before the last workgroup's reads
+// without the whole-L2 write-back and invalidate that release and acquire
+// fences cost.
+__global__ __launch_bounds__(kRouteDecodeThreads) void route_decode_kernel(
+    const LogitSrc logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
+    float *weights, int32_t *offsets, int32_t *sorted_pairs, uint32_t *ticket) {
   __shared__ int32_t first[kMaxRouteExperts];
-  const int lane = threadIdx.x;
+  __shared__ uint64_t cand[kMaxRouteExperts / 8];
+  __shared__ float lgt[kMaxRouteExperts];
+  __shared__ uint32_t last;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int t = blockIdx.x;
-  wave_topk_merge(logits, t, E, k, renormalize, ids + (int64_t)t * k, weights + (int64_t)t * k,
-                  nullptr, true);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's ids stores complete
-  uint32_t mine = 0;
-  if (lane == 0)
-    mine = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  mine = __builtin_amdgcn_readfirstlane(mine);
-  if (mine != (uint32_t)T - 1) return;
-  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-
+  int id;
+  float wgt;
+  block_topk8(logits, t, E, k, renormalize, cand, lgt, id, wgt);
+  if (wave == 0) {
+    if (lane < k) {
+      __hip_atomic_store(ids + (int64_t)t * k + lane, id, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      weights[(int64_t)t * k + lane] = wgt;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's ids stores complete
+    uint32_t mine = 0;
+    if (lane == 0)
+      mine = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    mine = __builtin_amdgcn_readfirstlane(mine);
+    if (lane == 0) {
+      last = mine == (uint32_t)T - 1 ? 1u : 0u;
+      if (mine == (uint32_t)T - 1)
+        __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (!last) return;   // (uniform: the whole workgroup)
   wave_permute_small(
       [&](int p) { return __hip_atomic_load(ids + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); },
-      (int)T * k, E, offsets, sorted_pairs, first);
+      (int)T * k, E, offsets, sorted_pairs, first, wave == 0);
 }
 
 int permute_words(int64_t T, int E) {
@@ -594,8 +609,8 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
                         int32_t *ids, float *weights, int32_t *offsets, int32_t *sorted_pairs,
                         uint32_t *ticket, hipStream_t s) {
   if (ticket && route_decode_supported(T, E, k)) {
-    launch_kernel(route_decode_kernel, dim3((unsigned)T), dim3(64), 0, s, logits, T, E, k,
-                  renormalize, ids, weights, offsets, sorted_pairs, ticket);
+    launch_kernel(route_decode_kernel, dim3((unsigned)T), dim3(kRouteDecodeThreads), 0, s, logits,
+                  T, E, k, renormalize, ids, weights, offsets, sorted_pairs, ticket);
     return hipGetLastError();
   }
   hipError_t e = launch_topk(logits, T, E, k, renormalize, ids, weights, s);

@@ -556,49 +556,23 @@ __global__ __launch_bounds__(64 * kFfnWaves) void row_ffn_kernel(const GemmArgs 
       for (int j = 0; j < 4; ++j) a[4 * q + j] = v[j];
     }
   }
-  // Routed here, while the x row loads are in flight: waves 0..7 each take
-  // the 8 best of 64 logits (keys and order of the routing kernels), wave 0
-  // the 8 best of those 64 and the weights with the routing kernels'
-  // arithmetic in the same lanes, so ids and weights are theirs bit for bit;
-  // the workgroup of slot 0, slice 0 publishes them.
+  // Routed here, while the x row loads are in flight (block_topk8: ids and
+  // weights are the routing kernels' bit for bit); the workgroup of slot 0,
+  // slice 0 publishes them.
   int e = e_given;
   float route_w = 0.0f;
   if (fr.logits) {   // uniform
-    const int j = pair - token * rt.k, k = rt.k, E = fr.E;
-    if (wave < kMaxRouteExperts / 64) {
-      const int ex = 64 * wave + lane;
-      const float v = ex < E ? fr.logits[(int64_t)token * E + ex] : 0.0f;
-      r_logit[ex] = v;
-      const uint64_t key = wave_top8_lanes(ex < E ? topk_key(v, ex) : 0ull, lane);
-      if (lane < 8) r_cand[8 * wave + lane] = key;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const uint64_t mine = wave_top8_lanes(r_cand[lane], lane);   // lane j: the j-th key
-      const int my_idx = (int)~(uint32_t)mine;
-      const uint32_t m = (uint32_t)(mine >> 32);
-      const float my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
-      const float lmax =
-          __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
-      const float ex = lane < k ? expf(my_val - lmax) : 0.0f;
-      float denom;
-      if (fr.renormalize) {
-        denom = wave_sum(ex);
-      } else {   // this lane's logits lane + 64 i in i order, as the routing kernels add them
-        float sm = 0.0f;
-#pragma unroll
-        for (int i = 0; i < kMaxRouteExperts / 64; ++i)
-          if (lane + 64 * i < E) sm += expf(r_logit[lane + 64 * i] - lmax);
-        denom = wave_sum(sm);
-      }
-      if (lane < k) {
-        const float wgt = ex / denom;
-        r_ids[lane] = my_idx;
-        r_wts[lane] = wgt;
-        if (j == 0 && c == 0) {
-          fr.ids_out[(int64_t)token * k + lane] = my_idx;
-          fr.weights_out[(int64_t)token * k + lane] = wgt;
-        }
+    const int j = pair - token * rt.k, k = rt.k;
+    int id;
+    float wgt;
+    block_topk8(LogitSrc{fr.logits, 0, 1, nullptr, nullptr}, token, fr.E, k, fr.renormalize,
+                r_cand, r_logit, id, wgt);
+    if (wave == 0 && lane < k) {
+      r_ids[lane] = id;
+      r_wts[lane] = wgt;
+      if (j == 0 && c == 0) {
+        fr.ids_out[(int64_t)token * k + lane] = id;
+        fr.weights_out[(int64_t)token * k + lane] = wgt;
       }
     }
     __syncthreads();

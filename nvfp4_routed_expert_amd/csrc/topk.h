@@ -217,6 +217,52 @@ __device__ __forceinline__ uint64_t wave_top8_lanes(uint64_t key, int lane) {
   return key;
 }
 
+// Top-k (k <= 8) of token t's logits (E <= 512) by a workgroup of at least
+// 8 waves, every wave of which calls it (it holds one barrier): waves 0..7
+// each rank 64 logits (the logits as load_logits forms them), wave 0 ranks
+// the 64 candidates and computes the weights with wave_topk_merge's
+// arithmetic in the same lanes, so both the selection and the weights are
+// that function's bit for bit.  On return lane j < k of wave 0 holds the
+// j-th id and weight (other lanes and waves: unspecified).  cand: 64 keys
+// and lgt: kMaxRouteExperts floats of LDS.
+__device__ __forceinline__ void block_topk8(const LogitSrc &src, int64_t t, int E, int k,
+                                            int renormalize, uint64_t *cand, float *lgt,
+                                            int &id, float &wgt) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (wave < kMaxRouteExperts / 64) {
+    const int e = 64 * wave + lane;
+    float v[1];
+    load_logits(src, t, E, e, v);   // (the element at e, and its store to src.out)
+    lgt[e] = v[0];
+    const uint64_t key = wave_top8_lanes(e < E ? topk_key(v[0], e) : 0ull, lane);
+    if (lane < 8) cand[8 * wave + lane] = key;
+  }
+  __syncthreads();
+  id = 0;
+  wgt = 0.0f;
+  if (wave == 0) {
+    const uint64_t mine = wave_top8_lanes(cand[lane], lane);   // lane j: the j-th key
+    id = (int)~(uint32_t)mine;
+    const uint32_t m = (uint32_t)(mine >> 32);
+    const float my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
+    const float lmax =
+        __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, my_val), 0));
+    const float ex = lane < k ? expf(my_val - lmax) : 0.0f;
+    float denom;
+    if (renormalize) {
+      denom = wave_sum(ex);
+    } else {   // this lane's logits lane + 64 i in i order, as wave_topk_merge adds them
+      float sm = 0.0f;
+#pragma unroll
+      for (int i = 0; i < kMaxRouteExperts / 64; ++i)
+        if (lane + 64 * i < E) sm += expf(lgt[lane + 64 * i] - lmax);
+      denom = wave_sum(sm);
+    }
+    wgt = ex / denom;
+  }
+}
+
 // Permutation by bit-sliced matching: pair p = lane + 64 s sits in slot s of
 // its lane (pairs past P carry expert E, above every real one).  Ten ballots
 // per slot hold the bits of every pair's expert; walking them from the top
@@ -243,11 +289,18 @@ __device__ __forceinline__ int wave_incl_min(int x) {
 // by one wavefront (the workgroup is that one wave: its barriers order the
 // LDS array `first`, kMaxRouteExperts entries).  id_of(p) gives pair p's
 // expert, an id in 0..E-1.
+// With active false a wave only takes part in the barriers (the other waves
+// of a larger workgroup).
 template <class IdOf>
 __device__ void wave_permute_small(IdOf id_of, int P, int E, int32_t *offsets,
-                                   int32_t *sorted_pairs, int32_t *first) {
+                                   int32_t *sorted_pairs, int32_t *first, bool active = true) {
   constexpr int kSlots = kSmallPairs / 64;
   const int lane = threadIdx.x & 63;
+  if (!active) {
+    __syncthreads();
+    __syncthreads();
+    return;
+  }
   const int nslot = (P + 63) / 64;   // uniform, <= kSlots
   int ev[kSlots];
   uint64_t bits[kSlots][kRouteBits];

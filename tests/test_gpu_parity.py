@@ -472,7 +472,8 @@ def test_route_ffn_decode_bit_identical(T, I, E, k, renorm, ties):
     """moe_route_ffn_decode (each FFN workgroup routes its own token; the
     combine launch makes the permutation) equals moe_route_topk followed by
     moe_grouped_nvfp4_ffn bit for bit in all five outputs, and its ids equal
-    the oracle's top-k."""
+    the oracle's top-k; the decode routing's workgroup-wide top-k equals the
+    per-lane merge network's bit for bit."""
     H = 2048
     say("route + ffn decode", T, H, I, E, k, renorm, ties)
     x = synth.activations(T, H, 5).to(DEV)
@@ -481,6 +482,10 @@ def test_route_ffn_decode_bit_identical(T, I, E, k, renorm, ties):
         lg = np.round(lg * 2) / 2
     logits = torch.from_numpy(lg).to(DEV)
     ids, wts, off, pairs = native.moe_route_topk(logits, k, renorm)
+    # the top-k alone runs the per-lane merge network instead of the
+    # workgroup-wide one: the same ids and weights, bit for bit
+    ids1, wts1, _, _ = native.moe_route_topk(logits, k, renorm, permute=False)
+    assert torch.equal(ids1, ids) and torch.equal(_bits(wts1), _bits(wts))
     rids, _ = O.route_topk(lg, k, renorm)
     w = weights.synthetic_experts(E, H, I, 5, DEV, experts=np.unique(to_np(ids)))
     for dt in (torch.bfloat16, torch.float32):
