@@ -63,9 +63,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle sample (0 = workload default)")
     ap.add_argument("--eager", action="store_true", help="no graph capture")
-    ap.add_argument("--separate-routing", action="store_true",
-                    help="decode: route in its own launch (moe_route_topk) instead of inside "
-                         "the FFN launch (moe_route_ffn_decode)")
+    ap.add_argument("--fused-routing", action="store_true",
+                    help="decode: route inside the FFN launch (moe_route_ffn_decode) instead "
+                         "of in a launch of its own (moe_route_topk)")
     ap.add_argument("--given-globals", action="store_true",
                     help="W4A4: static activation scales given by the caller (g_x from the "
                          "input's amax, g_h a fixed calibration value) instead of online ones")
@@ -96,8 +96,8 @@ def parse():
 # Sources each timed kernel is built from; a stored counter reading is used
 # only while these files are byte-identical to the ones it was taken on.
 KERNEL_SOURCES = {
-    "row_ffn_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
-    "row_gemv_kernel": ["rowgemv.hip", "common.h", "kernels.h"],
+    "row_ffn_kernel": ["rowgemv.hip", "topk.h", "common.h", "kernels.h"],
+    "row_gemv_kernel": ["rowgemv.hip", "topk.h", "common.h", "kernels.h"],
     "tile_gemm_kernel": ["tile_gemm.hip", "common.h", "kernels.h"],
     "dense_gemv_kernel": ["densegemv.hip", "common.h", "kernels.h"],
     "grouped_gemm_kernel": ["gemm.hip", "common.h", "kernels.h"],
@@ -328,11 +328,11 @@ def measure(args, name, gumbel=False, steps=200, warmup=20):
                                          act_globals=ag, out_dtype=out.dtype, workspace=ws_,
                                          out=out)
 
-    # Decode on the fused kernel: the routing runs inside the FFN launch (each
-    # workgroup takes its token's top-k) and the permutation beside the combine.
+    # --fused-routing on the fused decode kernel: the routing runs inside the
+    # FFN launch (each workgroup takes its token's top-k) and the permutation
+    # beside the combine.
     fused_route = (route and not with_router and act == native.W4A16 and
-                   not args.separate_routing and
-                   native.route_ffn_decode_supported(T, H, I, E, k))
+                   args.fused_routing and native.route_ffn_decode_supported(T, H, I, E, k))
     if fused_route:
         fws = torch.empty(native.lib().moe_route_ffn_decode_workspace_size(T, H, I, E, k),
                           dtype=torch.uint8, device=dev)
