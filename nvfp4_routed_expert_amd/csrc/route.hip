@@ -99,6 +99,24 @@ __device__ void wave_topk(const LogitSrc &src, int64_t t, int E, int k, int reno
   }
 }
 
+// One workgroup of 8 waves per token (more than 256 experts: the
+// workgroup-wide ranking, block_topk8).
+__global__ __launch_bounds__(kRouteDecodeThreads) void topk_block_kernel(
+    const LogitSrc logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
+    float *weights) {
+  __shared__ uint64_t cand[kMaxRouteExperts / 8];
+  __shared__ float lgt[kMaxRouteExperts];
+  const int64_t t = blockIdx.x;
+  int id;
+  float wgt;
+  block_topk8(logits, t, E, k, renormalize, cand, lgt, id, wgt);
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == 0 && lane < k) {
+    ids[t * k + lane] = id;
+    weights[t * k + lane] = wgt;
+  }
+}
+
 // One wavefront per token.
 __global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(
     const LogitSrc logits, int64_t T, int E, int k, int renormalize, int32_t *ids,
@@ -623,7 +641,10 @@ hipError_t launch_topk(const LogitSrc &logits, int64_t T, int E, int k, int reno
   // one wavefront per token, four per workgroup, so a decode batch spreads
   // over several CUs (one wave per SIMD) instead of sharing one
   const int64_t blocks = (T + 3) / 4;
-  if (E <= 512 && k <= 8)
+  if (E > 256 && E <= 512 && k <= 8)
+    launch_kernel(topk_block_kernel, dim3((unsigned)T), dim3(kRouteDecodeThreads), 0, s, logits,
+                  T, E, k, renormalize, ids, weights);
+  else if (E <= 512 && k <= 8)
     launch_kernel(topk_merge_kernel, dim3((unsigned)blocks), dim3(kTopkThreads), 0, s, logits, T,
                   E, k, renormalize, ids, weights);
   else

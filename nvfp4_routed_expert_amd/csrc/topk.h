@@ -217,10 +217,11 @@ __device__ __forceinline__ uint64_t wave_top8_lanes(uint64_t key, int lane) {
   return key;
 }
 
-// Top-k (k <= 8) of token t's logits (E <= 512) by a workgroup of at least
-// 8 waves, every wave of which calls it (it holds one barrier): waves 0..7
-// each rank 64 logits (the logits as load_logits forms them), wave 0 ranks
-// the 64 candidates and computes the weights with wave_topk_merge's
+// Top-k (k <= 8) of token t's logits (E <= 512) by a workgroup of W waves,
+// 64 W >= E, every wave of which calls it (it holds one barrier): waves
+// 0..min(W, 8)-1 each rank 64 logits (the logits as load_logits forms
+// them), wave 0 ranks their 8 best each and computes the weights with
+// wave_topk_merge's
 // arithmetic in the same lanes, so both the selection and the weights are
 // that function's bit for bit.  On return lane j < k of wave 0 holds the
 // j-th id and weight (other lanes and waves: unspecified).  cand: 64 keys
@@ -230,7 +231,9 @@ __device__ __forceinline__ void block_topk8(const LogitSrc &src, int64_t t, int 
                                             int &id, float &wgt) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  if (wave < kMaxRouteExperts / 64) {
+  const int nw = (int)(blockDim.x >> 6) < kMaxRouteExperts / 64 ? (int)(blockDim.x >> 6)
+                                                                  : kMaxRouteExperts / 64;
+  if (wave < nw) {
     const int e = 64 * wave + lane;
     float v[1];
     load_logits(src, t, E, e, v);   // (the element at e, and its store to src.out)
@@ -242,7 +245,7 @@ __device__ __forceinline__ void block_topk8(const LogitSrc &src, int64_t t, int 
   id = 0;
   wgt = 0.0f;
   if (wave == 0) {
-    const uint64_t mine = wave_top8_lanes(cand[lane], lane);   // lane j: the j-th key
+    const uint64_t mine = wave_top8_lanes(lane < 8 * nw ? cand[lane] : 0ull, lane);   // lane j: the j-th key
     id = (int)~(uint32_t)mine;
     const uint32_t m = (uint32_t)(mine >> 32);
     const float my_val = __uint_as_float((m & 0x80000000u) ? (m & 0x7FFFFFFFu) : ~m);
