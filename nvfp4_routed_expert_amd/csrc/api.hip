@@ -897,6 +897,11 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   const bool rows = small && !a4 && row_gemv_supported((int)H) && row_gemv_supported((int)I);
   // ... and the down projection sums each token's slots itself (no combine)
   const bool fused_sum = rows && row_down_sum_supported((int)I, k);
+  // A single expert (one slot per token) on the dense GEMV: the down
+  // projection's reduce writes y itself (a combine of one slot is a copy)
+  // and the x pass zeroes the rows of tokens whose id is dropped.
+  const bool dense = ffn_dense(T, H, I, E, k);
+  const bool dense_direct = dense && !a4;
 
   // 1-2. plan (m-blocks per expert), zeroed scratch words and x -> fp16 rows
   if (rows) {   // no plan: the stream kernels read the routing directly
@@ -910,7 +915,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     mark(NVFP4_STAGE_X_PREP, false, stream);
     LAUNCH(launch_moe_prep(xb, T, H, ws.x16, ws.xshift, expert_offsets, E, bm, ws.mblocks,
                            ws.n_mblocks, bm_down, split_down ? ws.mblocks_down : nullptr,
-                           ws.n_mblocks_down, ws.slots, zero_words, stream),
+                           ws.n_mblocks_down, ws.slots, zero_words, stream,
+                           dense_direct ? topk_ids : nullptr, dense_direct ? y : nullptr,
+                           yt == OutType::F32),
            "plan + x prep");
     mark(NVFP4_STAGE_X_PREP, true, stream);
   } else {
@@ -962,7 +969,6 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.amax_slot = a4 ? ws.slots : nullptr;
   // W4A4 with a given h global on the tiled path: the gate/up epilogue
   // quantises h itself and writes the down GEMM's fp16 operand directly
-  const bool dense = ffn_dense(T, H, I, E, k);
   const bool h_fused = given && !small && !dense && !g_separate_h_quant &&
                        tile_gemm_supported((int)H) && plans.gate_up.ksplit == 1;
   if (h_fused) {
@@ -1076,8 +1082,14 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     }
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
-  else if (dense)
+  else if (dense) {
+    if (dense_direct) {   // the reduce writes y (pair t is token t)
+      d.out = y;
+      d.ldo = H;
+      d.out_type = yt;
+    }
     LAUNCH(launch_dense_gemv(Epi::DOWN, d, (int)P, plans.down, nullptr, stream), "down");
+  }
   else
     LAUNCH(tile_gemm_supported((int)I)
                ? launch_tile_gemm(Epi::DOWN, d, bm_down, plans.down, topk_ids, (int)P, stream)
@@ -1085,7 +1097,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
            "down");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order
-  if (fused_sum) {   // done by the down kernel: an empty stage
+  if (fused_sum || dense_direct) {   // done by the down kernel: an empty stage
     mark(NVFP4_STAGE_COMBINE, false, stream);
     mark(NVFP4_STAGE_COMBINE, true, stream);
     return NVFP4_OK;

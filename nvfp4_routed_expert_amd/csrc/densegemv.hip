@@ -31,6 +31,8 @@
 // for both operands; a lane then needs 32 code bytes and 4 scale bytes of
 // its weight row per chunk.  LDS pieces of 16 bytes are XOR-swizzled by the
 // row so that the 16 rows of a fragment spread over the banks.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -269,8 +271,13 @@ __global__ __launch_bounds__(64 * kDWaves, MS == 1 ? 2 : 1) void dense_gemv_kern
 
 // Output element (m, n): the partials of tile t = n / kCols from the
 // workgroups that own its units, added in workgroup order, then the epilogue
-// (as the tile GEMM's).  Rows m are the dense rows (positions) 0..M-1.
-template <Epi EPI>
+// (as the tile GEMM's).  Rows m are the dense rows (positions) 0..M-1.  The
+// owners' partials are loaded kReduceBatch at a time before they are added
+// (the same order), and the unit arithmetic runs in 32 bits when U32 (the
+// host checks that units * grid fits): 64-bit divisions before every load
+// serialised a tile's dozen round trips.
+constexpr int kReduceBatch = 16;
+template <Epi EPI, bool U32>
 __global__ __launch_bounds__(256) void dense_reduce_kernel(const GemmArgs p, int M,
                                                            const StreamSplit sk,
                                                            const float *partial) {
@@ -283,18 +290,43 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const GemmArgs p, int
     const int t = n / kCols, cl = n - t * kCols;
     const int pr = p.a_rowmap ? p.a_rowmap[m] : m;
     if (pr >= 0) {   // (a dropped pair: no h row, no output)
-      const int64_t g_lo = unit_owner(sk, (int64_t)t * sk.nch);
-      const int64_t g_hi = unit_owner(sk, (int64_t)t * sk.nch + sk.nch - 1);
+      const uint32_t units32 = (uint32_t)sk.units, grid32 = (uint32_t)sk.grid;
+      const uint32_t nch32 = (uint32_t)sk.nch;
+      auto owner = [&](int64_t u) -> int64_t {
+        if constexpr (U32)
+          return (int64_t)(((uint32_t)u + 1u) * grid32 + units32 - 1u) / units32 - 1;
+        else
+          return unit_owner(sk, u);
+      };
+      auto first_tile = [&](int64_t g) -> int {   // tile of workgroup g's first unit
+        if constexpr (U32)
+          return (int)((uint32_t)g * units32 / grid32 / nch32);
+        else
+          return (int)(unit_first(sk, g) / sk.nch);
+      };
+      const int64_t g_lo = owner((int64_t)t * sk.nch);
+      const int64_t g_hi = owner((int64_t)t * sk.nch + sk.nch - 1);
       float s0 = 0.0f, s1 = 0.0f;
-      for (int64_t g = g_lo; g <= g_hi; ++g) {
-        const int slot = t - (int)(unit_first(sk, g) / sk.nch);
-        const float *part = partial + (g * sk.slots + slot) * 32 * kDPartCols + m * kDPartCols;
-        if (g == g_lo) {
-          s0 = part[cl];
-          if constexpr (EPI == Epi::SWIGLU) s1 = part[64 + cl];
-        } else {
-          s0 += part[cl];
-          if constexpr (EPI == Epi::SWIGLU) s1 += part[64 + cl];
+      for (int64_t g0 = g_lo; g0 <= g_hi; g0 += kReduceBatch) {
+        float v0[kReduceBatch], v1[kReduceBatch];
+#pragma unroll
+        for (int q = 0; q < kReduceBatch; ++q) {
+          const int64_t g = g0 + q <= g_hi ? g0 + q : g_hi;   // (past the end: reread, unused)
+          const int slot = t - first_tile(g);
+          const float *part = partial + (g * sk.slots + slot) * 32 * kDPartCols + m * kDPartCols;
+          v0[q] = part[cl];
+          v1[q] = EPI == Epi::SWIGLU ? part[64 + cl] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < kReduceBatch; ++q) {
+          if (g0 + q > g_hi) break;
+          if (g0 + q == g_lo) {
+            s0 = v0[q];
+            s1 = v1[q];
+          } else {
+            s0 += v0[q];
+            if constexpr (EPI == Epi::SWIGLU) s1 += v1[q];
+          }
         }
       }
       const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
@@ -385,18 +417,27 @@ hipError_t launch_dense_gemv(Epi epi, const GemmArgs &a, int M, const TilePlan &
   hipError_t e = M <= 16 ? launch_ms<1>(epi, a, M, sk, s) : launch_ms<2>(epi, a, M, sk, s);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(((int64_t)M * a.N + 255) / 256)), block(256);
+  const bool u32 = (uint64_t)(sk.units + 1) * (uint64_t)sk.grid + (uint64_t)sk.units <
+                   ((uint64_t)1 << 32);
+  auto reduce = [&](auto epi_c, auto u32_c) {
+    launch_kernel((dense_reduce_kernel<decltype(epi_c)::value, decltype(u32_c)::value>), grid,
+                  block, 0, s, a, M, sk, (const float *)a.partial);
+  };
+  auto with_u32 = [&](auto epi_c) {
+    if (u32)
+      reduce(epi_c, std::true_type{});
+    else
+      reduce(epi_c, std::false_type{});
+  };
   switch (epi) {
     case Epi::LINEAR:
-      launch_kernel(dense_reduce_kernel<Epi::LINEAR>, grid, block, 0, s, a, M, sk,
-                    (const float *)a.partial);
+      with_u32(std::integral_constant<Epi, Epi::LINEAR>{});
       break;
     case Epi::SWIGLU:
-      launch_kernel(dense_reduce_kernel<Epi::SWIGLU>, grid, block, 0, s, a, M, sk,
-                    (const float *)a.partial);
+      with_u32(std::integral_constant<Epi, Epi::SWIGLU>{});
       break;
     case Epi::DOWN:
-      launch_kernel(dense_reduce_kernel<Epi::DOWN>, grid, block, 0, s, a, M, sk,
-                    (const float *)a.partial);
+      with_u32(std::integral_constant<Epi, Epi::DOWN>{});
       break;
   }
   return hipGetLastError();

@@ -278,11 +278,14 @@ hipError_t launch_row_down_sum(const GemmArgs &a, const int32_t *ids, int k, int
 // FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
 // workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.
 // (mblocks2 set: also a list of bm2-row blocks, for the down projection)
+// y_zero (with ids [T], one slot per token): the rows of y of tokens whose
+// id lies outside 0..E-1 are zeroed (f32 or bf16 rows of H).
 hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x16,
                            int32_t *xshift, const int32_t *offsets, int E, int bm,
                            int4 *mblocks, int32_t *n_mblocks, int bm2, int4 *mblocks2,
                            int32_t *n_mblocks2, uint32_t *zero, int64_t zero_words,
-                           hipStream_t s);
+                           hipStream_t s, const int32_t *ids = nullptr, void *y_zero = nullptr,
+                           bool y_f32 = false);
 int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
 
 // FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.

@@ -778,6 +778,36 @@ def test_dense_mlp_prefill_full_size_sampled(M):
     assert_close_f32(to_np(y)[rows], ref, "dense mlp prefill")
 
 
+def test_dense_gemv_mlp_writes_y_with_dropped_rows():
+    """One expert on the dense GEMV: the down projection's reduce writes y
+    itself and the x pass zeroes the rows of tokens whose id is dropped (-1,
+    or 1 with E = 1); kept rows match the oracle in fp32 and as its bf16
+    rounding, dropped rows are 0 (y is filled with NaN first)."""
+    import bench
+    T, H, I = 8, 512, 768
+    assert bench.gate_up_kernel(T, H, I, 1, 1, "w4a16") == "dense_gemv_kernel"
+    say("dense gemv, dropped rows", T, H, I)
+    x = synth.activations(T, H, 3)
+    ids = np.zeros((T, 1), dtype=np.int32)
+    ids[1, 0], ids[5, 0], ids[6, 0] = -1, -1, 1
+    wts = np.ones((T, 1), dtype=np.float32)
+    ids_t, wts_t = torch.from_numpy(ids).to(DEV), torch.from_numpy(wts).to(DEV)
+    off, pairs = native.moe_permute_pairs(ids_t, 1)
+    w_gpu = weights.synthetic_experts(1, H, I, 3, DEV)
+    ys = {}
+    for dt in (torch.float32, torch.bfloat16):
+        y = torch.full((T, H), float("nan"), dtype=dt, device=DEV)
+        native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids_t, wts_t, off, pairs, 1,
+                                     out_dtype=dt, out=y)
+        ys[dt] = to_np(y.float())
+        assert np.all(ys[dt][[1, 5, 6]] == 0.0), dt
+    ref, _ = O.moe_ffn(x.float().numpy(), ids, wts, oracle_experts(1, H, I, [0], 3))
+    keep = [0, 2, 3, 4, 7]
+    assert_close_f32(ys[torch.float32][keep], ref[keep], "dense gemv kept rows")
+    assert_bf16_output(ys[torch.bfloat16][keep], ys[torch.float32][keep], ref[keep],
+                       "dense gemv kept rows (bf16)")
+
+
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_dense_mlp_decode_full_size(M):
     """The dense NVFP4 MLP decode at full size, every row."""
