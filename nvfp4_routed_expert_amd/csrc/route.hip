@@ -638,8 +638,9 @@ hipError_t launch_route(const LogitSrc &logits, int64_t T, int E, int k, int ren
 
 hipError_t launch_topk(const LogitSrc &logits, int64_t T, int E, int k, int renormalize,
                        int32_t *ids, float *weights, hipStream_t s) {
-  // one wavefront per token, four per workgroup, so a decode batch spreads
-  // over several CUs (one wave per SIMD) instead of sharing one
+  // over 256 experts one 8-wave workgroup per token (block_topk8); else one
+  // wavefront per token, four per workgroup, so a decode batch spreads over
+  // several CUs (one wave per SIMD) instead of sharing one
   const int64_t blocks = (T + 3) / 4;
   if (E > 256 && E <= 512 && k <= 8)
     launch_kernel(topk_block_kernel, dim3((unsigned)T), dim3(kRouteDecodeThreads), 0, s, logits,
