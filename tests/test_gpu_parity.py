@@ -848,6 +848,14 @@ def test_empty_batch():
     for act in (native.W4A16, native.W4A4):
         y, _ = native.moe_grouped_nvfp4_ffn(x0, w, ids0, wts0, off, pairs0, k, act=act)
         assert y.shape == (0, H)
+    # routing + FFN in one call (its decode shapes need H = 2048)
+    x0d = torch.empty((0, 2048), dtype=torch.bfloat16, device=DEV)
+    wd = weights.synthetic_experts(E, 2048, 256, 0, DEV, experts=[0])
+    off.fill_(7)
+    yd, _ = native.moe_route_ffn_decode(torch.empty((0, E), dtype=torch.float32, device=DEV), x0d,
+                                        wd, k, route_out=(ids0, wts0, off, pairs0))
+    torch.cuda.synchronize()
+    assert yd.shape == (0, 2048) and torch.equal(off, torch.zeros_like(off))
     sh = [t.to(DEV) for t in synth.shared_expert_weights(H, I)]
     assert native.moe_shared_expert_ffn(x0, *sh).shape == (0, H)
     yl, _ = native.nvfp4_linear(x0, w.gate_codes[0], w.gate_scales[0], w.gate_global[:1])
