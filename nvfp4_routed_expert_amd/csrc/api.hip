@@ -235,7 +235,9 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.n_mblocks = c.take<int32_t>(4);
   w.mblocks_down = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
   w.n_mblocks_down = c.take<int32_t>(4);
-  w.slots = c.take<uint32_t>(4);
+  // 4 scratch words, then (the dense GEMV path) the max |h| of each
+  // 256-element segment of h
+  w.slots = c.take<uint32_t>((size_t)(4 + (ffn_dense(T, H, I, E, k) ? P * (I / 256) : 0)));
   w.partials = c.take<float>(kMaxPartials);
   const FfnPlans pl = ffn_plans(T, H, I, E, k);
   w.split = c.take<float>(pl.gate_up.partial_floats > pl.down.partial_floats
@@ -890,7 +892,6 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   const bool small = ffn_small(T, E, k);
   const OutType yt = y_dtype == NVFP4_DT_F32 ? OutType::F32 : OutType::BF16;
   const uint16_t *xb = static_cast<const uint16_t *>(x);
-  const int64_t zero_words = 4;
 
   // W4A16 decode: both projections stream whole weight rows against the bf16
   // activations as given (no fp16 operand passes)
@@ -902,6 +903,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   // and the x pass zeroes the rows of tokens whose id is dropped.
   const bool dense = ffn_dense(T, H, I, E, k);
   const bool dense_direct = dense && !a4;
+  const int64_t zero_words = 4;   // scratch words the plan zeroes
 
   // 1-2. plan (m-blocks per expert), zeroed scratch words and x -> fp16 rows
   if (rows) {   // no plan: the stream kernels read the routing directly
@@ -967,6 +969,8 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.ldo = I;
   g.out_type = OutType::BF16;
   g.amax_slot = a4 ? ws.slots : nullptr;
+  // (the dense reduce keeps each 256-element segment's max |h| for the h pass)
+  g.row_part = dense_direct ? reinterpret_cast<float *>(ws.slots + 4) : nullptr;
   // W4A4 with a given h global on the tiled path: the gate/up epilogue
   // quantises h itself and writes the down GEMM's fp16 operand directly
   const bool h_fused = given && !small && !dense && !g_separate_h_quant &&
@@ -1027,7 +1031,11 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   mark(NVFP4_STAGE_H_PREP, false, stream);
   const bool h_inline = small && !a4;
   if (!a4) {
-    if (!h_inline && !rows)
+    if (dense_direct)   // the row maxima are known: one elementwise pass
+      LAUNCH(launch_row_shift_parts(ws.h, P, I, reinterpret_cast<const float *>(ws.slots + 4),
+                                    ws.h16, ws.hshift, stream),
+             "h prep");
+    else if (!h_inline && !rows)
       LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::SHIFT, ws.h16, ws.hshift, nullptr, 0, nullptr,
                              nullptr, nullptr, stream),
              "h prep");

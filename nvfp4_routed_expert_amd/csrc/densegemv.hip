@@ -357,6 +357,14 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const GemmArgs p, int
     }
   }
   if constexpr (EPI == Epi::SWIGLU) {
+    if (p.row_part) {   // this workgroup's max |h| (its 256 elements lie in one row)
+      __shared__ float wmax[4];
+      const float wm = wave_max(amax);
+      if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = wm;
+      __syncthreads();
+      if (threadIdx.x == 0 && idx < (int64_t)M * N)
+        p.row_part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    }
     if (p.amax_slot) {
       amax = wave_max(amax);
       if ((threadIdx.x & 63) == 0 && amax > 0.0f) atomicMax(p.amax_slot, __float_as_uint(amax));

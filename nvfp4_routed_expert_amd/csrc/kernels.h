@@ -64,6 +64,13 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols,
                            PrepMode mode, _Float16 *out, int32_t *shift,
                            const float *amax_src, int n_amax, const float *g_given,
                            float *g_out, float *g_out2, hipStream_t s);
+// SHIFT with each row's max |x| given as the maxima of its 256-element
+// segments (cols % 256 == 0; row r's at parts[r * cols / 256 ...], kept by
+// the producer of x): one elementwise pass, the same shifts and values as
+// SHIFT mode.
+hipError_t launch_row_shift_parts(const uint16_t *x, int64_t rows, int64_t cols,
+                                  const float *parts, _Float16 *out, int32_t *shift,
+                                  hipStream_t s);
 
 // ---- routing (route.hip, router.hip) ---------------------------------------------
 
@@ -170,6 +177,9 @@ struct GemmArgs {
   int64_t ldo;
   OutType out_type;
   uint32_t *amax_slot;            // SWIGLU: running max of |h| (float bits) or null
+  // SWIGLU, dense reduce with N % 256 == 0: the max |h| of each workgroup's
+  // 256 elements (one row's segment), or null
+  float *row_part;
   // SWIGLU, tile GEMM without a K split: when set, h is quantised to NVFP4
   // with this (given) global in the epilogue and out receives the exact fp16
   // products e2m1 * e4m3 (what the down GEMM consumes) instead of bf16 h
