@@ -539,6 +539,52 @@ def test_moe_ffn_in_a_graph():
         assert torch.equal(y2, eager)
 
 
+def test_route_ffn_decode_in_a_graph():
+    """moe_route_ffn_decode (routing inside the fused decode launch, the
+    permutation beside the combine) captured into a graph: every replay,
+    with eager calls between them, writes the eager call's five outputs bit
+    for bit (all outputs are cleared before each replay)."""
+    T, H, I, E, k = 16, 2048, 512, 512, 8
+    say("route + ffn decode graph", T, H, I, E, k)
+    x = synth.activations(T, H, 6).to(DEV)
+    logits = torch.from_numpy(synth.router_logits(T, E, 6)).to(DEV)
+    ids0, _, _, _ = native.moe_route_topk(logits, k)
+    w = weights.synthetic_experts(E, H, I, 6, DEV, experts=np.unique(to_np(ids0)))
+    outs = (torch.empty((T, k), dtype=torch.int32, device=DEV),
+            torch.empty((T, k), dtype=torch.float32, device=DEV),
+            torch.empty(E + 1, dtype=torch.int32, device=DEV),
+            torch.empty(T * k, dtype=torch.int32, device=DEV))
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(native.lib().moe_route_ffn_decode_workspace_size(T, H, I, E, k),
+                     dtype=torch.uint8, device=DEV)
+
+    def call():
+        native.moe_route_ffn_decode(logits, x, w, k, route_out=outs, out=y, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs] + [y.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        for t in list(outs) + [y]:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(outs) + [y]
+        assert all(torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a, b.view(
+            torch.int16) if b.dtype == torch.bfloat16 else b) for a, b in zip(got, eager)), i
+        y2, _ = native.moe_route_ffn_decode(logits, x, w, k)   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(y2.view(torch.int16), eager[4].view(torch.int16))
+
+
 def _w4a4_device_h_check(x, rids, rw, w_ref, st, y, g_out, T, H, I, E, k, tokens=None,
                          given=False, ws=None):
     """Reads the device's bf16 h and W4A4 operand from the FFN's workspace
