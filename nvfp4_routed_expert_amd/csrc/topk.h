@@ -221,11 +221,10 @@ __device__ __forceinline__ uint64_t wave_top8_lanes(uint64_t key, int lane) {
 // 64 W >= E, every wave of which calls it (it holds one barrier): waves
 // 0..min(W, 8)-1 each rank 64 logits (the logits as load_logits forms
 // them), wave 0 ranks their 8 best each and computes the weights with
-// wave_topk_merge's
-// arithmetic in the same lanes, so both the selection and the weights are
-// that function's bit for bit.  On return lane j < k of wave 0 holds the
-// j-th id and weight (other lanes and waves: unspecified).  cand: 64 keys
-// and lgt: kMaxRouteExperts floats of LDS.
+// wave_topk_merge's arithmetic in the same lanes, so both the selection
+// and the weights are that function's bit for bit.  On return lane j < k
+// of wave 0 holds the j-th id and weight (other lanes and waves:
+// unspecified).  cand: 64 keys and lgt: kMaxRouteExperts floats of LDS.
 __device__ __forceinline__ void block_topk8(const LogitSrc &src, int64_t t, int E, int k,
                                             int renormalize, uint64_t *cand, float *lgt,
                                             int &id, float &wgt) {
