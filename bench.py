@@ -221,7 +221,10 @@ def main():
     name = args.workload or "moe_decode"
     failed = []
     try:
+        t_w = time.perf_counter()
         out = measure(args, name, gumbel=args.gumbel, steps=args.steps, warmup=args.warmup)
+        print(f"bench: {name} measured in {time.perf_counter() - t_w:.1f} s", file=sys.stderr,
+              flush=True)
     except GateFailure as e:
         print(json.dumps({"error": f"correctness gate failed before timing: {e}"}), flush=True)
         sys.exit(3)
@@ -234,7 +237,10 @@ def main():
             steps = min(args.steps, SIDE_STEPS[wname])
             warm = min(args.warmup, 10)
             try:
+                t_w = time.perf_counter()
                 sub = measure(args, wname, gumbel=gumbel, steps=steps, warmup=warm)
+                print(f"bench: {key} measured in {time.perf_counter() - t_w:.1f} s",
+                      file=sys.stderr, flush=True)
             except GateFailure as e:
                 sub = {"error": f"correctness gate failed before timing: {e}"}
                 failed.append(key)
