@@ -192,6 +192,11 @@ bool ffn_pair_order_ok(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, nv
   return act == NVFP4_W4A16 && ffn_small(T, E, k) && row_gemv_supported((int)H) &&
          row_gemv_supported((int)I) && row_ffn_supported((int)H, (int)I);
 }
+// A single expert (a dense MLP) with one row, W4A16: the gate/up rows dealt
+// out evenly over the CUs (row_mlp_gate_up_kernel)
+bool ffn_row_mlp(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, nvfp4_act_mode act) {
+  return act == NVFP4_W4A16 && E == 1 && T * k == 1 && row_mlp_supported((int)H, (int)I);
+}
 // A single expert (a dense MLP) with 3 to 32 rows: one weight stream shared
 // by every row in the dense GEMV (K of both projections a multiple of 256).
 bool ffn_dense(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k) {
@@ -987,8 +992,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
     g.a_shift = nullptr;
   }
-  // W4A16 decode with H = 2048: both projections in one launch
-  if (rows && row_ffn_supported((int)H, (int)I)) {
+  // W4A16 decode with H = 2048: both projections in one launch (one dense
+  // row instead deals its gate/up rows out over every CU, below)
+  if (rows && row_ffn_supported((int)H, (int)I) && !ffn_row_mlp(T, H, I, E, k, act)) {
     GemmArgs dd = {};
     dd.b_codes[0] = w->down_codes;
     dd.b_scales[0] = w->down_scales;
@@ -1013,7 +1019,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     return NVFP4_OK;
   }
   mark_kernel(NVFP4_STAGE_GATE_UP, stream);
-  if (rows)
+  if (rows && ffn_row_mlp(T, H, I, E, k, act))   // one dense row: rows dealt out evenly
+    LAUNCH(launch_row_mlp_gate_up(g, topk_ids, stream), "gate/up");
+  else if (rows)
     LAUNCH(launch_row_gemv(Epi::SWIGLU, g, sorted_pairs, topk_ids, k, (int)P, stream, fused_sum),
            "gate/up");
   else if (small)

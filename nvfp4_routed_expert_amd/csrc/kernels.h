@@ -277,6 +277,15 @@ hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, co
                               int E, void *y, OutType yt, hipStream_t s,
                               int32_t *offsets = nullptr, int32_t *sorted_pairs = nullptr);
 
+// Gate/up projection of a dense MLP's one row (W4A16, one expert, one
+// token; H a multiple of 1024 up to 5120, I a multiple of 16 up to 32768):
+// h = bf16(silu(g_gate x Wg^T) * g_up x Wu^T) into g.out [I] (bf16), the
+// rows dealt out as whole 16-column blocks of I over at most 256
+// workgroups.  Writes nothing when ids[0] lies outside 0..g.n_experts-1.
+// g: A = the bf16 x row, b_* the gate (0) and up (1) matrices of expert 0.
+bool row_mlp_supported(int H, int I);
+hipError_t launch_row_mlp_gate_up(const GemmArgs &g, const int32_t *ids, hipStream_t s);
+
 // Token-major down projection for decode with the combine folded in: y[t] =
 // sum over slots j (in order) of w[t k + j] * g * (h[t k + j] . W_down[e]);
 // A = h rows in pair order (bf16), out = y.  Supported for K (= I) in

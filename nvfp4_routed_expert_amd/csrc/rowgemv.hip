@@ -725,6 +725,173 @@ __global__ __launch_bounds__(kCombineThreads) void ffn_combine_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dense MLP decode of one row: the gate/up projection over even slices of I
+// ---------------------------------------------------------------------------
+//
+// The decode form of a dense NVFP4 MLP (Eider page, "Qwen3.8 27B": NVFP4 for
+// most MLP weights) for a single activation row, where the gate and up rows
+// are two thirds of the weight stream.  The rows are dealt out as whole
+// 16-column scale blocks of I: with nbt = I / 16 blocks and G = min(nbt,
+// kMlpGrid) workgroups, workgroup w takes blocks [w nbt / G, (w + 1) nbt /
+// G), at most kMlpMaxNb of them (I = 17408: 1088 blocks, four or five per
+// workgroup), so every CU streams the same share (a grid that is not a
+// multiple of the CU count would give some CUs two workgroups and double the
+// kernel's time; the row GEMV's persistent units do not divide such an I
+// evenly either).  Wave v takes the rows c0 + 16 i + v (i < nb) of both
+// matrices, whole rows of H per load step with the next row's loads in
+// flight, dot products with x held in registers, one cross-lane sum per
+// row, and lane 0 writes SiLU * up rounded to bf16.  Sixteen waves per
+// workgroup (one workgroup per CU) keep enough loads in flight.  The down
+// projection then streams whole rows of K = I in the row GEMV.
+// (Carrying each workgroup's h slice on into the matching columns of every
+// down row, as the fused routed kernel does, was measured: with slices of
+// 64-80 columns each down row gives a workgroup 32-40 bytes, and that
+// scattered stream ran at ~1.1 TB/s.)
+//
+// Lane layout of a row of H = 2048 NP2 + 1024 HALF elements: NP2 pieces of
+// 2048 (lane l: elements 32 l .. 32 l + 31 of the piece, 16 code bytes and
+// two scale bytes, as in the other row kernels) and, when HALF, one piece of
+// 1024 (lane l: 16 elements, 8 code bytes, one scale byte).  x is held in
+// registers in the same layout.
+constexpr int kMlpWaves = 16;
+constexpr int kMlpGrid = 256;    // workgroups: one per CU
+constexpr int kMlpMaxNb = 8;     // blocks per workgroup (I <= 16 * 8 * 256)
+
+// 16 codes of one lane -> 8 exact bf16 pairs
+__device__ __forceinline__ void decode16(const u32x2 codes, uint32_t (&w)[8]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    w[4 * q + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 0));
+    w[4 * q + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 1));
+    w[4 * q + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 2));
+    w[4 * q + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes[q], 1.0f, 3));
+  }
+}
+
+// one 16-element block, its sum scaled once by the block's scale
+__device__ __forceinline__ float dot16(const uint32_t (&w)[8], const uint32_t (&a)[8], float s) {
+  float b = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w[i]),
+                                        __builtin_bit_cast(bf16x2_t, a[i]), b, false);
+  return b * s;
+}
+
+template <int NP2, bool HALF>
+__global__ __launch_bounds__(64 * kMlpWaves, 4) void row_mlp_gate_up_kernel(const GemmArgs g,
+                                                                            const int32_t *ids,
+                                                                            int nbt, int n_wg) {
+  constexpr int H = 2048 * NP2 + (HALF ? 1024 : 0);
+  constexpr int NQ = NP2 > 0 ? NP2 : 1;   // (array extents)
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int per = (n_wg + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int w = (blockIdx.x % kXcds) * per + slot;
+  if (slot >= per || w >= n_wg) return;   // whole workgroup (uniform)
+  // a dropped token (id outside the experts): no h; the down projection
+  // skips it too
+  if ((unsigned)ids[0] >= (unsigned)g.n_experts) return;
+  const int b0 = (int)((int64_t)w * nbt / n_wg);
+  const int nb = (int)((int64_t)(w + 1) * nbt / n_wg) - b0;   // 1 .. kMlpMaxNb (uniform)
+  const int c0 = 16 * b0;
+
+  // ---- x row in registers
+  uint32_t ax[NQ][16], axh[8];
+  {
+    const uint16_t *xr = reinterpret_cast<const uint16_t *>(g.A);
+#pragma unroll
+    for (int q = 0; q < NP2; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(xr + 2048 * q + 32 * lane + 8 * j);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ax[q][4 * j + t] = v[t];
+      }
+    if constexpr (HALF) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(xr + 2048 * NP2 + 16 * lane + 8 * j);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) axh[4 * j + t] = v[t];
+      }
+    }
+  }
+
+  // ---- gate / up: rows c0 + 16 i + wave (i < nb) of both matrices
+  constexpr uint32_t code_row = H / 2, scale_row = H / 16;
+  u32x4 bq[2][2][NQ];   // [buffer][matrix][piece]
+  u32x2 bh[2][2];
+  uint32_t sq[2][2][NQ], sh[2][2];
+  auto load_row = [&](int buf, int i) {
+    const uint32_t row = (uint32_t)(c0 + 16 * i + wave);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint8_t *cr = g.b_codes[m] + row * code_row;
+      const uint8_t *sr = g.b_scales[m] + row * scale_row;
+#pragma unroll
+      for (int q = 0; q < NP2; ++q) {
+        bq[buf][m][q] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(cr + 1024 * q + 16 * lane));
+        sq[buf][m][q] = *reinterpret_cast<const uint16_t *>(sr + 128 * q + 2 * lane);
+      }
+      if constexpr (HALF) {
+        bh[buf][m] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x2 *>(cr + 1024 * NP2 + 8 * lane));
+        sh[buf][m] = sr[128 * NP2 + lane];
+      }
+    }
+  };
+  // row i from buffer buf: the two sums over the wave (gate in lanes 0..31,
+  // up in lanes 32..63 after the first swap), then SiLU * up by lane 0
+  auto row_h = [&](int buf, int i) {
+    float p[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NP2; ++q) {
+        const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sq[buf][m][q], 1.0f, false);
+        uint32_t wd[16];
+        decode32(bq[buf][m][q], wd);
+        acc += dot32(wd, ax[q], sc[0], sc[1]);
+      }
+      if constexpr (HALF) {
+        const f32x2_t sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sh[buf][m], 1.0f, false);
+        uint32_t wd[8];
+        decode16(bh[buf][m], wd);
+        acc += dot16(wd, axh, sc[0]);
+      }
+      p[m] = acc;
+    }
+    swap32(p[0], p[1]);        // p[0] = [gate lo, up lo], p[1] = [gate hi, up hi]
+    float r = p[0] + p[1];     // lanes 0..31: gate, 32..63: up (32 partial sums each)
+    float r2 = r;
+    swap16(r, r2);
+    r += r2;
+    r += dpp_f32<0x128>(r);    // row_ror:8, 4, 2, 1: every lane of a 16-lane row gets its sum
+    r += dpp_f32<0x124>(r);
+    r += dpp_f32<0x122>(r);
+    r += dpp_f32<0x121>(r);
+    const float G = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), 0)) *
+                    g.b_global[0][0];
+    const float U = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, r), 32)) *
+                    g.b_global[1][0];
+    if (lane == 0)
+      static_cast<uint16_t *>(g.out)[c0 + 16 * i + wave] =
+          (uint16_t)f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
+  };
+  load_row(0, 0);
+  for (int i = 0; i < nb; i += 2) {   // (nb uniform: scalar loop and branches)
+    if (i + 1 < nb) load_row(1, i + 1);
+    row_h(0, i);
+    if (i + 2 < nb) load_row(0, i + 2);
+    if (i + 1 < nb) row_h(1, i + 1);
+  }
+
+}
+
 }  // namespace
 
 bool row_down_sum_supported(int K, int k) {
@@ -773,6 +940,33 @@ hipError_t launch_row_ffn(const GemmArgs &g, const GemmArgs &d, const int32_t *s
   const Routing rt{sorted_pairs, ids, k, false};
   launch_kernel(row_ffn_kernel, dim3((unsigned)grid), dim3(64 * kFfnWaves), 0, s, g, d, rt, fr, P,
                 n_c, ypart);
+  return hipGetLastError();
+}
+
+// (H up to 5120: x and two rows' loads stay within the 128 VGPRs of four
+// waves per SIMD)
+bool row_mlp_supported(int H, int I) {
+  return H % 1024 == 0 && H >= 1024 && H <= 5120 && I % 16 == 0 && I >= 16 &&
+         (I / 16 + kMlpGrid - 1) / kMlpGrid <= kMlpMaxNb && (int64_t)I * H < ((int64_t)1 << 32);
+}
+
+hipError_t launch_row_mlp_gate_up(const GemmArgs &g, const int32_t *ids, hipStream_t s) {
+  const int H = g.K, I = g.N;
+  if (!row_mlp_supported(H, I)) return hipErrorInvalidValue;
+  const int nbt = I / 16, n_wg = nbt < kMlpGrid ? nbt : kMlpGrid;
+  const int64_t grid = ((int64_t)n_wg + kXcds - 1) / kXcds * kXcds;
+  const dim3 gd((unsigned)grid), bd(64 * kMlpWaves);
+#define NVFP4_ROW_MLP(NP2, HALF) \
+  launch_kernel((row_mlp_gate_up_kernel<NP2, HALF>), gd, bd, 0, s, g, ids, nbt, n_wg)
+  switch (H / 1024) {
+    case 1: NVFP4_ROW_MLP(0, true); break;
+    case 2: NVFP4_ROW_MLP(1, false); break;
+    case 3: NVFP4_ROW_MLP(1, true); break;
+    case 4: NVFP4_ROW_MLP(2, false); break;
+    case 5: NVFP4_ROW_MLP(2, true); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef NVFP4_ROW_MLP
   return hipGetLastError();
 }
 

@@ -656,6 +656,80 @@ def test_moe_single_expert_is_dense_mlp():
     assert_close_f32(to_np(y), ref, "dense mlp via moe")
 
 
+@pytest.mark.parametrize("H,I", [(1024, 256), (2048, 4352), (3072, 2112), (5120, 1024),
+                                 (4096, 2048), (1024, 32768)])
+def test_one_row_dense_mlp(H, I):
+    """One row of a dense MLP (one expert, one slot) takes the gate/up kernel
+    that deals I out evenly as whole 16-column blocks (then the row GEMV's
+    down projection): against the oracle's dense MLP in fp32 and as its bf16
+    rounding.  Cases: 16 to 132 workgroups of one block (132: a ragged last
+    XCD range), 256 workgroups of one or two blocks (4352) and of eight
+    (32768, the most a workgroup takes), and a 1024-element piece in the x
+    row for odd H / 1024."""
+    import bench
+    assert bench.gate_up_kernel(1, H, I, 1, 1, "w4a16") == "row_mlp_gate_up_kernel"
+    say("one-row dense mlp", H, I)
+    x, rids, rw, y, _, w_ref, st = _moe_run(1, H, I, 1, 1, seed=H + I)
+    ref = O.dense_mlp(x.float().numpy(), (w_ref.gate_codes[0], w_ref.gate_scales[0], w_ref.gate_global[0]),
+                      (w_ref.up_codes[0], w_ref.up_scales[0], w_ref.up_global[0]),
+                      (w_ref.down_codes[0], w_ref.down_scales[0], w_ref.down_global[0]))
+    assert_close_f32(to_np(y), ref, "one-row dense mlp")
+    ids, wts, off, pairs, w_gpu = st
+    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, 1,
+                                         out_dtype=torch.bfloat16)
+    assert_bf16_output(to_np(yb.float()), to_np(y), ref, "one-row dense mlp (bf16)")
+
+
+def test_one_row_dense_mlp_dropped_and_repeated():
+    """The one-row path with a dropped id writes zeros (y filled with NaN
+    first); repeated calls through one workspace, and a captured graph's
+    replays with eager calls between them, give the eager result bit for
+    bit."""
+    H, I = 2048, 2112
+    say("one-row dense mlp dropped / graph", H, I)
+    x = synth.activations(1, H, 5).to(DEV)
+    w_gpu = weights.synthetic_experts(1, H, I, 5, DEV)
+    wts = torch.ones((1, 1), dtype=torch.float32, device=DEV)
+    ws = torch.empty(native.ffn_workspace_bytes(1, H, I, 1, 1), dtype=torch.uint8, device=DEV)
+    for bad in (-1, 1):
+        ids = torch.full((1, 1), bad, dtype=torch.int32, device=DEV)
+        off, pairs = native.moe_permute_pairs(ids, 1)
+        y = torch.full((1, H), float("nan"), dtype=torch.float32, device=DEV)
+        native.moe_grouped_nvfp4_ffn(x, w_gpu, ids, wts, off, pairs, 1, out_dtype=torch.float32,
+                                     workspace=ws, out=y)
+        torch.cuda.synchronize()
+        assert torch.all(y == 0.0), bad
+    ids = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    off, pairs = native.moe_permute_pairs(ids, 1)
+    out = torch.empty((1, H), dtype=torch.float32, device=DEV)
+
+    def call():
+        native.moe_grouped_nvfp4_ffn(x, w_gpu, ids, wts, off, pairs, 1, out_dtype=torch.float32,
+                                     workspace=ws, out=out)
+    call()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert torch.isfinite(eager).all()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for i in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {i}"
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+
+
 # ---- the full-size workloads, checked on sampled tokens ----------------------------
 
 def test_moe_decode_full_size():

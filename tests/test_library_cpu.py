@@ -316,7 +316,9 @@ def test_bench_names_the_kernel_the_library_dispatches():
     assert bench.gate_up_kernel(16, 1024, 512, 512, 8, "w4a16") == "row_gemv_kernel"
     assert bench.gate_up_kernel(512, 2048, 512, 512, 8, "w4a16") == "tile_gemm_kernel"
     assert bench.gate_up_kernel(2048, 4096, 1536, 128, 8, "w4a4") == "tile_gemm_kernel"
-    assert bench.gate_up_kernel(1, 5120, 17408, 1, 1, "w4a16") == "row_gemv_kernel"
+    assert bench.gate_up_kernel(1, 5120, 17408, 1, 1, "w4a16") == "row_mlp_gate_up_kernel"
+    assert bench.gate_up_kernel(1, 6144, 17408, 1, 1, "w4a16") == "row_gemv_kernel"
+    assert bench.gate_up_kernel(2, 5120, 17408, 1, 1, "w4a16") == "row_gemv_kernel"
     assert bench.gate_up_kernel(8, 5120, 17408, 1, 1, "w4a16") == "dense_gemv_kernel"
     assert bench.gate_up_kernel(32, 5120, 17408, 1, 1, "w4a16") == "dense_gemv_kernel"
     assert bench.gate_up_kernel(33, 5120, 17408, 1, 1, "w4a16") == "tile_gemm_kernel"
@@ -348,3 +350,4 @@ def test_bench_and_entry_reference_only_defined_names():
                 bound.add(node.id)
         used = {n.id for n in ast.walk(tree) if isinstance(n, ast.Name) and isinstance(n.ctx, ast.Load)}
         assert not (used - bound), (fname, sorted(used - bound))
+
