@@ -146,8 +146,8 @@ def gate_up_kernel(T, H, I, E, k, act):
         return "dense_gemv_kernel"   # a dense MLP with a few rows: one shared weight stream
     if small:
         if act == "w4a16" and row_ok(H) and row_ok(I):
-            if (E == 1 and P == 1 and H % 1024 == 0 and H <= 5120 and I % 16 == 0
-                    and (I // 16 + 255) // 256 <= 8):
+            if (E == 1 and P == 1 and H % 1024 == 0 and H <= 5120 and I % 32 == 0
+                    and (I // 16 + 255) // 256 <= 8 and 2 * I + 2048 <= 65536):
                 return "row_mlp_gate_up_kernel"   # one dense row: gate/up rows dealt out evenly
             # H = 2048 and I a multiple of 256: both projections in one launch
             return "row_ffn_kernel" if H == 2048 and I % 256 == 0 else "row_gemv_kernel"

@@ -192,10 +192,12 @@ bool ffn_pair_order_ok(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, nv
   return act == NVFP4_W4A16 && ffn_small(T, E, k) && row_gemv_supported((int)H) &&
          row_gemv_supported((int)I) && row_ffn_supported((int)H, (int)I);
 }
-// A single expert (a dense MLP) with one row, W4A16: the gate/up rows dealt
-// out evenly over the CUs (row_mlp_gate_up_kernel)
+// A single expert (a dense MLP) with one row, W4A16: the gate/up rows and
+// then the down rows dealt out evenly over the CUs (row_mlp_gate_up_kernel,
+// row_mlp_down_kernel, which writes y itself)
 bool ffn_row_mlp(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, nvfp4_act_mode act) {
-  return act == NVFP4_W4A16 && E == 1 && T * k == 1 && row_mlp_supported((int)H, (int)I);
+  return act == NVFP4_W4A16 && E == 1 && T * k == 1 && row_mlp_supported((int)H, (int)I) &&
+         row_mlp_down_supported((int)H, (int)I);
 }
 // A single expert (a dense MLP) with 3 to 32 rows: one weight stream shared
 // by every row in the dense GEMV (K of both projections a multiple of 256).
@@ -1085,7 +1087,12 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   d.partial = ws.split;
   d.partial_rows = P;
   mark_kernel(NVFP4_STAGE_DOWN, stream);
-  if (rows) {
+  const bool mlp_row = rows && ffn_row_mlp(T, H, I, E, k, act);
+  if (mlp_row) {
+    d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
+    d.a_shift = nullptr;
+    LAUNCH(launch_row_mlp_down(d, topk_ids, y, yt, stream), "down");
+  } else if (rows) {
     d.A = reinterpret_cast<const _Float16 *>(ws.h);   // bf16 h, read as given
     d.a_shift = nullptr;
     if (fused_sum) {
@@ -1113,7 +1120,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
            "down");
   g_timed_launch = TimedLaunch{nullptr, nullptr};
   // 6. combine the k pairs of every token in slot order
-  if (fused_sum || dense_direct) {   // done by the down kernel: an empty stage
+  if (fused_sum || dense_direct || mlp_row) {   // done by the down kernel: an empty stage
     mark(NVFP4_STAGE_COMBINE, false, stream);
     mark(NVFP4_STAGE_COMBINE, true, stream);
     return NVFP4_OK;

@@ -286,6 +286,15 @@ hipError_t launch_ffn_combine(const float *ypart, int T, int H, int I, int k, co
 bool row_mlp_supported(int H, int I);
 hipError_t launch_row_mlp_gate_up(const GemmArgs &g, const int32_t *ids, hipStream_t s);
 
+// Down projection of the same row: y [H] = g_down w (h . Wd^T) in y's type
+// (zeros when ids[0] lies outside 0..d.n_experts-1), the output rows dealt
+// out evenly over at most 256 workgroups; d: A = h [I] (bf16), the down
+// matrix of expert 0, pair_weights[0] = w.  I a multiple of 32 up to 31744,
+// H up to 8192.
+bool row_mlp_down_supported(int H, int I);
+hipError_t launch_row_mlp_down(const GemmArgs &d, const int32_t *ids, void *y, OutType yt,
+                               hipStream_t s);
+
 // Token-major down projection for decode with the combine folded in: y[t] =
 // sum over slots j (in order) of w[t k + j] * g * (h[t k + j] . W_down[e]);
 // A = h rows in pair order (bf16), out = y.  Supported for K (= I) in

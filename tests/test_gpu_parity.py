@@ -657,15 +657,17 @@ def test_moe_single_expert_is_dense_mlp():
 
 
 @pytest.mark.parametrize("H,I", [(1024, 256), (2048, 4352), (3072, 2112), (5120, 1024),
-                                 (4096, 2048), (1024, 32768)])
+                                 (4096, 2048), (1024, 31744)])
 def test_one_row_dense_mlp(H, I):
     """One row of a dense MLP (one expert, one slot) takes the gate/up kernel
-    that deals I out evenly as whole 16-column blocks (then the row GEMV's
-    down projection): against the oracle's dense MLP in fp32 and as its bf16
+    that deals I out evenly as whole 16-column blocks and the down kernel
+    that deals the H output rows out evenly and writes y: against the oracle's dense MLP in fp32 and as its bf16
     rounding.  Cases: 16 to 132 workgroups of one block (132: a ragged last
-    XCD range), 256 workgroups of one or two blocks (4352) and of eight
-    (32768, the most a workgroup takes), and a 1024-element piece in the x
-    row for odd H / 1024."""
+    XCD range), 256 workgroups of one or two blocks (4352) and of up to
+    eight (31744, the most a workgroup takes, and the longest h the down
+    kernel stages in LDS), a 1024-element piece in the x row for odd
+    H / 1024, and K slices of the down rows cut short (I % 2048 = 256, 64,
+    1024)."""
     import bench
     assert bench.gate_up_kernel(1, H, I, 1, 1, "w4a16") == "row_mlp_gate_up_kernel"
     say("one-row dense mlp", H, I)
