@@ -242,9 +242,7 @@ FfnWs carve_ffn(Carver &c, int64_t T, int64_t H, int64_t I, int64_t E, int64_t k
   w.n_mblocks = c.take<int32_t>(4);
   w.mblocks_down = c.take<int4>((size_t)ffn_max_mblocks(P, E, 16));
   w.n_mblocks_down = c.take<int32_t>(4);
-  // 4 scratch words, then (the dense GEMV path) the max |h| of each
-  // 256-element segment of h
-  w.slots = c.take<uint32_t>((size_t)(4 + (ffn_dense(T, H, I, E, k) ? P * (I / 256) : 0)));
+  w.slots = c.take<uint32_t>(4);   // scratch words
   w.partials = c.take<float>(kMaxPartials);
   const FfnPlans pl = ffn_plans(T, H, I, E, k);
   w.split = c.take<float>(pl.gate_up.partial_floats > pl.down.partial_floats
@@ -905,9 +903,9 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   const bool rows = small && !a4 && row_gemv_supported((int)H) && row_gemv_supported((int)I);
   // ... and the down projection sums each token's slots itself (no combine)
   const bool fused_sum = rows && row_down_sum_supported((int)I, k);
-  // A single expert (one slot per token) on the dense GEMV: the down
-  // projection's reduce writes y itself (a combine of one slot is a copy)
-  // and the x pass zeroes the rows of tokens whose id is dropped.
+  // A single expert (one slot per token) on the dense GEMV: bf16 x and h as
+  // given (no fp16 operand passes), and the down projection's reduce writes y
+  // itself (a combine of one slot is a copy), zeros for a dropped token.
   const bool dense = ffn_dense(T, H, I, E, k);
   const bool dense_direct = dense && !a4;
   const int64_t zero_words = 4;   // scratch words the plan zeroes
@@ -918,15 +916,18 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
     mark(NVFP4_STAGE_X_PREP, true, stream);
+  } else if (dense_direct) {   // bf16 operands as given: no plan, no x pass
+    mark(NVFP4_STAGE_PLAN, false, stream);
+    mark(NVFP4_STAGE_PLAN, true, stream);
+    mark(NVFP4_STAGE_X_PREP, false, stream);
+    mark(NVFP4_STAGE_X_PREP, true, stream);
   } else if (!a4) {
     mark(NVFP4_STAGE_PLAN, false, stream);
     mark(NVFP4_STAGE_PLAN, true, stream);
     mark(NVFP4_STAGE_X_PREP, false, stream);
     LAUNCH(launch_moe_prep(xb, T, H, ws.x16, ws.xshift, expert_offsets, E, bm, ws.mblocks,
                            ws.n_mblocks, bm_down, split_down ? ws.mblocks_down : nullptr,
-                           ws.n_mblocks_down, ws.slots, zero_words, stream,
-                           dense_direct ? topk_ids : nullptr, dense_direct ? y : nullptr,
-                           yt == OutType::F32),
+                           ws.n_mblocks_down, ws.slots, zero_words, stream),
            "plan + x prep");
     mark(NVFP4_STAGE_X_PREP, true, stream);
   } else {
@@ -976,8 +977,6 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.ldo = I;
   g.out_type = OutType::BF16;
   g.amax_slot = a4 ? ws.slots : nullptr;
-  // (the dense reduce keeps each 256-element segment's max |h| for the h pass)
-  g.row_part = dense_direct ? reinterpret_cast<float *>(ws.slots + 4) : nullptr;
   // W4A4 with a given h global on the tiled path: the gate/up epilogue
   // quantises h itself and writes the down GEMM's fp16 operand directly
   const bool h_fused = given && !small && !dense && !g_separate_h_quant &&
@@ -990,6 +989,11 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   g.sorted_pairs = sorted_pairs;   // (split-K reduce: expert of each tile row)
   g.partial = ws.split;
   g.partial_rows = P;
+  if (dense_direct) {
+    g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
+    g.a_shift = nullptr;
+    g.a_bf16 = true;
+  }
   if (rows) {
     g.A = reinterpret_cast<const _Float16 *>(x);   // bf16 rows, read as given
     g.a_shift = nullptr;
@@ -1041,11 +1045,7 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   mark(NVFP4_STAGE_H_PREP, false, stream);
   const bool h_inline = small && !a4;
   if (!a4) {
-    if (dense_direct)   // the row maxima are known: one elementwise pass
-      LAUNCH(launch_row_shift_parts(ws.h, P, I, reinterpret_cast<const float *>(ws.slots + 4),
-                                    ws.h16, ws.hshift, stream),
-             "h prep");
-    else if (!h_inline && !rows)
+    if (!h_inline && !rows && !dense_direct)
       LAUNCH(launch_row_prep(ws.h, P, I, PrepMode::SHIFT, ws.h16, ws.hshift, nullptr, 0, nullptr,
                              nullptr, nullptr, stream),
              "h prep");
@@ -1106,7 +1106,11 @@ nvfp4_status moe_grouped_nvfp4_ffn(const void *x, int64_t T, int64_t H, int64_t 
   } else if (small)
     LAUNCH(launch_gemv(Epi::DOWN, d, h_inline, stream), "down");
   else if (dense) {
-    if (dense_direct) {   // the reduce writes y (pair t is token t)
+    if (dense_direct) {   // bf16 h as given; the reduce writes y (pair t is token t)
+      d.A = reinterpret_cast<const _Float16 *>(ws.h);
+      d.a_shift = nullptr;
+      d.a_bf16 = true;
+      d.drop_ids = topk_ids;
       d.out = y;
       d.ldo = H;
       d.out_type = yt;

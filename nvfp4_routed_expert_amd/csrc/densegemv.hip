@@ -36,6 +36,9 @@
 #include "common.h"
 #include "kernels.h"
 
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 namespace nvfp4 {
 namespace {
 
@@ -87,7 +90,28 @@ __host__ __device__ inline int64_t unit_owner(const StreamSplit &s, int64_t u) {
   return ((u + 1) * s.grid + s.units - 1) / s.units - 1;
 }
 
-template <int MS, Epi EPI>
+// E2M1 codes of one word -> eight exact bf16 products with the block scale
+// (through fp32: gfx950 has no packed bf16 multiply; e2m1 * e4m3 has at most
+// six significant bits, so every step is exact)
+__device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t word, float s) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+  bf16x8 r;
+  r[0] = (__bf16)(v0[0] * s); r[1] = (__bf16)(v0[1] * s);
+  r[2] = (__bf16)(v1[0] * s); r[3] = (__bf16)(v1[1] * s);
+  r[4] = (__bf16)(v2[0] * s); r[5] = (__bf16)(v2[1] * s);
+  r[6] = (__bf16)(v3[0] * s); r[7] = (__bf16)(v3[1] * s);
+  return r;
+}
+
+// BF: the activation rows are bf16 as given (a dense MLP's x and h), the
+// weights are dequantised to bf16 and multiplied by v_mfma_f32_16x16x32_bf16;
+// the products are the same exact values as in the fp16 form, which needs
+// its operand rows converted to fp16 with a power-of-two row shift by
+// passes of their own.
+template <int MS, Epi EPI, bool BF>
 __global__ __launch_bounds__(64 * kDWaves, MS == 1 ? 2 : 1) void dense_gemv_kernel(
     const GemmArgs p, int M, const StreamSplit sk, float *partial) {
   using C = DenseCfg<MS>;
@@ -202,26 +226,51 @@ __global__ __launch_bounds__(64 * kDWaves, MS == 1 ? 2 : 1) void dense_gemv_kern
         cw[f][h] = *reinterpret_cast<const u32x4 *>(row + 16 * ((2 * lg + h) ^ (R & 7)));
       sw[f] = *reinterpret_cast<const uint32_t *>(st + C::B_BYTES + R * kDScaleRow + 4 * lg);
     }
-    f16x2 sp[2][4];
-#pragma unroll
-    for (int f = 0; f < 2; ++f) {
-      e4m3x2_to_f16_pairs(sw[f], sp[f][0], sp[f][1]);
-      e4m3x2_to_f16_pairs(sw[f] >> 16, sp[f][2], sp[f][3]);
-    }
     const uint8_t *abase = st + C::B_BYTES + C::S_BYTES;
+    if constexpr (BF) {
+      f32x2 sf[2][2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      f16x8 b[2];
+      for (int f = 0; f < 2; ++f) {
+        sf[f][0] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[f], 1.0f, false);
+        sf[f][1] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sw[f], 1.0f, true);
+      }
 #pragma unroll
-      for (int f = 0; f < 2; ++f) b[f] = dequant8_f16(cw[f][s >> 2][s & 3], sp[f][s >> 1]);
-#pragma unroll
-      for (int ms = 0; ms < MS; ++ms) {
-        const int m = 16 * ms + lr;
-        const f16x8 a = *reinterpret_cast<const f16x8 *>(abase + m * (kDC * 2) +
-                                                         16 * ((8 * lg + s) ^ (m & 7)));
+      for (int s = 0; s < 8; ++s) {
+        bf16x8 b[2];
 #pragma unroll
         for (int f = 0; f < 2; ++f)
-          acc[ms][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[f], acc[ms][f], 0, 0, 0);
+          b[f] = dequant8_bf16(cw[f][s >> 2][s & 3], sf[f][s >> 2][(s >> 1) & 1]);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const int m = 16 * ms + lr;
+          const bf16x8 a = *reinterpret_cast<const bf16x8 *>(abase + m * (kDC * 2) +
+                                                             16 * ((8 * lg + s) ^ (m & 7)));
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            acc[ms][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[ms][f], 0, 0, 0);
+        }
+      }
+    } else {
+      f16x2 sp[2][4];
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        e4m3x2_to_f16_pairs(sw[f], sp[f][0], sp[f][1]);
+        e4m3x2_to_f16_pairs(sw[f] >> 16, sp[f][2], sp[f][3]);
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        f16x8 b[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) b[f] = dequant8_f16(cw[f][s >> 2][s & 3], sp[f][s >> 1]);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const int m = 16 * ms + lr;
+          const f16x8 a = *reinterpret_cast<const f16x8 *>(abase + m * (kDC * 2) +
+                                                           16 * ((8 * lg + s) ^ (m & 7)));
+#pragma unroll
+          for (int f = 0; f < 2; ++f)
+            acc[ms][f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[f], acc[ms][f], 0, 0, 0);
+        }
       }
     }
   };
@@ -287,6 +336,16 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const GemmArgs p, int
   float amax = 0.0f;
   if (idx < (int64_t)M * N) {
     const int m = (int)(idx / N), n = (int)(idx - (int64_t)m * N);
+    if constexpr (EPI == Epi::DOWN) {
+      // row m of out as a token's row: zeros for a dropped token (no kept
+      // position writes that row)
+      if (p.drop_ids && (unsigned)p.drop_ids[m] >= (unsigned)p.n_experts) {
+        if (p.out_type == OutType::F32)
+          static_cast<float *>(p.out)[(int64_t)m * p.ldo + n] = 0.0f;
+        else
+          static_cast<uint16_t *>(p.out)[(int64_t)m * p.ldo + n] = 0;
+      }
+    }
     const int t = n / kCols, cl = n - t * kCols;
     const int pr = p.a_rowmap ? p.a_rowmap[m] : m;
     if (pr >= 0) {   // (a dropped pair: no h row, no output)
@@ -357,14 +416,6 @@ __global__ __launch_bounds__(256) void dense_reduce_kernel(const GemmArgs p, int
     }
   }
   if constexpr (EPI == Epi::SWIGLU) {
-    if (p.row_part) {   // this workgroup's max |h| (its 256 elements lie in one row)
-      __shared__ float wmax[4];
-      const float wm = wave_max(amax);
-      if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = wm;
-      __syncthreads();
-      if (threadIdx.x == 0 && idx < (int64_t)M * N)
-        p.row_part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    }
     if (p.amax_slot) {
       amax = wave_max(amax);
       if ((threadIdx.x & 63) == 0 && amax > 0.0f) atomicMax(p.amax_slot, __float_as_uint(amax));
@@ -389,13 +440,25 @@ hipError_t launch_ms(Epi epi, const GemmArgs &a, int M, const StreamSplit &sk, h
   const dim3 grid((unsigned)sk.grid), block(64 * kDWaves);
   switch (epi) {
     case Epi::LINEAR:
-      launch_kernel((dense_gemv_kernel<MS, Epi::LINEAR>), grid, block, 0, s, a, M, sk, a.partial);
+      if (a.a_bf16) return hipErrorInvalidValue;
+      launch_kernel((dense_gemv_kernel<MS, Epi::LINEAR, false>), grid, block, 0, s, a, M, sk,
+                    a.partial);
       break;
     case Epi::SWIGLU:
-      launch_kernel((dense_gemv_kernel<MS, Epi::SWIGLU>), grid, block, 0, s, a, M, sk, a.partial);
+      if (a.a_bf16)
+        launch_kernel((dense_gemv_kernel<MS, Epi::SWIGLU, true>), grid, block, 0, s, a, M, sk,
+                      a.partial);
+      else
+        launch_kernel((dense_gemv_kernel<MS, Epi::SWIGLU, false>), grid, block, 0, s, a, M, sk,
+                      a.partial);
       break;
     case Epi::DOWN:
-      launch_kernel((dense_gemv_kernel<MS, Epi::DOWN>), grid, block, 0, s, a, M, sk, a.partial);
+      if (a.a_bf16)
+        launch_kernel((dense_gemv_kernel<MS, Epi::DOWN, true>), grid, block, 0, s, a, M, sk,
+                      a.partial);
+      else
+        launch_kernel((dense_gemv_kernel<MS, Epi::DOWN, false>), grid, block, 0, s, a, M, sk,
+                      a.partial);
       break;
   }
   return hipGetLastError();

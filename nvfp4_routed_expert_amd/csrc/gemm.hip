@@ -263,17 +263,14 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int32_t *offsets, 
 // Blocks before the last: x rows -> fp16 with their power-of-two shift (as
 // the row preparation kernel's SHIFT mode), one wavefront per row, or for
 // few rows (wide) one workgroup per row.  The last block builds the plan and
-// zeroes the scratch words.  With y_zero (a single expert and slot, whose
-// down projection writes y itself), the row of y of a token whose id is
-// dropped (outside 0..E-1) is set to zero here, as the combine would.
+// zeroes the scratch words.
 __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_t T, int64_t H,
                                                        _Float16 *x16, int32_t *xshift,
                                                        const int32_t *offsets, int E, int bm,
                                                        int4 *mblocks, int32_t *n_mblocks, int bm2,
                                                        int4 *mblocks2, int32_t *n_mblocks2,
                                                        uint32_t *zero, int64_t zero_words,
-                                                       int wide, const int32_t *ids, void *y_zero,
-                                                       int y_f32) {
+                                                       int wide) {
   if (blockIdx.x == gridDim.x - 1) {
     for (int64_t i = threadIdx.x; i < zero_words; i += blockDim.x) zero[i] = 0u;
     build_plan(offsets, E, bm, mblocks, n_mblocks);
@@ -287,8 +284,6 @@ __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_
   const int t0 = wide ? threadIdx.x : lane;
   const int step = wide ? 256 * 8 : 512;
   const uint16_t *row = x + r * H;
-  // (loaded first: its latency then overlaps the row's)
-  const bool zero_y = y_zero && (unsigned)ids[r] >= (unsigned)E;
   float m = 0.0f;
   for (int64_t c = t0 * 8; c < H; c += step) {
     const u32x4 w = *reinterpret_cast<const u32x4 *>(row + c);
@@ -313,16 +308,6 @@ __global__ __launch_bounds__(256) void moe_prep_kernel(const uint16_t *x, int64_
       h[2 * i + 1] = (_Float16)__builtin_ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -s);
     }
     *reinterpret_cast<f16x8 *>(x16 + r * H + c) = h;
-    if (zero_y) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      if (y_f32) {
-        u32x4 *o = reinterpret_cast<u32x4 *>(static_cast<float *>(y_zero) + r * H + c);
-        o[0] = z;
-        o[1] = z;
-      } else {
-        *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(y_zero) + r * H + c) = z;
-      }
-    }
   }
   if (t0 == 0) xshift[r] = s;
 }
@@ -385,13 +370,12 @@ hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x1
                            int32_t *xshift, const int32_t *offsets, int E, int bm,
                            int4 *mblocks, int32_t *n_mblocks, int bm2, int4 *mblocks2,
                            int32_t *n_mblocks2, uint32_t *zero, int64_t zero_words,
-                           hipStream_t s, const int32_t *ids, void *y_zero, bool y_f32) {
-  if (y_zero && (!ids || H % 8 != 0)) return hipErrorInvalidValue;
+                           hipStream_t s) {
   const int wide = T <= 1024;
   const int64_t blocks = (wide ? T : (T + 3) / 4) + 1;
   launch_kernel(moe_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, T, H, x16, xshift,
                 offsets, E, bm, mblocks, n_mblocks, bm2, mblocks2, n_mblocks2, zero, zero_words,
-                wide, ids, y_zero, y_f32 ? 1 : 0);
+                wide);
   return hipGetLastError();
 }
 

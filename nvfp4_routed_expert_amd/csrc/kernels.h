@@ -64,13 +64,6 @@ hipError_t launch_row_prep(const uint16_t *x, int64_t rows, int64_t cols,
                            PrepMode mode, _Float16 *out, int32_t *shift,
                            const float *amax_src, int n_amax, const float *g_given,
                            float *g_out, float *g_out2, hipStream_t s);
-// SHIFT with each row's max |x| given as the maxima of its 256-element
-// segments (cols % 256 == 0; row r's at parts[r * cols / 256 ...], kept by
-// the producer of x): one elementwise pass, the same shifts and values as
-// SHIFT mode.
-hipError_t launch_row_shift_parts(const uint16_t *x, int64_t rows, int64_t cols,
-                                  const float *parts, _Float16 *out, int32_t *shift,
-                                  hipStream_t s);
 
 // ---- routing (route.hip, router.hip) ---------------------------------------------
 
@@ -177,9 +170,6 @@ struct GemmArgs {
   int64_t ldo;
   OutType out_type;
   uint32_t *amax_slot;            // SWIGLU: running max of |h| (float bits) or null
-  // SWIGLU, dense reduce with N % 256 == 0: the max |h| of each workgroup's
-  // 256 elements (one row's segment), or null
-  float *row_part;
   // SWIGLU, tile GEMM without a K split: when set, h is quantised to NVFP4
   // with this (given) global in the epilogue and out receives the exact fp16
   // products e2m1 * e4m3 (what the down GEMM consumes) instead of bf16 h
@@ -193,6 +183,12 @@ struct GemmArgs {
   int ksplit;
   float *partial;
   int64_t partial_rows;
+  // dense GEMV (SWIGLU / DOWN): A holds bf16 rows as given (no shift), the
+  // weights are dequantised to bf16 and multiplied by bf16 MFMA
+  bool a_bf16;
+  // dense GEMV, DOWN: rows t of out whose id drop_ids[t] lies outside
+  // 0..n_experts-1 (tokens of one slot each) are written as zeros
+  const int32_t *drop_ids;
 };
 
 hipError_t launch_gemm(Epi epi, const GemmArgs &a, int bm, hipStream_t s);
@@ -222,7 +218,7 @@ hipError_t launch_split_reduce(Epi epi, const GemmArgs &a, int rows, const int32
 // Dense GEMV for M <= 32 rows (densegemv.hip): one weight stream shared by
 // all rows (dense mode: A rows pos = 0..M-1 through a_rowmap / a_shift as in
 // the tile GEMM, expert 0), weights in 128-byte row lines through an LDS
-// ring, MFMA 16x16x32 f16.  Needs K % 256 == 0.  dense_gemv_plan picks the
+// ring, MFMA 16x16x32 f16 (or bf16 with a_bf16).  Needs K % 256 == 0.  dense_gemv_plan picks the
 // K split (partial_floats floats of workspace in GemmArgs::partial).
 bool dense_gemv_supported(int64_t M, int64_t K);
 TilePlan dense_gemv_plan(Epi epi, int64_t N, int64_t K, int64_t M);
@@ -306,14 +302,11 @@ hipError_t launch_row_down_sum(const GemmArgs &a, const int32_t *ids, int k, int
 // FFN prep for W4A16: x rows -> fp16 + shift (SHIFT), plus (one extra
 // workgroup) the m-block plan and zeroing of `zero_words` words at `zero`.
 // (mblocks2 set: also a list of bm2-row blocks, for the down projection)
-// y_zero (with ids [T], one slot per token): the rows of y of tokens whose
-// id lies outside 0..E-1 are zeroed (f32 or bf16 rows of H).
 hipError_t launch_moe_prep(const uint16_t *x, int64_t T, int64_t H, _Float16 *x16,
                            int32_t *xshift, const int32_t *offsets, int E, int bm,
                            int4 *mblocks, int32_t *n_mblocks, int bm2, int4 *mblocks2,
                            int32_t *n_mblocks2, uint32_t *zero, int64_t zero_words,
-                           hipStream_t s, const int32_t *ids = nullptr, void *y_zero = nullptr,
-                           bool y_f32 = false);
+                           hipStream_t s);
 int gemm_block_rows(int64_t rows_hint);   // M-tile (multiple of 16) for a workload
 
 // FFN plan: m-blocks from expert offsets; zeroes `zero_words` words at `zero`.

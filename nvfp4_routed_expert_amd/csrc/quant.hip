@@ -163,34 +163,6 @@ __global__ __launch_bounds__(kThreads) void row_shift_wide_kernel(const uint16_t
   if (tid == 0) shift[r] = s;
 }
 
-// SHIFT with the row maxima given as segment maxima (cols / 256 per row):
-// workgroup (r, j) folds row r's segment maxima, then converts elements
-// 2048 j .. 2048 j + 2047 of the row (8 per thread), the shift as
-// row_shift_wide_kernel takes it.
-__global__ __launch_bounds__(kThreads) void row_shift_parts_kernel(const uint16_t *x, int64_t cols,
-                                                                   int64_t wg_per_row,
-                                                                   const float *parts,
-                                                                   _Float16 *out, int32_t *shift) {
-  __shared__ float lds[4];
-  const int64_t r = blockIdx.x / wg_per_row, j = blockIdx.x - r * wg_per_row;
-  const int tid = threadIdx.x;
-  const int64_t n_parts = cols / 256;
-  float m = 0.0f;
-  for (int64_t q = tid; q < n_parts; q += kThreads) m = fmaxf(m, parts[r * n_parts + q]);
-  m = block_max(m, lds);
-  const int s = m > 0.0f ? exponent_of(m) - 15 : 0;
-  const int64_t c = j * (kThreads * 8) + tid * 8;
-  if (c < cols) {
-    float v[8];
-    load8(x + r * cols, InType::BF16, c, v);
-    f16x8 h;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) h[i] = (_Float16)__builtin_ldexpf(v[i], -s);
-    *reinterpret_cast<f16x8 *>(out + r * cols + c) = h;
-  }
-  if (j == 0 && tid == 0) shift[r] = s;
-}
-
 // One wavefront per row.
 __global__ __launch_bounds__(kThreads) void row_prep_kernel(
     const uint16_t *x, int64_t rows, int64_t cols, PrepMode mode, _Float16 *out,
@@ -306,17 +278,6 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *scales, const 
                              int64_t rows, int64_t cols, float *out, hipStream_t s) {
   launch_kernel(dequantize_kernel, dim3(grid_for(rows * (cols / 8), kThreads)),
                      dim3(kThreads), 0, s, codes, scales, g, rows, cols, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_row_shift_parts(const uint16_t *x, int64_t rows, int64_t cols,
-                                  const float *parts, _Float16 *out, int32_t *shift,
-                                  hipStream_t s) {
-  if (cols % 256 != 0) return hipErrorInvalidValue;
-  if (rows == 0) return hipSuccess;
-  const int64_t wpr = (cols + kThreads * 8 - 1) / (kThreads * 8);
-  launch_kernel(row_shift_parts_kernel, dim3((unsigned)(rows * wpr)), dim3(kThreads), 0, s, x,
-                cols, wpr, parts, out, shift);
   return hipGetLastError();
 }
 
