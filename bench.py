@@ -558,9 +558,11 @@ def measure(args, name, gumbel=False, steps=200, warmup=20):
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": steps, "warmup": warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        # the decode row kernels multiply bf16 weights by bf16 activations
-        # (fp32 sums); the MFMA kernels multiply fp16 operands
-        "dtype": "bf16" if kname.startswith("row_") else "f16", "data": "synthetic",
+        # the decode row kernels and the dense MLP's GEMV multiply bf16 weights
+        # by bf16 activations (fp32 sums); the other MFMA kernels fp16 operands
+        "dtype": "bf16" if kname.startswith("row_") or (kname == "dense_gemv_kernel"
+                                                        and wl.act == "w4a16") else "f16",
+        "data": "synthetic",
         "config": {"workload": wname, "tokens": T, "hidden": H, "intermediate": I,
                    "experts": E, "top_k": k, "act": wl.act,
                    "router_logits": ("N(0,1)" if not gumbel else "Gumbel") +
