@@ -957,8 +957,10 @@ def oracle_leg(args, wl, gumbel, x, x_cpu, logits_np, ids, wts, off, pairs, w0, 
         logits_np = O.router_logits(xf, router_w.float().cpu().numpy(),
                                     None if router_b is None else router_b.cpu().numpy())
     rids, rw = O.route_topk(logits_np, k)
-    n_tok = args.cpu_tokens or {"moe_decode": T, "moe_prefill": 8,
-                                "moe_prefill_w4a4": 2}.get(wl.name, min(T, 4))
+    # (bounded samples: the oracle then runs for a few seconds per workload;
+    # the gate checks the same tokens)
+    n_tok = args.cpu_tokens or {"moe_decode": T, "moe_prefill": 128,
+                                "moe_prefill_w4a4": 4}.get(wl.name, min(T, 4))
     tokens = list(range(T)) if n_tok >= T else spread_tokens(rids, n_tok)
     need = np.unique(rids[tokens])
     w_ref = LazyOracleExperts(E, H, I, need, 0, 16)        # weight quantisation is offline
