@@ -743,7 +743,7 @@ __global__ __launch_bounds__(kCombineThreads) void ffn_combine_kernel(
 // flight, dot products with x held in registers, one cross-lane sum per
 // row, and lane 0 writes SiLU * up rounded to bf16.  Sixteen waves per
 // workgroup (one workgroup per CU) keep enough loads in flight.  The down
-// projection then streams whole rows of K = I in the row GEMV.
+// projection then streams whole rows of K = I (row_mlp_down_kernel below).
 // (Carrying each workgroup's h slice on into the matching columns of every
 // down row, as the fused routed kernel does, was measured: with slices of
 // 64-80 columns each down row gives a workgroup 32-40 bytes, and that
