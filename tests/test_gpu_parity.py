@@ -930,6 +930,28 @@ def test_dense_gemv_mlp_writes_y_with_dropped_rows():
                        "dense gemv kept rows (bf16)")
 
 
+@pytest.mark.parametrize("T,H,I", [(3, 256, 256), (16, 1024, 768), (17, 512, 2304),
+                                   (32, 2048, 512), (5, 768, 1280)])
+def test_dense_mlp_bf16_gemv_shapes(T, H, I):
+    """A dense MLP of 3 to 32 rows on the bf16 GEMV (x and h as given, the
+    weights dequantised to bf16): one and two 16-row subtiles (17 rows: a
+    second subtile with one row), one-chunk K (256) and K splits over
+    several owners per tile; fp32 output against the oracle's dense MLP and
+    bf16 output as its rounding."""
+    import bench
+    assert bench.gate_up_kernel(T, H, I, 1, 1, "w4a16") == "dense_gemv_kernel"
+    say("dense mlp bf16 gemv", T, H, I)
+    x, rids, rw, y, _, w_ref, st = _moe_run(T, H, I, 1, 1, seed=T + H)
+    ref = O.dense_mlp(x.float().numpy(), (w_ref.gate_codes[0], w_ref.gate_scales[0], w_ref.gate_global[0]),
+                      (w_ref.up_codes[0], w_ref.up_scales[0], w_ref.up_global[0]),
+                      (w_ref.down_codes[0], w_ref.down_scales[0], w_ref.down_global[0]))
+    assert_close_f32(to_np(y), ref, "dense mlp bf16 gemv")
+    ids, wts, off, pairs, w_gpu = st
+    yb, _ = native.moe_grouped_nvfp4_ffn(x.to(DEV), w_gpu, ids, wts, off, pairs, 1,
+                                         out_dtype=torch.bfloat16)
+    assert_bf16_output(to_np(yb.float()), to_np(y), ref, "dense mlp bf16 gemv (bf16)")
+
+
 @pytest.mark.parametrize("M", [1, 8, 32])
 def test_dense_mlp_decode_full_size(M):
     """The dense NVFP4 MLP decode at full size, every row."""
