@@ -33,7 +33,9 @@ def _inputs(T, H, I, E, k, seed, zipf=None):
 def test_static_scratch_ffn_equals_workspace_ffn(act):
     L = native.lib()
     cases = [(512, 2048, 512, 512, 8, 1.1),   # the 512-token chunk: tile path, large scratch
-             (16, 2048, 512, 512, 8, None)]   # then decode: a smaller call on the same array
+             (16, 2048, 512, 512, 8, None),   # then decode: a smaller call on the same array
+             (8, 1024, 768, 1, 1, None),      # a dense MLP of 8 rows (bf16 GEMV, split K)
+             (1, 1024, 2048, 1, 1, None)]     # and of one row (the one-row kernels)
     if act == native.W4A4:
         cases = [(512, 1024, 512, 64, 4, None), (24, 512, 256, 16, 2, None)]
     for T, H, I, E, k, zipf in cases:
