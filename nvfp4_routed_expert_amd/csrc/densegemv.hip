@@ -326,92 +326,110 @@ __global__ __launch_bounds__(64 * kDWaves, MS == 1 ? 2 : 1) void dense_gemv_kern
 // host checks that units * grid fits): 64-bit divisions before every load
 // serialised a tile's dozen round trips.
 constexpr int kReduceBatch = 16;
+// Lanes per output element: the gate/up tiles have two or three owners, the
+// down and linear tiles a dozen or more (K is long), whose loads four lanes
+// of a quad share (owners q, q + 4, ... in order per lane, then the quad's
+// four sums added by two DPP exchanges: a fixed order, the same in each lane).
+template <Epi EPI>
+constexpr int reduce_lanes() { return EPI == Epi::SWIGLU ? 1 : 4; }
 template <Epi EPI, bool U32>
 __global__ __launch_bounds__(256) void dense_reduce_kernel(const GemmArgs p, int M,
                                                            const StreamSplit sk,
                                                            const float *partial) {
   constexpr int kCols = dense_cols<EPI>();
+  constexpr int Q = reduce_lanes<EPI>();
   const int N = p.N;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tidx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = tidx / Q;
+  const int q = (int)(tidx - idx * Q);
+  const bool in = idx < (int64_t)M * N;
   float amax = 0.0f;
-  if (idx < (int64_t)M * N) {
-    const int m = (int)(idx / N), n = (int)(idx - (int64_t)m * N);
-    if constexpr (EPI == Epi::DOWN) {
-      // row m of out as a token's row: zeros for a dropped token (no kept
-      // position writes that row)
-      if (p.drop_ids && (unsigned)p.drop_ids[m] >= (unsigned)p.n_experts) {
-        if (p.out_type == OutType::F32)
-          static_cast<float *>(p.out)[(int64_t)m * p.ldo + n] = 0.0f;
-        else
-          static_cast<uint16_t *>(p.out)[(int64_t)m * p.ldo + n] = 0;
+  const int m = in ? (int)(idx / N) : 0, n = in ? (int)(idx - (int64_t)m * N) : 0;
+  if constexpr (EPI == Epi::DOWN) {
+    // row m of out as a token's row: zeros for a dropped token (no kept
+    // position writes that row)
+    if (in && q == 0 && p.drop_ids && (unsigned)p.drop_ids[m] >= (unsigned)p.n_experts) {
+      if (p.out_type == OutType::F32)
+        static_cast<float *>(p.out)[(int64_t)m * p.ldo + n] = 0.0f;
+      else
+        static_cast<uint16_t *>(p.out)[(int64_t)m * p.ldo + n] = 0;
+    }
+  }
+  const int t = n / kCols, cl = n - t * kCols;
+  const int pr = p.a_rowmap ? p.a_rowmap[m] : m;
+  const bool valid = in && pr >= 0;   // (a dropped pair: no h row, no output)
+  float s0 = 0.0f, s1 = 0.0f;
+  if (valid) {
+    const uint32_t units32 = (uint32_t)sk.units, grid32 = (uint32_t)sk.grid;
+    const uint32_t nch32 = (uint32_t)sk.nch;
+    auto owner = [&](int64_t u) -> int64_t {
+      if constexpr (U32)
+        return (int64_t)(((uint32_t)u + 1u) * grid32 + units32 - 1u) / units32 - 1;
+      else
+        return unit_owner(sk, u);
+    };
+    auto first_tile = [&](int64_t g) -> int {   // tile of workgroup g's first unit
+      if constexpr (U32)
+        return (int)((uint32_t)g * units32 / grid32 / nch32);
+      else
+        return (int)(unit_first(sk, g) / sk.nch);
+    };
+    const int64_t g_lo = owner((int64_t)t * sk.nch) + q;   // this lane's first owner
+    const int64_t g_hi = owner((int64_t)t * sk.nch + sk.nch - 1);
+    for (int64_t g0 = g_lo; g0 <= g_hi; g0 += (int64_t)kReduceBatch * Q) {
+      float v0[kReduceBatch], v1[kReduceBatch];
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u) {
+        const int64_t gu = g0 + (int64_t)u * Q;
+        const int64_t g = gu <= g_hi ? gu : g0;   // (past the end: reread, unused)
+        const int slot = t - first_tile(g);
+        const float *part = partial + (g * sk.slots + slot) * 32 * kDPartCols + m * kDPartCols;
+        v0[u] = part[cl];
+        v1[u] = EPI == Epi::SWIGLU ? part[64 + cl] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kReduceBatch; ++u) {
+        if (g0 + (int64_t)u * Q > g_hi) break;
+        if (g0 + u == g_lo) {
+          s0 = v0[u];
+          s1 = v1[u];
+        } else {
+          s0 += v0[u];
+          if constexpr (EPI == Epi::SWIGLU) s1 += v1[u];
+        }
       }
     }
-    const int t = n / kCols, cl = n - t * kCols;
-    const int pr = p.a_rowmap ? p.a_rowmap[m] : m;
-    if (pr >= 0) {   // (a dropped pair: no h row, no output)
-      const uint32_t units32 = (uint32_t)sk.units, grid32 = (uint32_t)sk.grid;
-      const uint32_t nch32 = (uint32_t)sk.nch;
-      auto owner = [&](int64_t u) -> int64_t {
-        if constexpr (U32)
-          return (int64_t)(((uint32_t)u + 1u) * grid32 + units32 - 1u) / units32 - 1;
-        else
-          return unit_owner(sk, u);
-      };
-      auto first_tile = [&](int64_t g) -> int {   // tile of workgroup g's first unit
-        if constexpr (U32)
-          return (int)((uint32_t)g * units32 / grid32 / nch32);
-        else
-          return (int)(unit_first(sk, g) / sk.nch);
-      };
-      const int64_t g_lo = owner((int64_t)t * sk.nch);
-      const int64_t g_hi = owner((int64_t)t * sk.nch + sk.nch - 1);
-      float s0 = 0.0f, s1 = 0.0f;
-      for (int64_t g0 = g_lo; g0 <= g_hi; g0 += kReduceBatch) {
-        float v0[kReduceBatch], v1[kReduceBatch];
-#pragma unroll
-        for (int q = 0; q < kReduceBatch; ++q) {
-          const int64_t g = g0 + q <= g_hi ? g0 + q : g_hi;   // (past the end: reread, unused)
-          const int slot = t - first_tile(g);
-          const float *part = partial + (g * sk.slots + slot) * 32 * kDPartCols + m * kDPartCols;
-          v0[q] = part[cl];
-          v1[q] = EPI == Epi::SWIGLU ? part[64 + cl] : 0.0f;
-        }
-#pragma unroll
-        for (int q = 0; q < kReduceBatch; ++q) {
-          if (g0 + q > g_hi) break;
-          if (g0 + q == g_lo) {
-            s0 = v0[q];
-            s1 = v1[q];
-          } else {
-            s0 += v0[q];
-            if constexpr (EPI == Epi::SWIGLU) s1 += v1[q];
-          }
-        }
+  }
+  if constexpr (Q == 4) {   // every lane (no divergence around the exchanges)
+    s0 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                        0, __builtin_bit_cast(int, s0), 0xB1, 0xF, 0xF, false));
+    s0 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                        0, __builtin_bit_cast(int, s0), 0x4E, 0xF, 0xF, false));
+  }
+  if (valid && q == 0) {
+    const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
+    const int arow = p.a_rowmap ? pr / p.a_rowdiv : pr;
+    const int sh = p.a_shift ? p.a_shift[arow] : 0;
+    if constexpr (EPI == Epi::SWIGLU) {
+      const float G = __builtin_ldexpf(s0, sh) * (p.b_global[0][0] * extra);
+      const float U = __builtin_ldexpf(s1, sh) * (p.b_global[1][0] * extra);
+      const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
+      static_cast<uint16_t *>(p.out)[(int64_t)m * p.ldo + n] = (uint16_t)hb;
+      amax = __builtin_fabsf(bf16_bits_to_f32(hb));
+    } else {
+      float v = __builtin_ldexpf(s0, sh) * (p.b_global[0][0] * extra);
+      int64_t orow = m;
+      bool ok = true;
+      if constexpr (EPI == Epi::DOWN) {
+        orow = p.sorted_pairs ? p.sorted_pairs[m] : m;
+        ok = orow >= 0;
+        if (ok) v *= p.pair_weights[orow];
       }
-      const float extra = p.extra_scale ? *p.extra_scale : 1.0f;
-      const int arow = p.a_rowmap ? pr / p.a_rowdiv : pr;
-      const int sh = p.a_shift ? p.a_shift[arow] : 0;
-      if constexpr (EPI == Epi::SWIGLU) {
-        const float G = __builtin_ldexpf(s0, sh) * (p.b_global[0][0] * extra);
-        const float U = __builtin_ldexpf(s1, sh) * (p.b_global[1][0] * extra);
-        const uint32_t hb = f32_to_bf16_bits(G / (1.0f + expf(-G)) * U);
-        static_cast<uint16_t *>(p.out)[(int64_t)m * p.ldo + n] = (uint16_t)hb;
-        amax = __builtin_fabsf(bf16_bits_to_f32(hb));
-      } else {
-        float v = __builtin_ldexpf(s0, sh) * (p.b_global[0][0] * extra);
-        int64_t orow = m;
-        bool ok = true;
-        if constexpr (EPI == Epi::DOWN) {
-          orow = p.sorted_pairs ? p.sorted_pairs[m] : m;
-          ok = orow >= 0;
-          if (ok) v *= p.pair_weights[orow];
-        }
-        if (ok) {
-          if (p.out_type == OutType::F32)
-            static_cast<float *>(p.out)[orow * p.ldo + n] = v;
-          else
-            static_cast<uint16_t *>(p.out)[orow * p.ldo + n] = (uint16_t)f32_to_bf16_bits(v);
-        }
+      if (ok) {
+        if (p.out_type == OutType::F32)
+          static_cast<float *>(p.out)[orow * p.ldo + n] = v;
+        else
+          static_cast<uint16_t *>(p.out)[orow * p.ldo + n] = (uint16_t)f32_to_bf16_bits(v);
       }
     }
   }
@@ -487,12 +505,14 @@ hipError_t launch_dense_gemv(Epi epi, const GemmArgs &a, int M, const TilePlan &
     return hipErrorInvalidValue;
   hipError_t e = M <= 16 ? launch_ms<1>(epi, a, M, sk, s) : launch_ms<2>(epi, a, M, sk, s);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)(((int64_t)M * a.N + 255) / 256)), block(256);
+  const dim3 block(256);
   const bool u32 = (uint64_t)(sk.units + 1) * (uint64_t)sk.grid + (uint64_t)sk.units <
                    ((uint64_t)1 << 32);
   auto reduce = [&](auto epi_c, auto u32_c) {
-    launch_kernel((dense_reduce_kernel<decltype(epi_c)::value, decltype(u32_c)::value>), grid,
-                  block, 0, s, a, M, sk, (const float *)a.partial);
+    constexpr Epi E = decltype(epi_c)::value;
+    const dim3 grid((unsigned)(((int64_t)M * a.N * reduce_lanes<E>() + 255) / 256));
+    launch_kernel((dense_reduce_kernel<E, decltype(u32_c)::value>), grid, block, 0, s, a, M, sk,
+                  (const float *)a.partial);
   };
   auto with_u32 = [&](auto epi_c) {
     if (u32)
