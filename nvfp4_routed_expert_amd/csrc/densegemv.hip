@@ -51,10 +51,10 @@ constexpr int kDCUs = 256;
 
 template <int MS>
 struct DenseCfg {
-  // two workgroups share a CU: three stages with one 16-row subtile, two
-  // with two (34 KB stages)
-  static constexpr int STAGES = MS == 1 ? 3 : 2;
-  static constexpr int PER_CU = 2;
+  // two-stage rings: three workgroups with one 16-row subtile (26 KB
+  // stages) or two with two (34 KB stages) share a CU
+  static constexpr int STAGES = 2;
+  static constexpr int PER_CU = MS == 1 ? 3 : 2;
   static constexpr int MP = 16 * MS;                        // activation rows staged
   static constexpr int B_BYTES = kDRows * kDCodeRow;        // 16 KB
   static constexpr int S_BYTES = kDRows * kDScaleRow;       // 2 KB
@@ -113,7 +113,7 @@ __device__ __forceinline__ bf16x8 dequant8_bf16(uint32_t word, float s) {
 // its operand rows converted to fp16 with a power-of-two row shift by
 // passes of their own.
 template <int MS, Epi EPI, bool BF>
-__global__ __launch_bounds__(64 * kDWaves, 2) void dense_gemv_kernel(
+__global__ __launch_bounds__(64 * kDWaves, MS == 1 ? 3 : 2) void dense_gemv_kernel(
     const GemmArgs p, int M, const StreamSplit sk, float *partial) {
   using C = DenseCfg<MS>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::STAGES * C::STAGE];
